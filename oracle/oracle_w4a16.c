@@ -1,0 +1,356 @@
+/*
+ * oracle_w4a16.c -- plain, slow, obviously correct fp64 CPU oracle for the
+ * batch-1 W4A16 GEMV (4-bit weights, one fp16 scale and one 4-bit zero point
+ * per group of 128 consecutive weights along K, fp16 activations).
+ *
+ * TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's
+ * cpu_baseline leg may load this library. It shares no source, header, table
+ * or helper with the HIP library; the two meet only through the seeded input
+ * generators (synthetic.py), which hold none of the method's arithmetic.
+ *
+ * What is computed, and from which passage:
+ *  - w[n][k] = (q[n][k] - z[n][g]) * s[n][g], g = floor(k/128): one fp16
+ *    scale per group of 128 weights of one output row ("Building an LLM
+ *    Inference Runtime ... Qwen2.5-Coder-7B on NVIDIA H100", section "The
+ *    Stack Architecture"; "CodeAlign-Runtime", Level 3, "Quantization
+ *    Scheme"), with the unsigned-q / 4-bit-zero-point form of the workload
+ *    definition. The signed symmetric form of those pages is the special
+ *    case q = t xor 8, z = 8.
+ *  - y[m][n] = sum_k w[n][k] * x[m][k]: the row-major matrix-vector product
+ *    of "CodeAlign-Runtime", Level 1 (one output per row of an N x K matrix),
+ *    done in one pass without materialising W (Level 3).
+ *  - The sum runs over k in ascending order in fp64; absref = sum_k |w*x|.
+ *  - fp16 values are decoded and encoded (round to nearest, ties to even)
+ *    from the IEEE-754 binary16 definition, written out below.
+ *
+ * The packed layout (ID 1) is this project's own device layout; pack/unpack
+ * here follow its written definition element by element. The nibble order
+ * inside a 32-bit word is the interleave of "Building an LLM Inference
+ * Runtime", Bug #3 (the ValueShuffle shift table), which is also the
+ * interleaved order of "Custom AWQ Dequantization Kernel", Part 2.
+ *
+ * Layout ID 1, for an N x K matrix (K a multiple of 128, G = K/128):
+ *   NP = N rounded up to 16, GP = G rounded up to 8, rows n >= N are zero.
+ *   weights: NP/16 * G tiles of 1024 bytes; tile (t, g) starts at byte
+ *     (t*G + g)*1024. Its 32-bit little-endian word (lane, kb), lane in
+ *     [0,64), kb in [0,4), sits at byte lane*16 + kb*4 of the tile and holds
+ *     row 16t + lane%16, columns k = 128g + 32kb + 8*(lane/16) + j, j in
+ *     [0,8); weight j occupies bits 4*SLOT[j] .. 4*SLOT[j]+3,
+ *     SLOT = {0,4,1,5,2,6,3,7}.
+ *   scales: fp16 bits, element n*GP + g; padding elements are 0.
+ *   zeros:  4-bit values, row n group g in byte n*GP/2 + g/2, low nibble for
+ *     even g, high nibble for odd g; padding nibbles are 0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_GROUP 128
+
+/* Deliberate mistakes, compiled in only by the planted-mistake test to show
+ * that the pins catch them. The default build plants nothing. */
+#ifndef OR_PLANT
+#define OR_PLANT 0
+#endif
+
+int or_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+int or_plant(void) { return OR_PLANT; }
+
+/* ---------------------------------------------------------------- fp16 --- */
+
+/* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits. Exponent field 0: subnormal, value = f * 2^-24. Field 31: inf/NaN.
+ * Otherwise value = (1024 + f) * 2^(e - 25). */
+double or_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int f = h & 1023;
+  double v;
+  if (e == 0)
+#if OR_PLANT == 7
+    v = ldexp((double)(1024 + f), -25); /* planted: hidden bit on subnormals */
+#else
+    v = ldexp((double)f, -24);
+#endif
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16, ties to even. */
+uint16_t or_f64_to_f16(double v) {
+  if (isnan(v)) return 0x7E00;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isinf(a)) return sign | 0x7C00;
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);           /* a = f * 2^e, f in [0.5, 1) : a in [2^(e-1), 2^e) */
+  int ulp = e - 11;       /* spacing of binary16 numbers in that binade */
+  if (ulp < -24) ulp = -24; /* subnormal spacing */
+#if OR_PLANT == 6
+  double r = floor(ldexp(a, -ulp)); /* planted: truncation instead of rounding */
+#else
+  double r = rint(ldexp(a, -ulp)); /* exact scaling, then ties-to-even */
+#endif
+  if (r >= 2048.0) {      /* rounded up into the next binade */
+    r /= 2.0;
+    ulp += 1;
+  }
+  if (ulp == -24 && r <= 1024.0) /* subnormal, or exactly the smallest normal */
+    return sign | (uint16_t)r;
+  int field = ulp + 25;   /* value = (1024 + frac) * 2^(field - 25) */
+  if (field >= 31) return sign | 0x7C00;
+  return sign | (uint16_t)(field << 10) | (uint16_t)((int)r - 1024);
+}
+
+void or_f16_to_f64_array(const uint16_t* h, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = or_f16_to_f64(h[i]);
+}
+
+void or_f64_to_f16_array(const double* v, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = or_f64_to_f16(v[i]);
+}
+
+/* ------------------------------------------------------ layout ID 1 --- */
+
+static const int SLOT[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+
+static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+static int shape_ok(int64_t N, int64_t K) {
+  return N >= 0 && K >= OR_GROUP && K % OR_GROUP == 0;
+}
+
+int or_layout_id(void) { return 1; }
+
+/* out[0] = weight bytes, out[1] = scale bytes, out[2] = zero bytes */
+int or_layout_sizes(int64_t N, int64_t K, int64_t* out) {
+  if (!shape_ok(N, K)) return -1;
+  int64_t NP = round_up(N, 16), G = K / OR_GROUP, GP = round_up(G, 8);
+  out[0] = NP * K / 2;
+  out[1] = NP * GP * 2;
+  out[2] = NP * GP / 2;
+  return 0;
+}
+
+/* Where weight (n, k) lives: byte offset of its 32-bit word, and bit shift. */
+static void locate_weight(int64_t n, int64_t k, int64_t G, int64_t* word_byte, int* shift) {
+  int64_t t = n / 16, i = n % 16, g = k / OR_GROUP, r = k % OR_GROUP;
+  int64_t kb = r / 32, lane_group = (r % 32) / 8, j = r % 8;
+  int64_t lane = i + 16 * lane_group;
+#if OR_PLANT == 5
+  j = 7 - j; /* planted: nibble order reversed */
+#endif
+  *word_byte = (t * G + g) * 1024 + lane * 16 + kb * 4;
+  *shift = 4 * SLOT[j];
+}
+
+static uint32_t read_u32le(const uint8_t* p) {
+  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+static void write_u32le(uint8_t* p, uint32_t v) {
+  p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); p[2] = (uint8_t)(v >> 16); p[3] = (uint8_t)(v >> 24);
+}
+
+static int weight_at(const uint8_t* wq, int64_t n, int64_t k, int64_t G) {
+  int64_t wb; int sh;
+  locate_weight(n, k, G, &wb, &sh);
+  return (int)((read_u32le(wq + wb) >> sh) & 15u);
+}
+
+static uint16_t scale_at(const uint8_t* sp, int64_t n, int64_t g, int64_t GP) {
+  const uint8_t* p = sp + 2 * (n * GP + g);
+  return (uint16_t)(p[0] | (p[1] << 8));
+}
+
+static int zero_at(const uint8_t* zp, int64_t n, int64_t g, int64_t GP) {
+  uint8_t b = zp[n * GP / 2 + g / 2];
+  return (g & 1) ? (b >> 4) : (b & 15);
+}
+
+/* q: [N][K] values 0..15; s: [N][G] fp16 bits; z: [N][G] values 0..15.
+ * Outputs are overwritten entirely (padding included). */
+int or_pack(int64_t N, int64_t K, const uint8_t* q, const uint16_t* s, const uint8_t* z,
+            uint8_t* wq, uint8_t* sp, uint8_t* zp) {
+  int64_t sz[3];
+  if (or_layout_sizes(N, K, sz)) return -1;
+  int64_t G = K / OR_GROUP, GP = round_up(G, 8);
+  memset(wq, 0, (size_t)sz[0]);
+  memset(sp, 0, (size_t)sz[1]);
+  memset(zp, 0, (size_t)sz[2]);
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t k = 0; k < K; k++) {
+      uint8_t v = q[n * K + k];
+      if (v > 15) return -1;
+      int64_t wb; int sh;
+      locate_weight(n, k, G, &wb, &sh);
+      write_u32le(wq + wb, read_u32le(wq + wb) | ((uint32_t)v << sh));
+    }
+    for (int64_t g = 0; g < G; g++) {
+      uint16_t sv = s[n * G + g];
+      sp[2 * (n * GP + g)] = (uint8_t)(sv & 0xFF);
+      sp[2 * (n * GP + g) + 1] = (uint8_t)(sv >> 8);
+      uint8_t zv = z[n * G + g];
+      if (zv > 15) return -1;
+      zp[n * GP / 2 + g / 2] |= (uint8_t)((g & 1) ? (zv << 4) : zv);
+    }
+  }
+  return 0;
+}
+
+int or_unpack(int64_t N, int64_t K, const uint8_t* wq, const uint8_t* sp, const uint8_t* zp,
+              uint8_t* q, uint16_t* s, uint8_t* z) {
+  if (!shape_ok(N, K)) return -1;
+  int64_t G = K / OR_GROUP, GP = round_up(G, 8);
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t k = 0; k < K; k++) q[n * K + k] = (uint8_t)weight_at(wq, n, k, G);
+    for (int64_t g = 0; g < G; g++) {
+      s[n * G + g] = scale_at(sp, n, g, GP);
+      z[n * G + g] = (uint8_t)zero_at(zp, n, g, GP);
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------ arithmetic --- */
+
+/* The dequantized weight, exact in fp64 (|q - z| <= 15 has 4 bits, s has an
+ * 11-bit significand). */
+static double dequant_one(int q, int z, uint16_t s_bits) {
+#if OR_PLANT == 1
+  (void)z;
+  return (double)q * or_f16_to_f64(s_bits); /* planted: zero point dropped */
+#elif OR_PLANT == 2
+  return (double)(z - q) * or_f16_to_f64(s_bits); /* planted: sign flipped */
+#else
+  return (double)(q - z) * or_f16_to_f64(s_bits);
+#endif
+}
+
+static int64_t group_of(int64_t k) {
+#if OR_PLANT == 3
+  return k / OR_GROUP / 2; /* planted: neighbouring groups share a scale */
+#else
+  return k / OR_GROUP;
+#endif
+}
+
+/* w: [N][K] doubles */
+int or_dequant(int64_t N, int64_t K, const uint8_t* q, const uint16_t* s, const uint8_t* z, double* w) {
+  if (!shape_ok(N, K)) return -1;
+  int64_t G = K / OR_GROUP;
+  for (int64_t n = 0; n < N; n++)
+    for (int64_t k = 0; k < K; k++) {
+      int64_t g = group_of(k);
+      w[n * K + k] = dequant_one(q[n * K + k], z[n * G + g], s[n * G + g]);
+    }
+  return 0;
+}
+
+/* ref, absref: [M][N] doubles; x: [M][K] fp16 bits. */
+int or_gemv(int64_t M, int64_t N, int64_t K, const uint8_t* q, const uint16_t* s, const uint8_t* z,
+            const uint16_t* x, double* ref, double* absref) {
+  if (M < 0 || !shape_ok(N, K)) return -1;
+  if (M == 0 || N == 0) return 0;
+  int64_t G = K / OR_GROUP;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  if (!xd) return -2;
+  for (int64_t i = 0; i < M * K; i++) xd[i] = or_f16_to_f64(x[i]);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t m = 0; m < M; m++) {
+      double acc = 0.0, aacc = 0.0;
+      for (int64_t k = 0; k < K; k++) {
+        int64_t g = group_of(k);
+        double w = dequant_one(q[n * K + k], z[n * G + g], s[n * G + g]);
+#if OR_PLANT == 4
+        double xv = xd[k * M + m]; /* planted: activations read as [K][M] */
+#else
+        double xv = xd[m * K + k];
+#endif
+        acc += w * xv;
+        aacc += fabs(w * xv);
+      }
+      ref[m * N + n] = acc;
+      absref[m * N + n] = aacc;
+    }
+  }
+  free(xd);
+  return 0;
+}
+
+/* Same product with the weights given in layout ID 1: every element is
+ * located through the layout definition, then the same formula applies. */
+int or_gemv_packed(int64_t M, int64_t N, int64_t K, const uint8_t* wq, const uint8_t* sp,
+                   const uint8_t* zp, const uint16_t* x, double* ref, double* absref) {
+  if (M < 0 || !shape_ok(N, K)) return -1;
+  if (M == 0 || N == 0) return 0;
+  int64_t G = K / OR_GROUP, GP = round_up(G, 8);
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+  if (!xd) return -2;
+  for (int64_t i = 0; i < M * K; i++) xd[i] = or_f16_to_f64(x[i]);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t m = 0; m < M; m++) {
+      double acc = 0.0, aacc = 0.0;
+      for (int64_t k = 0; k < K; k++) {
+        int64_t g = group_of(k);
+        double w = dequant_one(weight_at(wq, n, k, G), zero_at(zp, n, g, GP), scale_at(sp, n, g, GP));
+        double xv = xd[m * K + k];
+        acc += w * xv;
+        aacc += fabs(w * xv);
+      }
+      ref[m * N + n] = acc;
+      absref[m * N + n] = aacc;
+    }
+  }
+  free(xd);
+  return 0;
+}
+
+/* Rows listed in `rows` only (for sampled checks at full size):
+ * ref/absref are [M][nrows]. */
+int or_gemv_packed_rows(int64_t M, int64_t N, int64_t K, const uint8_t* wq, const uint8_t* sp,
+                        const uint8_t* zp, const uint16_t* x, const int64_t* rows, int64_t nrows,
+                        double* ref, double* absref) {
+  if (M < 0 || !shape_ok(N, K)) return -1;
+  int64_t G = K / OR_GROUP, GP = round_up(G, 8);
+  for (int64_t r = 0; r < nrows; r++)
+    if (rows[r] < 0 || rows[r] >= N) return -1;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K + 1));
+  if (!xd) return -2;
+  for (int64_t i = 0; i < M * K; i++) xd[i] = or_f16_to_f64(x[i]);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t n = rows[r];
+    for (int64_t m = 0; m < M; m++) {
+      double acc = 0.0, aacc = 0.0;
+      for (int64_t k = 0; k < K; k++) {
+        int64_t g = group_of(k);
+        double w = dequant_one(weight_at(wq, n, k, G), zero_at(zp, n, g, GP), scale_at(sp, n, g, GP));
+        double xv = xd[m * K + k];
+        acc += w * xv;
+        aacc += fabs(w * xv);
+      }
+      ref[m * nrows + r] = acc;
+      absref[m * nrows + r] = aacc;
+    }
+  }
+  free(xd);
+  return 0;
+}

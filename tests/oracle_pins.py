@@ -1,0 +1,322 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Each pin is a function taking an ``oracle.Oracle`` and raising AssertionError
+when the oracle disagrees with the pages, with closed forms, with exact
+rational arithmetic or with an independent library routine (numpy's binary16
+conversions, numpy's float64 matmul). They are collected by
+test_oracle_pins.py, and test_planted_mistakes.py runs them against oracle
+builds with one deliberate mistake each to show that every mistake is caught.
+"""
+import bisect
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+GROUP = 128
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f16_bits(v):
+    return np.array(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+# ---------------------------------------------------------------- fp16 codec
+
+def pin_f16_decode_exhaustive(o):
+    """All 65,536 binary16 patterns decode as numpy's float16 does."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.f16_to_f64(bits)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def _f16_finite_positive():
+    bits = np.arange(0, 0x7C00, dtype=np.uint16)
+    return bits, bits.view(np.float16).astype(np.float64)
+
+
+def pin_f16_encode_rne(o):
+    """Rounding to binary16 (ties to even) agrees with numpy on every finite
+    value, every midpoint, both neighbours of every midpoint, overflow edges
+    and random doubles over the whole range."""
+    bits, vals = _f16_finite_positive()
+    assert np.array_equal(o.f64_to_f16(vals), bits)
+    assert np.array_equal(o.f64_to_f16(-vals), bits | 0x8000)
+    mids = (vals[:-1] + vals[1:]) / 2.0          # exact in float64
+    probes = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf)])
+    probes = np.concatenate([probes, -probes])
+    edge = np.array([65504.0, 65519.999, 65520.0, 65536.0, 1e300, 2.0 ** -25,
+                     3 * 2.0 ** -26, 2.0 ** -26, 2.0 ** -14 - 2.0 ** -25, 1e-300])
+    rng = np.random.default_rng(7)
+    rnd = np.exp(rng.uniform(np.log(1e-9), np.log(7e4), 200000)) * rng.choice([-1.0, 1.0], 200000)
+    for arr in (probes, edge, -edge, rnd):
+        want = arr.astype(np.float16).view(np.uint16)
+        got = o.f64_to_f16(arr)
+        assert np.array_equal(got, want), np.flatnonzero(got != want)[:5]
+    assert o.f64_to_f16(np.array([np.nan]))[0] & 0x7C00 == 0x7C00
+    assert o.f64_to_f16(np.array([np.nan]))[0] & 0x03FF != 0
+
+
+# ------------------------------------------------------------------ layout
+
+def pin_layout_worked_word(o):
+    """The nibble interleave reproduces the ValueShuffle word of the H100
+    runtime page (and is AWQ's interleaved order)."""
+    g = _load("valueshuffle_word.json")
+    assert [s // 4 for s in g["shift_of_weight"]] == g["awq_order"]
+    slots = [int(name[1:]) for name in g["slot_contents"]]
+    assert [slots.index(j) for j in range(8)] == g["awq_order"]
+    N, K = 1, 128
+    q = np.zeros((N, K), np.uint8)
+    q[0, :8] = g["worked_example"]["weights"]
+    s = np.zeros((N, 1), np.uint16)
+    z = np.zeros((N, 1), np.uint8)
+    wq, _, _ = o.pack(q, s, z)
+    word = int(wq[:4].view("<u4")[0])
+    assert word == int(g["worked_example"]["word_hex"], 16), hex(word)
+
+
+def pin_layout_tile_locality(o):
+    """Layout statement: tile (t, g) is 1024 bytes holding rows 16t..16t+15 and
+    columns 128g..128g+127; within it, the 16 bytes of lane l hold one row,
+    16t + l % 16. Checked by lighting one weight at a time."""
+    N, K = 37, 512
+    G = K // GROUP
+    rng = np.random.default_rng(3)
+    for _ in range(60):
+        n, k = int(rng.integers(N)), int(rng.integers(K))
+        q = np.zeros((N, K), np.uint8)
+        q[n, k] = 15
+        wq, _, _ = o.pack(q, np.zeros((N, G), np.uint16), np.zeros((N, G), np.uint8))
+        nz = np.flatnonzero(wq)
+        assert nz.size == 1
+        byte = int(nz[0])
+        tile = byte // 1024
+        assert tile == (n // 16) * G + k // GROUP
+        lane = (byte % 1024) // 16
+        assert lane % 16 == n % 16
+        kb = (byte % 16) // 4
+        assert kb == (k % GROUP) // 32
+        assert lane // 16 == (k % 32) // 8
+
+
+def pin_layout_roundtrip(o):
+    """unpack(pack(q, s, z)) == (q, s, z) bit for bit, on random data, ragged
+    N, G not a multiple of 8, and the all-0 / all-15 / walking-nibble cases."""
+    rng = np.random.default_rng(11)
+    for N, K in [(1, 128), (17, 384), (40, 1152), (16, 896), (3, 2048)]:
+        G = K // GROUP
+        cases = [
+            (rng.integers(0, 16, (N, K), dtype=np.uint8), rng.integers(0, 65536, (N, G), dtype=np.uint16),
+             rng.integers(0, 16, (N, G), dtype=np.uint8)),
+            (np.zeros((N, K), np.uint8), np.zeros((N, G), np.uint16), np.zeros((N, G), np.uint8)),
+            (np.full((N, K), 15, np.uint8), np.full((N, G), 0xFFFF, np.uint16), np.full((N, G), 15, np.uint8)),
+        ]
+        walk = np.zeros((N, K), np.uint8)
+        walk[np.arange(N)[:, None], (np.arange(N)[:, None] * 7 + np.arange(0, K, 9)[None, :]) % K] = \
+            (np.arange(N)[:, None] % 15 + 1)
+        cases.append((walk, np.arange(N * G, dtype=np.uint16).reshape(N, G),
+                      (np.arange(N * G) % 16).astype(np.uint8).reshape(N, G)))
+        for q, s, z in cases:
+            wq, sp, zp = o.pack(q, s, z)
+            q2, s2, z2 = o.unpack(N, K, wq, sp, zp)
+            assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(z, z2)
+
+
+def pin_layout_padding_zero(o):
+    """Rows past N and groups past G are zero in every buffer."""
+    N, K = 5, 640
+    G = K // GROUP
+    q = np.full((N, K), 15, np.uint8)
+    wq, sp, zp = o.pack(q, np.full((N, G), 0x3C00, np.uint16), np.full((N, G), 15, np.uint8))
+    q16, s16, z16 = o.unpack(16, K, wq, sp, zp)
+    assert not q16[N:].any() and not s16[N:].any() and not z16[N:].any()
+    assert (q16[:N] == 15).all()
+    assert int(np.unpackbits(wq).sum()) == N * K * 4
+    GP = (G + 7) // 8 * 8
+    assert not sp.view(np.uint16).reshape(16, GP)[:, G:].any()
+
+
+# ------------------------------------------------------------- arithmetic
+
+def pin_dequant_special_cases(o):
+    """s = 1, z = 0 gives w = q; q = z gives 0; the signed symmetric format of
+    the pages (two's-complement nibble t, zero point 0) stored as q = t xor 8,
+    z = 8 gives w = t * s; 128 consecutive weights share one scale."""
+    rng = np.random.default_rng(5)
+    N, K = 9, 768
+    G = K // GROUP
+    q = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    w = o.dequant(q, np.full((N, G), 0x3C00, np.uint16), np.zeros((N, G), np.uint8))
+    assert np.array_equal(w, q.astype(np.float64))
+    zz = rng.integers(0, 16, (N, G), dtype=np.uint8)
+    w = o.dequant(np.repeat(zz, GROUP, axis=1), rng.integers(0, 0x7C00, (N, G), dtype=np.uint16), zz)
+    assert not w.any()
+    nib = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    t = np.where(nib >= 8, nib.astype(np.int64) - 16, nib.astype(np.int64))  # sign extension
+    s = _f16_bits(np.abs(rng.normal(0, 0.02, (N, G))) + 1e-3)
+    w = o.dequant(nib ^ 8, s, np.full((N, G), 8, np.uint8))
+    sd = np.repeat(s.view(np.float16).astype(np.float64), GROUP, axis=1)
+    assert np.array_equal(w, t * sd)
+    pow2 = _f16_bits(2.0 ** (np.arange(G) - 3))[None, :].repeat(N, 0)
+    w = o.dequant(np.full((N, K), 9, np.uint8), pow2, np.full((N, G), 8, np.uint8))
+    assert np.array_equal(w, np.repeat(2.0 ** (np.arange(G) - 3), GROUP)[None, :].repeat(N, 0))
+
+
+def _case_inputs(c):
+    M, N, K = c["M"], c["N"], c["K"]
+    G = K // GROUP
+    q = np.full((N, K), c["q"], np.uint8)
+    for n, k, v in c.get("q_at", []):
+        q[n, k] = v
+    z = np.full((N, G), c["z"], np.uint8)
+    if "s_groups" in c:
+        s = _f16_bits(np.array(c["s_groups"]))[None, :].repeat(N, 0)
+    else:
+        s = np.full((N, G), _f16_bits(c["s"]), np.uint16)
+    if "x_rows" in c:
+        x = _f16_bits(np.array(c["x_rows"])[:, None].repeat(K, 1))
+    else:
+        x = np.full((M, K), _f16_bits(c["x"]), np.uint16)
+    for m, k, v in c.get("x_at", []):
+        x[m, k] = _f16_bits(v)
+    return q, s, z, x
+
+
+def pin_gemv_tiny_cases(o):
+    """Hand-derived closed forms (tests/golden/tiny_gemv_cases.json)."""
+    for c in _load("tiny_gemv_cases.json")["cases"]:
+        q, s, z, x = _case_inputs(c)
+        ref, absref = o.gemv(q, s, z, x)
+        assert np.array_equal(ref, np.array(c["y"])), (c["name"], ref)
+        assert np.array_equal(absref, np.array(c["absref"])), (c["name"], absref)
+        assert np.array_equal(o.f64_to_f16(ref), _f16_bits(np.array(c["y"]))), c["name"]
+
+
+def _fp16_table():
+    bits, vals = _f16_finite_positive()
+    return bits, [Fraction(float(v)) for v in vals]
+
+
+def _rne16_exact(value, table):
+    """Nearest binary16 to an exact rational, ties to even mantissa, by search."""
+    bits, fr = table
+    a = abs(value)
+    if a >= Fraction(65520):
+        b = 0x7C00
+    else:
+        i = bisect.bisect_left(fr, a)
+        if i < len(fr) and fr[i] == a:
+            b = int(bits[i])
+        else:
+            lo, hi = i - 1, i
+            dl, dh = a - fr[lo], fr[hi] - a
+            if dl < dh or (dl == dh and int(bits[lo]) % 2 == 0):
+                b = int(bits[lo])
+            else:
+                b = int(bits[hi])
+    return b | (0x8000 if value < 0 else 0)
+
+
+def pin_gemv_exact_rational(o):
+    """On small random inputs, the oracle's fp64 sum lies within its
+    accumulation bound of the exact rational sum, and its rounding of the
+    fp64 sum to fp16 equals exact rounding of the exact sum (away from ties
+    that the fp64 sum cannot resolve)."""
+    rng = np.random.default_rng(19)
+    table = _fp16_table()
+    for M, N, K in [(2, 3, 256), (1, 4, 384), (3, 2, 128)]:
+        q, s, z = synthetic.weights(N, K, seed=int(rng.integers(1 << 30)))
+        x = synthetic.activations(M, K, seed=int(rng.integers(1 << 30)))
+        ref, absref = o.gemv(q, s, z, x)
+        sf = s.view(np.float16).astype(np.float64)
+        xf = x.view(np.float16).astype(np.float64)
+        for m in range(M):
+            for n in range(N):
+                exact = Fraction(0)
+                for k in range(K):
+                    g = k // GROUP
+                    exact += (int(q[n, k]) - int(z[n, g])) * Fraction(float(sf[n, g])) * Fraction(float(xf[m, k]))
+                err = abs(Fraction(float(ref[m, n])) - exact)
+                assert err <= Fraction(K * 2.0 ** -52) * Fraction(float(absref[m, n])), (m, n)
+                want16 = _rne16_exact(exact, table)
+                got16 = int(o.f64_to_f16(np.array([ref[m, n]]))[0])
+                assert got16 == want16, (m, n, hex(got16), hex(want16))
+
+
+def pin_gemv_vs_numpy(o):
+    """The oracle's matvec equals numpy's float64 matmul of its own dequantized
+    W (a library routine) to within fp64 accumulation error; this fixes the
+    row/column roles for non-square shapes and M > 1."""
+    rng = np.random.default_rng(23)
+    for M, N, K in [(1, 48, 896), (3, 17, 1280), (8, 5, 256)]:
+        q, s, z = synthetic.weights(N, K, seed=int(rng.integers(1 << 30)))
+        x = synthetic.activations(M, K, seed=int(rng.integers(1 << 30)))
+        ref, absref = o.gemv(q, s, z, x)
+        w = o.dequant(q, s, z)
+        want = x.view(np.float16).astype(np.float64) @ w.T
+        assert np.all(np.abs(ref - want) <= 4 * K * 2.0 ** -53 * absref + 1e-300)
+        assert np.allclose(absref, np.abs(x.view(np.float16).astype(np.float64)) @ np.abs(w.T), rtol=1e-12, atol=0)
+
+
+def pin_gemv_one_hot(o):
+    """x = e_k picks column k: y[n] = w[n][k] exactly."""
+    rng = np.random.default_rng(29)
+    N, K = 21, 512
+    q, s, z = synthetic.weights(N, K, seed=4)
+    w = o.dequant(q, s, z)
+    for k in rng.integers(0, K, 12):
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = 0x3C00
+        ref, _ = o.gemv(q, s, z, x)
+        assert np.array_equal(ref[0], w[:, k])
+        sk = s[:, k // GROUP].view(np.float16).astype(np.float64)
+        assert np.array_equal(ref[0], (q[:, k].astype(np.float64) - z[:, k // GROUP]) * sk)
+
+
+def pin_gemv_invariants(o):
+    """Scaling x by 2 scales y by 2 exactly; permuting rows of W permutes y;
+    swapping activation rows swaps output rows."""
+    rng = np.random.default_rng(31)
+    M, N, K = 3, 33, 640
+    q, s, z = synthetic.weights(N, K, seed=8)
+    x = synthetic.activations(M, K, seed=9)
+    ref, absref = o.gemv(q, s, z, x)
+    x2 = _f16_bits(x.view(np.float16).astype(np.float64) * 2.0)
+    ref2, _ = o.gemv(q, s, z, x2)
+    assert np.array_equal(ref2, 2.0 * ref)
+    p = rng.permutation(N)
+    refp, _ = o.gemv(q[p], s[p], z[p], x)
+    assert np.array_equal(refp, ref[:, p])
+    refm, _ = o.gemv(q, s, z, x[::-1].copy())
+    assert np.array_equal(refm, ref[::-1])
+
+
+def pin_gemv_packed_matches_logical(o):
+    """The product computed from packed buffers equals the product from the
+    logical tensors bit for bit (full and sampled rows)."""
+    for M, N, K in [(1, 40, 896), (5, 19, 1152)]:
+        q, s, z = synthetic.weights(N, K, seed=N)
+        x = synthetic.activations(M, K, seed=K)
+        ref, absref = o.gemv(q, s, z, x)
+        wq, sp, zp = o.pack(q, s, z)
+        ref2, absref2 = o.gemv_packed(M, N, K, wq, sp, zp, x)
+        assert np.array_equal(ref, ref2) and np.array_equal(absref, absref2)
+        rows = np.array([0, N - 1, N // 2, 7])
+        ref3, _ = o.gemv_packed(M, N, K, wq, sp, zp, x, rows=rows)
+        assert np.array_equal(ref3, ref[:, rows])
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
