@@ -1,0 +1,157 @@
+/*
+ * w4a16.h -- C ABI of libw4a16.so: batch-1 (M <= 8) matrix-vector product
+ * y = W x with 4-bit weights, dequantized inside the kernel (W4A16 GEMV),
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation. W is N x K (N output features, K input features, row-major
+ * like the matrix of the row-per-output GEMV of "CodeAlign-Runtime", Level 1).
+ * Every run of 128 consecutive weights along K in one row is a group g with
+ * one fp16 scale s[n][g] and one 4-bit zero point z[n][g]; weight values q are
+ * unsigned 4-bit integers and
+ *     w[n][k] = (q[n][k] - z[n][g]) * s[n][g],   g = k / 128
+ * ("Building an LLM Inference Runtime ... Qwen2.5-Coder-7B on NVIDIA H100",
+ * section "The Stack Architecture": one fp16 scale per group of 128 per
+ * output row; "CodeAlign-Runtime", Level 3, "Quantization Scheme"). The
+ * pages' signed symmetric format (two's-complement nibble t, zero point 0)
+ * is the special case q = t xor 8, z = 8. Activations x are fp16 [M][K]
+ * row-major, products accumulate in fp32, and y is fp16 [M][N] row-major,
+ * rounded to nearest even:
+ *     y[m][n] = sum_k w[n][k] * x[m][k].
+ * The weights are never materialised: dequantization happens in registers
+ * ("CodeAlign-Runtime", Level 3).
+ *
+ * Conventions for every entry point:
+ *  - Return 0 (W4A16_OK) or a negative W4A16_E* code; nothing throws.
+ *  - The caller owns every buffer: host memory for pack/unpack, device memory
+ *    for the rest. The library never allocates, frees or synchronizes.
+ *  - Device entry points are asynchronous on `stream` (a hipStream_t; NULL is
+ *    the null stream). Faults during execution surface at the caller's next
+ *    synchronization. They do no host synchronization, allocation or
+ *    host read of device memory, so they can be captured into a hipGraph.
+ *  - Shapes: K must be a multiple of 128 and >= 128; 1 <= M <= 8 for the
+ *    GEMV entry points. M == 0 or N == 0 is a valid empty call: it returns
+ *    W4A16_OK without touching any pointer and without launching.
+ *  - Device pointers must be 16-byte aligned. Outputs of a call that
+ *    returns an error are unspecified.
+ *  - No global state: every entry point is reentrant.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_OK 0
+#define W4A16_EINVAL (-1)      /* bad shape, null or misaligned pointer, bad value */
+#define W4A16_EUNSUPPORTED (-2) /* M > 8: prefill-sized batches are not served */
+#define W4A16_ELAYOUT (-3)     /* layout ID mismatch (see w4a16_layout_id) */
+#define W4A16_EHIP (-4)        /* the HIP runtime refused a launch */
+
+#define W4A16_GROUP 128
+#define W4A16_MAX_M 8
+
+/*
+ * Layout identifier of the packed buffers this library reads and writes: 1.
+ * The runtime only ever understands this one layout, fixed with the packer
+ * (the practice of "Building an LLM Inference Runtime", Bug #3, where the
+ * runtime refuses weights of any other layout ID). Layout ID 1, for N x K:
+ *   NP = N rounded up to 16, G = K/128, GP = G rounded up to 8.
+ *   Wq: NP/16 * G tiles of 1024 bytes, tile (t, g) at byte (t*G + g)*1024.
+ *     The little-endian 32-bit word at byte lane*16 + kb*4 of a tile
+ *     (lane in [0,64), kb in [0,4)) holds row 16t + lane%16, columns
+ *     k = 128g + 32kb + 8*(lane/16) + j (j in [0,8)), weight j in bits
+ *     4*SLOT[j] .. 4*SLOT[j]+3 with SLOT = {0,4,1,5,2,6,3,7} -- the
+ *     ValueShuffle interleave of that page, which is also AWQ's
+ *     interleaved order ("Custom AWQ Dequantization Kernel", Part 2).
+ *   scales: fp16 [NP][GP] row-major (element n*GP + g).
+ *   zeros: 4-bit [NP][GP] row-major, two per byte, even g in the low nibble.
+ *   Padding rows (n >= N) and padding groups (g >= G) are zero.
+ */
+int w4a16_layout_id(void);
+
+/*
+ * Sizes in bytes of the three packed buffers for an N x K matrix.
+ * N >= 0; K a multiple of 128 and >= 128. Any of the size pointers may be
+ * NULL. Errors: W4A16_EINVAL for a bad shape.
+ */
+int w4a16_packed_sizes(int N, int K, size_t* wq_bytes, size_t* s_bytes, size_t* z_bytes);
+
+/*
+ * Host packer: logical tensors -> layout ID 1 (host memory to host memory).
+ *   q  [N][K]    uint8, each 0..15 (the 4-bit weights)
+ *   s  [N][K/128] uint16, fp16 bit patterns (any pattern is accepted)
+ *   z  [N][K/128] uint8, each 0..15 (the zero points)
+ *   wq_out, s_out, z_out: caller buffers of w4a16_packed_sizes() bytes;
+ *   they are overwritten entirely, padding included.
+ * Errors: W4A16_EINVAL for a bad shape, a NULL pointer (when N > 0), or a
+ * q or z value above 15. Runs on the calling thread (no GPU needed).
+ */
+int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, const uint8_t* z,
+               void* wq_out, void* s_out, void* z_out);
+
+/*
+ * Inverse of w4a16_pack (host to host): recovers q [N][K], s [N][K/128] and
+ * z [N][K/128] exactly. Errors: W4A16_EINVAL for a bad shape or NULL pointer.
+ */
+int w4a16_unpack(int N, int K, const void* wq, const void* s_packed, const void* z_packed,
+                 uint8_t* q, uint16_t* s, uint8_t* z);
+
+/*
+ * y = W x on the GPU (the hot path).
+ *   M: activation rows, 1..8 (a decode token plus speculative drafts);
+ *   N, K: weight shape (K multiple of 128); Wq, scales, zeros: device
+ *   buffers in layout ID 1; x: device fp16 [M][K]; y: device fp16 [M][N].
+ * Each output is a fixed-order fp32 sum (no atomics): repeated calls give
+ * bit-identical results. Errors: W4A16_EINVAL (shape, NULL, alignment),
+ * W4A16_EUNSUPPORTED (M > 8), W4A16_EHIP (launch refused).
+ */
+int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,
+               const void* x, void* y, void* stream);
+
+/*
+ * Workspace bytes w4a16_gemv_splitk needs: 4 * splits * M * N (fp32
+ * partial sums). Returns 0 for a negative argument.
+ */
+size_t w4a16_splitk_workspace_bytes(int M, int N, int splits);
+
+/*
+ * Split-K variant of w4a16_gemv for matrices with few rows: the K groups are
+ * divided into `splits` contiguous ranges, one fp32 partial product per
+ * range is written to `workspace` ([splits][M][N]), then a second kernel adds
+ * the partials in ascending split order and rounds to fp16 into y. This is
+ * the two-stage partial/final shape of "CodeAlign-Runtime", Level 4, applied
+ * to K; the fixed order keeps results bit-identical run to run, the rule of
+ * the qengine page ("Learnings": float atomics made runs differ, a fixed
+ * summation order fixed it). 1 <= splits <= K/128. workspace: device memory,
+ * 16-byte aligned, ws_bytes >= w4a16_splitk_workspace_bytes(M, N, splits).
+ * Results may differ in rounding from w4a16_gemv (another summation order)
+ * but lie within the same accuracy bound. Errors as w4a16_gemv, plus
+ * W4A16_EINVAL for a bad split count or a short workspace.
+ */
+int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq, const void* scales,
+                      const void* zeros, const void* x, void* y, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * Test hook: W_out[n][k] = float(q - z) * float(s) for n < N, k < K (device
+ * fp32 [N][K] row-major), computed with the same in-register unpack as the
+ * GEMV. The product is exact in fp32 (|q - z| <= 15 needs 4 bits, s has an
+ * 11-bit significand), so the result is comparable bit for bit. This is the
+ * dequantize entry point of "Custom AWQ Dequantization Kernel" for layout 1.
+ * Errors: W4A16_EINVAL (shape, NULL, alignment), W4A16_EHIP.
+ */
+int w4a16_dequant_f32(int N, int K, const void* Wq, const void* scales, const void* zeros,
+                      float* W_out, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* w4a16_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

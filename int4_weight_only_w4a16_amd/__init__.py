@@ -1,0 +1,154 @@
+"""Python binding of libw4a16.so (the MI355X W4A16 GEMV).
+
+Argument marshalling only: every function forwards to the C entry point of the
+same name declared in include/w4a16.h. Host functions take numpy arrays;
+device functions take torch tensors (or raw integer device pointers), torch
+being used only for device memory and streams. Nothing here computes: if the
+HIP library is not built, importing the functions fails loudly.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libw4a16.so")
+
+W4A16_OK = 0
+W4A16_EINVAL = -1
+W4A16_EUNSUPPORTED = -2
+W4A16_ELAYOUT = -3
+W4A16_EHIP = -4
+GROUP = 128
+MAX_M = 8
+
+# Every symbol the header declares.
+EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_unpack", "w4a16_gemv",
+           "w4a16_splitk_workspace_bytes", "w4a16_gemv_splitk", "w4a16_dequant_f32", "w4a16_strerror")
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {w4a16_strerror(status)} (status {status})")
+
+
+_lib = None
+_i = ctypes.c_int
+_p = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+def lib():
+    """The loaded ctypes library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError(f"libw4a16.so is not built ({LIBRARY}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIBRARY)
+        L.w4a16_layout_id.restype = _i
+        L.w4a16_layout_id.argtypes = []
+        L.w4a16_packed_sizes.argtypes = [_i, _i, _p, _p, _p]
+        L.w4a16_pack.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p]
+        L.w4a16_unpack.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p]
+        L.w4a16_gemv.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
+        L.w4a16_splitk_workspace_bytes.restype = _sz
+        L.w4a16_splitk_workspace_bytes.argtypes = [_i, _i, _i]
+        L.w4a16_gemv_splitk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+        L.w4a16_dequant_f32.argtypes = [_i, _i, _p, _p, _p, _p, _p]
+        L.w4a16_strerror.restype = ctypes.c_char_p
+        L.w4a16_strerror.argtypes = [_i]
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Device pointer of a torch tensor, or an int passed through (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, where):
+    if status != W4A16_OK:
+        raise W4A16Error(status, where)
+
+
+def w4a16_strerror(status):
+    return lib().w4a16_strerror(int(status)).decode()
+
+
+def w4a16_layout_id():
+    return lib().w4a16_layout_id()
+
+
+def w4a16_packed_sizes(N, K):
+    a, b, c = _sz(), _sz(), _sz()
+    _check(lib().w4a16_packed_sizes(N, K, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "w4a16_packed_sizes")
+    return a.value, b.value, c.value
+
+
+def w4a16_pack(q, s, z):
+    """Host: q uint8 [N][K], s uint16 fp16 bits [N][K/128], z uint8 [N][K/128]
+    -> (wq, s_packed, z_packed) uint8 numpy arrays in layout ID 1."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint16)
+    z = np.ascontiguousarray(z, dtype=np.uint8)
+    N, K = q.shape
+    if K % GROUP or s.shape != (N, K // GROUP) or z.shape != (N, K // GROUP):
+        raise W4A16Error(W4A16_EINVAL, "w4a16_pack")
+    wb, sb, zb = w4a16_packed_sizes(N, K)
+    wq, sp, zp = np.empty(wb, np.uint8), np.empty(sb, np.uint8), np.empty(zb, np.uint8)
+    _check(lib().w4a16_pack(N, K, q.ctypes.data, s.ctypes.data, z.ctypes.data,
+                            wq.ctypes.data, sp.ctypes.data, zp.ctypes.data), "w4a16_pack")
+    return wq, sp, zp
+
+
+def w4a16_unpack(N, K, wq, s_packed, z_packed):
+    """Host inverse of w4a16_pack -> (q, s, z)."""
+    wq, sp, zp = (np.ascontiguousarray(a, dtype=np.uint8) for a in (wq, s_packed, z_packed))
+    wb, sb, zb = w4a16_packed_sizes(N, K)
+    if wq.size < wb or sp.size < sb or zp.size < zb:
+        raise W4A16Error(W4A16_EINVAL, "w4a16_unpack")
+    G = K // GROUP
+    q, s, z = np.empty((N, K), np.uint8), np.empty((N, G), np.uint16), np.empty((N, G), np.uint8)
+    _check(lib().w4a16_unpack(N, K, wq.ctypes.data, sp.ctypes.data, zp.ctypes.data,
+                              q.ctypes.data, s.ctypes.data, z.ctypes.data), "w4a16_unpack")
+    return q, s, z
+
+
+def w4a16_gemv(M, N, K, Wq, scales, zeros, x, y, stream=None):
+    """Device: y[M][N] (fp16) = W x[M][K] (fp16) with W in layout ID 1."""
+    _check(lib().w4a16_gemv(M, N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
+                            _stream(stream)), "w4a16_gemv")
+
+
+def w4a16_splitk_workspace_bytes(M, N, splits):
+    return lib().w4a16_splitk_workspace_bytes(M, N, splits)
+
+
+def w4a16_gemv_splitk(M, N, K, splits, Wq, scales, zeros, x, y, workspace, ws_bytes=None, stream=None):
+    """Device: split-K GEMV; workspace holds [splits][M][N] fp32 partials."""
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().w4a16_gemv_splitk(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x),
+                                   _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)),
+           "w4a16_gemv_splitk")
+
+
+def w4a16_dequant_f32(N, K, Wq, scales, zeros, W_out, stream=None):
+    """Device test hook: W_out[N][K] fp32 = (q - z) * s."""
+    _check(lib().w4a16_dequant_f32(N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(W_out),
+                                   _stream(stream)), "w4a16_dequant_f32")

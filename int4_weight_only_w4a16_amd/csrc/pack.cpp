@@ -1,0 +1,144 @@
+// Host packer and unpacker for layout ID 1 (declared in include/w4a16.h).
+//
+// A tile is 16 rows x one group of 128 columns, 1024 bytes: 64 lanes of
+// 16 bytes, lane l carrying row l%16 and four 8-column pieces
+// (k = 32*kb + 8*(l/16) .. +7, kb = 0..3), one 32-bit word each. That is the
+// A-operand footprint of a 16x16x32 fp16 MFMA and, for the VALU kernel, a
+// lane-private run of 32 weights of one row, so one 16-byte load per lane
+// fetches a wave's whole kilobyte contiguously.
+//
+// Inside a word the 8 weights follow the ValueShuffle interleave of
+// "Building an LLM Inference Runtime ... H100", Bug #3 (weight j at nibble
+// slot {0,4,1,5,2,6,3,7}[j]; AWQ's order in "Custom AWQ Dequantization
+// Kernel", Part 2). With it, masking a word with 0x000F000F (and 0x00F000F0,
+// then both again after a shift by 8) yields the fp16 pairs (w0,w1),
+// (w2,w3), (w4,w5), (w6,w7) in column order, which is what the kernels use.
+#include <cstring>
+
+#include "w4a16.h"
+#include "w4a16_internal.h"
+
+namespace {
+
+// Bit position of weight j within its 32-bit word.
+constexpr int kShift[8] = {0, 16, 4, 20, 8, 24, 12, 28};
+
+bool shape_ok(int N, int K) { return N >= 0 && K >= W4A16_GROUP && K % W4A16_GROUP == 0; }
+
+inline void store_le32(uint8_t* p, uint32_t v) {
+  p[0] = uint8_t(v);
+  p[1] = uint8_t(v >> 8);
+  p[2] = uint8_t(v >> 16);
+  p[3] = uint8_t(v >> 24);
+}
+
+inline uint32_t load_le32(const uint8_t* p) {
+  return uint32_t(p[0]) | (uint32_t(p[1]) << 8) | (uint32_t(p[2]) << 16) | (uint32_t(p[3]) << 24);
+}
+
+}  // namespace
+
+extern "C" int w4a16_layout_id(void) { return w4a16::kLayoutId; }
+
+extern "C" int w4a16_packed_sizes(int N, int K, size_t* wq_bytes, size_t* s_bytes, size_t* z_bytes) {
+  if (!shape_ok(N, K)) return W4A16_EINVAL;
+  const w4a16::Geometry geo(N, K);
+  if (wq_bytes) *wq_bytes = geo.wq_bytes();
+  if (s_bytes) *s_bytes = geo.s_bytes();
+  if (z_bytes) *z_bytes = geo.z_bytes();
+  return W4A16_OK;
+}
+
+extern "C" int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, const uint8_t* z,
+                          void* wq_out, void* s_out, void* z_out) {
+  if (!shape_ok(N, K)) return W4A16_EINVAL;
+  if (N == 0) return W4A16_OK;
+  if (!q || !s || !z || !wq_out || !s_out || !z_out) return W4A16_EINVAL;
+  const w4a16::Geometry geo(N, K);
+  uint8_t* wq = static_cast<uint8_t*>(wq_out);
+  uint8_t* sp = static_cast<uint8_t*>(s_out);
+  uint8_t* zp = static_cast<uint8_t*>(z_out);
+
+  unsigned bad = 0;  // any bit above the low nibble of a q or z value
+  for (int64_t t = 0; t < geo.row_tiles; ++t) {
+    for (int64_t g = 0; g < geo.groups; ++g) {
+      uint8_t* tile = wq + (t * geo.groups + g) * w4a16::kTileBytes;
+      for (int lane = 0; lane < 64; ++lane) {
+        const int64_t row = 16 * t + (lane & 15);
+        for (int kb = 0; kb < 4; ++kb) {
+          uint32_t word = 0;
+          if (row < N) {
+            const uint8_t* src = q + row * int64_t(K) + g * W4A16_GROUP + 32 * kb + 8 * (lane >> 4);
+            for (int j = 0; j < 8; ++j) {
+              bad |= src[j];
+              word |= uint32_t(src[j] & 15u) << kShift[j];
+            }
+          }
+          store_le32(tile + lane * 16 + kb * 4, word);
+        }
+      }
+    }
+  }
+  bad &= ~15u;
+
+  std::memset(sp, 0, geo.s_bytes());
+  std::memset(zp, 0, geo.z_bytes());
+  for (int64_t n = 0; n < N; ++n) {
+    uint8_t* srow = sp + 2 * n * geo.groups_padded;
+    uint8_t* zrow = zp + n * geo.groups_padded / 2;
+    for (int64_t g = 0; g < geo.groups; ++g) {
+      const uint16_t sv = s[n * geo.groups + g];
+      srow[2 * g] = uint8_t(sv);
+      srow[2 * g + 1] = uint8_t(sv >> 8);
+      const uint8_t zv = z[n * geo.groups + g];
+      bad |= zv & ~15u;
+      zrow[g >> 1] |= uint8_t((zv & 15u) << ((g & 1) * 4));
+    }
+  }
+  return bad ? W4A16_EINVAL : W4A16_OK;
+}
+
+extern "C" int w4a16_unpack(int N, int K, const void* wq_in, const void* s_packed, const void* z_packed,
+                            uint8_t* q, uint16_t* s, uint8_t* z) {
+  if (!shape_ok(N, K)) return W4A16_EINVAL;
+  if (N == 0) return W4A16_OK;
+  if (!wq_in || !s_packed || !z_packed || !q || !s || !z) return W4A16_EINVAL;
+  const w4a16::Geometry geo(N, K);
+  const uint8_t* wq = static_cast<const uint8_t*>(wq_in);
+  const uint8_t* sp = static_cast<const uint8_t*>(s_packed);
+  const uint8_t* zp = static_cast<const uint8_t*>(z_packed);
+  for (int64_t t = 0; t < geo.row_tiles; ++t) {
+    for (int64_t g = 0; g < geo.groups; ++g) {
+      const uint8_t* tile = wq + (t * geo.groups + g) * w4a16::kTileBytes;
+      for (int lane = 0; lane < 64; ++lane) {
+        const int64_t row = 16 * t + (lane & 15);
+        if (row >= N) continue;
+        for (int kb = 0; kb < 4; ++kb) {
+          const uint32_t word = load_le32(tile + lane * 16 + kb * 4);
+          uint8_t* dst = q + row * int64_t(K) + g * W4A16_GROUP + 32 * kb + 8 * (lane >> 4);
+          for (int j = 0; j < 8; ++j) dst[j] = uint8_t((word >> kShift[j]) & 15u);
+        }
+      }
+    }
+  }
+  for (int64_t n = 0; n < N; ++n) {
+    const uint8_t* srow = sp + 2 * n * geo.groups_padded;
+    const uint8_t* zrow = zp + n * geo.groups_padded / 2;
+    for (int64_t g = 0; g < geo.groups; ++g) {
+      s[n * geo.groups + g] = uint16_t(srow[2 * g] | (srow[2 * g + 1] << 8));
+      z[n * geo.groups + g] = uint8_t((zrow[g >> 1] >> ((g & 1) * 4)) & 15u);
+    }
+  }
+  return W4A16_OK;
+}
+
+extern "C" const char* w4a16_strerror(int status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_EINVAL: return "invalid argument (shape, pointer, alignment or value)";
+    case W4A16_EUNSUPPORTED: return "unsupported: more than 8 activation rows";
+    case W4A16_ELAYOUT: return "packed layout ID mismatch";
+    case W4A16_EHIP: return "HIP runtime refused the launch";
+    default: return "unknown status";
+  }
+}

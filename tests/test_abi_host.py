@@ -1,0 +1,129 @@
+"""Host-side checks of libw4a16.so (no GPU): exports, layout sizes, the packer
+against the oracle's packing (bit-exact), unpack, and argument errors that are
+decided before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import int4_weight_only_w4a16_amd as w
+import oracle
+import synthetic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "w4a16.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = w.lib()
+    decl = declared_symbols()
+    assert decl == sorted(w.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_layout_id_and_status_text():
+    assert w.w4a16_layout_id() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert w.w4a16_strerror(code)
+    assert w.w4a16_strerror(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (16, 128), (17, 896), (896, 896), (128, 4864), (37, 1152)])
+def test_packed_sizes_match_oracle(orc, N, K):
+    assert w.w4a16_packed_sizes(N, K) == orc.layout_sizes(N, K)
+
+
+@pytest.mark.parametrize("N,K,seed", [(1, 128, 0), (15, 256, 1), (17, 896, 2), (40, 1152, 3),
+                                      (896, 896, 0), (128, 4864, 5), (33, 18944, 6)])
+def test_pack_matches_oracle_bytes(orc, N, K, seed):
+    q, s, z = synthetic.weights(N, K, seed=seed)
+    mine = w.w4a16_pack(q, s, z)
+    ref = orc.pack(q, s, z)
+    for a, b in zip(mine, ref):
+        assert np.array_equal(a, b)
+    q2, s2, z2 = w.w4a16_unpack(N, K, *mine)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(z, z2)
+
+
+def test_pack_edge_patterns(orc):
+    N, K = 19, 640
+    G = K // 128
+    for q, s, z in [
+        (np.zeros((N, K), np.uint8), np.zeros((N, G), np.uint16), np.zeros((N, G), np.uint8)),
+        (np.full((N, K), 15, np.uint8), np.full((N, G), 0xFFFF, np.uint16), np.full((N, G), 15, np.uint8)),
+        ((np.arange(N * K) % 16).astype(np.uint8).reshape(N, K), np.arange(N * G, dtype=np.uint16).reshape(N, G),
+         (np.arange(N * G) * 7 % 16).astype(np.uint8).reshape(N, G)),
+    ]:
+        for a, b in zip(w.w4a16_pack(q, s, z), orc.pack(q, s, z)):
+            assert np.array_equal(a, b)
+
+
+def test_pack_rejects_bad_values_and_shapes():
+    L = w.lib()
+    q = np.zeros((2, 128), np.uint8)
+    s = np.zeros((2, 1), np.uint16)
+    z = np.zeros((2, 1), np.uint8)
+    wb, sb, zb = w.w4a16_packed_sizes(2, 128)
+    out = [np.empty(n, np.uint8) for n in (wb, sb, zb)]
+    args = lambda qq, zz: (2, 128, qq.ctypes.data, s.ctypes.data, zz.ctypes.data, *(o.ctypes.data for o in out))
+    assert L.w4a16_pack(*args(q, z)) == w.W4A16_OK
+    q_bad = q.copy(); q_bad[1, 77] = 16
+    assert L.w4a16_pack(*args(q_bad, z)) == w.W4A16_EINVAL
+    z_bad = z.copy(); z_bad[0, 0] = 200
+    assert L.w4a16_pack(*args(q, z_bad)) == w.W4A16_EINVAL
+    assert L.w4a16_pack(2, 100, q.ctypes.data, s.ctypes.data, z.ctypes.data, *(o.ctypes.data for o in out)) == w.W4A16_EINVAL
+    assert L.w4a16_pack(2, 128, None, s.ctypes.data, z.ctypes.data, *(o.ctypes.data for o in out)) == w.W4A16_EINVAL
+    assert L.w4a16_pack(0, 128, None, None, None, None, None, None) == w.W4A16_OK
+    assert L.w4a16_packed_sizes(4, 129, None, None, None) == w.W4A16_EINVAL
+    assert L.w4a16_packed_sizes(-1, 128, None, None, None) == w.W4A16_EINVAL
+
+
+def test_device_entry_points_reject_before_launch():
+    """Argument errors are returned without touching the GPU (none here)."""
+    L = w.lib()
+    fake = 1 << 20  # aligned, never dereferenced: every call below fails its checks first
+    ptrs = [fake] * 5
+    for M, N, K, want in [(1, 16, 100, w.W4A16_EINVAL), (1, 16, 0, w.W4A16_EINVAL), (-1, 16, 128, w.W4A16_EINVAL),
+                          (1, -3, 128, w.W4A16_EINVAL), (9, 16, 128, w.W4A16_EUNSUPPORTED),
+                          (0, 16, 128, w.W4A16_OK), (1, 0, 128, w.W4A16_OK)]:
+        assert L.w4a16_gemv(M, N, K, *ptrs, None) == want, (M, N, K)
+    # null and misaligned pointers
+    assert L.w4a16_gemv(1, 16, 128, fake, fake, None, fake, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemv(1, 16, 128, fake, fake, fake, fake + 2, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemv(1, 16, 128, fake + 8, fake, fake, fake, fake, None) == w.W4A16_EINVAL
+    # split-K: split count and workspace size
+    ws = w.w4a16_splitk_workspace_bytes(2, 16, 3)
+    assert ws == 4 * 3 * 2 * 16
+    assert w.w4a16_splitk_workspace_bytes(-1, 16, 3) == 0
+    for splits, wsb, want in [(0, ws, w.W4A16_EINVAL), (3, ws - 4, w.W4A16_EINVAL), (3, ws, None),
+                              (8, 10 ** 9, w.W4A16_EINVAL)]:
+        if want is None:
+            continue
+        assert L.w4a16_gemv_splitk(2, 16, 768, splits, *ptrs, fake, wsb, None) == want, splits
+    assert L.w4a16_gemv_splitk(9, 16, 768, 2, *ptrs, fake, 10 ** 9, None) == w.W4A16_EUNSUPPORTED
+    assert L.w4a16_gemv_splitk(2, 0, 768, 2, *ptrs, fake, 0, None) == w.W4A16_OK
+    # dequant hook
+    assert L.w4a16_dequant_f32(16, 200, fake, fake, fake, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_dequant_f32(0, 128, None, None, None, None, None) == w.W4A16_OK
+    assert L.w4a16_dequant_f32(16, 128, fake, fake, fake, fake + 4, None) == w.W4A16_EINVAL
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
+    """No fallback: a missing library is an ImportError, not a CPU path."""
+    monkeypatch.setattr(w, "LIBRARY", os.path.join(tmp_path, "missing.so"))
+    monkeypatch.setattr(w, "_lib", None)
+    with pytest.raises(ImportError):
+        w.lib()
