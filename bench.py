@@ -1,0 +1,308 @@
+#!/usr/bin/env python
+"""Benchmark: one Qwen2.5-7B-shaped decode step of batch-1 W4A16 GEMVs on one MI355X.
+
+A step is the whole hot path over one token: 28 layers x (fused qkv 4608x3584,
+o 3584x3584, fused gate+up 37888x3584, down 3584x18944) plus an int4 lm_head
+152064x3584, all int4 g=128 with fp16 scales and 4-bit zero points, M=1:
+113 w4a16_gemv launches, stream-ordered and replayed as one captured graph.
+The 3.68 GB of packed weights are distinct per layer and resident in HBM
+before timing starts, so every step streams them from HBM (they exceed the
+256 MB last-level cache). Inputs are seeded synthetic data with the
+workload's laws (synthetic.py).
+
+Prints one JSON line:
+  value      = algorithmic bytes of the step / step time, GB/s (whole job),
+  roofline   = the dominant kernel (the gate+up GEMV launch) timed with HIP
+               events over back-to-back launches,
+  cpu_baseline = the fp64 oracle on the host cores over a bounded sample of
+               the same step (also used to check sampled outputs).
+
+  python bench.py [--steps K] [--warmup W]
+  python bench.py --trace-summary DIR   # summarize a rocprofv3 kernel trace
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synthetic  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+GROUP = 128
+KERNEL_SOURCE = os.path.join(ROOT, "int4_weight_only_w4a16_amd", "csrc", "w4a16_kernels.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_gate_up_7b_counters.txt")
+
+
+def algorithmic_bytes(M, N, K):
+    """Minimum bytes of one GEMV: packed 4-bit weights, fp16 scales, 4-bit
+    zeros, fp16 x and fp16 y (no padding)."""
+    G = K // GROUP
+    return N * K // 2 + 2 * N * G + N * G // 2 + 2 * M * K + 2 * M * N
+
+
+def step_shapes():
+    shapes = []
+    for layer in range(synthetic.QWEN7B_LAYERS):
+        for name, N, K in synthetic.QWEN7B_LAYER:
+            shapes.append((f"L{layer}.{name}", N, K))
+    shapes.append(synthetic.QWEN7B_LM_HEAD)
+    return shapes
+
+
+def kernel_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """Per-launch HBM traffic of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    for line in open(COUNTERS_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Step:
+    """Device buffers and the captured graph of one decode step."""
+
+    def __init__(self, seed, torch):
+        import int4_weight_only_w4a16_amd as w
+        self.w, self.torch = w, torch
+        dev = torch.device("cuda:0")
+        self.shapes = step_shapes()
+        self.bufs = []
+        for i, (name, N, K) in enumerate(self.shapes):
+            wq, sc, zp = synthetic.device_packed_weights(N, K, seed, i, dev)
+            x = synthetic.device_activations(1, K, seed, i, dev)
+            y = torch.empty((1, N), dtype=torch.int16, device=dev)
+            self.bufs.append((name, N, K, wq, sc, zp, x, y))
+        torch.cuda.synchronize()
+        self.bytes = sum(algorithmic_bytes(1, N, K) for _, N, K in self.shapes)
+        self.stream = torch.cuda.Stream()
+
+    def launch_all(self, stream, only=None):
+        for name, N, K, wq, sc, zp, x, y in self.bufs:
+            if only is None or name.endswith(only):
+                self.w.w4a16_gemv(1, N, K, wq, sc, zp, x, y, stream=stream)
+
+    def capture(self, only=None):
+        torch = self.torch
+        self.stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(self.stream):
+            self.launch_all(self.stream, only)  # warm: first launches load code objects
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream):
+                self.launch_all(self.stream, only)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(self, g, reps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            e0.record(self.stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3  # seconds
+
+    def time_eager(self, reps):
+        torch = self.torch
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            e0.record(self.stream)
+            for _ in range(reps):
+                self.launch_all(self.stream)
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+
+def cpu_baseline(step, budget_s):
+    """The fp64 oracle, as it stands, over whole GEMVs of the same step in
+    step order (lm_head first, then layers 0, 1, ...) until about budget_s
+    seconds of oracle time are spent. Also checks those GEMVs' GPU outputs
+    (from the last replay) against the oracle bound."""
+    import oracle
+    orc = oracle.get()
+    order = [step.bufs[-1]] + step.bufs[:-1]
+    done_bytes, spent, worst, names = 0, 0.0, 0.0, []
+    for name, N, K, wq, sc, zp, x, y in order:
+        host = [t.cpu().numpy() for t in (wq, sc, zp, x, y)]
+        wq_h, sc_h, zp_h = host[0], host[1].view(np.uint8), host[2]
+        x_h, y_h = host[3].view(np.uint16), host[4].view(np.uint16)
+        t0 = time.perf_counter()
+        ref, absref = orc.gemv_packed(1, N, K, wq_h, sc_h, zp_h, x_h)
+        spent += time.perf_counter() - t0
+        done_bytes += algorithmic_bytes(1, N, K)
+        names.append(name)
+        ok, r = oracle.bound_report(y_h, ref, absref, orc)
+        worst = max(worst, r)
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(done_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": f"{len(names)} of the step's 113 GEMVs, whole ({names[0]}, {names[1] if len(names) > 1 else ''}"
+                  f"{', ...' if len(names) > 2 else ''}), {done_bytes / 1e9:.3f} GB of algorithmic bytes, "
+                  f"{spent:.1f} s of oracle time",
+        "us_per_step_extrapolated": round(spent / done_bytes * step.bytes * 1e6, 1),
+    }, worst, len(names)
+
+
+def trace_summary(directory):
+    """Per-shape kernel durations from a rocprofv3 --kernel-trace CSV: the
+    gemv kernel launches grouped by grid size (one grid size per shape)."""
+    paths = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no *kernel_trace.csv under {directory}")
+    import csv
+    groups = {}
+    for path in paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row.get("Kernel_Name", "")
+                if "w4a16" not in name:
+                    continue
+                dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3  # us
+                key = (name.split("(")[0][-60:], row.get("Grid_Size_X", row.get("Grid_Size", "?")),
+                       row.get("Workgroup_Size_X", row.get("Workgroup_Size", "?")))
+                groups.setdefault(key, []).append(dur)
+    print(f"{'kernel':60s} {'grid_x':>10s} {'wg_x':>5s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s}")
+    for key, durs in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        d = np.array(durs)
+        print(f"{key[0]:60s} {key[1]:>10s} {key[2]:>5s} {len(d):6d} {d.mean():9.2f} {np.median(d):9.2f} {d.min():9.2f}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--roofline-reps", type=int, default=100)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--trace-summary", metavar="DIR")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 512 MiB device copy kernel (counter scaling)")
+    args = ap.parse_args()
+
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the W4A16 GEMV path here is single-GPU "
+              "(--gpus 1 only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        n = (512 << 20) // 4
+        a = torch.ones(n, dtype=torch.int32, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+        return
+
+    t_setup = time.perf_counter()
+    step = Step(args.seed, torch)
+    graph = step.capture()
+    setup_s = time.perf_counter() - t_setup
+
+    elapsed = step.time_graph(graph, args.steps, args.warmup)
+    us_step = elapsed / args.steps * 1e6
+    value = step.bytes * args.steps / elapsed / 1e9
+    eager_us = step.time_eager(max(3, args.steps // 10)) / max(3, args.steps // 10) * 1e6
+
+    # Dominant kernel: the gate+up GEMV (58% of the step's bytes), 28 distinct
+    # weight sets back to back in one graph.
+    dom = step.capture(only="gate_up_proj")
+    reps = args.roofline_reps
+    dom_s = step.time_graph(dom, reps, 3)
+    n_dom = synthetic.QWEN7B_LAYERS
+    _, Nd, Kd = synthetic.QWEN7B_LAYER[2]
+    dom_bytes = algorithmic_bytes(1, Nd, Kd)
+    dom_us = dom_s / (reps * n_dom) * 1e6
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+
+    # Outputs of the last full replay, for the sampled check.
+    graph.replay()
+    torch.cuda.synchronize()
+
+    out = {
+        "metric": "achieved HBM GB/s for batch-1 W4A16 GEMV over a 7B decode step (us per step in ms_per_step)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 5),
+        "us_per_step": round(us_step, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 x fp16 -> fp32",
+        "data": "synthetic (seeded; packed int4 weights, fp16 scales |N(0,0.02)|+1e-3, uniform 4-bit zeros, x ~ N(0,1))",
+        "config": {
+            "workload": "Qwen2.5-7B-shaped decode step at M=1: 28 x (qkv 4608x3584, o 3584x3584, "
+                        "gate_up 37888x3584, down 3584x18944) + lm_head 152064x3584, int4 g=128",
+            "launches_per_step": len(step.shapes),
+            "bytes_per_step": step.bytes,
+            "submission": "one captured graph per step",
+            "eager_us_per_step": round(eager_us, 1),
+            "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        },
+        "roofline": {
+            "kernel": "w4a16 gemv, gate_up 37888x3584 M=1",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(),
+            "bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_us, 3),
+        },
+        "setup_s": round(setup_s, 1),
+    }
+    if args.cpu_budget > 0:
+        cpu, worst, n_checked = cpu_baseline(step, args.cpu_budget)
+        out["cpu_baseline"] = cpu
+        out["parity_sample"] = {"gemvs_checked": n_checked, "worst_err_over_bound": round(worst, 4),
+                                "ok": bool(worst <= 1.0)}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -72,3 +72,33 @@ VERIFY_M = (1, 2, 5, 8)
 
 SINGLE_896 = ("single_896", 896, 896)
 
+
+
+def device_packed_weights(N, K, seed, tensor_id, device):
+    """Weights drawn directly in layout-ID-1 form on the GPU (for large
+    benchmark sets, where drawing logical q on the host would dominate).
+
+    Same law as packing weights(): packed nibbles of uniform q (and z) are
+    uniform random bytes; scales are fp16(|N(0, 0.02)| + 1e-3) in every
+    [row][group] slot, padding slots included (they are never read).
+    Uses torch's seeded device generator. Returns (wq, scales, zeros) as
+    uint8/int16/uint8 torch tensors of the packed sizes."""
+    import torch
+    NP = (N + 15) // 16 * 16
+    G = K // GROUP
+    GP = (G + 7) // 8 * 8
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1000003 + int(tensor_id))
+    wq = torch.randint(0, 256, (NP * K // 2,), dtype=torch.uint8, device=device, generator=gen)
+    sv = torch.randn((NP, GP), dtype=torch.float32, device=device, generator=gen).mul_(0.02).abs_().add_(1e-3)
+    sc = sv.to(torch.float16).view(torch.int16).reshape(-1)
+    zp = torch.randint(0, 256, (NP * GP // 2,), dtype=torch.uint8, device=device, generator=gen)
+    return wq, sc, zp
+
+
+def device_activations(M, K, seed, tensor_id, device):
+    """fp16 x [M][K] ~ N(0, 1) drawn on the GPU (int16 view of the bits)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1000003 + 500009 + int(tensor_id))
+    return torch.randn((M, K), dtype=torch.float32, device=device, generator=gen).to(torch.float16).view(torch.int16)
