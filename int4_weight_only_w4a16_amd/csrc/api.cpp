@@ -24,16 +24,39 @@ bool pointers_ok(std::initializer_list<const void*> ptrs) {
   return true;
 }
 
-// Waves per workgroup grow with the number of groups so that long rows are
-// streamed by more waves at once.
-w4a16::LaunchPlan plan_for(int M, int K, int splits) {
+// Smallest instantiated share size that holds `tiles` tiles (10 at most;
+// longer shares run in several rounds).
+int share_for(int tiles) {
+  static const int kShares[] = {2, 3, 4, 5, 7, 8, 10};
+  for (int s : kShares)
+    if (tiles <= s) return s;
+  return 10;
+}
+
+// Launch plan for one shape. Waves per workgroup and the share size depend
+// on N and K only (never on M), so row m of an M-row call is bit-identical to
+// the same row computed alone: every engine below performs the same fp32
+// operations in the same order for a given (waves, K range). Shares of about
+// 8 tiles per wave when there are many row tiles (enough workgroups to fill
+// the GPU), about 5 (2 for K <= 1024) when there are few, at most 16 waves.
+// MFMA with x from LDS when the per-wave x slices fit, else from global memory.
+w4a16::LaunchPlan plan_for(int M, int N, int K, int splits) {
   const int groups = K / W4A16_GROUP;
-  const int per_split = (groups + splits - 1) / splits;
+  const int range = (groups + splits - 1) / splits;
+  const int64_t row_tiles = (int64_t(N) + 15) / 16;
+  const int target = row_tiles >= 1024 ? 8 : (range <= 8 ? 2 : 5);
   w4a16::LaunchPlan plan;
-  plan.waves = per_split >= 64 ? 16 : per_split >= 16 ? 8 : 4;
+  plan.engine = w4a16::kEngineMfma;
   plan.splits = splits;
-  const int cap = w4a16::max_slice_groups(M);
-  plan.slice_groups = per_split < cap ? per_split : cap;
+  plan.tiles_per_wg = 1;
+  plan.waves = 1;
+  while (plan.waves < 16 && (range + plan.waves - 1) / plan.waves > target) plan.waves *= 2;
+  const int per_wave = (range + plan.waves - 1) / plan.waves;
+  plan.share = share_for(per_wave);
+  if (!w4a16::plan_supported(M, K, plan)) {
+    plan.engine = w4a16::kEngineMfmaGlobalX;
+    plan.share = plan.waves == 16 ? 3 : 4;
+  }
   return plan;
 }
 
@@ -44,7 +67,7 @@ extern "C" int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scale
   const int rc = check_shape(M, N, K);
   if (rc != W4A16_OK) return rc == 1 ? W4A16_OK : rc;
   if (!pointers_ok({Wq, scales, zeros, x, y})) return W4A16_EINVAL;
-  const w4a16::LaunchPlan plan = plan_for(M, K, 1);
+  const w4a16::LaunchPlan plan = plan_for(M, N, K, 1);
   if (w4a16::launch_gemv(M, N, K, plan, Wq, scales, zeros, x, y, nullptr, stream) != 0) return W4A16_EHIP;
   return W4A16_OK;
 }
@@ -63,7 +86,7 @@ extern "C" int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq
   if (rc == 1) return W4A16_OK;
   if (!pointers_ok({Wq, scales, zeros, x, y, workspace})) return W4A16_EINVAL;
   if (ws_bytes < w4a16_splitk_workspace_bytes(M, N, splits)) return W4A16_EINVAL;
-  const w4a16::LaunchPlan plan = plan_for(M, K, splits);
+  const w4a16::LaunchPlan plan = plan_for(M, N, K, splits);
   float* partials = static_cast<float*>(workspace);
   if (w4a16::launch_gemv(M, N, K, plan, Wq, scales, zeros, x, y, partials, stream) != 0) return W4A16_EHIP;
   if (w4a16::launch_splitk_reduce(M, N, splits, partials, y, stream) != 0) return W4A16_EHIP;

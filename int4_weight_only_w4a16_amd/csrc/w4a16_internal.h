@@ -26,15 +26,30 @@ struct Geometry {
   size_t z_bytes() const { return size_t(row_tiles) * kTileRows * size_t(groups_padded) / 2; }
 };
 
-// Launch parameters chosen by the front end for one GEMV shape.
-struct LaunchPlan {
-  int waves;         // waves per workgroup (4, 8 or 16)
-  int splits;        // K ranges (gridDim.y); 1 for the plain GEMV
-  int slice_groups;  // groups of x staged in LDS at a time
+// Inner-product engine of the GEMV kernel.
+enum Engine : int {
+  kEngineDot2 = 0,      // v_dot2_f32_f16 on the VALU (M <= 2), x staged in LDS
+  kEngineMfma = 1,      // v_mfma_f32_16x16x32_f16, x staged in LDS
+  kEngineMfmaGlobalX = 2  // v_mfma_f32_16x16x32_f16, x read straight from global memory
 };
 
-// Largest number of groups of x (for M activation rows) one workgroup stages in LDS.
-int max_slice_groups(int M);
+// Launch parameters chosen by the front end for one GEMV shape.
+struct LaunchPlan {
+  int engine;  // Engine
+  int waves;   // waves per workgroup: 1, 2, 4, 8 or 16
+  int share;   // tiles a wave requests at once (2, 4, 8 or 12); longer shares take several rounds
+  int splits;  // K ranges (gridDim.y); 1 for the plain GEMV
+  int tiles_per_wg;  // row tiles per workgroup (gridDim.x = ceil(row tiles / this))
+};
+
+// Largest dynamic LDS a GEMV workgroup may use.
+constexpr size_t kMaxLdsBytes = 64 * 1024;
+
+// Dynamic LDS bytes of a GEMV launch (0 for kEngineMfmaGlobalX).
+size_t lds_bytes(int M, int K, const LaunchPlan& plan);
+
+// Whether the kernel set has an instantiation for this plan, within the LDS limit.
+bool plan_supported(int M, int K, const LaunchPlan& plan);
 
 // Kernel launchers (w4a16_kernels.hip). They return a hipError_t value as int.
 int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,

@@ -123,14 +123,28 @@ def test_row_permutation_permutes_output():
 
 
 def test_activation_rows_are_independent():
-    """Row m of an M-row call equals the same x row alone (same kernel path
-    for M whose x slices coincide)."""
+    """Permuting the rows of x permutes the rows of y bit for bit."""
     N, K = 512, 2048
     q, s, z = synthetic.weights(N, K, seed=7)
     x = synthetic.activations(4, K, seed=7)
     y4 = Problem(4, N, K, q=q, s=s, z=z, x=x).gemv()
     y4b = Problem(4, N, K, q=q, s=s, z=z, x=x[[2, 0, 3, 1]].copy()).gemv()
     assert np.array_equal(y4b, y4[[2, 0, 3, 1]])
+
+
+@pytest.mark.parametrize("N,K", [(128, 896), (4608, 3584), (3584, 18944), (17408, 5120), (5120, 17408)])
+def test_batch_invariance(N, K):
+    """Row m of an M-row call is bit-identical to that row computed alone,
+    for every M up to 8 (the verify pass of a speculative decoder must give
+    the same row r whether it processes 1 row or 8)."""
+    _say("batch invariance", N, K)
+    q, s, z = synthetic.weights(N, K, seed=11)
+    x = synthetic.activations(8, K, seed=11)
+    alone = [Problem(1, N, K, q=q, s=s, z=z, x=x[m:m + 1].copy()).gemv() for m in range(8)]
+    for M in range(2, 9):
+        yM = Problem(M, N, K, q=q, s=s, z=z, x=x[:M].copy()).gemv()
+        for m in range(M):
+            assert np.array_equal(yM[m], alone[m][0]), (M, m)
 
 
 # ---------------------------------------------------------------- split-K
