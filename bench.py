@@ -38,7 +38,10 @@ import synthetic  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 GROUP = 128
-KERNEL_SOURCE = os.path.join(ROOT, "int4_weight_only_w4a16_amd", "csrc", "w4a16_kernels.hip")
+# Sources that decide the GEMV kernel's code and launch shape: a counter
+# summary taken on other sources is not used.
+KERNEL_SOURCES = [os.path.join(ROOT, "int4_weight_only_w4a16_amd", "csrc", f)
+                  for f in ("gemv_kernel.h", "w4a16_device.h", "w4a16_internal.h", "api.cpp")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemv_gate_up_7b_counters.txt")
 
 
@@ -59,8 +62,11 @@ def step_shapes():
 
 
 def kernel_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic():

@@ -55,11 +55,12 @@ extern "C" {
 #define W4A16_MAX_M 8
 
 /*
- * Layout identifier of the packed buffers this library reads and writes: 1.
+ * Layout identifier of the packed buffers this library reads and writes: 2.
  * The runtime only ever understands this one layout, fixed with the packer
  * (the practice of "Building an LLM Inference Runtime", Bug #3, where the
- * runtime refuses weights of any other layout ID). Layout ID 1, for N x K:
- *   NP = N rounded up to 16, G = K/128, GP = G rounded up to 8.
+ * runtime refuses weights of any other layout ID). Layout ID 2, for N x K:
+ *   NP = N rounded up to 16, G = K/128. Tile (t, g) is rows 16t .. 16t+15
+ *   of group g; all three buffers list tiles in the order t*G + g.
  *   Wq: NP/16 * G tiles of 1024 bytes, tile (t, g) at byte (t*G + g)*1024.
  *     The little-endian 32-bit word at byte lane*16 + kb*4 of a tile
  *     (lane in [0,64), kb in [0,4)) holds row 16t + lane%16, columns
@@ -67,9 +68,11 @@ extern "C" {
  *     4*SLOT[j] .. 4*SLOT[j]+3 with SLOT = {0,4,1,5,2,6,3,7} -- the
  *     ValueShuffle interleave of that page, which is also AWQ's
  *     interleaved order ("Custom AWQ Dequantization Kernel", Part 2).
- *   scales: fp16 [NP][GP] row-major (element n*GP + g).
- *   zeros: 4-bit [NP][GP] row-major, two per byte, even g in the low nibble.
- *   Padding rows (n >= N) and padding groups (g >= G) are zero.
+ *   scales: 16 fp16 per tile, row n group g at element (t*G + g)*16 + n%16
+ *     (t = n/16): NP*G*2 bytes.
+ *   zeros: 16 nibbles per tile, row n group g in byte (t*G + g)*8 + (n%16)/2,
+ *     low nibble for even n, high nibble for odd n: NP*G/2 bytes.
+ *   Padding rows (n >= N) are zero in all three buffers.
  */
 int w4a16_layout_id(void);
 
@@ -81,7 +84,7 @@ int w4a16_layout_id(void);
 int w4a16_packed_sizes(int N, int K, size_t* wq_bytes, size_t* s_bytes, size_t* z_bytes);
 
 /*
- * Host packer: logical tensors -> layout ID 1 (host memory to host memory).
+ * Host packer: logical tensors -> layout ID 2 (host memory to host memory).
  *   q  [N][K]    uint8, each 0..15 (the 4-bit weights)
  *   s  [N][K/128] uint16, fp16 bit patterns (any pattern is accepted)
  *   z  [N][K/128] uint8, each 0..15 (the zero points)
@@ -104,7 +107,7 @@ int w4a16_unpack(int N, int K, const void* wq, const void* s_packed, const void*
  * y = W x on the GPU (the hot path).
  *   M: activation rows, 1..8 (a decode token plus speculative drafts);
  *   N, K: weight shape (K multiple of 128); Wq, scales, zeros: device
- *   buffers in layout ID 1; x: device fp16 [M][K]; y: device fp16 [M][N].
+ *   buffers in layout ID 2; x: device fp16 [M][K]; y: device fp16 [M][N].
  * Each output is a fixed-order fp32 sum (no atomics): repeated calls give
  * bit-identical results. Errors: W4A16_EINVAL (shape, NULL, alignment),
  * W4A16_EUNSUPPORTED (M > 8), W4A16_EHIP (launch refused).
@@ -141,7 +144,7 @@ int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq, const voi
  * fp32 [N][K] row-major), computed with the same in-register unpack as the
  * GEMV. The product is exact in fp32 (|q - z| <= 15 needs 4 bits, s has an
  * 11-bit significand), so the result is comparable bit for bit. This is the
- * dequantize entry point of "Custom AWQ Dequantization Kernel" for layout 1.
+ * dequantize entry point of "Custom AWQ Dequantization Kernel" for layout 2.
  * Errors: W4A16_EINVAL (shape, NULL, alignment), W4A16_EHIP.
  */
 int w4a16_dequant_f32(int N, int K, const void* Wq, const void* scales, const void* zeros,

@@ -102,7 +102,7 @@ def w4a16_packed_sizes(N, K):
 
 def w4a16_pack(q, s, z):
     """Host: q uint8 [N][K], s uint16 fp16 bits [N][K/128], z uint8 [N][K/128]
-    -> (wq, s_packed, z_packed) uint8 numpy arrays in layout ID 1."""
+    -> (wq, s_packed, z_packed) uint8 numpy arrays in layout ID 2."""
     q = np.ascontiguousarray(q, dtype=np.uint8)
     s = np.ascontiguousarray(s, dtype=np.uint16)
     z = np.ascontiguousarray(z, dtype=np.uint8)
@@ -130,7 +130,7 @@ def w4a16_unpack(N, K, wq, s_packed, z_packed):
 
 
 def w4a16_gemv(M, N, K, Wq, scales, zeros, x, y, stream=None):
-    """Device: y[M][N] (fp16) = W x[M][K] (fp16) with W in layout ID 1."""
+    """Device: y[M][N] (fp16) = W x[M][K] (fp16) with W in layout ID 2."""
     _check(lib().w4a16_gemv(M, N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
                             _stream(stream)), "w4a16_gemv")
 

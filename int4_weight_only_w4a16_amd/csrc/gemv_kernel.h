@@ -1,0 +1,380 @@
+// The GEMV kernel template and its launchers (included by one translation
+// unit per activation-row count M, so the instantiations compile in parallel).
+//
+// GEMV y = W x with W in layout ID 2 (16-row x 128-column tiles of 1 KiB,
+// each with 32 bytes of scales and 8 bytes of zero points).
+// Per tile a lane issues one 16-byte non-temporal load (32 weights of its
+// row), turns the nibbles into exact fp16 (q - z) pairs in registers and
+// feeds them to the inner product; each group's fp32 sum is scaled once by s.
+// All sums run in a fixed order, so results are bit-identical run to run
+// (the determinism rule of the qengine page, "Learnings").
+#pragma once
+
+#include "w4a16_device.h"
+
+namespace w4a16 {
+namespace dev {
+
+// Workgroup = WAVES waves over R row tiles, t = blockIdx.x + r * gridDim.x
+// (r < R), and one K range blockIdx.y of gridDim.y. The waves take
+// contiguous shares of the range's groups, in rounds of at most SHARE tiles
+// (one round for every shape the launch table picks: a wave then stages its
+// x slice in its private LDS region once and reuses it for all R row tiles,
+// and requests the next row tile's round before computing the current one).
+// The waves' partial sums meet in LDS (double-buffered across row tiles, one
+// barrier per row tile) and are added in wave order.
+// Writes fp16 y[MR][N] when `part` is null, else fp32 part[split][MR][N].
+template <int MR, int WAVES, int SHARE, int ENGINE, int R>
+__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
+    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, const _Float16* __restrict__ x, _Float16* __restrict__ y,
+    float* __restrict__ part, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr bool kGlobalX = ENGINE == kEngineMfmaGlobalX;
+  // Accumulators per lane: MR for dot2; for MFMA the D rows a lane can hold
+  // (4*piece + r) that are activation rows, at most 4.
+  constexpr int kAcc = ENGINE == kEngineDot2 ? MR : (MR < 4 ? MR : 4);
+  constexpr int kXRow = SHARE * kGroup;                  // halves per staged x row of a wave
+  // Per-wave partial sums in LDS: every lane writes its kRows accumulators
+  // (no lane-dependent branch, which would let the compiler move the whole
+  // scale chain, and the scale loads with it, behind the barrier).
+  constexpr int kRows = ENGINE == kEngineDot2 ? MR : (MR < 4 ? MR : 4);
+  constexpr int kRedWave = 4 * kRows * 16;               // floats per wave: [piece][kRows][16]
+  constexpr int kRed = WAVES * kRedWave;                 // floats per reduction buffer
+  float* red = reinterpret_cast<float*>(smem);           // [2][WAVES][4][kRows][16]
+
+  const int G = K / kGroup;
+  const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;
+  const int split = blockIdx.y, splits = gridDim.y;
+  const int g_beg = int(int64_t(split) * G / splits);
+  const int g_end = int(int64_t(split + 1) * G / splits);
+  const int ng = g_end - g_beg;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps share bounds scalar
+  const int piece = lane >> 4;  // which 8-column piece of each 32 columns
+  const int rlane = lane & 15;  // weight row within the tile
+  const uint32_t magic = kMagic1024;
+  const int share_beg = g_beg + (wave * ng) / WAVES;
+  const int share_end = g_beg + ((wave + 1) * ng) / WAVES;
+  const int mm = rlane < MR ? rlane : MR - 1;  // activation row feeding A-operand row rlane
+  _Float16* xw = reinterpret_cast<_Float16*>(smem + 2 * kRed * sizeof(float)) +
+                 (kGlobalX ? 0 : wave * MR * kXRow);  // this wave's x slice [MR][SHARE*128]
+  int parity = 0;
+
+  // Copy x[:, 128*g0 : 128*(g0+n)) into this wave's LDS slice (synchronous).
+  auto stage_x = [&](int g0, int n) {
+    if constexpr (!kGlobalX) {
+      const int xchunks = n * (kGroup / 8), xtotal = MR * xchunks;
+      for (int c = lane; c < xtotal; c += 64) {
+        const int m = c / xchunks, cc = c - m * xchunks;
+        *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) =
+            *reinterpret_cast<const u32x4*>(x + int64_t(m) * K + int64_t(g0) * kGroup + cc * 8);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
+  };
+
+  // A round = SHARE tiles of one row tile. load_round() requests them all
+  // (indices past the share's end are clamped to its last tile: always in
+  // bounds, discarded later) with their scales and zero bytes as
+  // straight-line code; compute_round() then uses them in request order, so
+  // each wait is for exactly the tile about to be used (loads retire in
+  // order). Every tile is computed -- a branch would let the compiler sink a
+  // tile's load next to its use -- and the clamped duplicates are discarded
+  // by a select.
+  struct Round {
+    u32x4 w[SHARE];
+    uint32_t sv[SHARE], zb[SHARE];
+    half8_t xa[kGlobalX ? SHARE : 1][4];
+  };
+  auto load_round = [&](Round& r, const u32x4* wlane, const uint16_t* srow, const uint8_t* zrow, int g0, int n) {
+#pragma unroll
+    for (int u = 0; u < SHARE; ++u) {
+      const int gg = g0 + min(u, n - 1);
+      r.w[u] = __builtin_nontemporal_load(wlane + int64_t(gg) * (kTileBytes / 16));
+      r.sv[u] = srow[gg * kTileRows];
+      r.zb[u] = zrow[gg * (kTileRows / 2)];
+      if constexpr (kGlobalX) {
+        const _Float16* xl = x + int64_t(mm) * K + int64_t(gg) * kGroup + 8 * piece;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) r.xa[u][kb] = *reinterpret_cast<const half8_t*>(xl + 32 * kb);
+      }
+    }
+  };
+  auto compute_round = [&](const Round& r, int g0, int n, float (&acc)[kAcc]) {
+    // The staged x slice does not change between row tiles, so the compiler
+    // would reuse every x read across row tiles and keep the whole slice in
+    // registers (100+ VGPRs, a quarter of the occupancy). An opaque copy of
+    // the lane's offset keeps the reads next to their use. (The offset, not
+    // the pointer: an opaque pointer would lose its LDS address space.)
+    int xoff = 8 * piece;
+    asm volatile("" : "+v"(xoff));
+    const _Float16* xbase = xw + xoff;
+    // MFMA: each tile's group sums stay in their own registers and are scaled
+    // after the last tile, so a tile's unpack never waits for the previous
+    // tile's MFMA chain to finish (same fp32 operations, same order).
+    f32x4 dsave[ENGINE == kEngineDot2 ? 1 : SHARE];
+    float ssave[ENGINE == kEngineDot2 ? 1 : SHARE];
+#pragma unroll
+    for (int u = 0; u < SHARE; ++u) {
+      const bool valid = u < n;
+      __builtin_amdgcn_sched_barrier(0);  // keep tiles in request order
+      // Pass this tile's registers through an (empty) volatile asm: the
+      // asm statements stay in program order, and nothing computed from the
+      // tile can move above its asm, so no tile's unpack is hoisted ahead of
+      // earlier tiles (which would wait for every load at once).
+      u32x4 wt = r.w[u];
+      uint32_t zt = r.zb[u], st = r.sv[u];
+      asm volatile("" : "+v"(wt), "+v"(zt), "+v"(st));
+      const ZeroPairs zp = zero_pairs((zt >> ((rlane & 1) * 4)) & 15u);
+      const float s = half_bits_to_float(st);
+      const _Float16* xg = xbase + u * kGroup;
+      if constexpr (ENGINE == kEngineDot2) {
+        float dot[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) dot[m] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          half2_t p[4];
+          unpack8(wt[kb], magic, zp, p);
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            const u32x4 xq = *reinterpret_cast<const u32x4*>(xg + m * kXRow + 32 * kb);
+            dot[m] = __builtin_amdgcn_fdot2(p[0], as_h2(xq.x), dot[m], false);
+            dot[m] = __builtin_amdgcn_fdot2(p[1], as_h2(xq.y), dot[m], false);
+            dot[m] = __builtin_amdgcn_fdot2(p[2], as_h2(xq.z), dot[m], false);
+            dot[m] = __builtin_amdgcn_fdot2(p[3], as_h2(xq.w), dot[m], false);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[m] = valid ? __builtin_fmaf(dot[m], s, acc[m]) : acc[m];
+      } else {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          half2_t p[4];
+          unpack8(wt[kb], magic, zp, p);
+          const half8_t bw = {p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
+          half8_t ax;
+          if constexpr (kGlobalX)
+            ax = r.xa[u][kb];
+          else
+            ax = *reinterpret_cast<const half8_t*>(xg + mm * kXRow + 32 * kb);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, d, 0, 0, 0);
+        }
+        dsave[u] = d;
+        ssave[u] = s;
+      }
+    }
+    if constexpr (ENGINE != kEngineDot2) {
+#pragma unroll
+      for (int u = 0; u < SHARE; ++u) {
+        const bool valid = u < n;
+#pragma unroll
+        for (int r2 = 0; r2 < kAcc; ++r2)
+          acc[r2] = valid ? __builtin_fmaf(dsave[u][r2], ssave[u], acc[r2]) : acc[r2];
+      }
+    }
+  };
+
+  const int share_n = share_end - share_beg;
+  const bool one_round = share_n <= SHARE;
+
+  // Cross-wave sum of one row tile: each wave's partials go to LDS and the
+  // first threads add them in wave order. One barrier per row tile: the next
+  // tile writes the other buffer, and the tile after that is behind this
+  // tile's next barrier. The sums stay in registers and are stored after the
+  // last tile, so no store sits between a weight request and its use.
+  constexpr int kOut = (MR * 16 + WAVES * 64 - 1) / (WAVES * 64);  // outputs per thread per tile
+  auto reduce_tile = [&](float (&acc)[kAcc], float (&out)[kOut]) {
+    float* rb = red + parity * kRed;
+    if constexpr (ENGINE == kEngineDot2) {
+      // Lanes l, l^16, l^32, l^48 hold the same row: fold them.
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        float v = acc[m];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[m] = v;
+      }
+    }
+    // MFMA: lane l holds D[4*(l/16) + r][l%16], i.e. activation row
+    // 4*piece + r of weight row rlane. Dot2: every piece holds the full sums.
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) rb[wave * kRedWave + (piece * kRows + r) * 16 + rlane] = acc[r];
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int idx = min(tid + j * WAVES * 64, MR * 16 - 1);  // one wave has fewer lanes than 8 x 16 outputs
+      const int m = idx >> 4, i = idx & 15;
+      const int slot = ENGINE == kEngineDot2 ? m * 16 + i : ((m >> 2) * kRows + (m & 3)) * 16 + i;
+      float sum = rb[slot];
+#pragma unroll
+      for (int w2 = 1; w2 < WAVES; ++w2) sum += rb[w2 * kRedWave + slot];
+      out[j] = sum;
+    }
+    parity ^= 1;
+  };
+  auto store_tile = [&](int64_t t, const float (&out)[kOut]) {
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int idx = tid + j * WAVES * 64;
+      const int m = idx >> 4, i = idx & 15;
+      const int64_t nn = t * kTileRows + i;
+      if (idx < MR * 16 && nn < N) {
+        if (part)
+          part[(int64_t(split) * MR + m) * N + nn] = out[j];
+        else
+          y[int64_t(m) * N + nn] = (_Float16)out[j];
+      }
+    }
+  };
+
+  struct TilePtrs {
+    const u32x4* wlane;
+    const uint16_t* srow;
+    const uint8_t* zrow;
+  };
+  auto tile_ptrs = [&](int64_t t) {  // t < row tiles: always valid memory
+    const int64_t q0 = t * G;           // index of tile (t, 0)
+    return TilePtrs{reinterpret_cast<const u32x4*>(wq + q0 * kTileBytes) + lane,
+                    scales + q0 * kTileRows + rlane, zeros + q0 * (kTileRows / 2) + (rlane >> 1)};
+  };
+
+  // This workgroup's row tiles: t0 + r * gridDim.x for r < R (the host
+  // launches ceil(row tiles / R) workgroups, so t0 is in range). Tiles past
+  // the end are computed on a clamped (valid) tile and never stored.
+  const int64_t t0 = blockIdx.x;
+  auto tile_of = [&](int r) { return t0 + int64_t(r) * gridDim.x; };
+  auto clamp_tile = [&](int64_t t) { return t < row_tiles ? t : row_tiles - 1; };
+  float sums[R][kOut];
+
+  if (one_round && share_n > 0) {
+    // Straight-line software pipeline over the R row tiles: the next tile's
+    // round is requested before the current one is computed, in two register
+    // sets. No branch and no store on this path, so every wait is exact.
+    Round rr[2];
+    {
+      const TilePtrs p = tile_ptrs(t0);
+      if constexpr (!kGlobalX) {
+        // x requests go out just ahead of the first weight requests, so the
+        // wait before the LDS store is for x alone; the staged slice then
+        // serves all of this workgroup's row tiles.
+        constexpr int kXSteps = (MR * SHARE * 16 + 63) / 64;
+        const int xchunks = share_n * (kGroup / 8), xtotal = MR * xchunks;
+        u32x4 xv[kXSteps];
+#pragma unroll
+        for (int j = 0; j < kXSteps; ++j) {  // clamped: unconditional, in bounds
+          const int c = min(lane + 64 * j, xtotal - 1);
+          const int m = c / xchunks, cc = c - m * xchunks;
+          xv[j] = *reinterpret_cast<const u32x4*>(x + int64_t(m) * K + int64_t(share_beg) * kGroup + cc * 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_round(rr[0], p.wlane, p.srow, p.zrow, share_beg, share_n);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kXSteps; ++j) {  // clamped steps rewrite the last chunk with its own data
+          const int c = min(lane + 64 * j, xtotal - 1);
+          const int m = c / xchunks, cc = c - m * xchunks;
+          *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) = xv[j];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      } else {
+        load_round(rr[0], p.wlane, p.srow, p.zrow, share_beg, share_n);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r + 1 < R) {
+        const TilePtrs p = tile_ptrs(clamp_tile(tile_of(r + 1)));
+        load_round(rr[(r + 1) & 1], p.wlane, p.srow, p.zrow, share_beg, share_n);
+      }
+      float acc[kAcc];
+#pragma unroll
+      for (int i = 0; i < kAcc; ++i) acc[i] = 0.f;
+      compute_round(rr[r & 1], share_beg, share_n, acc);
+      reduce_tile(acc, sums[r]);
+    }
+  } else {
+    // Long K (several rounds per share, x restaged per round) or an empty
+    // share (a K range with fewer groups than waves): plain loop.
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const TilePtrs p = tile_ptrs(clamp_tile(tile_of(r)));
+      float acc[kAcc];
+#pragma unroll
+      for (int i = 0; i < kAcc; ++i) acc[i] = 0.f;
+      for (int g0 = share_beg; g0 < share_end; g0 += SHARE) {
+        const int n = min(SHARE, share_end - g0);
+        stage_x(g0, n);
+        Round rd;
+        load_round(rd, p.wlane, p.srow, p.zrow, g0, n);
+        compute_round(rd, g0, n, acc);
+      }
+      reduce_tile(acc, sums[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) store_tile(tile_of(r), sums[r]);
+}
+
+template <int MR, int WAVES, int SHARE, int ENGINE>
+constexpr size_t lds_for() {
+  return reduction_lds_bytes(MR, WAVES, ENGINE) +
+         (ENGINE == kEngineMfmaGlobalX ? 0 : size_t(WAVES) * MR * SHARE * kGroup * 2);
+}
+
+template <int MR, int WAVES, int SHARE, int ENGINE, int R>
+hipError_t launch_typed(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
+                        const void* zeros, const void* x, void* y, float* partials, hipStream_t stream) {
+  const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;
+  const int64_t grid = (row_tiles + R - 1) / R;
+  constexpr size_t lds = lds_for<MR, WAVES, SHARE, ENGINE>();
+  hipLaunchKernelGGL((gemv_kernel<MR, WAVES, SHARE, ENGINE, R>), dim3(unsigned(grid), unsigned(plan.splits)),
+                     dim3(WAVES * 64), lds, stream, static_cast<const uint8_t*>(wq),
+                     static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
+                     static_cast<const _Float16*>(x), static_cast<_Float16*>(y), partials, N, K);
+  return hipGetLastError();
+}
+
+template <int MR, int ENGINE>
+hipError_t launch_shape(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
+                        const void* zeros, const void* x, void* y, float* partials, hipStream_t stream) {
+#define W4A16_CASE(W, S, RR)                                                                            \
+  if constexpr (instantiated(MR, W, S, ENGINE, RR)) {                                                  \
+    if (plan.waves == W && plan.share == S && plan.tiles_per_wg == RR)                                 \
+      return launch_typed<MR, W, S, ENGINE, RR>(N, K, plan, wq, scales, zeros, x, y, partials, stream); \
+  }
+#define W4A16_SHARES(W, RR)                                                                             \
+  W4A16_CASE(W, 2, RR) W4A16_CASE(W, 3, RR) W4A16_CASE(W, 4, RR) W4A16_CASE(W, 5, RR) W4A16_CASE(W, 7, RR) \
+  W4A16_CASE(W, 8, RR) W4A16_CASE(W, 10, RR)
+  W4A16_SHARES(1, 1) W4A16_SHARES(2, 1) W4A16_SHARES(4, 1) W4A16_SHARES(8, 1) W4A16_SHARES(16, 1)
+  W4A16_SHARES(4, 2) W4A16_SHARES(8, 2) W4A16_SHARES(4, 3) W4A16_SHARES(8, 3)
+#undef W4A16_SHARES
+#undef W4A16_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int MR>
+hipError_t launch_engine(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
+                         const void* zeros, const void* x, void* y, float* partials, hipStream_t stream) {
+  switch (plan.engine) {
+    case kEngineMfma:
+      return launch_shape<MR, kEngineMfma>(N, K, plan, wq, scales, zeros, x, y, partials, stream);
+    case kEngineMfmaGlobalX:
+      return launch_shape<MR, kEngineMfmaGlobalX>(N, K, plan, wq, scales, zeros, x, y, partials, stream);
+    case kEngineDot2:
+      if constexpr (MR == 1)
+        return launch_shape<MR, kEngineDot2>(N, K, plan, wq, scales, zeros, x, y, partials, stream);
+      return hipErrorInvalidValue;
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dev
+}  // namespace w4a16

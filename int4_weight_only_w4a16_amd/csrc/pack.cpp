@@ -1,4 +1,4 @@
-// Host packer and unpacker for layout ID 1 (declared in include/w4a16.h).
+// Host packer and unpacker for layout ID 2 (declared in include/w4a16.h).
 //
 // A tile is 16 rows x one group of 128 columns, 1024 bytes: 64 lanes of
 // 16 bytes, lane l carrying row l%16 and four 8-column pieces
@@ -13,6 +13,10 @@
 // Kernel", Part 2). With it, masking a word with 0x000F000F (and 0x00F000F0,
 // then both again after a shift by 8) yields the fp16 pairs (w0,w1),
 // (w2,w3), (w4,w5), (w6,w7) in column order, which is what the kernels use.
+//
+// The 16 scales and 16 zero points of a tile sit next to each other in tile
+// order (32 and 8 bytes), so the scale and zero requests of a wave touch one
+// cache line each instead of one line per row.
 #include <cstring>
 
 #include "w4a16.h"
@@ -84,15 +88,14 @@ extern "C" int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, con
   std::memset(sp, 0, geo.s_bytes());
   std::memset(zp, 0, geo.z_bytes());
   for (int64_t n = 0; n < N; ++n) {
-    uint8_t* srow = sp + 2 * n * geo.groups_padded;
-    uint8_t* zrow = zp + n * geo.groups_padded / 2;
     for (int64_t g = 0; g < geo.groups; ++g) {
+      const int64_t e = geo.meta_index(n, g);
       const uint16_t sv = s[n * geo.groups + g];
-      srow[2 * g] = uint8_t(sv);
-      srow[2 * g + 1] = uint8_t(sv >> 8);
+      sp[2 * e] = uint8_t(sv);
+      sp[2 * e + 1] = uint8_t(sv >> 8);
       const uint8_t zv = z[n * geo.groups + g];
       bad |= zv & ~15u;
-      zrow[g >> 1] |= uint8_t((zv & 15u) << ((g & 1) * 4));
+      zp[e >> 1] |= uint8_t((zv & 15u) << ((n & 1) * 4));
     }
   }
   return bad ? W4A16_EINVAL : W4A16_OK;
@@ -122,11 +125,10 @@ extern "C" int w4a16_unpack(int N, int K, const void* wq_in, const void* s_packe
     }
   }
   for (int64_t n = 0; n < N; ++n) {
-    const uint8_t* srow = sp + 2 * n * geo.groups_padded;
-    const uint8_t* zrow = zp + n * geo.groups_padded / 2;
     for (int64_t g = 0; g < geo.groups; ++g) {
-      s[n * geo.groups + g] = uint16_t(srow[2 * g] | (srow[2 * g + 1] << 8));
-      z[n * geo.groups + g] = uint8_t((zrow[g >> 1] >> ((g & 1) * 4)) & 15u);
+      const int64_t e = geo.meta_index(n, g);
+      s[n * geo.groups + g] = uint16_t(sp[2 * e] | (sp[2 * e + 1] << 8));
+      z[n * geo.groups + g] = uint8_t((zp[e >> 1] >> ((n & 1) * 4)) & 15u);
     }
   }
   return W4A16_OK;

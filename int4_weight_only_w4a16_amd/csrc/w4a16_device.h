@@ -1,0 +1,82 @@
+// Device helpers shared by the HIP kernels of libw4a16.so (gfx950): packed
+// fp16 types, the in-register unpack of one packed word, and an LDS-only
+// workgroup barrier.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+namespace dev {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kMagic1024 = 0x64006400u;  // fp16 pair (1024, 1024)
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+// fp16 pairs (1024 + z, 1024 + z) and (64 + z, 64 + z) for a zero point z.
+// 1024 + z has bits 0x6400 | z (spacing 1 in [1024, 2048)); 64 + z has bits
+// 0x5400 | (z << 4) (spacing 1/16 in [64, 128)).
+struct ZeroPairs {
+  half2_t z1024, z64;
+};
+
+__device__ __forceinline__ ZeroPairs zero_pairs(uint32_t z) {
+  return {as_h2((0x6400u | z) * 0x00010001u), as_h2((0x5400u | (z << 4)) * 0x00010001u)};
+}
+
+// (w & mask) | magic in one VALU op. gfx9 VOP3 has no literal operand, so the
+// compiler splits this into v_and_b32 + v_or_b32 with literals; with the mask
+// in an SGPR and the magic in a VGPR a single v_and_or_b32 does it.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+  return r;
+}
+
+// Eight weights of one ValueShuffle word -> (q - z) as four fp16 pairs in
+// column order (w0,w1), (w2,w3), (w4,w5), (w6,w7). OR-ing a nibble into the
+// mantissa of 1024.0 gives 1024 + q exactly; a nibble four bits higher gives
+// 1024 + 16q, and (1024 + 16q)/16 - (64 + z) = q - z. Every step is exact in
+// fp16 (all values are integers or sixteenths below 2048).
+__device__ __forceinline__ void unpack8(uint32_t w, uint32_t magic, const ZeroPairs& zp, half2_t p[4]) {
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t w8 = w >> 8;
+  p[0] = as_h2(and_or(w, 0x000F000Fu, magic)) - zp.z1024;
+  p[1] = __builtin_elementwise_fma(as_h2(and_or(w, 0x00F000F0u, magic)), sixteenth, -zp.z64);
+  p[2] = as_h2(and_or(w8, 0x000F000Fu, magic)) - zp.z1024;
+  p[3] = __builtin_elementwise_fma(as_h2(and_or(w8, 0x00F000F0u, magic)), sixteenth, -zp.z64);
+}
+
+// Workgroup barrier that orders LDS only. __syncthreads() also fences global
+// memory, which makes every wave wait for all of its outstanding loads
+// (vmcnt(0)) -- including weight tiles requested ahead -- before the barrier.
+// No thread here communicates through global memory, so an LDS-scope fence
+// (lgkmcnt only) is all the barriers need.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Inner-product engines. kEngineDot2: v_dot2_f32_f16 on the VALU, lane-private
+// partial sums over 8-column pieces. kEngineMfma*: v_mfma_f32_16x16x32_f16
+// with the activations as the A operand (row m of A = x[m]; rows >= M repeat
+// the last x row and are ignored) and the unpacked weights as the B operand
+// (column j of B = weight row j of the tile), so D[m][j] = sum_k x[m][k]
+// w[j][k]; the multiply-adds leave the VALU, which then only unpacks. The
+// A operand comes from LDS (kEngineMfma) or, when x of the K range does not
+// fit in LDS, straight from global memory with the weights of the batch
+// (kEngineMfmaGlobalX).
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+}  // namespace dev
+}  // namespace w4a16

@@ -7,28 +7,31 @@
 
 namespace w4a16 {
 
-constexpr int kLayoutId = 1;
+constexpr int kLayoutId = 2;
 constexpr int kGroup = 128;
 constexpr int kTileRows = 16;
 constexpr int kTileBytes = 1024;  // 16 rows x 128 weights x 4 bits
 
-// Geometry of the layout-ID-1 buffers of an N x K matrix.
+// Geometry of the layout-ID-2 buffers of an N x K matrix. Tile (t, g) is
+// rows 16t..16t+15 of group g; all three buffers list tiles in the order
+// t*G + g: 1024 weight bytes, 16 fp16 scales and 8 zero-point bytes each.
 struct Geometry {
-  int64_t rows, cols, row_tiles, groups, groups_padded;
+  int64_t rows, cols, row_tiles, groups;
   Geometry(int64_t N, int64_t K)
-      : rows(N),
-        cols(K),
-        row_tiles((N + kTileRows - 1) / kTileRows),
-        groups(K / kGroup),
-        groups_padded((K / kGroup + 7) / 8 * 8) {}
+      : rows(N), cols(K), row_tiles((N + kTileRows - 1) / kTileRows), groups(K / kGroup) {}
   size_t wq_bytes() const { return size_t(row_tiles) * size_t(groups) * kTileBytes; }
-  size_t s_bytes() const { return size_t(row_tiles) * kTileRows * size_t(groups_padded) * 2; }
-  size_t z_bytes() const { return size_t(row_tiles) * kTileRows * size_t(groups_padded) / 2; }
+  size_t s_bytes() const { return size_t(row_tiles) * kTileRows * size_t(groups) * 2; }
+  size_t z_bytes() const { return size_t(row_tiles) * kTileRows * size_t(groups) / 2; }
+  // Scale element of row n, group g (the zero point is nibble n&1 of byte
+  // meta_index/2).
+  int64_t meta_index(int64_t n, int64_t g) const {
+    return ((n / kTileRows) * groups + g) * kTileRows + n % kTileRows;
+  }
 };
 
 // Inner-product engine of the GEMV kernel.
 enum Engine : int {
-  kEngineDot2 = 0,      // v_dot2_f32_f16 on the VALU (M <= 2), x staged in LDS
+  kEngineDot2 = 0,      // v_dot2_f32_f16 on the VALU (M = 1), x staged in LDS
   kEngineMfma = 1,      // v_mfma_f32_16x16x32_f16, x staged in LDS
   kEngineMfmaGlobalX = 2  // v_mfma_f32_16x16x32_f16, x read straight from global memory
 };
@@ -39,8 +42,29 @@ struct LaunchPlan {
   int waves;   // waves per workgroup: 1, 2, 4, 8 or 16
   int share;   // tiles a wave requests at once (2, 4, 8 or 12); longer shares take several rounds
   int splits;  // K ranges (gridDim.y); 1 for the plain GEMV
-  int tiles_per_wg;  // row tiles per workgroup (gridDim.x = ceil(row tiles / this))
+  int tiles_per_wg;  // row tiles per workgroup, 1..3 (gridDim.x = ceil(row tiles / this))
 };
+
+// Instantiated (waves, share, row tiles per workgroup) per engine and M:
+// those that fit in registers without spilling. Several row tiles per
+// workgroup (R > 1, software-pipelined) only for the MFMA engine with x in
+// LDS; the VALU dot2 engine only for M = 1.
+constexpr bool instantiated(int mr, int waves, int share, int engine, int r) {
+  if (r > 1)
+    return engine == kEngineMfma && (waves == 4 || waves == 8) &&
+           (share == 4 || share == 5 || share == 7 || share == 8) && !(waves == 8 && share == 8) &&
+           !(mr >= 3 && share >= 7);
+  if (engine == kEngineMfmaGlobalX) return waves == 16 ? share <= 3 : share <= 4;
+  if (engine == kEngineDot2) return mr == 1 && !(waves == 16 && share >= 4) && !(waves == 8 && share >= 10);
+  if (waves == 16) return mr <= 2 ? share <= 10 : share <= 5;
+  return !(waves == 8 && mr >= 3 && share >= 8);
+}
+
+// LDS of the cross-wave reduction: two buffers of [waves][4 pieces][rows][16]
+// floats, rows = accumulators per lane (M for dot2, min(M, 4) for MFMA).
+constexpr size_t reduction_lds_bytes(int mr, int waves, int engine) {
+  return 2 * size_t(waves) * 4 * (engine == kEngineDot2 ? mr : (mr < 4 ? mr : 4)) * 16 * sizeof(float);
+}
 
 // Largest dynamic LDS a GEMV workgroup may use.
 constexpr size_t kMaxLdsBytes = 64 * 1024;
@@ -54,6 +78,12 @@ bool plan_supported(int M, int K, const LaunchPlan& plan);
 // Kernel launchers (w4a16_kernels.hip). They return a hipError_t value as int.
 int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
                 const void* zeros, const void* x, void* y, float* partials, void* stream);
+#define W4A16_DECLARE_M(MR)                                                                            \
+  int launch_gemv_m##MR(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales, \
+                        const void* zeros, const void* x, void* y, float* partials, void* stream);
+W4A16_DECLARE_M(1) W4A16_DECLARE_M(2) W4A16_DECLARE_M(3) W4A16_DECLARE_M(4)
+W4A16_DECLARE_M(5) W4A16_DECLARE_M(6) W4A16_DECLARE_M(7) W4A16_DECLARE_M(8)
+#undef W4A16_DECLARE_M
 int launch_splitk_reduce(int M, int N, int splits, const float* partials, void* y, void* stream);
 int launch_dequant(int N, int K, const void* wq, const void* scales, const void* zeros, float* out,
                    void* stream);

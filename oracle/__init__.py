@@ -72,7 +72,7 @@ class Oracle:
     def num_threads(self):
         return self.lib.or_num_threads()
 
-    # -- layout ID 1 --------------------------------------------------------
+    # -- layout ID 2 --------------------------------------------------------
     def layout_sizes(self, N, K):
         out = np.zeros(3, dtype=np.int64)
         if self.lib.or_layout_sizes(N, K, out.ctypes.data):

@@ -23,23 +23,26 @@
  *  - fp16 values are decoded and encoded (round to nearest, ties to even)
  *    from the IEEE-754 binary16 definition, written out below.
  *
- * The packed layout (ID 1) is this project's own device layout; pack/unpack
+ * The packed layout (ID 2) is this project's own device layout; pack/unpack
  * here follow its written definition element by element. The nibble order
  * inside a 32-bit word is the interleave of "Building an LLM Inference
  * Runtime", Bug #3 (the ValueShuffle shift table), which is also the
  * interleaved order of "Custom AWQ Dequantization Kernel", Part 2.
  *
- * Layout ID 1, for an N x K matrix (K a multiple of 128, G = K/128):
- *   NP = N rounded up to 16, GP = G rounded up to 8, rows n >= N are zero.
+ * Layout ID 2, for an N x K matrix (K a multiple of 128, G = K/128):
+ *   NP = N rounded up to 16, rows n >= N are zero. Tile (t, g) covers rows
+ *   16t .. 16t+15 and group g; all three buffers list tiles in the order
+ *   q = t*G + g.
  *   weights: NP/16 * G tiles of 1024 bytes; tile (t, g) starts at byte
  *     (t*G + g)*1024. Its 32-bit little-endian word (lane, kb), lane in
  *     [0,64), kb in [0,4), sits at byte lane*16 + kb*4 of the tile and holds
  *     row 16t + lane%16, columns k = 128g + 32kb + 8*(lane/16) + j, j in
  *     [0,8); weight j occupies bits 4*SLOT[j] .. 4*SLOT[j]+3,
  *     SLOT = {0,4,1,5,2,6,3,7}.
- *   scales: fp16 bits, element n*GP + g; padding elements are 0.
- *   zeros:  4-bit values, row n group g in byte n*GP/2 + g/2, low nibble for
- *     even g, high nibble for odd g; padding nibbles are 0.
+ *   scales: 16 fp16 values per tile; row n group g is element
+ *     (t*G + g)*16 + n%16, t = n/16.
+ *   zeros: 8 bytes per tile; row n group g is in byte (t*G + g)*8 + (n%16)/2,
+ *     low nibble for even n, high nibble for odd n.
  */
 #include <math.h>
 #include <stdint.h>
@@ -125,7 +128,7 @@ void or_f64_to_f16_array(const double* v, uint16_t* out, int64_t n) {
   for (int64_t i = 0; i < n; i++) out[i] = or_f64_to_f16(v[i]);
 }
 
-/* ------------------------------------------------------ layout ID 1 --- */
+/* ------------------------------------------------------ layout ID 2 --- */
 
 static const int SLOT[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 
@@ -135,15 +138,15 @@ static int shape_ok(int64_t N, int64_t K) {
   return N >= 0 && K >= OR_GROUP && K % OR_GROUP == 0;
 }
 
-int or_layout_id(void) { return 1; }
+int or_layout_id(void) { return 2; }
 
 /* out[0] = weight bytes, out[1] = scale bytes, out[2] = zero bytes */
 int or_layout_sizes(int64_t N, int64_t K, int64_t* out) {
   if (!shape_ok(N, K)) return -1;
-  int64_t NP = round_up(N, 16), G = K / OR_GROUP, GP = round_up(G, 8);
+  int64_t NP = round_up(N, 16), G = K / OR_GROUP;
   out[0] = NP * K / 2;
-  out[1] = NP * GP * 2;
-  out[2] = NP * GP / 2;
+  out[1] = NP * G * 2;
+  out[2] = NP * G / 2;
   return 0;
 }
 
@@ -173,14 +176,20 @@ static int weight_at(const uint8_t* wq, int64_t n, int64_t k, int64_t G) {
   return (int)((read_u32le(wq + wb) >> sh) & 15u);
 }
 
-static uint16_t scale_at(const uint8_t* sp, int64_t n, int64_t g, int64_t GP) {
-  const uint8_t* p = sp + 2 * (n * GP + g);
+/* Element index of (n, g) in the scale buffer; the zero buffer holds half
+ * as many bytes per tile (two nibbles per byte). */
+static int64_t scale_index(int64_t n, int64_t g, int64_t G) {
+  return ((n / 16) * G + g) * 16 + n % 16;
+}
+
+static uint16_t scale_at(const uint8_t* sp, int64_t n, int64_t g, int64_t G) {
+  const uint8_t* p = sp + 2 * scale_index(n, g, G);
   return (uint16_t)(p[0] | (p[1] << 8));
 }
 
-static int zero_at(const uint8_t* zp, int64_t n, int64_t g, int64_t GP) {
-  uint8_t b = zp[n * GP / 2 + g / 2];
-  return (g & 1) ? (b >> 4) : (b & 15);
+static int zero_at(const uint8_t* zp, int64_t n, int64_t g, int64_t G) {
+  uint8_t b = zp[scale_index(n, g, G) / 2];
+  return (n & 1) ? (b >> 4) : (b & 15);
 }
 
 /* q: [N][K] values 0..15; s: [N][G] fp16 bits; z: [N][G] values 0..15.
@@ -189,7 +198,7 @@ int or_pack(int64_t N, int64_t K, const uint8_t* q, const uint16_t* s, const uin
             uint8_t* wq, uint8_t* sp, uint8_t* zp) {
   int64_t sz[3];
   if (or_layout_sizes(N, K, sz)) return -1;
-  int64_t G = K / OR_GROUP, GP = round_up(G, 8);
+  int64_t G = K / OR_GROUP;
   memset(wq, 0, (size_t)sz[0]);
   memset(sp, 0, (size_t)sz[1]);
   memset(zp, 0, (size_t)sz[2]);
@@ -203,11 +212,12 @@ int or_pack(int64_t N, int64_t K, const uint8_t* q, const uint16_t* s, const uin
     }
     for (int64_t g = 0; g < G; g++) {
       uint16_t sv = s[n * G + g];
-      sp[2 * (n * GP + g)] = (uint8_t)(sv & 0xFF);
-      sp[2 * (n * GP + g) + 1] = (uint8_t)(sv >> 8);
+      int64_t e = scale_index(n, g, G);
+      sp[2 * e] = (uint8_t)(sv & 0xFF);
+      sp[2 * e + 1] = (uint8_t)(sv >> 8);
       uint8_t zv = z[n * G + g];
       if (zv > 15) return -1;
-      zp[n * GP / 2 + g / 2] |= (uint8_t)((g & 1) ? (zv << 4) : zv);
+      zp[e / 2] |= (uint8_t)((n & 1) ? (zv << 4) : zv);
     }
   }
   return 0;
@@ -216,12 +226,12 @@ int or_pack(int64_t N, int64_t K, const uint8_t* q, const uint16_t* s, const uin
 int or_unpack(int64_t N, int64_t K, const uint8_t* wq, const uint8_t* sp, const uint8_t* zp,
               uint8_t* q, uint16_t* s, uint8_t* z) {
   if (!shape_ok(N, K)) return -1;
-  int64_t G = K / OR_GROUP, GP = round_up(G, 8);
+  int64_t G = K / OR_GROUP;
   for (int64_t n = 0; n < N; n++) {
     for (int64_t k = 0; k < K; k++) q[n * K + k] = (uint8_t)weight_at(wq, n, k, G);
     for (int64_t g = 0; g < G; g++) {
-      s[n * G + g] = scale_at(sp, n, g, GP);
-      z[n * G + g] = (uint8_t)zero_at(zp, n, g, GP);
+      s[n * G + g] = scale_at(sp, n, g, G);
+      z[n * G + g] = (uint8_t)zero_at(zp, n, g, G);
     }
   }
   return 0;
@@ -294,13 +304,13 @@ int or_gemv(int64_t M, int64_t N, int64_t K, const uint8_t* q, const uint16_t* s
   return 0;
 }
 
-/* Same product with the weights given in layout ID 1: every element is
+/* Same product with the weights given in layout ID 2: every element is
  * located through the layout definition, then the same formula applies. */
 int or_gemv_packed(int64_t M, int64_t N, int64_t K, const uint8_t* wq, const uint8_t* sp,
                    const uint8_t* zp, const uint16_t* x, double* ref, double* absref) {
   if (M < 0 || !shape_ok(N, K)) return -1;
   if (M == 0 || N == 0) return 0;
-  int64_t G = K / OR_GROUP, GP = round_up(G, 8);
+  int64_t G = K / OR_GROUP;
   double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
   if (!xd) return -2;
   for (int64_t i = 0; i < M * K; i++) xd[i] = or_f16_to_f64(x[i]);
@@ -310,7 +320,7 @@ int or_gemv_packed(int64_t M, int64_t N, int64_t K, const uint8_t* wq, const uin
       double acc = 0.0, aacc = 0.0;
       for (int64_t k = 0; k < K; k++) {
         int64_t g = group_of(k);
-        double w = dequant_one(weight_at(wq, n, k, G), zero_at(zp, n, g, GP), scale_at(sp, n, g, GP));
+        double w = dequant_one(weight_at(wq, n, k, G), zero_at(zp, n, g, G), scale_at(sp, n, g, G));
         double xv = xd[m * K + k];
         acc += w * xv;
         aacc += fabs(w * xv);
@@ -329,7 +339,7 @@ int or_gemv_packed_rows(int64_t M, int64_t N, int64_t K, const uint8_t* wq, cons
                         const uint8_t* zp, const uint16_t* x, const int64_t* rows, int64_t nrows,
                         double* ref, double* absref) {
   if (M < 0 || !shape_ok(N, K)) return -1;
-  int64_t G = K / OR_GROUP, GP = round_up(G, 8);
+  int64_t G = K / OR_GROUP;
   for (int64_t r = 0; r < nrows; r++)
     if (rows[r] < 0 || rows[r] >= N) return -1;
   double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K + 1));
@@ -342,7 +352,7 @@ int or_gemv_packed_rows(int64_t M, int64_t N, int64_t K, const uint8_t* wq, cons
       double acc = 0.0, aacc = 0.0;
       for (int64_t k = 0; k < K; k++) {
         int64_t g = group_of(k);
-        double w = dequant_one(weight_at(wq, n, k, G), zero_at(zp, n, g, GP), scale_at(sp, n, g, GP));
+        double w = dequant_one(weight_at(wq, n, k, G), zero_at(zp, n, g, G), scale_at(sp, n, g, G));
         double xv = xd[m * K + k];
         acc += w * xv;
         aacc += fabs(w * xv);

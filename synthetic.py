@@ -75,24 +75,23 @@ SINGLE_896 = ("single_896", 896, 896)
 
 
 def device_packed_weights(N, K, seed, tensor_id, device):
-    """Weights drawn directly in layout-ID-1 form on the GPU (for large
+    """Weights drawn directly in layout-ID-2 form on the GPU (for large
     benchmark sets, where drawing logical q on the host would dominate).
 
     Same law as packing weights(): packed nibbles of uniform q (and z) are
     uniform random bytes; scales are fp16(|N(0, 0.02)| + 1e-3) in every
-    [row][group] slot, padding slots included (they are never read).
+    (row, group) slot, padding rows included (their outputs are never stored).
     Uses torch's seeded device generator. Returns (wq, scales, zeros) as
     uint8/int16/uint8 torch tensors of the packed sizes."""
     import torch
     NP = (N + 15) // 16 * 16
     G = K // GROUP
-    GP = (G + 7) // 8 * 8
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed) * 1000003 + int(tensor_id))
     wq = torch.randint(0, 256, (NP * K // 2,), dtype=torch.uint8, device=device, generator=gen)
-    sv = torch.randn((NP, GP), dtype=torch.float32, device=device, generator=gen).mul_(0.02).abs_().add_(1e-3)
+    sv = torch.randn((NP * G,), dtype=torch.float32, device=device, generator=gen).mul_(0.02).abs_().add_(1e-3)
     sc = sv.to(torch.float16).view(torch.int16).reshape(-1)
-    zp = torch.randint(0, 256, (NP * GP // 2,), dtype=torch.uint8, device=device, generator=gen)
+    zp = torch.randint(0, 256, (NP * G // 2,), dtype=torch.uint8, device=device, generator=gen)
     return wq, sc, zp
 
 

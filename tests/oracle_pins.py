@@ -136,7 +136,7 @@ def pin_layout_roundtrip(o):
 
 
 def pin_layout_padding_zero(o):
-    """Rows past N and groups past G are zero in every buffer."""
+    """Rows past N are zero in every buffer."""
     N, K = 5, 640
     G = K // GROUP
     q = np.full((N, K), 15, np.uint8)
@@ -145,8 +145,13 @@ def pin_layout_padding_zero(o):
     assert not q16[N:].any() and not s16[N:].any() and not z16[N:].any()
     assert (q16[:N] == 15).all()
     assert int(np.unpackbits(wq).sum()) == N * K * 4
-    GP = (G + 7) // 8 * 8
-    assert not sp.view(np.uint16).reshape(16, GP)[:, G:].any()
+    # One 16-row tile per group: 16 scales and 8 zero bytes each, rows past
+    # N zero, so each group's block holds exactly N nonzero entries.
+    assert sp.size == 16 * G * 2 and zp.size == 16 * G // 2
+    blocks = sp.view(np.uint16).reshape(G, 16)
+    assert (blocks[:, :N] == 0x3C00).all() and not blocks[:, N:].any()
+    zb = zp.reshape(G, 8)
+    assert (zb[:, :N // 2] == 0xFF).all() and (zb[:, N // 2] == 0x0F).all() and not zb[:, N // 2 + 1:].any()
 
 
 # ------------------------------------------------------------- arithmetic

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_layout_id_and_status_text():
-    assert w.w4a16_layout_id() == 1
+    assert w.w4a16_layout_id() == 2
     for code in (0, -1, -2, -3, -4):
         assert w.w4a16_strerror(code)
     assert w.w4a16_strerror(-99) == "unknown status"
