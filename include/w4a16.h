@@ -116,23 +116,40 @@ int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scales, const vo
                const void* x, void* y, void* stream);
 
 /*
- * Workspace bytes w4a16_gemv_splitk needs: 4 * splits * M * N (fp32
- * partial sums). Returns 0 for a negative argument.
+ * Workspace bytes w4a16_gemv_splitk needs for (M, N, splits): fp32 partial
+ * sums [splits][M][N], then one uint32 arrival counter per 16-row tile of
+ * y, each part rounded up to a multiple of 16 bytes. Returns 0 for a
+ * negative argument.
  */
 size_t w4a16_splitk_workspace_bytes(int M, int N, int splits);
 
 /*
- * Split-K variant of w4a16_gemv for matrices with few rows: the K groups are
- * divided into `splits` contiguous ranges, one fp32 partial product per
- * range is written to `workspace` ([splits][M][N]), then a second kernel adds
- * the partials in ascending split order and rounds to fp16 into y. This is
+ * Split count this library would use for an M x N x K split-K call: 1 when
+ * the matrix has enough 16-row tiles to fill the GPU on its own, more for
+ * skinny N with a long K. Returns 0 for an invalid shape.
+ */
+int w4a16_splitk_choose(int M, int N, int K);
+
+/*
+ * Split-K variant of w4a16_gemv for matrices with few rows. The K groups are
+ * divided into `splits` contiguous ranges, and each (16-row tile, range)
+ * workgroup writes one fp32 partial product to `workspace`. The last
+ * workgroup of a tile to finish adds that tile's partials in ascending split
+ * order, rounds them to fp16 into y and resets the tile's counter. This is
  * the two-stage partial/final shape of "CodeAlign-Runtime", Level 4, applied
- * to K; the fixed order keeps results bit-identical run to run, the rule of
- * the qengine page ("Learnings": float atomics made runs differ, a fixed
- * summation order fixed it). 1 <= splits <= K/128. workspace: device memory,
- * 16-byte aligned, ws_bytes >= w4a16_splitk_workspace_bytes(M, N, splits).
+ * to K, in one launch. The fixed order keeps results bit-identical run to
+ * run: the qengine page ("Learnings") found float atomics made runs differ,
+ * and a fixed summation order fixed it. No workgroup ever waits for another.
+ *   1 <= splits <= K/128; splits == 1 is w4a16_gemv and does not touch
+ *   the workspace.
+ *   workspace: device memory, 16-byte aligned, of at least
+ *   ws_bytes >= w4a16_splitk_workspace_bytes(M, N, splits) bytes. It must
+ *   be zero-filled once before its first use. Every completed call leaves
+ *   its counters at zero again, so one workspace serves any later call on
+ *   the same stream, and graph replays too. Calls that may overlap in time
+ *   (different streams) need different workspaces.
  * Results may differ in rounding from w4a16_gemv (another summation order)
- * but lie within the same accuracy bound. Errors as w4a16_gemv, plus
+ * but lie within the same accuracy bound. Errors are as w4a16_gemv, plus
  * W4A16_EINVAL for a bad split count or a short workspace.
  */
 int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq, const void* scales,

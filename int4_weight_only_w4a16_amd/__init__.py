@@ -24,7 +24,8 @@ MAX_M = 8
 
 # Every symbol the header declares.
 EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_unpack", "w4a16_gemv",
-           "w4a16_splitk_workspace_bytes", "w4a16_gemv_splitk", "w4a16_dequant_f32", "w4a16_strerror")
+           "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose", "w4a16_gemv_splitk", "w4a16_dequant_f32",
+           "w4a16_strerror")
 
 
 class W4A16Error(RuntimeError):
@@ -54,6 +55,8 @@ def lib():
         L.w4a16_gemv.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_splitk_workspace_bytes.restype = _sz
         L.w4a16_splitk_workspace_bytes.argtypes = [_i, _i, _i]
+        L.w4a16_splitk_choose.restype = _i
+        L.w4a16_splitk_choose.argtypes = [_i, _i, _i]
         L.w4a16_gemv_splitk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.w4a16_dequant_f32.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_strerror.restype = ctypes.c_char_p
@@ -139,8 +142,14 @@ def w4a16_splitk_workspace_bytes(M, N, splits):
     return lib().w4a16_splitk_workspace_bytes(M, N, splits)
 
 
+def w4a16_splitk_choose(M, N, K):
+    return lib().w4a16_splitk_choose(M, N, K)
+
+
 def w4a16_gemv_splitk(M, N, K, splits, Wq, scales, zeros, x, y, workspace, ws_bytes=None, stream=None):
-    """Device: split-K GEMV; workspace holds [splits][M][N] fp32 partials."""
+    """Device: split-K GEMV in one launch. workspace: zero-filled once before
+    first use ([splits][M][N] fp32 partials, then per-tile counters that every
+    call leaves at zero)."""
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().w4a16_gemv_splitk(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x),

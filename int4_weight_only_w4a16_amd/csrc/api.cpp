@@ -63,6 +63,22 @@ w4a16::LaunchPlan plan_for(int M, int N, int K, int splits) {
   return plan;
 }
 
+// Split count for w4a16_gemv_splitk. Each split workgroup pays one
+// device-scope release (a write-back of its XCD's L2) and the last arriver
+// one device-scope acquire; measured on MI355X that costs more than it gains
+// once a matrix has a few hundred 16-row tiles (3584 x 18944: 9.4 us
+// unsplit, 15.3 us at 2 splits). It pays for skinny N with a long K
+// (128 x 18944: 6 splits fastest): about 24 groups per split, at most 8
+// splits, and at most 128 (tile, split) pairs.
+int choose_splits(int N, int K) {
+  const int groups = K / W4A16_GROUP;
+  const int64_t row_tiles = (int64_t(N) + 15) / 16;
+  int64_t splits = groups / 24;
+  if (splits > 128 / row_tiles) splits = 128 / row_tiles;
+  if (splits > 8) splits = 8;
+  return splits < 1 ? 1 : int(splits);
+}
+
 }  // namespace
 
 extern "C" int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,
@@ -77,7 +93,12 @@ extern "C" int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scale
 
 extern "C" size_t w4a16_splitk_workspace_bytes(int M, int N, int splits) {
   if (M < 0 || N < 0 || splits < 0) return 0;
-  return size_t(4) * size_t(splits) * size_t(M) * size_t(N);
+  return w4a16::splitk_workspace_bytes(M, N, splits);
+}
+
+extern "C" int w4a16_splitk_choose(int M, int N, int K) {
+  if (check_shape(M, N, K) < 0) return 0;
+  return choose_splits(N, K);
 }
 
 extern "C" int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq, const void* scales,
@@ -87,12 +108,12 @@ extern "C" int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq
   if (rc < 0) return rc;
   if (splits < 1 || splits > K / W4A16_GROUP) return W4A16_EINVAL;
   if (rc == 1) return W4A16_OK;
+  if (splits == 1) return w4a16_gemv(M, N, K, Wq, scales, zeros, x, y, stream);
   if (!pointers_ok({Wq, scales, zeros, x, y, workspace})) return W4A16_EINVAL;
-  if (ws_bytes < w4a16_splitk_workspace_bytes(M, N, splits)) return W4A16_EINVAL;
+  if (ws_bytes < w4a16::splitk_workspace_bytes(M, N, splits)) return W4A16_EINVAL;
   const w4a16::LaunchPlan plan = plan_for(M, N, K, splits);
   float* partials = static_cast<float*>(workspace);
   if (w4a16::launch_gemv(M, N, K, plan, Wq, scales, zeros, x, y, partials, stream) != 0) return W4A16_EHIP;
-  if (w4a16::launch_splitk_reduce(M, N, splits, partials, y, stream) != 0) return W4A16_EHIP;
   return W4A16_OK;
 }
 

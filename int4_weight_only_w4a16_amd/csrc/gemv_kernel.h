@@ -23,7 +23,12 @@ namespace dev {
 // and requests the next row tile's round before computing the current one).
 // The waves' partial sums meet in LDS (double-buffered across row tiles, one
 // barrier per row tile) and are added in wave order.
-// Writes fp16 y[MR][N] when `part` is null, else fp32 part[split][MR][N].
+// Writes fp16 y[MR][N] directly when `part` is null. Otherwise (split-K,
+// gridDim.y splits) each workgroup writes its fp32 partial to
+// part[split][MR][N] and counts its arrival in the row tile's counter (the
+// uint32 array after the partials, 16-byte aligned); the last of a tile's
+// splits to arrive adds the partials in split order, writes y and resets
+// the counter to zero for the next call.
 template <int MR, int WAVES, int SHARE, int ENGINE, int R>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales,
@@ -231,6 +236,31 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
       }
     }
   };
+  // Split-K: y for row tile t = the tile's partials summed in split order.
+  auto finish_tile = [&](int64_t t) {
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int idx = tid + j * WAVES * 64;
+      const int m = idx >> 4, i = idx & 15;
+      const int64_t nn = t * kTileRows + i;
+      if (idx < MR * 16 && nn < N) {
+        // Eight splits' partials requested at once (clamped indices stay in
+        // bounds), then added in split order.
+        const float* p = part + int64_t(m) * N + nn;
+        const int64_t stride = int64_t(MR) * N;
+        float sum = 0.f;
+        for (int s0 = 0; s0 < splits; s0 += 8) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = p[min(s0 + u, splits - 1) * stride];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (s0 + u < splits) sum = s0 + u == 0 ? v[u] : sum + v[u];
+        }
+        y[int64_t(m) * N + nn] = (_Float16)sum;
+      }
+    }
+  };
 
   struct TilePtrs {
     const u32x4* wlane;
@@ -320,6 +350,44 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) store_tile(tile_of(r), sums[r]);
+  if (!part) return;
+
+  // Split-K arrival. Each wave waits until its partial stores are complete
+  // and the workgroup synchronizes; then one thread releases them at device
+  // scope (other XCDs' L2s included: the release writes this L2's dirty
+  // lines back) and counts the arrival. The last arriver's thread acquires
+  // at device scope (invalidating stale lines) before the workgroup reads
+  // the other splits' partials. One device-scope fence per workgroup, not
+  // per wave: each is a whole-L2 operation. Nothing ever waits on another
+  // workgroup.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  __shared__ int last[R];
+  unsigned* counters = reinterpret_cast<unsigned*>(part + ((int64_t(splits) * MR * N + 3) & ~int64_t(3)));
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    int any_last = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t t = tile_of(r);
+      int is_last = 0;
+      if (t < row_tiles) {
+        const unsigned before = __hip_atomic_fetch_add(counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = before == unsigned(splits - 1);
+        // Every split of this tile has arrived: nothing else touches the
+        // counter during this call.
+        if (is_last) __hip_atomic_store(counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      last[r] = is_last;
+      any_last |= is_last;
+    }
+    if (any_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (last[r]) finish_tile(tile_of(r));
 }
 
 template <int MR, int WAVES, int SHARE, int ENGINE>

@@ -16,6 +16,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kMagic1024 = 0x64006400u;  // fp16 pair (1024, 1024)
 
+// s_waitcnt operand that waits for every outstanding vector memory operation
+// of the wave (vmcnt 0) and for nothing else (expcnt 7, lgkmcnt 15: the
+// field maxima in the gfx9 encoding).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
 // fp16 pairs (1024 + z, 1024 + z) and (64 + z, 64 + z) for a zero point z.

@@ -75,7 +75,17 @@ size_t lds_bytes(int M, int K, const LaunchPlan& plan);
 // Whether the kernel set has an instantiation for this plan, within the LDS limit.
 bool plan_supported(int M, int K, const LaunchPlan& plan);
 
+// Split-K workspace: fp32 partials [splits][M][N], then one uint32 arrival
+// counter per row tile, each part rounded up to 16 bytes.
+constexpr size_t splitk_partial_bytes(int M, int N, int splits) {
+  return (size_t(4) * size_t(splits) * size_t(M) * size_t(N) + 15) / 16 * 16;
+}
+constexpr size_t splitk_workspace_bytes(int M, int N, int splits) {
+  return splitk_partial_bytes(M, N, splits) + (size_t(4) * size_t((N + kTileRows - 1) / kTileRows) + 15) / 16 * 16;
+}
+
 // Kernel launchers (w4a16_kernels.hip). They return a hipError_t value as int.
+// `partials` non-null selects split-K: it is the workspace above, counters zero.
 int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
                 const void* zeros, const void* x, void* y, float* partials, void* stream);
 #define W4A16_DECLARE_M(MR)                                                                            \
@@ -84,7 +94,6 @@ int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, con
 W4A16_DECLARE_M(1) W4A16_DECLARE_M(2) W4A16_DECLARE_M(3) W4A16_DECLARE_M(4)
 W4A16_DECLARE_M(5) W4A16_DECLARE_M(6) W4A16_DECLARE_M(7) W4A16_DECLARE_M(8)
 #undef W4A16_DECLARE_M
-int launch_splitk_reduce(int M, int N, int splits, const float* partials, void* y, void* stream);
 int launch_dequant(int N, int K, const void* wq, const void* scales, const void* zeros, float* out,
                    void* stream);
 

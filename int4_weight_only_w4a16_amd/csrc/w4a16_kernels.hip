@@ -1,21 +1,10 @@
 // HIP kernels of libw4a16.so for gfx950 (CDNA4, wave64) other than the GEMV
-// template (gemv_kernel.h, instantiated per M in gemv_m*.hip): the split-K
-// fixed-order reduce, the dequant test hook, and the launchers.
+// template (gemv_kernel.h, instantiated per M in gemv_m*.hip): the dequant
+// test hook, and the launchers.
 #include "w4a16_device.h"
 
 namespace w4a16 {
 namespace dev {
-
-// y[i] = fp16(sum over splits of part[split][i]), splits in ascending order.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
-                                                            _Float16* __restrict__ y, int64_t count,
-                                                            int splits) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= count) return;
-  float sum = part[i];
-  for (int s = 1; s < splits; ++s) sum += part[int64_t(s) * count + i];
-  y[i] = (_Float16)sum;
-}
 
 // out[n][k] = float(q - z) * float(s): one thread per packed word.
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ wq,
@@ -74,14 +63,6 @@ int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, con
     case 8: return launch_gemv_m8(N, K, plan, wq, scales, zeros, x, y, partials, stream_ptr);
     default: return int(hipErrorInvalidValue);
   }
-}
-
-int launch_splitk_reduce(int M, int N, int splits, const float* partials, void* y, void* stream_ptr) {
-  const int64_t count = int64_t(M) * N;
-  const unsigned blocks = unsigned((count + 255) / 256);
-  hipLaunchKernelGGL(dev::splitk_reduce_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream_ptr),
-                     partials, static_cast<_Float16*>(y), count, splits);
-  return int(hipGetLastError());
 }
 
 int launch_dequant(int N, int K, const void* wq, const void* scales, const void* zeros, float* out,

@@ -52,13 +52,26 @@ class Problem:
         torch.cuda.synchronize()
         return y.cpu().numpy().view(np.uint16)
 
-    def gemv_splitk(self, splits):
+    def splitk_workspace(self, splits):
+        """Zero-filled workspace of exactly the size the library asks for."""
+        torch, dev = torch_dev()
+        return torch.zeros(max(16, w.w4a16_splitk_workspace_bytes(self.M, self.N, splits)),
+                           dtype=torch.uint8, device=dev)
+
+    def gemv_splitk(self, splits, ws=None):
         torch, dev = torch_dev()
         y = self.new_y()
-        ws = torch.empty(max(1, self.M * self.N * splits), dtype=torch.float32, device=dev)
+        if ws is None:
+            ws = self.splitk_workspace(splits)
         w.w4a16_gemv_splitk(self.M, self.N, self.K, splits, self.wq_d, self.sp_d, self.zp_d, self.x_d, y, ws)
         torch.cuda.synchronize()
         return y.cpu().numpy().view(np.uint16)
+
+    def splitk_counters(self, ws, splits):
+        """The per-tile arrival counters at the end of a split-K workspace."""
+        off = (4 * splits * self.M * self.N + 15) // 16 * 16
+        tiles = (self.N + 15) // 16
+        return ws[off:off + 4 * tiles].cpu().numpy().view(np.uint32)
 
     def check(self, y):
         ref, absref = self.reference()

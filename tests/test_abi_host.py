@@ -106,8 +106,13 @@ def test_device_entry_points_reject_before_launch():
     assert L.w4a16_gemv(1, 16, 128, fake + 8, fake, fake, fake, fake, None) == w.W4A16_EINVAL
     # split-K: split count and workspace size
     ws = w.w4a16_splitk_workspace_bytes(2, 16, 3)
-    assert ws == 4 * 3 * 2 * 16
+    assert ws == 4 * 3 * 2 * 16 + 16  # partials, then one counter (padded to 16 bytes)
+    assert w.w4a16_splitk_workspace_bytes(1, 33, 2) == 272 + 16
     assert w.w4a16_splitk_workspace_bytes(-1, 16, 3) == 0
+    assert w.w4a16_splitk_choose(1, 37888, 3584) == 1 and w.w4a16_splitk_choose(1, 3584, 18944) == 1
+    assert w.w4a16_splitk_choose(1, 128, 18944) == 6 and w.w4a16_splitk_choose(8, 512, 18944) == 4
+    assert w.w4a16_splitk_choose(1, 128, 896) == 1
+    assert w.w4a16_splitk_choose(1, 16, 200) == 0 and w.w4a16_splitk_choose(9, 16, 128) == 0
     for splits, wsb, want in [(0, ws, w.W4A16_EINVAL), (3, ws - 4, w.W4A16_EINVAL), (3, ws, None),
                               (8, 10 ** 9, w.W4A16_EINVAL)]:
         if want is None:

@@ -150,14 +150,49 @@ def test_batch_invariance(N, K):
 # ---------------------------------------------------------------- split-K
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 28])
-@pytest.mark.parametrize("M,N,K", [(1, 3584, 3584), (5, 128, 896 * 4), (1, 896, 4864)])
+@pytest.mark.parametrize("M,N,K", [(1, 3584, 3584), (5, 128, 896 * 4), (1, 896, 4864), (8, 200, 3584)])
 def test_splitk(M, N, K, splits):
+    """Split-K against the oracle; the workspace's counters are back at zero
+    after each call, so a second call on the same workspace gives the same
+    bits (a counter left behind would leave tiles unwritten)."""
     if splits > K // 128:
         pytest.skip("more splits than groups")
+    _say("splitk", M, N, K, splits)
     p = Problem(M, N, K, seed=splits)
-    y = p.gemv_splitk(splits)
+    ws = p.splitk_workspace(splits)
+    y = p.gemv_splitk(splits, ws)
     p.check(y)
-    assert np.array_equal(y, p.gemv_splitk(splits))
+    if splits > 1:
+        assert not p.splitk_counters(ws, splits).any()
+    assert np.array_equal(y, p.gemv_splitk(splits, ws))
+
+
+SKINNY = [("skinny_128x18944", 128, 18944), ("skinny_200x18944", 200, 18944), ("skinny_512x18944", 512, 18944),
+          ("skinny_64x7168", 64, 7168)]
+
+
+@pytest.mark.parametrize("name,N,K", synthetic.QWEN05B_LAYER + synthetic.QWEN7B_LAYER + synthetic.VERIFY27B + SKINNY)
+def test_splitk_chosen_full_size(name, N, K):
+    """The split count the library picks, at the full model shapes, M = 1
+    and 5, against the oracle on every output."""
+    for M in (1, 5):
+        splits = w.w4a16_splitk_choose(M, N, K)
+        assert 1 <= splits <= K // 128
+        _say("splitk chosen", name, M, splits)
+        p = Problem(M, N, K, seed=4)
+        y = p.gemv_splitk(splits)
+        _say(name, M, splits, "worst", p.check(y))
+
+
+def test_splitk_batch_invariance():
+    """Split-K rows do not depend on how many activation rows come along."""
+    N, K, splits = 3584, 18944, 4
+    _say("splitk batch invariance", N, K, splits)
+    q, s, z = synthetic.weights(N, K, seed=12)
+    x = synthetic.activations(8, K, seed=12)
+    alone = Problem(1, N, K, q=q, s=s, z=z, x=x[:1].copy()).gemv_splitk(splits)
+    y8 = Problem(8, N, K, q=q, s=s, z=z, x=x.copy()).gemv_splitk(splits)
+    assert np.array_equal(y8[0], alone[0])
 
 
 # ------------------------------------------------------------ graph replay
@@ -181,6 +216,33 @@ def test_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().view(np.uint16), eager)
+
+
+def test_graph_replay_splitk():
+    """A captured split-K call replays correctly many times: the counters
+    reset by each replay are what the next replay starts from."""
+    torch, dev = torch_dev()
+    p = Problem(1, 3584, 18944, seed=9)
+    splits = 4
+    ws = p.splitk_workspace(splits)
+    eager = p.gemv_splitk(splits, ws)
+    y = p.new_y()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        w.w4a16_gemv_splitk(1, p.N, p.K, splits, p.wq_d, p.sp_d, p.zp_d, p.x_d, y, ws, stream=stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            w.w4a16_gemv_splitk(1, p.N, p.K, splits, p.wq_d, p.sp_d, p.zp_d, p.x_d, y, ws, stream=stream)
+    for _ in range(4):
+        y.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), eager)
+        assert not p.splitk_counters(ws, splits).any()
+    p.check(eager)
 
 
 # --------------------------------------------------------- device errors
