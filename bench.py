@@ -105,20 +105,34 @@ class Step:
         self.bytes = sum(algorithmic_bytes(1, N, K) for _, N, K in self.shapes)
         self.stream = torch.cuda.Stream()
 
-    def launch_all(self, stream, only=None):
+    def launch_all(self, stream, only=None, swiglu=False, torch_act=False):
         for name, N, K, wq, sc, zp, x, y in self.bufs:
-            if only is None or name.endswith(only):
+            if only is not None and not name.endswith(only):
+                continue
+            if swiglu and name.endswith("gate_up_proj"):
+                # The same packed bytes read as the 16-row gate/up interleave.
+                self.w.w4a16_gemv_swiglu(1, N // 2, K, wq, sc, zp, x, self.y_act, stream=stream)
+            else:
                 self.w.w4a16_gemv(1, N, K, wq, sc, zp, x, y, stream=stream)
+                if torch_act and name.endswith("gate_up_proj"):
+                    # Comparison only: the unfused activation as separate
+                    # torch elementwise kernels (silu, then the product).
+                    h = y.view(self.torch.float16).view(1, 2, N // 2)
+                    self.torch.mul(self.torch.nn.functional.silu(h[:, 0]), h[:, 1], out=self.y_act_h)
 
-    def capture(self, only=None):
+    def capture(self, only=None, swiglu=False, torch_act=False):
         torch = self.torch
+        if (swiglu or torch_act) and not hasattr(self, "y_act"):
+            _, N, _ = synthetic.QWEN7B_LAYER[2]
+            self.y_act = torch.empty((1, N // 2), dtype=torch.int16, device="cuda:0")
+            self.y_act_h = self.y_act.view(torch.float16)
         self.stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(self.stream):
-            self.launch_all(self.stream, only)  # warm: first launches load code objects
+            self.launch_all(self.stream, only, swiglu, torch_act)  # warm: first launches load code objects
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=self.stream):
-                self.launch_all(self.stream, only)
+                self.launch_all(self.stream, only, swiglu, torch_act)
         torch.cuda.synchronize()
         return g
 
@@ -262,6 +276,18 @@ def main():
     dom_us = dom_s / (reps * n_dom) * 1e6
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
 
+    # Variant (reported beside, never as `value`): gate+up with the SwiGLU
+    # epilogue fused, y = silu(g) * u of width 18944, same weight bytes.
+    fused = step.capture(only="gate_up_proj", swiglu=True)
+    fused_s = step.time_graph(fused, reps, 3)
+    fused_us = fused_s / (reps * n_dom) * 1e6
+    fused_bytes = dom_bytes - 2 * Nd + 2 * (Nd // 2)
+    fused_step = step.capture(swiglu=True)
+    fused_step_s = step.time_graph(fused_step, args.steps, args.warmup)
+    unfused = step.capture(only="gate_up_proj", torch_act=True)
+    unfused_us = step.time_graph(unfused, reps, 3) / (reps * n_dom) * 1e6
+    del fused, fused_step, unfused
+
     # Outputs of the last full replay, for the sampled check.
     graph.replay()
     torch.cuda.synchronize()
@@ -299,6 +325,18 @@ def main():
             "traffic": load_traffic(),
             "bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_us, 3),
+        },
+        "variants": {
+            "gate_up_swiglu_fused": {
+                "kernel": "w4a16_gemv_swiglu, gate+up 37888x3584 -> silu(g)*u 18944, M=1",
+                "avg_launch_us": round(fused_us, 3),
+                "achieved_GBps": round(fused_bytes / (fused_us * 1e-6) / 1e9, 1),
+                "frac": round(fused_bytes / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                "bytes_per_launch": fused_bytes,
+                "plain_gate_up_us": round(dom_us, 3),
+                "unfused_gate_up_plus_torch_silu_mul_us": round(unfused_us, 3),
+                "step_us_with_fused_gate_up": round(fused_step_s / args.steps * 1e6, 2),
+            },
         },
         "setup_s": round(setup_s, 1),
     }

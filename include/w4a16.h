@@ -97,6 +97,21 @@ int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, const uint8_t*
                void* wq_out, void* s_out, void* z_out);
 
 /*
+ * Host packer for the fused gate/up + SwiGLU GEMV (w4a16_gemv_swiglu).
+ * Gate and up are two F x K matrices in the logical form of w4a16_pack
+ * (qg, sg, zg and qu, su, zu). Their 16-row blocks are interleaved -- gate
+ * rows 16j .. 16j+15, then the up rows 16j .. 16j+15 -- into one matrix of
+ * 2 * roundup(F, 16) rows (rows past F within a block are zero), which is
+ * packed as by w4a16_pack. That interleave is what lets SwiGLU run in
+ * registers (the 4-bit matrix-vector kernel of the qengine page, "How it
+ * works"). Output buffers: w4a16_packed_sizes(2 * roundup(F, 16), K) bytes.
+ * Errors: as w4a16_pack. Host only.
+ */
+int w4a16_pack_gate_up(int F, int K, const uint8_t* qg, const uint16_t* sg, const uint8_t* zg,
+                       const uint8_t* qu, const uint16_t* su, const uint8_t* zu, void* wq_out, void* s_out,
+                       void* z_out);
+
+/*
  * Inverse of w4a16_pack (host to host): recovers q [N][K], s [N][K/128] and
  * z [N][K/128] exactly. Errors: W4A16_EINVAL for a bad shape or NULL pointer.
  */
@@ -114,6 +129,25 @@ int w4a16_unpack(int N, int K, const void* wq, const void* s_packed, const void*
  */
 int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,
                const void* x, void* y, void* stream);
+
+/*
+ * Fused gate/up GEMV with a SwiGLU epilogue:
+ *   y[m][f] = fp16( silu(g) * u ),  g = sum_k Wgate[f][k] x[m][k],
+ *   u = sum_k Wup[f][k] x[m][k],  silu(g) = g / (1 + exp(-g)),
+ * with g and u the fp32 sums of the GEMV (never rounded to fp16) and the
+ * epilogue evaluated in fp32. Wq, scales, zeros: the interleaved matrix
+ * written by w4a16_pack_gate_up, on the device. x: fp16 [M][K];
+ * y: fp16 [M][F]. M: 1..8. The SwiGLU activation is the one of the Qwen2.5
+ * MLP the pages' 7B shapes come from; its placement in registers, right
+ * after the gate and up sums, follows the qengine page ("How it works").
+ * Saves the separate activation launch and the 2 * M * 2F bytes of the
+ * intermediate gate/up output. Deterministic and batch invariant like
+ * w4a16_gemv. Each wave's share of K must fit one round of requests: K is
+ * at most 5120 for every M (7168 for M <= 2), else W4A16_EUNSUPPORTED.
+ * Errors: as w4a16_gemv, plus that one.
+ */
+int w4a16_gemv_swiglu(int M, int F, int K, const void* Wq, const void* scales, const void* zeros,
+                      const void* x, void* y, void* stream);
 
 /*
  * Workspace bytes w4a16_gemv_splitk needs for (M, N, splits): fp32 partial

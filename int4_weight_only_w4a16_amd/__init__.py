@@ -23,9 +23,9 @@ GROUP = 128
 MAX_M = 8
 
 # Every symbol the header declares.
-EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_unpack", "w4a16_gemv",
-           "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose", "w4a16_gemv_splitk", "w4a16_dequant_f32",
-           "w4a16_strerror")
+EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_unpack",
+           "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
+           "w4a16_gemv_splitk", "w4a16_dequant_f32", "w4a16_strerror")
 
 
 class W4A16Error(RuntimeError):
@@ -51,8 +51,10 @@ def lib():
         L.w4a16_layout_id.argtypes = []
         L.w4a16_packed_sizes.argtypes = [_i, _i, _p, _p, _p]
         L.w4a16_pack.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p]
+        L.w4a16_pack_gate_up.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
         L.w4a16_unpack.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_gemv.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
+        L.w4a16_gemv_swiglu.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_splitk_workspace_bytes.restype = _sz
         L.w4a16_splitk_workspace_bytes.argtypes = [_i, _i, _i]
         L.w4a16_splitk_choose.restype = _i
@@ -119,6 +121,24 @@ def w4a16_pack(q, s, z):
     return wq, sp, zp
 
 
+def w4a16_pack_gate_up(qg, sg, zg, qu, su, zu):
+    """Host: gate and up in w4a16_pack's logical form (each F x K) -> the
+    interleaved (wq, s_packed, z_packed) uint8 arrays w4a16_gemv_swiglu reads."""
+    qg, qu = (np.ascontiguousarray(a, dtype=np.uint8) for a in (qg, qu))
+    sg, su = (np.ascontiguousarray(a, dtype=np.uint16) for a in (sg, su))
+    zg, zu = (np.ascontiguousarray(a, dtype=np.uint8) for a in (zg, zu))
+    F, K = qg.shape
+    G = K // GROUP if K % GROUP == 0 else -1
+    if qu.shape != (F, K) or any(a.shape != (F, G) for a in (sg, su, zg, zu)):
+        raise W4A16Error(W4A16_EINVAL, "w4a16_pack_gate_up")
+    wb, sb, zb = w4a16_packed_sizes(2 * ((F + 15) // 16 * 16), K)
+    wq, sp, zp = np.empty(wb, np.uint8), np.empty(sb, np.uint8), np.empty(zb, np.uint8)
+    _check(lib().w4a16_pack_gate_up(F, K, qg.ctypes.data, sg.ctypes.data, zg.ctypes.data, qu.ctypes.data,
+                                    su.ctypes.data, zu.ctypes.data, wq.ctypes.data, sp.ctypes.data,
+                                    zp.ctypes.data), "w4a16_pack_gate_up")
+    return wq, sp, zp
+
+
 def w4a16_unpack(N, K, wq, s_packed, z_packed):
     """Host inverse of w4a16_pack -> (q, s, z)."""
     wq, sp, zp = (np.ascontiguousarray(a, dtype=np.uint8) for a in (wq, s_packed, z_packed))
@@ -136,6 +156,12 @@ def w4a16_gemv(M, N, K, Wq, scales, zeros, x, y, stream=None):
     """Device: y[M][N] (fp16) = W x[M][K] (fp16) with W in layout ID 2."""
     _check(lib().w4a16_gemv(M, N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
                             _stream(stream)), "w4a16_gemv")
+
+
+def w4a16_gemv_swiglu(M, F, K, Wq, scales, zeros, x, y, stream=None):
+    """Device: y[M][F] (fp16) = silu(gate x) * (up x), W from w4a16_pack_gate_up."""
+    _check(lib().w4a16_gemv_swiglu(M, F, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
+                                   _stream(stream)), "w4a16_gemv_swiglu")
 
 
 def w4a16_splitk_workspace_bytes(M, N, splits):

@@ -51,6 +51,7 @@ w4a16::LaunchPlan plan_for(int M, int N, int K, int splits) {
   plan.engine = w4a16::kEngineMfma;
   plan.splits = splits;
   plan.tiles_per_wg = 1;
+  plan.epilogue = w4a16::kEpiStore;
   plan.waves = 1;
   while (plan.waves < 16 && (range + plan.waves - 1) / plan.waves > target) plan.waves *= 2;
   while (plan.waves > 1 && plan.waves > range) plan.waves /= 2;  // every wave gets at least one group
@@ -79,6 +80,27 @@ int choose_splits(int N, int K) {
   return splits < 1 ? 1 : int(splits);
 }
 
+// Plan of the fused gate/up + SwiGLU launch: one gate/up pair of row tiles
+// per workgroup, H waves on each tile (the fewest powers of two, at most 8,
+// whose shares hold at most 7 tiles), shares of 4, 5 or 7 (5 at most with 16
+// waves, the register rule for every M). Every share is one round, so K is
+// at most 8 * 5 * 128 = 5120; larger K is refused (plan_supported).
+// Depends on K only, so rows are batch invariant as in plan_for.
+w4a16::LaunchPlan plan_swiglu(int K) {
+  const int groups = K / W4A16_GROUP;
+  int half = 1;
+  while (half < 8 && (groups + half - 1) / half > 7) half *= 2;
+  const int per = (groups + half - 1) / half;
+  w4a16::LaunchPlan plan;
+  plan.engine = w4a16::kEngineMfma;
+  plan.splits = 1;
+  plan.tiles_per_wg = 1;
+  plan.epilogue = w4a16::kEpiSwiglu;
+  plan.waves = 2 * half;
+  plan.share = per <= 4 ? 4 : (per <= 5 ? 5 : 7);
+  return plan;
+}
+
 }  // namespace
 
 extern "C" int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,
@@ -88,6 +110,17 @@ extern "C" int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scale
   if (!pointers_ok({Wq, scales, zeros, x, y})) return W4A16_EINVAL;
   const w4a16::LaunchPlan plan = plan_for(M, N, K, 1);
   if (w4a16::launch_gemv(M, N, K, plan, Wq, scales, zeros, x, y, nullptr, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
+
+extern "C" int w4a16_gemv_swiglu(int M, int F, int K, const void* Wq, const void* scales, const void* zeros,
+                                 const void* x, void* y, void* stream) {
+  const int rc = check_shape(M, F, K);
+  if (rc != W4A16_OK) return rc == 1 ? W4A16_OK : rc;
+  if (!pointers_ok({Wq, scales, zeros, x, y})) return W4A16_EINVAL;
+  const w4a16::LaunchPlan plan = plan_swiglu(K);
+  if (!w4a16::plan_supported(M, K, plan)) return W4A16_EUNSUPPORTED;
+  if (w4a16::launch_gemv(M, F, K, plan, Wq, scales, zeros, x, y, nullptr, stream) != 0) return W4A16_EHIP;
   return W4A16_OK;
 }
 

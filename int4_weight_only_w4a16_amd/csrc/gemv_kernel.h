@@ -23,13 +23,23 @@ namespace dev {
 // and requests the next row tile's round before computing the current one).
 // The waves' partial sums meet in LDS (double-buffered across row tiles, one
 // barrier per row tile) and are added in wave order.
+// EPI == kEpiSwiglu: the matrix's row tiles alternate gate (2j) and up
+// (2j+1) rows of the same 16 outputs. Workgroup j runs both tiles at once:
+// waves [0, WAVES/2) split the K range of the gate tile, the other half the
+// same K range of the up tile (R = 1), and the sums meet in LDS, where
+// y[m][16j + i] = fp16(silu(g) * u), silu(g) = g / (1 + e^-g) in fp32. N is
+// the output width (the matrix has 2 * ceil(N/16) row tiles). Wave w of the
+// gate half stages the x slice that wave w of the up half also reads (one
+// LDS barrier after staging), and every share fits one round: the host
+// launches nothing else, and a workgroup exits at once (all of it) if the
+// shape would need more.
 // Writes fp16 y[MR][N] directly when `part` is null. Otherwise (split-K,
 // gridDim.y splits) each workgroup writes its fp32 partial to
 // part[split][MR][N] and counts its arrival in the row tile's counter (the
 // uint32 array after the partials, 16-byte aligned); the last of a tile's
 // splits to arrive adds the partials in split order, writes y and resets
 // the counter to zero for the next call.
-template <int MR, int WAVES, int SHARE, int ENGINE, int R>
+template <int MR, int WAVES, int SHARE, int ENGINE, int R, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, const _Float16* __restrict__ x, _Float16* __restrict__ y,
@@ -49,21 +59,31 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   float* red = reinterpret_cast<float*>(smem);           // [2][WAVES][4][kRows][16]
 
   const int G = K / kGroup;
-  const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;
+  constexpr bool kPair = EPI == kEpiSwiglu;
+  static_assert(!kPair || (R == 1 && WAVES % 2 == 0), "SwiGLU: one gate/up pair, half the waves on each");
+  constexpr int kHalf = kPair ? WAVES / 2 : WAVES;  // waves sharing one row tile's K range
+  const int64_t row_tiles = (kPair ? 2 : 1) * ((int64_t(N) + kTileRows - 1) / kTileRows);
   const int split = blockIdx.y, splits = gridDim.y;
   const int g_beg = int(int64_t(split) * G / splits);
   const int g_end = int(int64_t(split + 1) * G / splits);
   const int ng = g_end - g_beg;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps share bounds scalar
+  const int half = kPair ? wave / kHalf : 0;                   // SwiGLU: 0 gate, 1 up
+  const int wave_in = kPair ? wave - half * kHalf : wave;      // index among the tile's waves
   const int piece = lane >> 4;  // which 8-column piece of each 32 columns
   const int rlane = lane & 15;  // weight row within the tile
   const uint32_t magic = kMagic1024;
-  const int share_beg = g_beg + (wave * ng) / WAVES;
-  const int share_end = g_beg + ((wave + 1) * ng) / WAVES;
+  if constexpr (kPair) {
+    // Workgroup-uniform (K and the grid only): the single-round layout the
+    // shared x slices and the one staging barrier rely on.
+    if (splits != 1 || ng < kHalf || (ng + kHalf - 1) / kHalf > SHARE) return;
+  }
+  const int share_beg = g_beg + (wave_in * ng) / kHalf;
+  const int share_end = g_beg + ((wave_in + 1) * ng) / kHalf;
   const int mm = rlane < MR ? rlane : MR - 1;  // activation row feeding A-operand row rlane
   _Float16* xw = reinterpret_cast<_Float16*>(smem + 2 * kRed * sizeof(float)) +
-                 (kGlobalX ? 0 : wave * MR * kXRow);  // this wave's x slice [MR][SHARE*128]
+                 (kGlobalX ? 0 : (kPair ? wave_in : wave) * MR * kXRow);  // x slice [MR][SHARE*128]
   int parity = 0;
 
   // Copy x[:, 128*g0 : 128*(g0+n)) into this wave's LDS slice (synchronous).
@@ -91,16 +111,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   // by a select.
   struct Round {
     u32x4 w[SHARE];
-    uint32_t sv[SHARE], zb[SHARE];
+    // The aligned 32-bit words holding the lane's fp16 scale and zero
+    // nibble. Whole words need no widening after the load: a widening is
+    // placed where the value is used, and when a branch separates loads and
+    // uses the compiler puts all of them, and so all the waits, before the
+    // first tile. The fields are cut out inside each tile, after its wait.
+    uint32_t sw[SHARE], zw[SHARE];
     half8_t xa[kGlobalX ? SHARE : 1][4];
   };
-  auto load_round = [&](Round& r, const u32x4* wlane, const uint16_t* srow, const uint8_t* zrow, int g0, int n) {
+  auto load_round = [&](Round& r, const u32x4* wlane, const uint32_t* sword, const uint32_t* zword, int g0,
+                        int n) {
 #pragma unroll
     for (int u = 0; u < SHARE; ++u) {
       const int gg = g0 + min(u, n - 1);
       r.w[u] = __builtin_nontemporal_load(wlane + int64_t(gg) * (kTileBytes / 16));
-      r.sv[u] = srow[gg * kTileRows];
-      r.zb[u] = zrow[gg * (kTileRows / 2)];
+      r.sw[u] = sword[gg * (kTileRows / 2)];  // 16 scales = 8 words per tile
+      r.zw[u] = zword[gg * (kTileRows / 8)];  // 16 nibbles = 2 words per tile
       if constexpr (kGlobalX) {
         const _Float16* xl = x + int64_t(mm) * K + int64_t(gg) * kGroup + 8 * piece;
 #pragma unroll
@@ -131,10 +157,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
       // tile can move above its asm, so no tile's unpack is hoisted ahead of
       // earlier tiles (which would wait for every load at once).
       u32x4 wt = r.w[u];
-      uint32_t zt = r.zb[u], st = r.sv[u];
+      uint32_t zt = r.zw[u], st = r.sw[u];
       asm volatile("" : "+v"(wt), "+v"(zt), "+v"(st));
-      const ZeroPairs zp = zero_pairs((zt >> ((rlane & 1) * 4)) & 15u);
-      const float s = half_bits_to_float(st);
+      // Row rlane's zero nibble is nibble rlane % 8 of its word; its scale
+      // the half rlane % 2 of its word.
+      const ZeroPairs zp = zero_pairs((zt >> ((rlane & 7) * 4)) & 15u);
+      const float s = half_bits_to_float((st >> ((rlane & 1) * 16)) & 0xFFFFu);
       const _Float16* xg = xbase + u * kGroup;
       if constexpr (ENGINE == kEngineDot2) {
         float dot[MR];
@@ -217,7 +245,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
       const int slot = ENGINE == kEngineDot2 ? m * 16 + i : ((m >> 2) * kRows + (m & 3)) * 16 + i;
       float sum = rb[slot];
 #pragma unroll
-      for (int w2 = 1; w2 < WAVES; ++w2) sum += rb[w2 * kRedWave + slot];
+      for (int w2 = 1; w2 < kHalf; ++w2) sum += rb[w2 * kRedWave + slot];
+      if constexpr (kPair) {
+        float up = rb[kHalf * kRedWave + slot];
+#pragma unroll
+        for (int w2 = kHalf + 1; w2 < WAVES; ++w2) up += rb[w2 * kRedWave + slot];
+        sum = sum / (1.f + expf(-sum)) * up;  // silu(gate) * up
+      }
       out[j] = sum;
     }
     parity ^= 1;
@@ -264,20 +298,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
 
   struct TilePtrs {
     const u32x4* wlane;
-    const uint16_t* srow;
-    const uint8_t* zrow;
+    const uint32_t* sword;  // word of tile (t, 0)'s scale block holding row rlane's scale
+    const uint32_t* zword;  // word of tile (t, 0)'s zero block holding row rlane's nibble
   };
   auto tile_ptrs = [&](int64_t t) {  // t < row tiles: always valid memory
     const int64_t q0 = t * G;           // index of tile (t, 0)
     return TilePtrs{reinterpret_cast<const u32x4*>(wq + q0 * kTileBytes) + lane,
-                    scales + q0 * kTileRows + rlane, zeros + q0 * (kTileRows / 2) + (rlane >> 1)};
+                    reinterpret_cast<const uint32_t*>(scales) + q0 * (kTileRows / 2) + (rlane >> 1),
+                    reinterpret_cast<const uint32_t*>(zeros) + q0 * (kTileRows / 8) + (rlane >> 3)};
   };
 
   // This workgroup's row tiles: t0 + r * gridDim.x for r < R (the host
-  // launches ceil(row tiles / R) workgroups, so t0 is in range). Tiles past
-  // the end are computed on a clamped (valid) tile and never stored.
+  // launches ceil(row tiles / R) workgroups, so t0 is in range); for SwiGLU
+  // the wave's half of the pair 2 t0, 2 t0 + 1, while the outputs are tile
+  // t0 of y. Tiles past the end are computed on a clamped (valid) tile and
+  // never stored.
   const int64_t t0 = blockIdx.x;
-  auto tile_of = [&](int r) { return t0 + int64_t(r) * gridDim.x; };
+  auto tile_of = [&](int r) { return kPair ? 2 * t0 + half : t0 + int64_t(r) * gridDim.x; };
+  auto out_tile_of = [&](int r) { return kPair ? t0 : tile_of(r); };
   auto clamp_tile = [&](int64_t t) { return t < row_tiles ? t : row_tiles - 1; };
   float sums[R][kOut];
 
@@ -287,41 +325,50 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     // sets. No branch and no store on this path, so every wait is exact.
     Round rr[2];
     {
-      const TilePtrs p = tile_ptrs(t0);
+      const TilePtrs p = tile_ptrs(tile_of(0));
       if constexpr (!kGlobalX) {
         // x requests go out just ahead of the first weight requests, so the
         // wait before the LDS store is for x alone; the staged slice then
         // serves all of this workgroup's row tiles.
         constexpr int kXSteps = (MR * SHARE * 16 + 63) / 64;
         const int xchunks = share_n * (kGroup / 8), xtotal = MR * xchunks;
+        const bool stages_x = !kPair || half == 0;  // wave-uniform
         u32x4 xv[kXSteps];
+        if (stages_x) {
 #pragma unroll
-        for (int j = 0; j < kXSteps; ++j) {  // clamped: unconditional, in bounds
-          const int c = min(lane + 64 * j, xtotal - 1);
-          const int m = c / xchunks, cc = c - m * xchunks;
-          xv[j] = *reinterpret_cast<const u32x4*>(x + int64_t(m) * K + int64_t(share_beg) * kGroup + cc * 8);
+          for (int j = 0; j < kXSteps; ++j) {  // clamped: unconditional, in bounds
+            const int c = min(lane + 64 * j, xtotal - 1);
+            const int m = c / xchunks, cc = c - m * xchunks;
+            xv[j] = *reinterpret_cast<const u32x4*>(x + int64_t(m) * K + int64_t(share_beg) * kGroup + cc * 8);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
-        load_round(rr[0], p.wlane, p.srow, p.zrow, share_beg, share_n);
+        load_round(rr[0], p.wlane, p.sword, p.zword, share_beg, share_n);
         __builtin_amdgcn_sched_barrier(0);
+        if (stages_x) {
 #pragma unroll
-        for (int j = 0; j < kXSteps; ++j) {  // clamped steps rewrite the last chunk with its own data
-          const int c = min(lane + 64 * j, xtotal - 1);
-          const int m = c / xchunks, cc = c - m * xchunks;
-          *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) = xv[j];
+          for (int j = 0; j < kXSteps; ++j) {  // clamped steps rewrite the last chunk with its own data
+            const int c = min(lane + 64 * j, xtotal - 1);
+            const int m = c / xchunks, cc = c - m * xchunks;
+            *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) = xv[j];
+          }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        if constexpr (kPair) {
+          lds_barrier();  // the up half reads what the gate half staged; weights stay in flight
+        } else {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        }
       } else {
-        load_round(rr[0], p.wlane, p.srow, p.zrow, share_beg, share_n);
+        load_round(rr[0], p.wlane, p.sword, p.zword, share_beg, share_n);
       }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (r + 1 < R) {
         const TilePtrs p = tile_ptrs(clamp_tile(tile_of(r + 1)));
-        load_round(rr[(r + 1) & 1], p.wlane, p.srow, p.zrow, share_beg, share_n);
+        load_round(rr[(r + 1) & 1], p.wlane, p.sword, p.zword, share_beg, share_n);
       }
       float acc[kAcc];
 #pragma unroll
@@ -329,9 +376,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
       compute_round(rr[r & 1], share_beg, share_n, acc);
       reduce_tile(acc, sums[r]);
     }
-  } else {
+  } else if constexpr (!kPair) {
     // Long K (several rounds per share, x restaged per round) or an empty
-    // share (a K range with fewer groups than waves): plain loop.
+    // share (a K range with fewer groups than waves): plain loop. (Never for
+    // SwiGLU, whose shapes were checked above.)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const TilePtrs p = tile_ptrs(clamp_tile(tile_of(r)));
@@ -342,14 +390,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
         const int n = min(SHARE, share_end - g0);
         stage_x(g0, n);
         Round rd;
-        load_round(rd, p.wlane, p.srow, p.zrow, g0, n);
+        load_round(rd, p.wlane, p.sword, p.zword, g0, n);
         compute_round(rd, g0, n, acc);
       }
       reduce_tile(acc, sums[r]);
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) store_tile(tile_of(r), sums[r]);
+  for (int r = 0; r < R; ++r) store_tile(out_tile_of(r), sums[r]);
   if (!part) return;
 
   // Split-K arrival. Each wave waits until its partial stores are complete
@@ -390,19 +438,25 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     if (last[r]) finish_tile(tile_of(r));
 }
 
-template <int MR, int WAVES, int SHARE, int ENGINE>
+template <int MR, int WAVES, int SHARE, int ENGINE, int EPI>
 constexpr size_t lds_for() {
-  return reduction_lds_bytes(MR, WAVES, ENGINE) +
-         (ENGINE == kEngineMfmaGlobalX ? 0 : size_t(WAVES) * MR * SHARE * kGroup * 2);
+  return gemv_lds_bytes(MR, WAVES, SHARE, ENGINE, EPI);
 }
 
-template <int MR, int WAVES, int SHARE, int ENGINE, int R>
+template <int MR, int WAVES, int SHARE, int ENGINE, int R, int EPI>
 hipError_t launch_typed(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
                         const void* zeros, const void* x, void* y, float* partials, hipStream_t stream) {
-  const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;
+  const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;  // output tiles for SwiGLU
   const int64_t grid = (row_tiles + R - 1) / R;
-  constexpr size_t lds = lds_for<MR, WAVES, SHARE, ENGINE>();
-  hipLaunchKernelGGL((gemv_kernel<MR, WAVES, SHARE, ENGINE, R>), dim3(unsigned(grid), unsigned(plan.splits)),
+  constexpr size_t lds = lds_for<MR, WAVES, SHARE, ENGINE, EPI>();
+  if constexpr (lds > kDefaultLdsLimit) {
+    // Raise this instantiation's dynamic-LDS limit once per process.
+    static const hipError_t raised = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemv_kernel<MR, WAVES, SHARE, ENGINE, R, EPI>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (raised != hipSuccess) return raised;
+  }
+  hipLaunchKernelGGL((gemv_kernel<MR, WAVES, SHARE, ENGINE, R, EPI>), dim3(unsigned(grid), unsigned(plan.splits)),
                      dim3(WAVES * 64), lds, stream, static_cast<const uint8_t*>(wq),
                      static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
                      static_cast<const _Float16*>(x), static_cast<_Float16*>(y), partials, N, K);
@@ -412,16 +466,20 @@ hipError_t launch_typed(int N, int K, const LaunchPlan& plan, const void* wq, co
 template <int MR, int ENGINE>
 hipError_t launch_shape(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
                         const void* zeros, const void* x, void* y, float* partials, hipStream_t stream) {
-#define W4A16_CASE(W, S, RR)                                                                            \
-  if constexpr (instantiated(MR, W, S, ENGINE, RR)) {                                                  \
-    if (plan.waves == W && plan.share == S && plan.tiles_per_wg == RR)                                 \
-      return launch_typed<MR, W, S, ENGINE, RR>(N, K, plan, wq, scales, zeros, x, y, partials, stream); \
+#define W4A16_CASE(W, S, RR, EP)                                                                            \
+  if constexpr (instantiated(MR, W, S, ENGINE, RR, EP)) {                                                  \
+    if (plan.waves == W && plan.share == S && plan.tiles_per_wg == RR && plan.epilogue == EP)              \
+      return launch_typed<MR, W, S, ENGINE, RR, EP>(N, K, plan, wq, scales, zeros, x, y, partials, stream); \
   }
 #define W4A16_SHARES(W, RR)                                                                             \
-  W4A16_CASE(W, 2, RR) W4A16_CASE(W, 3, RR) W4A16_CASE(W, 4, RR) W4A16_CASE(W, 5, RR) W4A16_CASE(W, 7, RR) \
-  W4A16_CASE(W, 8, RR) W4A16_CASE(W, 10, RR)
+  W4A16_CASE(W, 2, RR, kEpiStore) W4A16_CASE(W, 3, RR, kEpiStore) W4A16_CASE(W, 4, RR, kEpiStore)        \
+  W4A16_CASE(W, 5, RR, kEpiStore) W4A16_CASE(W, 7, RR, kEpiStore) W4A16_CASE(W, 8, RR, kEpiStore)        \
+  W4A16_CASE(W, 10, RR, kEpiStore)
   W4A16_SHARES(1, 1) W4A16_SHARES(2, 1) W4A16_SHARES(4, 1) W4A16_SHARES(8, 1) W4A16_SHARES(16, 1)
   W4A16_SHARES(4, 2) W4A16_SHARES(8, 2) W4A16_SHARES(4, 3) W4A16_SHARES(8, 3)
+#define W4A16_PAIR(W) W4A16_CASE(W, 4, 1, kEpiSwiglu) W4A16_CASE(W, 5, 1, kEpiSwiglu) W4A16_CASE(W, 7, 1, kEpiSwiglu)
+  W4A16_PAIR(2) W4A16_PAIR(4) W4A16_PAIR(8) W4A16_PAIR(16)
+#undef W4A16_PAIR
 #undef W4A16_SHARES
 #undef W4A16_CASE
   return hipErrorInvalidValue;

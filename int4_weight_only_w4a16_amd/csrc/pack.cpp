@@ -18,6 +18,7 @@
 // order (32 and 8 bytes), so the scale and zero requests of a wave touch one
 // cache line each instead of one line per row.
 #include <cstring>
+#include <vector>
 
 #include "w4a16.h"
 #include "w4a16_internal.h"
@@ -101,6 +102,29 @@ extern "C" int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, con
   return bad ? W4A16_EINVAL : W4A16_OK;
 }
 
+extern "C" int w4a16_pack_gate_up(int F, int K, const uint8_t* qg, const uint16_t* sg, const uint8_t* zg,
+                                  const uint8_t* qu, const uint16_t* su, const uint8_t* zu, void* wq_out,
+                                  void* s_out, void* z_out) {
+  if (!shape_ok(F, K)) return W4A16_EINVAL;
+  if (F == 0) return W4A16_OK;
+  if (!qg || !sg || !zg || !qu || !su || !zu || !wq_out || !s_out || !z_out) return W4A16_EINVAL;
+  // Interleave 16-row blocks (gate block j, then up block j; rows past F in
+  // a block are zero) and pack the 2 * roundup(F, 16)-row result.
+  const int64_t G = K / W4A16_GROUP, blocks = (int64_t(F) + 15) / 16, rows = 32 * blocks;
+  std::vector<uint8_t> q(size_t(rows) * K, 0), z(size_t(rows) * G, 0);
+  std::vector<uint16_t> s(size_t(rows) * G, 0);
+  for (int64_t f = 0; f < F; ++f) {
+    const int64_t rg = 32 * (f / 16) + f % 16, ru = rg + 16;
+    std::memcpy(&q[rg * K], qg + f * K, size_t(K));
+    std::memcpy(&q[ru * K], qu + f * K, size_t(K));
+    std::memcpy(&s[rg * G], sg + f * G, size_t(G) * 2);
+    std::memcpy(&s[ru * G], su + f * G, size_t(G) * 2);
+    std::memcpy(&z[rg * G], zg + f * G, size_t(G));
+    std::memcpy(&z[ru * G], zu + f * G, size_t(G));
+  }
+  return w4a16_pack(int(rows), K, q.data(), s.data(), z.data(), wq_out, s_out, z_out);
+}
+
 extern "C" int w4a16_unpack(int N, int K, const void* wq_in, const void* s_packed, const void* z_packed,
                             uint8_t* q, uint16_t* s, uint8_t* z) {
   if (!shape_ok(N, K)) return W4A16_EINVAL;
@@ -138,7 +162,7 @@ extern "C" const char* w4a16_strerror(int status) {
   switch (status) {
     case W4A16_OK: return "ok";
     case W4A16_EINVAL: return "invalid argument (shape, pointer, alignment or value)";
-    case W4A16_EUNSUPPORTED: return "unsupported: more than 8 activation rows";
+    case W4A16_EUNSUPPORTED: return "unsupported: more than 8 activation rows, or a fused shape beyond its limits";
     case W4A16_ELAYOUT: return "packed layout ID mismatch";
     case W4A16_EHIP: return "HIP runtime refused the launch";
     default: return "unknown status";

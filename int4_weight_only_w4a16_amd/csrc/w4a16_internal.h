@@ -36,20 +36,32 @@ enum Engine : int {
   kEngineMfmaGlobalX = 2  // v_mfma_f32_16x16x32_f16, x read straight from global memory
 };
 
+// What the GEMV kernel does with its sums.
+enum Epilogue : int {
+  kEpiStore = 0,   // y = fp16(sum) (or split-K partials)
+  kEpiSwiglu = 1,  // row tiles 2j (gate) and 2j+1 (up), half the waves each -> y = fp16(silu(gate) * up)
+};
+
 // Launch parameters chosen by the front end for one GEMV shape.
 struct LaunchPlan {
   int engine;  // Engine
   int waves;   // waves per workgroup: 1, 2, 4, 8 or 16
-  int share;   // tiles a wave requests at once (2, 4, 8 or 12); longer shares take several rounds
+  int share;   // tiles a wave requests at once (2 .. 10); longer shares take several rounds
   int splits;  // K ranges (gridDim.y); 1 for the plain GEMV
   int tiles_per_wg;  // row tiles per workgroup, 1..3 (gridDim.x = ceil(row tiles / this))
+  int epilogue;      // Epilogue (kEpiSwiglu: tiles_per_wg 1, waves = 2 x the waves per row tile)
 };
 
 // Instantiated (waves, share, row tiles per workgroup) per engine and M:
 // those that fit in registers without spilling. Several row tiles per
 // workgroup (R > 1, software-pipelined) only for the MFMA engine with x in
-// LDS; the VALU dot2 engine only for M = 1.
-constexpr bool instantiated(int mr, int waves, int share, int engine, int r) {
+// LDS; the VALU dot2 engine only for M = 1. The SwiGLU epilogue: MFMA, one
+// gate/up pair per workgroup (2, 4, 8 or 16 waves in two halves), shares of
+// 4, 5 or 7, within the register rule of the plain kernel of as many waves.
+constexpr bool instantiated(int mr, int waves, int share, int engine, int r, int epi = kEpiStore) {
+  if (epi == kEpiSwiglu)
+    return r == 1 && engine == kEngineMfma && (waves == 2 || waves == 4 || waves == 8 || waves == 16) &&
+           (share == 4 || share == 5 || share == 7) && instantiated(mr, waves, share, engine, 1);
   if (r > 1)
     return engine == kEngineMfma && (waves == 4 || waves == 8) &&
            (share == 4 || share == 5 || share == 7 || share == 8) && !(waves == 8 && share == 8) &&
@@ -66,8 +78,19 @@ constexpr size_t reduction_lds_bytes(int mr, int waves, int engine) {
   return 2 * size_t(waves) * 4 * (engine == kEngineDot2 ? mr : (mr < 4 ? mr : 4)) * 16 * sizeof(float);
 }
 
-// Largest dynamic LDS a GEMV workgroup may use.
-constexpr size_t kMaxLdsBytes = 64 * 1024;
+// Dynamic LDS of a GEMV workgroup: the reduction buffers, then one x slice
+// [M][share * 128] fp16 per wave (per pair of waves for SwiGLU, whose gate
+// and up halves share the slices; none when x is read from global memory).
+constexpr size_t gemv_lds_bytes(int mr, int waves, int share, int engine, int epi) {
+  return reduction_lds_bytes(mr, waves, engine) +
+         (engine == kEngineMfmaGlobalX ? 0
+                                       : size_t(epi == kEpiSwiglu ? waves / 2 : waves) * mr * share * kGroup * 2);
+}
+
+// Largest dynamic LDS a GEMV workgroup may use: gfx950's 160 KiB per
+// workgroup (a launch above 64 KiB first raises the kernel's limit).
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+constexpr size_t kDefaultLdsLimit = 64 * 1024;
 
 // Dynamic LDS bytes of a GEMV launch (0 for kEngineMfmaGlobalX).
 size_t lds_bytes(int M, int K, const LaunchPlan& plan);

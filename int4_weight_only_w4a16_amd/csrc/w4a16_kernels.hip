@@ -34,9 +34,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 size_t lds_bytes(int M, int K, const LaunchPlan& plan) {
   (void)K;
-  const size_t red = reduction_lds_bytes(M, plan.waves, plan.engine);
-  if (plan.engine == kEngineMfmaGlobalX) return red;
-  return red + size_t(plan.waves) * M * plan.share * kGroup * 2;
+  return gemv_lds_bytes(M, plan.waves, plan.share, plan.engine, plan.epilogue);
 }
 
 bool plan_supported(int M, int K, const LaunchPlan& plan) {
@@ -46,7 +44,13 @@ bool plan_supported(int M, int K, const LaunchPlan& plan) {
   const int w = plan.waves, sh = plan.share;
   if (!(w == 1 || w == 2 || w == 4 || w == 8 || w == 16)) return false;
   if (!(sh == 2 || sh == 3 || sh == 4 || sh == 5 || sh == 7 || sh == 8 || sh == 10)) return false;
-  if (!instantiated(M, w, sh, plan.engine, plan.tiles_per_wg)) return false;
+  if (plan.epilogue == kEpiSwiglu) {
+    // One round per wave, every wave with at least one group (the kernel
+    // relies on it for its one staging barrier).
+    const int groups = K / kGroup, half = plan.waves / 2;
+    if (plan.splits != 1 || groups < half || (groups + half - 1) / half > plan.share) return false;
+  }
+  if (!instantiated(M, w, sh, plan.engine, plan.tiles_per_wg, plan.epilogue)) return false;
   return lds_bytes(M, K, plan) <= kMaxLdsBytes;
 }
 

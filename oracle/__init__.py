@@ -134,7 +134,7 @@ class Oracle:
         return ref, absref
 
     def gemv_packed(self, M, N, K, wq, sp, zp, x, rows=None):
-        """Product from layout-ID-1 buffers; with ``rows``, only those rows."""
+        """Product from layout-ID-2 buffers; with ``rows``, only those rows."""
         wq, sp, zp = (np.ascontiguousarray(a, dtype=np.uint8) for a in (wq, sp, zp))
         x = np.ascontiguousarray(x, dtype=np.uint16)
         if rows is None:
@@ -159,6 +159,46 @@ class Oracle:
 # fp64 reference.
 BOUND_REL = 2e-3
 BOUND_ABS = 1e-5
+
+# sup |d silu / dx| over the reals (attained near x = 2.40): silu' = s(1 + x(1 - s)),
+# s the logistic function. Pinned numerically in the oracle pins.
+SILU_LIPSCHITZ = 1.0999
+
+
+def silu(v):
+    """silu(v) = v / (1 + exp(-v)) in fp64 (the SwiGLU gate activation)."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def gemv_swiglu(oracle, qg, sg, zg, qu, su, zu, x):
+    """Fused gate/up + SwiGLU reference: y = silu(g) * u with g and u the
+    fp64 GEMVs of the gate and up matrices (logical form), and a per-output
+    acceptance bound derived from the GEMV bound:
+
+    the kernel's g and u are fp32 sums within dg = REL*|Wg||x| + ABS and
+    du = REL*|Wu||x| + ABS of the exact values (the GEMV bound, which also
+    covers an fp16 rounding the fused path does not even make), so
+        |silu(g~) u~ - silu(g) u| <= L dg (|u| + du) + |silu(g)| du,
+    L = SILU_LIPSCHITZ; the fp32 epilogue and the final fp16 rounding add at
+    most 2^-10 |y| more (plus ABS for underflow). Returns (ref, bound)."""
+    g, ag = oracle.gemv(qg, sg, zg, x)
+    u, au = oracle.gemv(qu, su, zu, x)
+    ref = silu(g) * u
+    dg = BOUND_REL * ag + BOUND_ABS
+    du = BOUND_REL * au + BOUND_ABS
+    bound = SILU_LIPSCHITZ * dg * (np.abs(u) + du) + np.abs(silu(g)) * du + 2.0 ** -10 * np.abs(ref) + BOUND_ABS
+    return ref, bound
+
+
+def swiglu_report(y_f16_bits, ref, bound, oracle):
+    """Returns (ok, worst) where worst = max |y-ref| / bound."""
+    y = oracle.f16_to_f64(np.asarray(y_f16_bits, dtype=np.uint16))
+    ratio = np.abs(y - ref) / bound
+    ratio[np.isnan(ratio)] = np.inf
+    worst = float(ratio.max()) if ratio.size else 0.0
+    return worst <= 1.0, worst
 
 
 def bound_report(y_f16_bits, ref, absref, oracle):

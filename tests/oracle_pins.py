@@ -324,4 +324,83 @@ def pin_gemv_packed_matches_logical(o):
         assert np.array_equal(ref3, ref[:, rows])
 
 
+# ------------------------------------------------------------------ SwiGLU
+
+def pin_silu_definition(o):
+    """silu(v) = v * logistic(v), against scipy's logistic function (an
+    independent library routine); silu(0) = 0; the reflection identity
+    silu(-v) = silu(v) - v; saturation to v and to 0."""
+    from scipy.special import expit
+    import oracle
+    v = np.concatenate([np.linspace(-30, 30, 6001), [0.0, 1e-300, -1e-300, 1e-8, 700.0, -700.0]])
+    got = oracle.silu(v)
+    assert np.allclose(got, v * expit(v), rtol=4e-16, atol=0)
+    assert oracle.silu(0.0) == 0.0
+    assert np.allclose(oracle.silu(-v[:6001]), got[:6001] - v[:6001], rtol=1e-12, atol=1e-12)
+    assert oracle.silu(80.0) == 80.0 and abs(oracle.silu(-80.0)) < 1e-30
+    assert oracle.silu(-1000.0) == 0.0  # exp overflow handled, no NaN
+
+
+def pin_silu_lipschitz_constant(o):
+    """SILU_LIPSCHITZ bounds |silu'| and is tight: central differences of
+    scipy's v * logistic(v) peak at 1.0998 near v = 2.4."""
+    from scipy.special import expit
+    import oracle
+    v = np.linspace(-40, 40, 400001)
+    h = 1e-5
+    d = ((v + h) * expit(v + h) - (v - h) * expit(v - h)) / (2 * h)
+    assert np.abs(d).max() <= oracle.SILU_LIPSCHITZ
+    assert np.abs(d).max() > oracle.SILU_LIPSCHITZ - 2e-4
+    assert 2.3 < v[np.argmax(d)] < 2.5
+
+
+def pin_swiglu_composition(o):
+    """x = e_k makes g and u single dequantized weights, so the fused
+    reference must be silu(w_gate[n][k]) * w_up[n][k] exactly; with an up
+    matrix whose column k dequantizes to 1 it must be silu(g) alone (which
+    fixes the gate/up roles); rows of gate and up stay paired."""
+    from scipy.special import expit
+    import oracle
+    F, K = 24, 384
+    qg, sg, zg = synthetic.weights(F, K, seed=41, tensor_id=1)
+    qu, su, zu = synthetic.weights(F, K, seed=41, tensor_id=2)
+    wg, wu = o.dequant(qg, sg, zg), o.dequant(qu, su, zu)
+    for k in (0, 129, 383):
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = 0x3C00
+        ref, bound = oracle.gemv_swiglu(o, qg, sg, zg, qu, su, zu, x)
+        want = wg[:, k] * expit(wg[:, k]) * wu[:, k]
+        assert np.allclose(ref[0], want, rtol=1e-15, atol=0) and (bound > 0).all()
+    ones_q = np.full((F, K), 1, np.uint8)
+    ones_s = np.full((F, K // GROUP), 0x3C00, np.uint16)
+    ones_z = np.zeros((F, K // GROUP), np.uint8)
+    x = synthetic.activations(2, K, seed=43)
+    x[:, :] = 0
+    x[:, 7] = 0x3C00  # one-hot: u = 1 for every row, g = w_gate[:, 7]
+    ref, _ = oracle.gemv_swiglu(o, qg, sg, zg, ones_q, ones_s, ones_z, x)
+    assert np.allclose(ref, wg[:, 7] * expit(wg[:, 7]), rtol=1e-15, atol=0)
+    p = np.random.default_rng(44).permutation(F)
+    x = synthetic.activations(1, K, seed=45)
+    ref, _ = oracle.gemv_swiglu(o, qg, sg, zg, qu, su, zu, x)
+    refp, _ = oracle.gemv_swiglu(o, qg[p], sg[p], zg[p], qu[p], su[p], zu[p], x)
+    assert np.array_equal(refp, ref[:, p])
+
+
+def pin_swiglu_bound_admits_rounded_reference(o):
+    """The acceptance bound is at least the fp16 rounding of the exact value
+    (a correct fp16 answer can always pass) and well below the output scale,
+    so an O(1) mistake cannot hide in it. (It inherits the GEMV bound's
+    2e-3 * sum|w x|, about 25 x |y| at K = 1024, once from g and once from
+    u: about 11% of the mean |y| here.)"""
+    import oracle
+    F, K = 64, 1024
+    qg, sg, zg = synthetic.weights(F, K, seed=47, tensor_id=1)
+    qu, su, zu = synthetic.weights(F, K, seed=47, tensor_id=2)
+    x = synthetic.activations(3, K, seed=48)
+    ref, bound = oracle.gemv_swiglu(o, qg, sg, zg, qu, su, zu, x)
+    r16 = o.f16_to_f64(o.f64_to_f16(ref))
+    assert (np.abs(r16 - ref) <= bound).all()
+    assert np.median(bound / np.abs(ref).mean()) < 0.2
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

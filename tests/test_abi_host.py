@@ -71,6 +71,33 @@ def test_pack_edge_patterns(orc):
             assert np.array_equal(a, b)
 
 
+def _interleave_16(a_gate, a_up, fill=0):
+    """Row blocks of 16: gate block j, then up block j (rows past F zero)."""
+    F = a_gate.shape[0]
+    blocks = (F + 15) // 16
+    out = np.full((32 * blocks,) + a_gate.shape[1:], fill, a_gate.dtype)
+    for f in range(F):
+        out[32 * (f // 16) + f % 16] = a_gate[f]
+        out[32 * (f // 16) + f % 16 + 16] = a_up[f]
+    return out
+
+
+@pytest.mark.parametrize("F,K", [(1, 128), (16, 256), (40, 896), (77, 640)])
+def test_pack_gate_up_is_the_16_row_interleave(orc, F, K):
+    """w4a16_pack_gate_up == the oracle's packing of the 16-row interleave."""
+    qg, sg, zg = synthetic.weights(F, K, seed=F, tensor_id=1)
+    qu, su, zu = synthetic.weights(F, K, seed=F, tensor_id=2)
+    mine = w.w4a16_pack_gate_up(qg, sg, zg, qu, su, zu)
+    ref = orc.pack(_interleave_16(qg, qu), _interleave_16(sg, su), _interleave_16(zg, zu))
+    for a, b in zip(mine, ref):
+        assert np.array_equal(a, b)
+    L = w.lib()
+    assert L.w4a16_pack_gate_up(F, K, None, sg.ctypes.data, zg.ctypes.data, qu.ctypes.data, su.ctypes.data,
+                                zu.ctypes.data, *(m.ctypes.data for m in mine)) == w.W4A16_EINVAL
+    assert L.w4a16_pack_gate_up(F, 200, *(a.ctypes.data for a in (qg, sg, zg, qu, su, zu)),
+                                *(m.ctypes.data for m in mine)) == w.W4A16_EINVAL
+
+
 def test_pack_rejects_bad_values_and_shapes():
     L = w.lib()
     q = np.zeros((2, 128), np.uint8)
@@ -120,6 +147,11 @@ def test_device_entry_points_reject_before_launch():
         assert L.w4a16_gemv_splitk(2, 16, 768, splits, *ptrs, fake, wsb, None) == want, splits
     assert L.w4a16_gemv_splitk(9, 16, 768, 2, *ptrs, fake, 10 ** 9, None) == w.W4A16_EUNSUPPORTED
     assert L.w4a16_gemv_splitk(2, 0, 768, 2, *ptrs, fake, 0, None) == w.W4A16_OK
+    # fused SwiGLU
+    assert L.w4a16_gemv_swiglu(1, 16, 200, *ptrs, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemv_swiglu(9, 16, 128, *ptrs, None) == w.W4A16_EUNSUPPORTED
+    assert L.w4a16_gemv_swiglu(1, 0, 128, *ptrs, None) == w.W4A16_OK
+    assert L.w4a16_gemv_swiglu(1, 16, 128, fake, fake, fake, fake + 2, fake, None) == w.W4A16_EINVAL
     # dequant hook
     assert L.w4a16_dequant_f32(16, 200, fake, fake, fake, fake, None) == w.W4A16_EINVAL
     assert L.w4a16_dequant_f32(0, 128, None, None, None, None, None) == w.W4A16_OK

@@ -1,0 +1,114 @@
+"""GPU parity of the fused gate/up + SwiGLU GEMV (w4a16_gemv_swiglu) through
+the C ABI against the oracle's fp64 silu(g) * u, within the bound derived in
+oracle.gemv_swiglu from the workload's GEMV bound."""
+import numpy as np
+import pytest
+
+import int4_weight_only_w4a16_amd as w
+import oracle
+import synthetic
+from tests.gpu_common import torch_dev, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[swiglu]", *a, flush=True)
+
+
+class SwigluProblem:
+    def __init__(self, M, F, K, seed=0, gate=None, up=None, x=None):
+        self.M, self.F, self.K = M, F, K
+        self.gate = gate if gate is not None else synthetic.weights(F, K, seed=seed, tensor_id=11)
+        self.up = up if up is not None else synthetic.weights(F, K, seed=seed, tensor_id=12)
+        self.x = x if x is not None else synthetic.activations(M, K, seed=seed, tensor_id=13)
+        packed = w.w4a16_pack_gate_up(*self.gate, *self.up)
+        self.wq_d, self.sp_d, self.zp_d = (upload(a) for a in packed)
+        self.x_d = upload(self.x)
+
+    def run(self, x_d=None, stream=None):
+        torch, dev = torch_dev()
+        y = torch.full((self.M, self.F), -1, dtype=torch.int16, device=dev)
+        w.w4a16_gemv_swiglu(self.M, self.F, self.K, self.wq_d, self.sp_d, self.zp_d,
+                            self.x_d if x_d is None else x_d, y, stream=stream)
+        torch.cuda.synchronize()
+        return y.cpu().numpy().view(np.uint16)
+
+    def check(self, y):
+        o = oracle.get()
+        ref, bound = oracle.gemv_swiglu(o, *self.gate, *self.up, self.x)
+        ok, worst = oracle.swiglu_report(y, ref, bound, o)
+        assert ok, f"M={self.M} F={self.F} K={self.K}: worst |y-ref|/bound = {worst}"
+        return worst
+
+
+@pytest.mark.parametrize("M,F,K", [(1, 4864, 896), (1, 18944, 3584), (5, 18944, 3584), (8, 17408, 5120),
+                                   (2, 33, 6144), (3, 1, 128), (7, 40, 256), (1, 16, 128), (4, 200, 5120),
+                                   (2, 48, 7168)])
+def test_swiglu_against_oracle(M, F, K):
+    _say("shape", M, F, K)
+    p = SwigluProblem(M, F, K, seed=M + F)
+    y = p.run()
+    _say(M, F, K, "worst", p.check(y))
+    assert np.array_equal(y, p.run()), "run-to-run difference"
+
+
+def test_swiglu_refuses_multi_round_shapes():
+    """Every share must fit one round: K up to 5120 for any M (7168 for
+    M <= 2); beyond that the call is refused before any launch."""
+    p = SwigluProblem(3, 32, 7168, seed=1)
+    with pytest.raises(w.W4A16Error) as e:
+        p.run()
+    assert e.value.status == w.W4A16_EUNSUPPORTED
+    p = SwigluProblem(1, 32, 18944, seed=1)
+    with pytest.raises(w.W4A16Error) as e:
+        p.run()
+    assert e.value.status == w.W4A16_EUNSUPPORTED
+
+
+def test_swiglu_batch_invariance():
+    """Row m of an 8-row call equals the same row computed alone, bit for bit."""
+    F, K = 18944, 3584
+    _say("batch invariance", F, K)
+    x = synthetic.activations(8, K, seed=21)
+    gate, up = synthetic.weights(F, K, seed=21, tensor_id=1), synthetic.weights(F, K, seed=21, tensor_id=2)
+    y8 = SwigluProblem(8, F, K, gate=gate, up=up, x=x).run()
+    for m in (0, 3, 7):
+        alone = SwigluProblem(1, F, K, gate=gate, up=up, x=x[m:m + 1].copy()).run()
+        assert np.array_equal(y8[m], alone[0]), m
+
+
+def test_swiglu_zero_gate_or_up_gives_zero():
+    """q = z in the up matrix makes u = 0 exactly, and in the gate matrix
+    g = 0 exactly (silu(0) = 0): either way every output is +-0."""
+    F, K = 96, 1024
+    _say("zeros", F, K)
+    qg, sg, zg = synthetic.weights(F, K, seed=5, tensor_id=1)
+    qu, su, zu = synthetic.weights(F, K, seed=5, tensor_id=2)
+    flat_u = (np.repeat(zu, 128, axis=1), su, zu)
+    y = SwigluProblem(2, F, K, gate=(qg, sg, zg), up=flat_u).run()
+    assert not (y & 0x7FFF).any()
+    flat_g = (np.repeat(zg, 128, axis=1), sg, zg)
+    y = SwigluProblem(2, F, K, gate=flat_g, up=(qu, su, zu)).run()
+    assert not (y & 0x7FFF).any()
+
+
+def test_swiglu_graph_replay():
+    torch, dev = torch_dev()
+    p = SwigluProblem(1, 4864, 896, seed=3)
+    eager = p.run()
+    y = torch.full((1, p.F), -1, dtype=torch.int16, device=dev)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        w.w4a16_gemv_swiglu(1, p.F, p.K, p.wq_d, p.sp_d, p.zp_d, p.x_d, y, stream=stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            w.w4a16_gemv_swiglu(1, p.F, p.K, p.wq_d, p.sp_d, p.zp_d, p.x_d, y, stream=stream)
+    for _ in range(3):
+        y.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), eager)

@@ -31,3 +31,47 @@ def test_plant_is_caught(tmp_path, plant):
         except (AssertionError, ValueError) as e:  # noqa: PERF203
             caught.append(pin.__name__)
     assert caught, f"no pin caught planted mistake {plant}: {PLANTS[plant]}"
+
+
+# Mistakes in the SwiGLU composition (the Python part of the oracle).
+def _swap_gate_up(real):
+    def mutant(o, qg, sg, zg, qu, su, zu, x):
+        return real(o, qu, su, zu, qg, sg, zg, x)
+    return mutant
+
+
+def _sigmoid_for_silu(real_silu):
+    def mutant(v):
+        v = oracle.np.asarray(v, dtype=oracle.np.float64)
+        return 1.0 / (1.0 + oracle.np.exp(-v))
+    return mutant
+
+
+def _silu_sign_flipped(real_silu):
+    def mutant(v):
+        v = oracle.np.asarray(v, dtype=oracle.np.float64)
+        return v / (1.0 + oracle.np.exp(v))
+    return mutant
+
+
+SWIGLU_PLANTS = {
+    "gate_and_up_swapped": ("gemv_swiglu", _swap_gate_up),
+    "sigmoid_instead_of_silu": ("silu", _sigmoid_for_silu),
+    "silu_exponent_sign_flipped": ("silu", _silu_sign_flipped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SWIGLU_PLANTS))
+def test_swiglu_plant_is_caught(monkeypatch, name):
+    attr, make = SWIGLU_PLANTS[name]
+    monkeypatch.setattr(oracle, attr, make(getattr(oracle, attr)))
+    o = oracle.get()
+    caught = []
+    for pin in oracle_pins.PINS:
+        if "silu" not in pin.__name__ and "swiglu" not in pin.__name__:
+            continue
+        try:
+            pin(o)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught planted SwiGLU mistake {name}"
