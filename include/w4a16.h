@@ -150,38 +150,49 @@ int w4a16_gemv_swiglu(int M, int F, int K, const void* Wq, const void* scales, c
                       const void* x, void* y, void* stream);
 
 /*
- * Workspace bytes w4a16_gemv_splitk needs for (M, N, splits): fp32 partial
- * sums [splits][M][N], then one uint32 arrival counter per 16-row tile of
- * y, each part rounded up to a multiple of 16 bytes. Returns 0 for a
- * negative argument.
+ * Workspace bytes w4a16_gemv_splitk needs for an M x N output: one uint64
+ * accumulation word per output, 8 * M * N rounded up to a multiple of 16
+ * (the same for every split count). Returns 0 for a negative argument.
  */
 size_t w4a16_splitk_workspace_bytes(int M, int N, int splits);
 
 /*
- * Split count this library would use for an M x N x K split-K call: 1 when
- * the matrix has enough 16-row tiles to fill the GPU on its own, more for
- * skinny N with a long K. Returns 0 for an invalid shape.
+ * Split count this library recommends for an M x N x K split-K call,
+ * measured on MI355X: about one split per 16 groups of 128 when K has at
+ * least 96 groups and the matrix 257 to 1023 tiles of 16 rows; about one
+ * per 12 groups when it has fewer than 128 tiles and K at least 24 groups;
+ * otherwise 1 (do not split). At most 16. It does not depend on M, so rows stay batch invariant
+ * for a caller who follows it. Returns 0 for an invalid shape.
  */
 int w4a16_splitk_choose(int M, int N, int K);
 
 /*
- * Split-K variant of w4a16_gemv for matrices with few rows. The K groups are
- * divided into `splits` contiguous ranges, and each (16-row tile, range)
- * workgroup writes one fp32 partial product to `workspace`. The last
- * workgroup of a tile to finish adds that tile's partials in ascending split
- * order, rounds them to fp16 into y and resets the tile's counter. This is
- * the two-stage partial/final shape of "CodeAlign-Runtime", Level 4, applied
- * to K, in one launch. The fixed order keeps results bit-identical run to
- * run: the qengine page ("Learnings") found float atomics made runs differ,
- * and a fixed summation order fixed it. No workgroup ever waits for another.
- *   1 <= splits <= K/128; splits == 1 is w4a16_gemv and does not touch
- *   the workspace.
- *   workspace: device memory, 16-byte aligned, of at least
- *   ws_bytes >= w4a16_splitk_workspace_bytes(M, N, splits) bytes. It must
- *   be zero-filled once before its first use. Every completed call leaves
- *   its counters at zero again, so one workspace serves any later call on
- *   the same stream, and graph replays too. Calls that may overlap in time
- *   (different streams) need different workspaces.
+ * Split-K variant of w4a16_gemv for long K. The K groups are divided into
+ * `splits` contiguous ranges, so a matrix with few rows still gets a grid
+ * large enough to fill the GPU. This is the two-stage partial/final shape of
+ * "CodeAlign-Runtime", Level 4, applied to K, done in one launch:
+ *   - each (16-row tile, range) workgroup turns its fp32 partial sums into
+ *     fixed point, round(p * 2^24), and adds them with a device-scope atomic
+ *     to one 64-bit word per output in `workspace`;
+ *   - the word also counts the arrivals, so the add that completes the count
+ *     returns the whole sum; that workgroup writes y = fp16(sum * 2^-24) and
+ *     sets the word back to zero.
+ * Integer addition is exact and order-free, so results are bit-identical run
+ * to run whatever the arrival order (the determinism rule of the qengine
+ * page, "Learnings": float atomics made runs differ). Each fixed-point
+ * partial is within 2^-25 of the fp32 one; a partial is clamped to
+ * |p| < 2^29 (past that the workload's error bound already exceeds the whole
+ * fp16 range, and a clamped sum still overflows to +-inf in fp16 as the
+ * exact one would), and a NaN partial counts as 0. No workgroup ever waits
+ * for another, and no fence is needed: each word is one atomic location.
+ *   1 <= splits <= min(K/128, 31); splits == 1 is w4a16_gemv and does not
+ *   touch the workspace.
+ *   workspace: device memory, 16-byte aligned, at least
+ *   w4a16_splitk_workspace_bytes(M, N, splits) bytes, zero-filled once
+ *   before its first use. Every completed call leaves it all zero again, so
+ *   one workspace serves any later call on the same stream, and graph
+ *   replays too. Calls that may overlap in time (different streams) need
+ *   different workspaces.
  * Results may differ in rounding from w4a16_gemv (another summation order)
  * but lie within the same accuracy bound. Errors are as w4a16_gemv, plus
  * W4A16_EINVAL for a bad split count or a short workspace.

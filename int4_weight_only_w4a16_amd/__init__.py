@@ -174,8 +174,8 @@ def w4a16_splitk_choose(M, N, K):
 
 def w4a16_gemv_splitk(M, N, K, splits, Wq, scales, zeros, x, y, workspace, ws_bytes=None, stream=None):
     """Device: split-K GEMV in one launch. workspace: zero-filled once before
-    first use ([splits][M][N] fp32 partials, then per-tile counters that every
-    call leaves at zero)."""
+    first use (one uint64 accumulation word per output; every call leaves it
+    zero again)."""
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().w4a16_gemv_splitk(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x),

@@ -46,7 +46,10 @@ w4a16::LaunchPlan plan_for(int M, int N, int K, int splits) {
   (void)N;
   const int groups = K / W4A16_GROUP;
   const int range = (groups + splits - 1) / splits;
-  const int target = 10;
+  // Split-K grids are large already: shorter shares (more waves per
+  // workgroup) measured faster there (3584 x 18944 at 8 splits: 4 waves x 5
+  // tiles 8.9 us, 2 waves x 10 tiles 9.6 us).
+  const int target = splits > 1 ? 5 : 10;
   w4a16::LaunchPlan plan;
   plan.engine = w4a16::kEngineMfma;
   plan.splits = splits;
@@ -64,20 +67,27 @@ w4a16::LaunchPlan plan_for(int M, int N, int K, int splits) {
   return plan;
 }
 
-// Split count for w4a16_gemv_splitk. Each split workgroup pays one
-// device-scope release (a write-back of its XCD's L2) and the last arriver
-// one device-scope acquire; measured on MI355X that costs more than it gains
-// once a matrix has a few hundred 16-row tiles (3584 x 18944: 9.4 us
-// unsplit, 15.3 us at 2 splits). It pays for skinny N with a long K
-// (128 x 18944: 6 splits fastest): about 24 groups per split, at most 8
-// splits, and at most 128 (tile, split) pairs.
+// Split count for w4a16_gemv_splitk (never depends on M, so a caller who
+// follows it keeps rows batch invariant). From a sweep of split counts on
+// MI355X, each with the plan plan_for gives it:
+//  - a long K (at least 96 groups) unsplit runs one 16-wave workgroup per
+//    row tile, one per CU at a time; with 256 to 1024 row tiles that takes
+//    two or more passes over the CUs, and splitting pays, about one split
+//    per 16 groups (5120 x 17408: 15.5 -> about 12 us at M = 1, 28 -> 16 us
+//    at M = 8). With at most 256 row tiles one pass holds them and it did
+//    not (3584 x 18944: 8.7 us unsplit, 9.4 us at 9 splits in a decode step);
+//  - fewer than 128 row tiles with K of 24 groups or more: about one split
+//    per 12 groups (128 x 18944: 7.3 -> 3.7 us);
+//  - elsewhere it lost (qkv 4608 x 3584: 4.65 us unsplit, 5.25 us at 2).
 int choose_splits(int N, int K) {
   const int groups = K / W4A16_GROUP;
   const int64_t row_tiles = (int64_t(N) + 15) / 16;
-  int64_t splits = groups / 24;
-  if (splits > 128 / row_tiles) splits = 128 / row_tiles;
-  if (splits > 8) splits = 8;
-  return splits < 1 ? 1 : int(splits);
+  int splits = 1;
+  if (groups >= 96 && row_tiles > 256 && row_tiles < 1024)
+    splits = groups / 16;
+  else if (row_tiles < 128 && groups >= 24)
+    splits = groups / 12 < 2 ? 2 : groups / 12;
+  return splits > 16 ? 16 : splits;
 }
 
 // Plan of the fused gate/up + SwiGLU launch: one gate/up pair of row tiles
@@ -126,7 +136,7 @@ extern "C" int w4a16_gemv_swiglu(int M, int F, int K, const void* Wq, const void
 
 extern "C" size_t w4a16_splitk_workspace_bytes(int M, int N, int splits) {
   if (M < 0 || N < 0 || splits < 0) return 0;
-  return w4a16::splitk_workspace_bytes(M, N, splits);
+  return w4a16::splitk_workspace_bytes(M, N);
 }
 
 extern "C" int w4a16_splitk_choose(int M, int N, int K) {
@@ -139,14 +149,14 @@ extern "C" int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq
                                  size_t ws_bytes, void* stream) {
   const int rc = check_shape(M, N, K);
   if (rc < 0) return rc;
-  if (splits < 1 || splits > K / W4A16_GROUP) return W4A16_EINVAL;
+  if (splits < 1 || splits > K / W4A16_GROUP || splits > w4a16::kMaxSplits) return W4A16_EINVAL;
   if (rc == 1) return W4A16_OK;
   if (splits == 1) return w4a16_gemv(M, N, K, Wq, scales, zeros, x, y, stream);
   if (!pointers_ok({Wq, scales, zeros, x, y, workspace})) return W4A16_EINVAL;
-  if (ws_bytes < w4a16::splitk_workspace_bytes(M, N, splits)) return W4A16_EINVAL;
+  if (ws_bytes < w4a16::splitk_workspace_bytes(M, N)) return W4A16_EINVAL;
   const w4a16::LaunchPlan plan = plan_for(M, N, K, splits);
-  float* partials = static_cast<float*>(workspace);
-  if (w4a16::launch_gemv(M, N, K, plan, Wq, scales, zeros, x, y, partials, stream) != 0) return W4A16_EHIP;
+  auto* acc = static_cast<unsigned long long*>(workspace);
+  if (w4a16::launch_gemv(M, N, K, plan, Wq, scales, zeros, x, y, acc, stream) != 0) return W4A16_EHIP;
   return W4A16_OK;
 }
 

@@ -33,17 +33,20 @@ namespace dev {
 // LDS barrier after staging), and every share fits one round: the host
 // launches nothing else, and a workgroup exits at once (all of it) if the
 // shape would need more.
-// Writes fp16 y[MR][N] directly when `part` is null. Otherwise (split-K,
-// gridDim.y splits) each workgroup writes its fp32 partial to
-// part[split][MR][N] and counts its arrival in the row tile's counter (the
-// uint32 array after the partials, 16-byte aligned); the last of a tile's
-// splits to arrive adds the partials in split order, writes y and resets
-// the counter to zero for the next call.
+// Writes fp16 y[MR][N] directly when `acc` is null. Otherwise (split-K,
+// gridDim.y splits) each workgroup adds its fp32 partial sums, in the
+// fixed-point word format of splitk_addend(), to acc[MR][N] (one uint64 per
+// output) with a relaxed device-scope atomic add. The word also counts the
+// arrivals, so the workgroup whose add completes the count finds the whole
+// sum in the value its atomic returned: it writes y and resets the word to
+// zero for the next call. Integer addition is exact and order-free, so y
+// does not depend on the order in which the splits arrive; and each output
+// lives in one atomic location, so no fence is needed.
 template <int MR, int WAVES, int SHARE, int ENGINE, int R, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, const _Float16* __restrict__ x, _Float16* __restrict__ y,
-    float* __restrict__ part, int N, int K) {
+    unsigned long long* __restrict__ acc, int N, int K) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr bool kGlobalX = ENGINE == kEngineMfmaGlobalX;
   // Accumulators per lane: MR for dot2; for MFMA the D rows a lane can hold
@@ -262,40 +265,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
       const int idx = tid + j * WAVES * 64;
       const int m = idx >> 4, i = idx & 15;
       const int64_t nn = t * kTileRows + i;
-      if (idx < MR * 16 && nn < N) {
-        if (part)
-          part[(int64_t(split) * MR + m) * N + nn] = out[j];
-        else
-          y[int64_t(m) * N + nn] = (_Float16)out[j];
-      }
+      if (idx < MR * 16 && nn < N) y[int64_t(m) * N + nn] = (_Float16)out[j];
     }
   };
-  // Split-K: y for row tile t = the tile's partials summed in split order.
-  auto finish_tile = [&](int64_t t) {
-#pragma unroll
-    for (int j = 0; j < kOut; ++j) {
-      const int idx = tid + j * WAVES * 64;
-      const int m = idx >> 4, i = idx & 15;
-      const int64_t nn = t * kTileRows + i;
-      if (idx < MR * 16 && nn < N) {
-        // Eight splits' partials requested at once (clamped indices stay in
-        // bounds), then added in split order.
-        const float* p = part + int64_t(m) * N + nn;
-        const int64_t stride = int64_t(MR) * N;
-        float sum = 0.f;
-        for (int s0 = 0; s0 < splits; s0 += 8) {
-          float v[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = p[min(s0 + u, splits - 1) * stride];
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (s0 + u < splits) sum = s0 + u == 0 ? v[u] : sum + v[u];
-        }
-        y[int64_t(m) * N + nn] = (_Float16)sum;
-      }
-    }
-  };
-
   struct TilePtrs {
     const u32x4* wlane;
     const uint32_t* sword;  // word of tile (t, 0)'s scale block holding row rlane's scale
@@ -396,46 +368,33 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
       reduce_tile(acc, sums[r]);
     }
   }
+  if (!acc) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) store_tile(out_tile_of(r), sums[r]);
-  if (!part) return;
-
-  // Split-K arrival. Each wave waits until its partial stores are complete
-  // and the workgroup synchronizes; then one thread releases them at device
-  // scope (other XCDs' L2s included: the release writes this L2's dirty
-  // lines back) and counts the arrival. The last arriver's thread acquires
-  // at device scope (invalidating stale lines) before the workgroup reads
-  // the other splits' partials. One device-scope fence per workgroup, not
-  // per wave: each is a whole-L2 operation. Nothing ever waits on another
-  // workgroup.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  __shared__ int last[R];
-  unsigned* counters = reinterpret_cast<unsigned*>(part + ((int64_t(splits) * MR * N + 3) & ~int64_t(3)));
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    int any_last = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t t = tile_of(r);
-      int is_last = 0;
-      if (t < row_tiles) {
-        const unsigned before = __hip_atomic_fetch_add(counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = before == unsigned(splits - 1);
-        // Every split of this tile has arrived: nothing else touches the
-        // counter during this call.
-        if (is_last) __hip_atomic_store(counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      last[r] = is_last;
-      any_last |= is_last;
-    }
-    if (any_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int r = 0; r < R; ++r) store_tile(out_tile_of(r), sums[r]);
+    return;
   }
-  __syncthreads();
+  // Split-K: one relaxed device-scope atomic add per output and row tile.
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (last[r]) finish_tile(tile_of(r));
+  for (int r = 0; r < R; ++r) {
+    const int64_t t = tile_of(r);
+#pragma unroll
+    for (int j = 0; j < kOut; ++j) {
+      const int idx = tid + j * WAVES * 64;
+      const int m = idx >> 4, i = idx & 15;
+      const int64_t nn = t * kTileRows + i;
+      if (idx < MR * 16 && nn < N && t < row_tiles) {
+        unsigned long long* word = acc + int64_t(m) * N + nn;
+        const unsigned long long add = splitk_addend(sums[r][j]);
+        const unsigned long long now =
+            __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+        if (splitk_count(now) == unsigned(splits)) {
+          y[int64_t(m) * N + nn] = splitk_value(now, splits);
+          // Every split has added: nothing else touches the word in this call.
+          __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
 }
 
 template <int MR, int WAVES, int SHARE, int ENGINE, int EPI>
@@ -445,7 +404,7 @@ constexpr size_t lds_for() {
 
 template <int MR, int WAVES, int SHARE, int ENGINE, int R, int EPI>
 hipError_t launch_typed(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
-                        const void* zeros, const void* x, void* y, float* partials, hipStream_t stream) {
+                        const void* zeros, const void* x, void* y, unsigned long long* acc, hipStream_t stream) {
   const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;  // output tiles for SwiGLU
   const int64_t grid = (row_tiles + R - 1) / R;
   constexpr size_t lds = lds_for<MR, WAVES, SHARE, ENGINE, EPI>();
@@ -459,17 +418,17 @@ hipError_t launch_typed(int N, int K, const LaunchPlan& plan, const void* wq, co
   hipLaunchKernelGGL((gemv_kernel<MR, WAVES, SHARE, ENGINE, R, EPI>), dim3(unsigned(grid), unsigned(plan.splits)),
                      dim3(WAVES * 64), lds, stream, static_cast<const uint8_t*>(wq),
                      static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
-                     static_cast<const _Float16*>(x), static_cast<_Float16*>(y), partials, N, K);
+                     static_cast<const _Float16*>(x), static_cast<_Float16*>(y), acc, N, K);
   return hipGetLastError();
 }
 
 template <int MR, int ENGINE>
 hipError_t launch_shape(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
-                        const void* zeros, const void* x, void* y, float* partials, hipStream_t stream) {
+                        const void* zeros, const void* x, void* y, unsigned long long* acc, hipStream_t stream) {
 #define W4A16_CASE(W, S, RR, EP)                                                                            \
   if constexpr (instantiated(MR, W, S, ENGINE, RR, EP)) {                                                  \
     if (plan.waves == W && plan.share == S && plan.tiles_per_wg == RR && plan.epilogue == EP)              \
-      return launch_typed<MR, W, S, ENGINE, RR, EP>(N, K, plan, wq, scales, zeros, x, y, partials, stream); \
+      return launch_typed<MR, W, S, ENGINE, RR, EP>(N, K, plan, wq, scales, zeros, x, y, acc, stream); \
   }
 #define W4A16_SHARES(W, RR)                                                                             \
   W4A16_CASE(W, 2, RR, kEpiStore) W4A16_CASE(W, 3, RR, kEpiStore) W4A16_CASE(W, 4, RR, kEpiStore)        \
@@ -487,15 +446,15 @@ hipError_t launch_shape(int N, int K, const LaunchPlan& plan, const void* wq, co
 
 template <int MR>
 hipError_t launch_engine(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
-                         const void* zeros, const void* x, void* y, float* partials, hipStream_t stream) {
+                         const void* zeros, const void* x, void* y, unsigned long long* acc, hipStream_t stream) {
   switch (plan.engine) {
     case kEngineMfma:
-      return launch_shape<MR, kEngineMfma>(N, K, plan, wq, scales, zeros, x, y, partials, stream);
+      return launch_shape<MR, kEngineMfma>(N, K, plan, wq, scales, zeros, x, y, acc, stream);
     case kEngineMfmaGlobalX:
-      return launch_shape<MR, kEngineMfmaGlobalX>(N, K, plan, wq, scales, zeros, x, y, partials, stream);
+      return launch_shape<MR, kEngineMfmaGlobalX>(N, K, plan, wq, scales, zeros, x, y, acc, stream);
     case kEngineDot2:
       if constexpr (MR == 1)
-        return launch_shape<MR, kEngineDot2>(N, K, plan, wq, scales, zeros, x, y, partials, stream);
+        return launch_shape<MR, kEngineDot2>(N, K, plan, wq, scales, zeros, x, y, acc, stream);
       return hipErrorInvalidValue;
     default:
       return hipErrorInvalidValue;

@@ -4,8 +4,8 @@
 namespace w4a16 {
 
 int launch_gemv_m2(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
-                    const void* zeros, const void* x, void* y, float* partials, void* stream) {
-  return int(dev::launch_engine<2>(N, K, plan, wq, scales, zeros, x, y, partials,
+                    const void* zeros, const void* x, void* y, unsigned long long* acc, void* stream) {
+  return int(dev::launch_engine<2>(N, K, plan, wq, scales, zeros, x, y, acc,
                                      static_cast<hipStream_t>(stream)));
 }
 

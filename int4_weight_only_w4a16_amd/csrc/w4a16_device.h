@@ -16,10 +16,32 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kMagic1024 = 0x64006400u;  // fp16 pair (1024, 1024)
 
-// s_waitcnt operand that waits for every outstanding vector memory operation
-// of the wave (vmcnt 0) and for nothing else (expcnt 7, lgkmcnt 15: the
-// field maxima in the gfx9 encoding).
-constexpr int kWaitVmcnt0 = 0x0F70;
+// Split-K accumulation word (uint64 per output). Bits 0..58 hold the sum of
+// the splits' biased fixed-point partials, bits 59..63 the number of splits
+// that have added. A partial p becomes f = round(p * 2^24) (RNE), clamped to
+// |f| < 2^53, i.e. |p| < 2^29; the addend is 2^59 + (f + 2^53), which lies in
+// [2^59, 2^59 + 2^54). With at most kMaxSplits = 31 splits the biased sum
+// stays below 31 * 2^54 < 2^59 and never carries into the count. A NaN
+// partial counts as 0. (2^29 is far past anything an fp16 output can hold:
+// where a partial reaches it, the GEMV bound 2e-3 * sum|w x| already exceeds
+// the whole fp16 range.)
+constexpr double kSplitkScale = 16777216.0;  // 2^24
+constexpr double kSplitkLimit = 9007199254740991.0;  // 2^53 - 1
+
+__device__ __forceinline__ unsigned long long splitk_addend(float p) {
+  double d = double(p) * kSplitkScale;  // exact: an fp32 times a power of two
+  d = d != d ? 0.0 : fmin(fmax(d, -kSplitkLimit), kSplitkLimit);
+  const long long f = (long long)rint(d);
+  return (1ull << 59) + (unsigned long long)(f + (1ll << 53));
+}
+
+__device__ __forceinline__ unsigned splitk_count(unsigned long long word) { return unsigned(word >> 59); }
+
+// fp16 of the exact fixed-point total of a complete word (via fp64 and fp32).
+__device__ __forceinline__ _Float16 splitk_value(unsigned long long word, int splits) {
+  const long long total = (long long)(word & ((1ull << 59) - 1)) - (long long)splits * (1ll << 53);
+  return (_Float16)(float)(double(total) / kSplitkScale);
+}
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 

@@ -38,7 +38,7 @@ enum Engine : int {
 
 // What the GEMV kernel does with its sums.
 enum Epilogue : int {
-  kEpiStore = 0,   // y = fp16(sum) (or split-K partials)
+  kEpiStore = 0,   // y = fp16(sum) (or the split-K atomic accumulation)
   kEpiSwiglu = 1,  // row tiles 2j (gate) and 2j+1 (up), half the waves each -> y = fp16(silu(gate) * up)
 };
 
@@ -98,22 +98,21 @@ size_t lds_bytes(int M, int K, const LaunchPlan& plan);
 // Whether the kernel set has an instantiation for this plan, within the LDS limit.
 bool plan_supported(int M, int K, const LaunchPlan& plan);
 
-// Split-K workspace: fp32 partials [splits][M][N], then one uint32 arrival
-// counter per row tile, each part rounded up to 16 bytes.
-constexpr size_t splitk_partial_bytes(int M, int N, int splits) {
-  return (size_t(4) * size_t(splits) * size_t(M) * size_t(N) + 15) / 16 * 16;
-}
-constexpr size_t splitk_workspace_bytes(int M, int N, int splits) {
-  return splitk_partial_bytes(M, N, splits) + (size_t(4) * size_t((N + kTileRows - 1) / kTileRows) + 15) / 16 * 16;
+// Split-K: at most this many splits (the 5-bit arrival count of the
+// accumulation word, see splitk_addend in w4a16_device.h), and a workspace of
+// one uint64 accumulation word per output, zero between calls.
+constexpr int kMaxSplits = 31;
+constexpr size_t splitk_workspace_bytes(int M, int N) {
+  return (size_t(8) * size_t(M) * size_t(N) + 15) / 16 * 16;
 }
 
 // Kernel launchers (w4a16_kernels.hip). They return a hipError_t value as int.
-// `partials` non-null selects split-K: it is the workspace above, counters zero.
+// `acc` non-null selects split-K: it is the workspace above, all zero.
 int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
-                const void* zeros, const void* x, void* y, float* partials, void* stream);
+                const void* zeros, const void* x, void* y, unsigned long long* acc, void* stream);
 #define W4A16_DECLARE_M(MR)                                                                            \
   int launch_gemv_m##MR(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales, \
-                        const void* zeros, const void* x, void* y, float* partials, void* stream);
+                        const void* zeros, const void* x, void* y, unsigned long long* acc, void* stream);
 W4A16_DECLARE_M(1) W4A16_DECLARE_M(2) W4A16_DECLARE_M(3) W4A16_DECLARE_M(4)
 W4A16_DECLARE_M(5) W4A16_DECLARE_M(6) W4A16_DECLARE_M(7) W4A16_DECLARE_M(8)
 #undef W4A16_DECLARE_M

@@ -38,7 +38,7 @@ size_t lds_bytes(int M, int K, const LaunchPlan& plan) {
 }
 
 bool plan_supported(int M, int K, const LaunchPlan& plan) {
-  if (M < 1 || M > 8 || plan.splits < 1 || plan.splits > K / kGroup) return false;
+  if (M < 1 || M > 8 || plan.splits < 1 || plan.splits > K / kGroup || plan.splits > kMaxSplits) return false;
   if (plan.tiles_per_wg < 1 || plan.tiles_per_wg > 3) return false;
   if (plan.engine < kEngineDot2 || plan.engine > kEngineMfmaGlobalX) return false;
   const int w = plan.waves, sh = plan.share;
@@ -55,16 +55,16 @@ bool plan_supported(int M, int K, const LaunchPlan& plan) {
 }
 
 int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
-                const void* zeros, const void* x, void* y, float* partials, void* stream_ptr) {
+                const void* zeros, const void* x, void* y, unsigned long long* acc, void* stream_ptr) {
   switch (M) {
-    case 1: return launch_gemv_m1(N, K, plan, wq, scales, zeros, x, y, partials, stream_ptr);
-    case 2: return launch_gemv_m2(N, K, plan, wq, scales, zeros, x, y, partials, stream_ptr);
-    case 3: return launch_gemv_m3(N, K, plan, wq, scales, zeros, x, y, partials, stream_ptr);
-    case 4: return launch_gemv_m4(N, K, plan, wq, scales, zeros, x, y, partials, stream_ptr);
-    case 5: return launch_gemv_m5(N, K, plan, wq, scales, zeros, x, y, partials, stream_ptr);
-    case 6: return launch_gemv_m6(N, K, plan, wq, scales, zeros, x, y, partials, stream_ptr);
-    case 7: return launch_gemv_m7(N, K, plan, wq, scales, zeros, x, y, partials, stream_ptr);
-    case 8: return launch_gemv_m8(N, K, plan, wq, scales, zeros, x, y, partials, stream_ptr);
+    case 1: return launch_gemv_m1(N, K, plan, wq, scales, zeros, x, y, acc, stream_ptr);
+    case 2: return launch_gemv_m2(N, K, plan, wq, scales, zeros, x, y, acc, stream_ptr);
+    case 3: return launch_gemv_m3(N, K, plan, wq, scales, zeros, x, y, acc, stream_ptr);
+    case 4: return launch_gemv_m4(N, K, plan, wq, scales, zeros, x, y, acc, stream_ptr);
+    case 5: return launch_gemv_m5(N, K, plan, wq, scales, zeros, x, y, acc, stream_ptr);
+    case 6: return launch_gemv_m6(N, K, plan, wq, scales, zeros, x, y, acc, stream_ptr);
+    case 7: return launch_gemv_m7(N, K, plan, wq, scales, zeros, x, y, acc, stream_ptr);
+    case 8: return launch_gemv_m8(N, K, plan, wq, scales, zeros, x, y, acc, stream_ptr);
     default: return int(hipErrorInvalidValue);
   }
 }

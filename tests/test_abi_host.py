@@ -133,19 +133,22 @@ def test_device_entry_points_reject_before_launch():
     assert L.w4a16_gemv(1, 16, 128, fake + 8, fake, fake, fake, fake, None) == w.W4A16_EINVAL
     # split-K: split count and workspace size
     ws = w.w4a16_splitk_workspace_bytes(2, 16, 3)
-    assert ws == 4 * 3 * 2 * 16 + 16  # partials, then one counter (padded to 16 bytes)
-    assert w.w4a16_splitk_workspace_bytes(1, 33, 2) == 272 + 16
+    assert ws == 8 * 2 * 16  # one uint64 word per output
+    assert w.w4a16_splitk_workspace_bytes(1, 33, 2) == 272 and w.w4a16_splitk_workspace_bytes(1, 33, 9) == 272
     assert w.w4a16_splitk_workspace_bytes(-1, 16, 3) == 0
-    assert w.w4a16_splitk_choose(1, 37888, 3584) == 1 and w.w4a16_splitk_choose(1, 3584, 18944) == 1
-    assert w.w4a16_splitk_choose(1, 128, 18944) == 6 and w.w4a16_splitk_choose(8, 512, 18944) == 4
-    assert w.w4a16_splitk_choose(1, 128, 896) == 1
+    assert w.w4a16_splitk_choose(1, 37888, 3584) == 1 and w.w4a16_splitk_choose(1, 3584, 7936) == 1
+    assert w.w4a16_splitk_choose(1, 3584, 18944) == 1 and w.w4a16_splitk_choose(8, 5120, 17408) == 8
+    assert w.w4a16_splitk_choose(1, 896, 4864) == 3 and w.w4a16_splitk_choose(5, 4608, 3584) == 1
+    assert len({w.w4a16_splitk_choose(m, 5120, 17408) for m in range(1, 9)}) == 1  # never depends on M
+    assert w.w4a16_splitk_choose(1, 128, 65536) == 16 and w.w4a16_splitk_choose(1, 8192, 131072) == 16
     assert w.w4a16_splitk_choose(1, 16, 200) == 0 and w.w4a16_splitk_choose(9, 16, 128) == 0
     for splits, wsb, want in [(0, ws, w.W4A16_EINVAL), (3, ws - 4, w.W4A16_EINVAL), (3, ws, None),
-                              (8, 10 ** 9, w.W4A16_EINVAL)]:
+                              (8, 10 ** 9, w.W4A16_EINVAL)]:  # K = 768: at most 6 splits
         if want is None:
             continue
         assert L.w4a16_gemv_splitk(2, 16, 768, splits, *ptrs, fake, wsb, None) == want, splits
     assert L.w4a16_gemv_splitk(9, 16, 768, 2, *ptrs, fake, 10 ** 9, None) == w.W4A16_EUNSUPPORTED
+    assert L.w4a16_gemv_splitk(1, 16, 128 * 40, 32, *ptrs, fake, 10 ** 9, None) == w.W4A16_EINVAL  # > 31 splits
     assert L.w4a16_gemv_splitk(2, 0, 768, 2, *ptrs, fake, 0, None) == w.W4A16_OK
     # fused SwiGLU
     assert L.w4a16_gemv_swiglu(1, 16, 200, *ptrs, None) == w.W4A16_EINVAL

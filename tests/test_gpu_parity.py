@@ -152,9 +152,9 @@ def test_batch_invariance(N, K):
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 28])
 @pytest.mark.parametrize("M,N,K", [(1, 3584, 3584), (5, 128, 896 * 4), (1, 896, 4864), (8, 200, 3584)])
 def test_splitk(M, N, K, splits):
-    """Split-K against the oracle; the workspace's counters are back at zero
-    after each call, so a second call on the same workspace gives the same
-    bits (a counter left behind would leave tiles unwritten)."""
+    """Split-K against the oracle; the workspace is back at zero after each
+    call, so a second call on the same workspace gives the same bits (a word
+    left behind would corrupt the next call's sums)."""
     if splits > K // 128:
         pytest.skip("more splits than groups")
     _say("splitk", M, N, K, splits)
@@ -162,8 +162,7 @@ def test_splitk(M, N, K, splits):
     ws = p.splitk_workspace(splits)
     y = p.gemv_splitk(splits, ws)
     p.check(y)
-    if splits > 1:
-        assert not p.splitk_counters(ws, splits).any()
+    assert p.workspace_is_zero(ws)
     assert np.array_equal(y, p.gemv_splitk(splits, ws))
 
 
@@ -182,6 +181,33 @@ def test_splitk_chosen_full_size(name, N, K):
         p = Problem(M, N, K, seed=4)
         y = p.gemv_splitk(splits)
         _say(name, M, splits, "worst", p.check(y))
+
+
+def test_splitk_overflowing_partials_match_plain():
+    """A single huge product (largest |q - z|, scale and x) makes a split's
+    partial far beyond the fixed-point range (2^29): it is clamped, and the
+    output still overflows fp16 to the same +-inf the plain GEMV gives;
+    ordinary rows of the same call stay within the bound."""
+    N, K, splits = 48, 4096, 4
+    _say("splitk overflow", N, K, splits)
+    G = K // 128
+    q = np.full((N, K), 8, np.uint8)
+    z = np.full((N, G), 8, np.uint8)
+    s = synthetic.scales(N, G, seed=13)
+    q[5, 1000] = 15
+    z[5, 1000 // 128] = 0      # row 5: (q - z) = 15 at k = 1000, otherwise 8 - 0 = 8 in that group
+    s[5, 1000 // 128] = 0x7BFF  # largest finite fp16 scale
+    x = synthetic.activations(1, K, seed=13)
+    x[0, 1000] = 0x7BFF         # 65504
+    p = Problem(1, N, K, q=q, s=s, z=z, x=x)
+    plain = p.gemv()
+    y = p.gemv_splitk(splits)
+    assert (plain[0, 5] & 0x7FFF) == 0x7C00  # the plain path overflows to inf
+    assert y[0, 5] == plain[0, 5]
+    ref, absref = p.reference()
+    rows = [n for n in range(N) if n != 5]
+    ok, worst = oracle.bound_report(y[:, rows], ref[:, rows], absref[:, rows], oracle.get())
+    assert ok, worst
 
 
 def test_splitk_batch_invariance():
@@ -219,8 +245,8 @@ def test_graph_replay_matches_eager():
 
 
 def test_graph_replay_splitk():
-    """A captured split-K call replays correctly many times: the counters
-    reset by each replay are what the next replay starts from."""
+    """A captured split-K call replays correctly many times: the zeroed words
+    each replay leaves are what the next replay starts from."""
     torch, dev = torch_dev()
     p = Problem(1, 3584, 18944, seed=9)
     splits = 4
@@ -241,7 +267,7 @@ def test_graph_replay_splitk():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().view(np.uint16), eager)
-        assert not p.splitk_counters(ws, splits).any()
+        assert p.workspace_is_zero(ws)
     p.check(eager)
 
 
