@@ -297,6 +297,17 @@ def main():
     unfused_us = step.time_graph(unfused, reps, 3) / (reps * n_dom) * 1e6
     del fused, fused_step, unfused
 
+    # Host quantizer (w4a16_quantize) on the qkv matrix's shape: fp16 in.
+    import int4_weight_only_w4a16_amd as wlib
+    _, Nq, Kq = synthetic.QWEN7B_LAYER[0]
+    wq16 = (np.random.default_rng(args.seed).standard_normal((Nq, Kq)) * 0.02).astype(np.float16)
+    quant = {}
+    for mode, label in ((0, "symmetric"), (1, "asymmetric")):
+        wlib.w4a16_quantize(wq16, mode)  # warm
+        t0 = time.perf_counter()
+        wlib.w4a16_quantize(wq16, mode)
+        quant[label] = round(wq16.nbytes / (time.perf_counter() - t0) / 1e9, 3)
+
     # Outputs of the last full replay, for the sampled check.
     graph.replay()
     torch.cuda.synchronize()
@@ -348,6 +359,8 @@ def main():
                 "step_us_with_fused_gate_up": round(fused_step_s / args.steps * 1e6, 2),
             },
         },
+        "host_quantize": {"shape": f"{Nq}x{Kq} fp16", "GBps_fp16_in": quant,
+                          "threads": os.cpu_count()},
         "setup_s": round(setup_s, 1),
     }
     if args.cpu_budget > 0:

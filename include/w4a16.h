@@ -112,6 +112,25 @@ int w4a16_pack_gate_up(int F, int K, const uint8_t* qg, const uint16_t* sg, cons
                        void* z_out);
 
 /*
+ * Host round-to-nearest quantizer: fp16 weights w [N][K] (bit patterns,
+ * row-major, all finite) -> the logical q [N][K], s [N][K/128] (fp16 bits)
+ * and z [N][K/128] that w4a16_pack takes. Each group of 128 consecutive
+ * weights of a row gets its own scale; values are computed in double
+ * precision, codes divide by the stored fp16 scale and round half to even.
+ *   mode 0, symmetric, the scheme of "Building an LLM Inference Runtime",
+ *     "The Stack Architecture" and "CodeAlign-Runtime", Level 3:
+ *     s = fp16(absmax / 7), t = clamp(round(w / s), -8, 7), stored as
+ *     q = t + 8 with z = 8, so (q - z) * s = t * s.
+ *   mode 1, asymmetric, for uint4 zero points: with lo = min(w, 0) and
+ *     hi = max(w, 0) over the group, s = fp16((hi - lo) / 15),
+ *     z = clamp(round(-lo / s), 0, 15), q = clamp(round(w / s) + z, 0, 15).
+ *   A group whose scale rounds to 0 gets q = z (it dequantizes to 0).
+ * Errors: W4A16_EINVAL for a bad shape or mode, a NULL pointer (when N > 0)
+ * or a non-finite weight. Runs on host threads (no GPU needed).
+ */
+int w4a16_quantize(int N, int K, const uint16_t* w, int mode, uint8_t* q, uint16_t* s, uint8_t* z);
+
+/*
  * Inverse of w4a16_pack (host to host): recovers q [N][K], s [N][K/128] and
  * z [N][K/128] exactly. Errors: W4A16_EINVAL for a bad shape or NULL pointer.
  */

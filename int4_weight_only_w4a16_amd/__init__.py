@@ -23,7 +23,8 @@ GROUP = 128
 MAX_M = 8
 
 # Every symbol the header declares.
-EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_unpack",
+EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_quantize",
+           "w4a16_unpack",
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
            "w4a16_gemv_splitk", "w4a16_dequant_f32", "w4a16_strerror")
 
@@ -53,6 +54,7 @@ def lib():
         L.w4a16_pack.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_pack_gate_up.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
         L.w4a16_unpack.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p]
+        L.w4a16_quantize.argtypes = [_i, _i, _p, _i, _p, _p, _p]
         L.w4a16_gemv.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_gemv_swiglu.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_splitk_workspace_bytes.restype = _sz
@@ -137,6 +139,18 @@ def w4a16_pack_gate_up(qg, sg, zg, qu, su, zu):
                                     su.ctypes.data, zu.ctypes.data, wq.ctypes.data, sp.ctypes.data,
                                     zp.ctypes.data), "w4a16_pack_gate_up")
     return wq, sp, zp
+
+
+def w4a16_quantize(w_f16_bits, mode):
+    """Host: fp16 weights (uint16 bits or float16) [N][K] -> (q, s, z) in
+    w4a16_pack's logical form; mode 0 symmetric absmax/7, 1 asymmetric."""
+    w_f16_bits = np.ascontiguousarray(np.asarray(w_f16_bits).view(np.uint16))
+    N, K = w_f16_bits.shape
+    G = K // GROUP if K % GROUP == 0 else 0
+    q, s, z = np.empty((N, K), np.uint8), np.empty((N, max(G, 1)), np.uint16), np.empty((N, max(G, 1)), np.uint8)
+    _check(lib().w4a16_quantize(N, K, w_f16_bits.ctypes.data, int(mode), q.ctypes.data, s.ctypes.data,
+                                z.ctypes.data), "w4a16_quantize")
+    return q, s, z
 
 
 def w4a16_unpack(N, K, wq, s_packed, z_packed):

@@ -54,6 +54,7 @@ class Oracle:
         lib.or_gemv.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]
         lib.or_gemv_packed.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]
         lib.or_gemv_packed_rows.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p, _p]
+        lib.or_quantize.argtypes = [_i64, _i64, _p, ctypes.c_int, _p, _p, _p]
         self.plant = lib.or_plant()
 
     # -- fp16 codec -------------------------------------------------------
@@ -116,6 +117,20 @@ class Oracle:
         if self.lib.or_dequant(N, K, q.ctypes.data, s.ctypes.data, z.ctypes.data, w.ctypes.data):
             raise ValueError("or_dequant rejected its input")
         return w
+
+    def quantize(self, w_f16_bits, mode):
+        """fp16 bits [N][K] -> (q, s, z) by round-to-nearest; mode 0 symmetric
+        (absmax / 7, z = 8), mode 1 asymmetric (min/max with 0, uint4 z)."""
+        w_f16_bits = np.ascontiguousarray(w_f16_bits, dtype=np.uint16)
+        N, K = w_f16_bits.shape
+        G = K // GROUP
+        q = np.empty((N, K), np.uint8)
+        s = np.empty((N, G), np.uint16)
+        z = np.empty((N, G), np.uint8)
+        if self.lib.or_quantize(N, K, w_f16_bits.ctypes.data, int(mode), q.ctypes.data, s.ctypes.data,
+                                z.ctypes.data):
+            raise ValueError("or_quantize rejected its input")
+        return q, s, z
 
     def gemv(self, q, s, z, x):
         """Returns (ref, absref), both float64 [M][N]."""

@@ -273,6 +273,72 @@ int or_dequant(int64_t N, int64_t K, const uint8_t* q, const uint16_t* s, const 
 }
 
 /* ref, absref: [M][N] doubles; x: [M][K] fp16 bits. */
+/* ------------------------------------------------------- quantizer --- */
+
+/* Round-to-nearest quantization of fp16 weights w[N][K] to (q, s, z), one
+ * group of 128 consecutive weights of a row at a time, in fp64.
+ *  mode 0, symmetric ("Building an LLM Inference Runtime", "The Stack
+ *    Architecture"; "CodeAlign-Runtime", Level 3, "Quantization Scheme"):
+ *    s = fp16(absmax / 7), t = clamp(round(w / s), -8, 7), stored unsigned
+ *    as q = t + 8 with z = 8 (so (q - z) * s = t * s).
+ *  mode 1, asymmetric (the uint4 zero points of the workload; the range is
+ *    widened to contain 0 so that 0 and constant groups stay exact):
+ *    lo = min(min(w), 0), hi = max(max(w), 0), s = fp16((hi - lo) / 15),
+ *    z = clamp(round(-lo / s), 0, 15), q = clamp(round(w / s) + z, 0, 15).
+ * round() is round-half-to-even; the division uses the stored fp16 scale.
+ * A group whose scale rounds to 0 gets q = z (mode 0: 8, mode 1: 0), which
+ * dequantizes to 0. */
+static double round_half_even(double v) {
+  double f = floor(v);
+  double d = v - f;
+  if (d > 0.5) return f + 1.0;
+  if (d < 0.5) return f;
+  return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+static double clamp_d(double v, double lo, double hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+int or_quantize(int64_t N, int64_t K, const uint16_t* w, int mode, uint8_t* q, uint16_t* s, uint8_t* z) {
+  if (!shape_ok(N, K) || (mode != 0 && mode != 1)) return -1;
+  int64_t G = K / OR_GROUP;
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t g = 0; g < G; g++) {
+      const uint16_t* wg = w + n * K + g * OR_GROUP;
+      double lo = 0.0, hi = 0.0, amax = 0.0;
+      for (int j = 0; j < OR_GROUP; j++) {
+        double v = or_f16_to_f64(wg[j]);
+        if (v != v || v - v != 0.0) return -1; /* NaN or infinite weight */
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+        if (fabs(v) > amax) amax = fabs(v);
+      }
+#if OR_PLANT == 8
+      uint16_t sb = mode == 0 ? or_f64_to_f16(amax / 8.0) : or_f64_to_f16((hi - lo) / 15.0); /* planted */
+#else
+      uint16_t sb = mode == 0 ? or_f64_to_f16(amax / 7.0) : or_f64_to_f16((hi - lo) / 15.0);
+#endif
+      double sd = or_f16_to_f64(sb);
+      int zz = mode == 0 ? 8 : 0;
+      if (sd > 0.0 && mode == 1) zz = (int)clamp_d(round_half_even(-lo / sd), 0.0, 15.0);
+      s[n * G + g] = sb;
+      z[n * G + g] = (uint8_t)zz;
+      for (int j = 0; j < OR_GROUP; j++) {
+        int qq = zz;
+        if (sd > 0.0) {
+          double r = round_half_even(or_f16_to_f64(wg[j]) / sd);
+#if OR_PLANT == 9
+          qq = mode == 0 ? (int)clamp_d(r, -8.0, 7.0) + 8 : (int)clamp_d(r, 0.0, 15.0); /* planted: z dropped */
+#else
+          qq = mode == 0 ? (int)clamp_d(r, -8.0, 7.0) + 8 : (int)clamp_d(r + zz, 0.0, 15.0);
+#endif
+        }
+        q[n * K + g * OR_GROUP + j] = (uint8_t)qq;
+      }
+    }
+  }
+  return 0;
+}
+
 int or_gemv(int64_t M, int64_t N, int64_t K, const uint8_t* q, const uint16_t* s, const uint8_t* z,
             const uint16_t* x, double* ref, double* absref) {
   if (M < 0 || !shape_ok(N, K)) return -1;

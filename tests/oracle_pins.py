@@ -324,6 +324,76 @@ def pin_gemv_packed_matches_logical(o):
         assert np.array_equal(ref3, ref[:, rows])
 
 
+# ---------------------------------------------------------------- quantizer
+
+def _quant_groups(seed, N=6, K=512):
+    """fp16 weights with the workload's spread plus awkward groups: all zero,
+    constant positive, constant negative, all positive, one huge outlier."""
+    rng = np.random.default_rng(seed)
+    w = rng.normal(0.0, 0.02, (N, K))
+    w[0, 0:128] = 0.0
+    w[1, 128:256] = 0.37
+    w[2, 256:384] = -1.5
+    w[3, 384:512] = np.abs(w[3, 384:512]) + 0.1
+    w[4, 5] = 300.0
+    return w.astype(np.float16).view(np.uint16)
+
+
+def pin_quantize_scale_definition(o):
+    """s is the fp16 rounding (numpy's own RNE conversion) of absmax / 7
+    (symmetric) or of (max(w, 0) - min(w, 0)) / 15 (asymmetric), per row and
+    group; symmetric z is 8 everywhere and q - 8 stays in [-8, 7]."""
+    w16 = _quant_groups(51)
+    wd = w16.view(np.float16).astype(np.float64)
+    N, K = wd.shape
+    g = wd.reshape(N, K // GROUP, GROUP)
+    q, s, z = o.quantize(w16, 0)
+    assert np.array_equal(s, (np.abs(g).max(axis=2) / 7.0).astype(np.float16).view(np.uint16))
+    assert (z == 8).all() and q.max() <= 15
+    q, s, z = o.quantize(w16, 1)
+    lo, hi = np.minimum(g.min(axis=2), 0.0), np.maximum(g.max(axis=2), 0.0)
+    assert np.array_equal(s, ((hi - lo) / 15.0).astype(np.float16).view(np.uint16))
+    assert q.max() <= 15 and z.max() <= 15
+
+
+def pin_quantize_nearest_code(o):
+    """Brute force: given the stored s and z, every weight's code is one of
+    the nearest of all 16 codes (round to nearest, then clamp to the code
+    range, can do no better); 0 is represented exactly in both modes."""
+    w16 = _quant_groups(53)
+    wd = w16.view(np.float16).astype(np.float64)
+    codes = np.arange(16, dtype=np.float64)
+    for mode in (0, 1):
+        q, s, z = o.quantize(w16, mode)
+        sd = np.repeat(s.view(np.float16).astype(np.float64), GROUP, axis=1)
+        zd = np.repeat(z.astype(np.float64), GROUP, axis=1)
+        err = np.abs(wd - (q - zd) * sd)
+        best = np.abs(wd[..., None] - (codes - zd[..., None]) * sd[..., None]).min(axis=2)
+        assert (err <= best * (1 + 1e-12) + 1e-300).all(), mode
+        assert not (((q - zd) * sd)[wd == 0.0]).any()  # zero weights dequantize to exactly 0
+        inside = (sd > 0)
+        assert (err[inside] <= sd[inside] / 2 * (1 + 1e-12) + 1e-300).all() or mode == 1
+
+
+def pin_quantize_degenerate_groups(o):
+    """An all-zero group gets scale 0 and q = z (dequantizes to 0); the
+    symmetric grid holds +-absmax at +-7; a group of multiples of a power of
+    two up to 7 times it quantizes exactly."""
+    w16 = _quant_groups(57)
+    for mode in (0, 1):
+        q, s, z = o.quantize(w16, mode)
+        assert s[0, 0] == 0 and (q[0, :128] == z[0, 0]).all()
+    c = 2.0 ** -6
+    t = np.tile(np.arange(-7, 8), 9)[:128].astype(np.float64)
+    w = np.zeros((1, 128))
+    w[0] = t * c
+    q, s, z = o.quantize(w.astype(np.float16).view(np.uint16), 0)
+    assert s[0, 0] == np.float16(c).view(np.uint16) and np.array_equal(q[0].astype(int) - 8, t.astype(int))
+    q, s, z = o.quantize(_quant_groups(57), 0)
+    row2 = q[2, 256:384].astype(int) - 8  # constant -1.5: absmax / 7 scale, every code -7
+    assert (row2 == -7).all()
+
+
 # ------------------------------------------------------------------ SwiGLU
 
 def pin_silu_definition(o):

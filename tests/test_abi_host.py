@@ -98,6 +98,40 @@ def test_pack_gate_up_is_the_16_row_interleave(orc, F, K):
                                 *(m.ctypes.data for m in mine)) == w.W4A16_EINVAL
 
 
+@pytest.mark.parametrize("N,K,seed", [(1, 128, 0), (6, 512, 1), (64, 896, 2), (37, 4864, 3), (300, 1152, 4)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_quantize_matches_oracle_bits(orc, N, K, seed, mode):
+    """The library's quantizer equals the oracle's bit for bit: codes, fp16
+    scales and zero points (both decide in fp64 with round half to even)."""
+    from tests.oracle_pins import _quant_groups
+    w16 = synthetic.activations(N, K, seed=seed, tensor_id=5)  # fp16 N(0,1) bits
+    w16 = (w16.view(np.float16).astype(np.float64) * 0.02).astype(np.float16).view(np.uint16)
+    if N >= 6 and K >= 512:
+        w16[:6, :512] = _quant_groups(seed)
+    for a, b in zip(w.w4a16_quantize(w16, mode), orc.quantize(w16, mode)):
+        assert np.array_equal(a, b)
+
+
+def test_quantize_ties_and_errors(orc):
+    """Weights exactly half-way between two codes round to the even code in
+    both quantizers; non-finite weights and bad modes are rejected."""
+    c = 2.0 ** -4
+    vals = np.zeros((1, 128))
+    vals[0, 0] = 7 * c                               # absmax 7c: symmetric scale exactly c
+    vals[0, 1:15] = (np.arange(-7, 7) + 0.5) * c     # the half-way points between codes
+    w16 = vals.astype(np.float16).view(np.uint16)
+    mine, ref = w.w4a16_quantize(w16, 0), orc.quantize(w16, 0)
+    assert all(np.array_equal(a, b) for a, b in zip(mine, ref))
+    assert orc.f16_to_f64(ref[1])[0, 0] == c
+    assert (((ref[0][0, 1:15].astype(int) - 8) % 2) == 0).all()
+    bad = w16.copy()
+    bad[0, 3] = 0x7C00  # +inf
+    with pytest.raises(w.W4A16Error):
+        w.w4a16_quantize(bad, 0)
+    with pytest.raises(w.W4A16Error):
+        w.w4a16_quantize(w16, 2)
+
+
 def test_pack_rejects_bad_values_and_shapes():
     L = w.lib()
     q = np.zeros((2, 128), np.uint8)

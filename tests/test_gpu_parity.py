@@ -271,6 +271,38 @@ def test_graph_replay_splitk():
     p.check(eager)
 
 
+# -------------------------------------------------- quantize -> pack -> GEMV
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("M,N,K", [(1, 3584, 3584), (5, 896, 4864)])
+def test_quantized_weights_end_to_end(mode, M, N, K):
+    """fp16 weights quantized by the library (w4a16_quantize), packed and
+    multiplied on the GPU stay within the closed-form quantization error of
+    the unquantized fp64 product: every weight moves at most s/2 (round to
+    nearest), except that an asymmetric code at the top of the range can
+    clamp from 16 to 15 when fp16 rounded s below (hi - lo)/15 and z rounded
+    up: at most (0.5 + 15 * 2^-11) s there. So |y - W x| <= sum_g 0.51 s_g *
+    sum_{k in g} |x_k|, plus the GEMV bound on the quantized product."""
+    _say("quantized end to end", mode, M, N, K)
+    rng = np.random.default_rng(60 + mode)
+    w16 = rng.normal(0.0, 0.02, (N, K)).astype(np.float16).view(np.uint16)
+    q, s, z = w.w4a16_quantize(w16, mode)
+    p = Problem(M, N, K, q=q, s=s, z=z, x=synthetic.activations(M, K, seed=61))
+    y = p.gemv()
+    o = oracle.get()
+    yd = o.f16_to_f64(y)
+    xd = o.f16_to_f64(p.x)
+    wd = o.f16_to_f64(w16)
+    exact = xd @ wd.T  # unquantized product (numpy float64)
+    ref, absref = p.reference()
+    G = K // 128
+    sd = o.f16_to_f64(s)  # [N][G]
+    xabs_g = np.abs(xd).reshape(M, G, 128).sum(axis=2)  # [M][G]
+    quant_err = 0.51 * xabs_g @ sd.T  # [M][N]
+    allow = quant_err + oracle.BOUND_REL * absref + oracle.BOUND_ABS
+    assert (np.abs(yd - exact) <= allow).all(), float((np.abs(yd - exact) / allow).max())
+
+
 # --------------------------------------------------------- device errors
 
 def test_misaligned_device_pointer_is_rejected():

@@ -16,6 +16,8 @@ PLANTS = {
     5: "nibble order reversed",
     6: "fp16 rounding truncates",
     7: "fp16 subnormals decoded with a hidden bit",
+    8: "symmetric quantizer scale absmax / 8",
+    9: "asymmetric quantizer drops the zero point",
 }
 
 
