@@ -39,6 +39,7 @@ import numpy as np  # noqa: E402
 import synthetic  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak (no sparsity)
 GROUP = 128
 # Sources that decide the GEMV kernel's code and launch shape: a counter
 # summary taken on other sources is not used.
@@ -297,8 +298,47 @@ def main():
     unfused_us = step.time_graph(unfused, reps, 3) / (reps * n_dom) * 1e6
     del fused, fused_step, unfused
 
+    # Prefill (M = 2048) on the gate+up shape: the fused W4A16 GEMM, the
+    # standalone fp16 dequantization, and for context the two-step route
+    # (that dequantization, then torch's fp16 library GEMM).
+    import int4_weight_only_w4a16_amd as wl
+    Mp = 2048
+    wq_g, sc_g, zp_g = step.bufs[2][3:6]  # layer 0 gate_up weights
+    xp = synthetic.device_activations(Mp, Kd, args.seed, 9999, torch.device("cuda:0"))
+    yp = torch.empty((Mp, Nd), dtype=torch.int16, device="cuda:0")
+    w16 = torch.empty((Nd, Kd), dtype=torch.float16, device="cuda:0")
+
+    def timed(fn, reps=10):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    gemm_us = timed(lambda: wl.w4a16_gemm(Mp, Nd, Kd, wq_g, sc_g, zp_g, xp, yp))
+    dq_us = timed(lambda: wl.w4a16_dequant_f16(Nd, Kd, wq_g, sc_g, zp_g, w16))
+    lib_us = timed(lambda: torch.matmul(xp.view(torch.float16), w16.t()))
+    flops = 2.0 * Mp * Nd * Kd
+    dq_bytes = algorithmic_bytes(0, Nd, Kd) + 2 * Nd * Kd
+    prefill = {
+        "shape": f"M={Mp} x gate_up {Nd}x{Kd}",
+        "w4a16_gemm_us": round(gemm_us, 1),
+        "w4a16_gemm_TFLOPs": round(flops / (gemm_us * 1e-6) / 1e12, 1),
+        "w4a16_gemm_frac_of_mfma_f16_peak": round(flops / (gemm_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "dequant_f16_us": round(dq_us, 1),
+        "dequant_f16_GBps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1),
+        "dequant_f16_frac_of_hbm_peak": round(dq_bytes / (dq_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "two_step_dequant_plus_torch_fp16_gemm_us": round(dq_us + lib_us, 1),
+    }
+    del xp, yp, w16
+
     # Host quantizer (w4a16_quantize) on the qkv matrix's shape: fp16 in.
-    import int4_weight_only_w4a16_amd as wlib
+    wlib = wl
     _, Nq, Kq = synthetic.QWEN7B_LAYER[0]
     wq16 = (np.random.default_rng(args.seed).standard_normal((Nq, Kq)) * 0.02).astype(np.float16)
     quant = {}
@@ -359,6 +399,7 @@ def main():
                 "step_us_with_fused_gate_up": round(fused_step_s / args.steps * 1e6, 2),
             },
         },
+        "prefill_gemm": prefill,
         "host_quantize": {"shape": f"{Nq}x{Kq} fp16", "GBps_fp16_in": quant,
                           "threads": os.cpu_count()},
         "setup_s": round(setup_s, 1),

@@ -221,6 +221,35 @@ int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq, const voi
                       void* stream);
 
 /*
+ * W4A16 GEMM for many activation rows (prefill, M > 8), on the matrix cores:
+ * y[M][N] = x[M][K] W^T. Wq, scales, zeros: device buffers in layout ID 2;
+ * x: device fp16 [M][K]; y: device fp16 [M][N]; any M >= 1 (for M <= 8
+ * w4a16_gemv is the faster path). The weights are dequantized in registers
+ * to fp16 (q - z) * s, each rounded once to nearest even (the values
+ * w4a16_dequant_f16 writes), and multiplied with fp32 accumulation; the
+ * products are exact, so each output is within fp32 accumulation and fp16
+ * output rounding of sum_k fp16w * x -- inside the workload's bound
+ * 2e-3 * sum|w x| + 1e-5, the weight rounding taking at most 2^-11 of it.
+ * Deterministic (fixed order), but not bit-equal to w4a16_gemv, whose
+ * weights are exact (q - z) scaled per group. The standalone dequant + MFMA
+ * GEMM variant the AWQ dequantization page builds in two steps, here in
+ * one. Errors: W4A16_EINVAL (shape, NULL, alignment), W4A16_EHIP.
+ */
+int w4a16_gemm(int M, int N, int K, const void* Wq, const void* scales, const void* zeros, const void* x,
+               void* y, void* stream);
+
+/*
+ * Standalone dequantization, for paths that want the fp16 matrix itself
+ * (a GEMM over many activation rows, for instance): W_out[n][k] =
+ * fp16((q - z) * s), the exact product rounded once to nearest even, for
+ * n < N, k < K. W_out: device fp16 [N][K] row-major, 16-byte aligned. This
+ * is the dequantize entry point of "Custom AWQ Dequantization Kernel" for
+ * layout 2. Errors: W4A16_EINVAL (shape, NULL, alignment), W4A16_EHIP.
+ */
+int w4a16_dequant_f16(int N, int K, const void* Wq, const void* scales, const void* zeros, void* W_out,
+                      void* stream);
+
+/*
  * Test hook: W_out[n][k] = float(q - z) * float(s) for n < N, k < K (device
  * fp32 [N][K] row-major), computed with the same in-register unpack as the
  * GEMV. The product is exact in fp32 (|q - z| <= 15 needs 4 bits, s has an

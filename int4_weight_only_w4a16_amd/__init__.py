@@ -26,7 +26,7 @@ MAX_M = 8
 EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_quantize",
            "w4a16_unpack",
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
-           "w4a16_gemv_splitk", "w4a16_dequant_f32", "w4a16_strerror")
+           "w4a16_gemv_splitk", "w4a16_gemm", "w4a16_dequant_f16", "w4a16_dequant_f32", "w4a16_strerror")
 
 
 class W4A16Error(RuntimeError):
@@ -47,6 +47,14 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIBRARY):
             raise ImportError(f"libw4a16.so is not built ({LIBRARY}); run __graft_entry__.build()")
+        # torch first: its HIP runtime then satisfies the library's
+        # libamdhip64.so.7 dependency. Loaded the other way round, the process
+        # holds two HIP (and HSA) runtimes, and one of them can fail to find
+        # the device (hipFuncSetAttribute returned "no ROCm-capable device").
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIBRARY)
         L.w4a16_layout_id.restype = _i
         L.w4a16_layout_id.argtypes = []
@@ -63,6 +71,8 @@ def lib():
         L.w4a16_splitk_choose.argtypes = [_i, _i, _i]
         L.w4a16_gemv_splitk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.w4a16_dequant_f32.argtypes = [_i, _i, _p, _p, _p, _p, _p]
+        L.w4a16_dequant_f16.argtypes = [_i, _i, _p, _p, _p, _p, _p]
+        L.w4a16_gemm.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_strerror.restype = ctypes.c_char_p
         L.w4a16_strerror.argtypes = [_i]
         _lib = L
@@ -195,6 +205,18 @@ def w4a16_gemv_splitk(M, N, K, splits, Wq, scales, zeros, x, y, workspace, ws_by
     _check(lib().w4a16_gemv_splitk(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x),
                                    _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)),
            "w4a16_gemv_splitk")
+
+
+def w4a16_gemm(M, N, K, Wq, scales, zeros, x, y, stream=None):
+    """Device: y[M][N] (fp16) = x[M][K] W^T for many rows (prefill), MFMA."""
+    _check(lib().w4a16_gemm(M, N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y), _stream(stream)),
+           "w4a16_gemm")
+
+
+def w4a16_dequant_f16(N, K, Wq, scales, zeros, W_out, stream=None):
+    """Device: W_out[N][K] fp16 = fp16((q - z) * s), rounded once to nearest even."""
+    _check(lib().w4a16_dequant_f16(N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(W_out),
+                                   _stream(stream)), "w4a16_dequant_f16")
 
 
 def w4a16_dequant_f32(N, K, Wq, scales, zeros, W_out, stream=None):

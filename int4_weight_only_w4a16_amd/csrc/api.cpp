@@ -160,6 +160,24 @@ extern "C" int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq
   return W4A16_OK;
 }
 
+extern "C" int w4a16_gemm(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,
+                          const void* x, void* y, void* stream) {
+  if (K < W4A16_GROUP || K % W4A16_GROUP != 0 || M < 0 || N < 0) return W4A16_EINVAL;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (!pointers_ok({Wq, scales, zeros, x, y})) return W4A16_EINVAL;
+  if (w4a16::launch_gemm(M, N, K, Wq, scales, zeros, x, y, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
+
+extern "C" int w4a16_dequant_f16(int N, int K, const void* Wq, const void* scales, const void* zeros,
+                                 void* W_out, void* stream) {
+  if (K < W4A16_GROUP || K % W4A16_GROUP != 0 || N < 0) return W4A16_EINVAL;
+  if (N == 0) return W4A16_OK;
+  if (!pointers_ok({Wq, scales, zeros, W_out})) return W4A16_EINVAL;
+  if (w4a16::launch_dequant_f16(N, K, Wq, scales, zeros, W_out, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
+
 extern "C" int w4a16_dequant_f32(int N, int K, const void* Wq, const void* scales, const void* zeros,
                                  float* W_out, void* stream) {
   if (K < W4A16_GROUP || K % W4A16_GROUP != 0 || N < 0) return W4A16_EINVAL;

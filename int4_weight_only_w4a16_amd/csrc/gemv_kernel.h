@@ -415,11 +415,10 @@ hipError_t launch_typed(int N, int K, const LaunchPlan& plan, const void* wq, co
         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (raised != hipSuccess) return raised;
   }
-  hipLaunchKernelGGL((gemv_kernel<MR, WAVES, SHARE, ENGINE, R, EPI>), dim3(unsigned(grid), unsigned(plan.splits)),
-                     dim3(WAVES * 64), lds, stream, static_cast<const uint8_t*>(wq),
-                     static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
-                     static_cast<const _Float16*>(x), static_cast<_Float16*>(y), acc, N, K);
-  return hipGetLastError();
+  return launch_kernel(&gemv_kernel<MR, WAVES, SHARE, ENGINE, R, EPI>, dim3(unsigned(grid), unsigned(plan.splits)),
+                       dim3(WAVES * 64), lds, stream, static_cast<const uint8_t*>(wq),
+                       static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
+                       static_cast<const _Float16*>(x), static_cast<_Float16*>(y), acc, N, K);
 }
 
 template <int MR, int ENGINE>

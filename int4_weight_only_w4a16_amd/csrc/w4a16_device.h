@@ -10,6 +10,22 @@
 namespace w4a16 {
 namespace dev {
 
+template <typename T>
+struct same_type {
+  using type = T;
+};
+
+// Launches `kernel` and returns the status of this launch alone (a launch
+// followed by hipGetLastError() would also report an error an earlier,
+// unrelated runtime call left behind in the thread). The arguments convert
+// to the kernel's parameter types; their copies are what the launch reads.
+template <typename... KArgs>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                         typename same_type<KArgs>::type... args) {
+  void* ptrs[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream);
+}
+
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

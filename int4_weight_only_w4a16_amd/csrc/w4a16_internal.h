@@ -116,6 +116,10 @@ int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, con
 W4A16_DECLARE_M(1) W4A16_DECLARE_M(2) W4A16_DECLARE_M(3) W4A16_DECLARE_M(4)
 W4A16_DECLARE_M(5) W4A16_DECLARE_M(6) W4A16_DECLARE_M(7) W4A16_DECLARE_M(8)
 #undef W4A16_DECLARE_M
+int launch_gemm(int M, int N, int K, const void* wq, const void* scales, const void* zeros, const void* x, void* y,
+                void* stream);
+int launch_dequant_f16(int N, int K, const void* wq, const void* scales, const void* zeros, void* out,
+                       void* stream);
 int launch_dequant(int N, int K, const void* wq, const void* scales, const void* zeros, float* out,
                    void* stream);
 

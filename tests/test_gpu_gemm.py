@@ -1,0 +1,71 @@
+"""GPU parity of the W4A16 GEMM for many activation rows (w4a16_gemm) and of
+its weights (w4a16_dequant_f16), through the C ABI, against the fp64 oracle.
+
+Bars: every output within the workload bound 2e-3 * sum|w x| + 1e-5 of the
+oracle's fp64 product; and, tighter, within fp32 accumulation and fp16
+output rounding of the product with the fp16-rounded weights fp16((q - z) s)
+(which the kernel multiplies exactly), so the weights it uses are pinned."""
+import numpy as np
+import pytest
+
+import int4_weight_only_w4a16_amd as w
+import oracle
+import synthetic
+from tests.gpu_common import Problem, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gemm]", *a, flush=True)
+
+
+def run_gemm(p):
+    torch, dev = torch_dev()
+    y = p.new_y()
+    w.w4a16_gemm(p.M, p.N, p.K, p.wq_d, p.sp_d, p.zp_d, p.x_d, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().view(np.uint16)
+
+
+def check_rounded_weights(p, y, rows=None):
+    """|y - x W16^T| <= 2^-11 |.| + 1e-4 * sum|W16 x| (+ 1e-5), with W16 the
+    fp16-rounded dequantized weights and the product in numpy float64."""
+    o = oracle.get()
+    rows = np.arange(p.N) if rows is None else rows
+    w16 = o.f16_to_f64(o.f64_to_f16(o.dequant(p.q[rows], p.s[rows], p.z[rows])))
+    xd = o.f16_to_f64(p.x)
+    ref = xd @ w16.T
+    absref = np.abs(xd) @ np.abs(w16).T
+    yd = o.f16_to_f64(y[:, rows])
+    allow = 2.0 ** -11 * np.abs(ref) + 1e-4 * absref + 1e-5
+    assert (np.abs(yd - ref) <= allow).all(), float((np.abs(yd - ref) / allow).max())
+
+
+@pytest.mark.parametrize("M,N,K", [(9, 37, 384), (16, 896, 896), (130, 200, 640), (128, 128, 128),
+                                   (300, 1000, 1152), (257, 4608, 3584)])
+def test_gemm_against_oracle(M, N, K):
+    _say("shape", M, N, K)
+    p = Problem(M, N, K, seed=M + N)
+    y = run_gemm(p)
+    _say(M, N, K, "worst", p.check(y))
+    check_rounded_weights(p, y)
+    assert np.array_equal(y, run_gemm(p)), "run-to-run difference"
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 37888, 3584), (1024, 3584, 18944)])
+def test_gemm_prefill_size_sampled(M, N, K):
+    """Prefill-sized calls: every row of a sample of 48 weight rows (tile
+    edges included) against the oracle, all M activation rows."""
+    _say("prefill sampled", M, N, K)
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, 15, 16, 127, 128, N - 1], rng.integers(0, N, 42)]))
+    q, s, z = synthetic.weights(N, K, seed=5)
+    p = Problem(M, N, K, q=q, s=s, z=z, x=synthetic.activations(M, K, seed=6))
+    y = run_gemm(p)
+    o = oracle.get()
+    ref, absref = o.gemv_packed(M, N, K, *p.packed, p.x, rows=rows)
+    ok, worst = oracle.bound_report(y[:, rows], ref, absref, o)
+    _say(M, N, K, "worst", worst)
+    assert ok, worst
+    check_rounded_weights(p, y, rows)

@@ -18,6 +18,31 @@ def _say(*a):
     print(*a, flush=True)
 
 
+# ------------------------------------------------------- dequant to fp16
+
+@pytest.mark.parametrize("N,K,scales_kind", [(896, 896, "workload"), (37, 384, "workload"),
+                                             (4608, 3584, "workload"), (5, 18944, "workload"),
+                                             (40, 1024, "any_bits")])
+def test_dequant_f16_bit_exact(N, K, scales_kind):
+    """fp16((q - z) * s) equals the oracle's fp64 product rounded to fp16 bit
+    for bit, including overflow to inf and subnormal results when the scale
+    bits are arbitrary (NaN scales excluded: any NaN payload is correct)."""
+    _say("dequant f16", N, K, scales_kind)
+    torch, dev = torch_dev()
+    q, s, z = synthetic.weights(N, K, seed=N + K)
+    if scales_kind == "any_bits":
+        s = np.random.default_rng(7).integers(0, 0x7C00, s.shape).astype(np.uint16)
+        s[::3] |= 0x8000
+    wq, sp, zp = w.w4a16_pack(q, s, z)
+    out = torch.empty((N, K), dtype=torch.int16, device=dev)
+    w.w4a16_dequant_f16(N, K, upload(wq), upload(sp), upload(zp), out)
+    torch.cuda.synchronize()
+    o = oracle.get()
+    want = o.f64_to_f16(o.dequant(q, s, z))
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+
+
 # ------------------------------------------------------------ dequant hook
 
 @pytest.mark.parametrize("N,K", [(896, 896), (37, 384), (4608, 3584), (5, 18944)])
