@@ -38,7 +38,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // this wave's 64 x 64 quarter
   const int rlane = lane & 15, piece = lane >> 4;
-  const int64_t m0 = int64_t(blockIdx.x) * kGemmBM;  // m fastest: neighbours share weights in L2
+  // m fastest: the workgroups resident at once share weight tiles in L2
+  // (making n fastest instead, to share x, measured no faster).
+  const int64_t m0 = int64_t(blockIdx.x) * kGemmBM;
   const int64_t tw = int64_t(blockIdx.y) * (kGemmBN / kTileRows) + wn * 4;  // wave's first row tile
 
   // The wave's four row tiles (clamped past the end: valid memory, never stored).
