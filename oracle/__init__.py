@@ -55,6 +55,8 @@ class Oracle:
         lib.or_gemv_packed.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]
         lib.or_gemv_packed_rows.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p, _p]
         lib.or_quantize.argtypes = [_i64, _i64, _p, ctypes.c_int, _p, _p, _p]
+        lib.or_act_quant_i8.argtypes = [_i64, _i64, _p, _p, _p, _p]
+        lib.or_gemv_a8.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _i64, _p, _p]
         self.plant = lib.or_plant()
 
     # -- fp16 codec -------------------------------------------------------
@@ -166,6 +168,42 @@ class Oracle:
                                               rows.size, ref.ctypes.data, absref.ctypes.data)
         if rc:
             raise ValueError("or_gemv_packed rejected its input")
+        return ref, absref
+
+    # -- INT8 activations -----------------------------------------------------
+    def act_quant_i8(self, x):
+        """fp16 bits [M][K] -> (xq int8 [M][K], sx float32 [M][G], xsum int32
+        [M][G]): symmetric codes per group of 128, decided in fp32."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        M, K = x.shape
+        G = K // GROUP
+        xq = np.empty((M, K), np.int8)
+        sx = np.empty((M, G), np.float32)
+        xsum = np.empty((M, G), np.int32)
+        if self.lib.or_act_quant_i8(M, K, x.ctypes.data, xq.ctypes.data, sx.ctypes.data, xsum.ctypes.data):
+            raise ValueError("or_act_quant_i8 rejected its input")
+        return xq, sx, xsum
+
+    def gemv_a8(self, q, s, z, xq, sx, rows=None):
+        """Integer-sum product with int8 activations; returns (ref, absref)
+        float64 [M][N], or [M][len(rows)] for the listed rows."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        s = np.ascontiguousarray(s, dtype=np.uint16)
+        z = np.ascontiguousarray(z, dtype=np.uint8)
+        xq = np.ascontiguousarray(xq, dtype=np.int8)
+        sx = np.ascontiguousarray(sx, dtype=np.float32)
+        N, K = q.shape
+        M = xq.shape[0]
+        if rows is not None:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+        R = N if rows is None else rows.size
+        ref = np.empty((M, R), np.float64)
+        absref = np.empty((M, R), np.float64)
+        rc = self.lib.or_gemv_a8(M, N, K, q.ctypes.data, s.ctypes.data, z.ctypes.data, xq.ctypes.data,
+                                 sx.ctypes.data, None if rows is None else rows.ctypes.data, R,
+                                 ref.ctypes.data, absref.ctypes.data)
+        if rc:
+            raise ValueError("or_gemv_a8 rejected its input")
         return ref, absref
 
 

@@ -22,6 +22,9 @@
  *  - The sum runs over k in ascending order in fp64; absref = sum_k |w*x|.
  *  - fp16 values are decoded and encoded (round to nearest, ties to even)
  *    from the IEEE-754 binary16 definition, written out below.
+ *  - The INT8-activation alternative of "Building an LLM Inference Runtime",
+ *    Bug #3 (Path A): per-group int8 activation codes and the integer-sum
+ *    product (or_act_quant_i8, or_gemv_a8, at the end of this file).
  *
  * The packed layout (ID 2) is this project's own device layout; pack/unpack
  * here follow its written definition element by element. The nibble order
@@ -428,5 +431,103 @@ int or_gemv_packed_rows(int64_t M, int64_t N, int64_t K, const uint8_t* wq, cons
     }
   }
   free(xd);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * INT8 activations: the alternative path of "Building an LLM Inference
+ * Runtime ... on NVIDIA H100", Bug #3 (Path A). A separate step turns the fp16
+ * activations into signed 8-bit codes with one scale per group; the weight
+ * codes and activation codes are multiplied and summed as integers; each
+ * group's integer sum is then brought back to a real value with the
+ * activation scale and the weight scale.
+ *
+ * The pages name the per-group activation scale but fix neither the group,
+ * the code range, the rounding nor the precision. Readings taken here:
+ *  - an activation group is 128 consecutive k of one activation row m, the
+ *    same k range as a weight group, so exactly one activation scale meets
+ *    one weight scale in each group sum;
+ *  - symmetric codes in [-127, 127]: sx = absmax / 127 and
+ *    xq = clamp(round_half_even(x / sx), -127, 127), a group of zeros giving
+ *    sx = 0 and xq = 0;
+ *  - the rounding decision is taken in IEEE single precision: absmax is
+ *    exact, sx is one correctly rounded division and x / sx another;
+ *  - xsum[m][g], the sum of the group's codes, is an output of the same step.
+ */
+int or_act_quant_i8(int64_t M, int64_t K, const uint16_t* x, int8_t* xq, float* sx, int32_t* xsum) {
+  if (M < 0 || K < OR_GROUP || K % OR_GROUP != 0) return -1;
+  int64_t G = K / OR_GROUP;
+  for (int64_t m = 0; m < M; m++) {
+    for (int64_t g = 0; g < G; g++) {
+      const uint16_t* xg = x + m * K + g * OR_GROUP;
+      float amax = 0.0f;
+      for (int j = 0; j < OR_GROUP; j++) {
+        double v = or_f16_to_f64(xg[j]);
+        if (v != v || v - v != 0.0) return -1; /* NaN or infinite activation */
+        float a = (float)fabs(v);              /* exact: fp16 values are floats */
+        if (a > amax) amax = a;
+      }
+#if OR_PLANT == 10
+      float scale = amax / 128.0f; /* planted: code range 128 */
+#else
+      float scale = amax / 127.0f;
+#endif
+      int32_t sum = 0;
+      for (int j = 0; j < OR_GROUP; j++) {
+        int code = 0;
+        if (scale > 0.0f) {
+          float r = (float)or_f16_to_f64(xg[j]) / scale;
+          code = (int)clamp_d(round_half_even((double)r), -127.0, 127.0);
+        }
+        xq[m * K + g * OR_GROUP + j] = (int8_t)code;
+        sum += code;
+      }
+      sx[m * G + g] = scale;
+      xsum[m * G + g] = sum;
+    }
+  }
+  return 0;
+}
+
+/* y[m][n] = sum_g s[n][g] * sx[m][g] * sum_{k in g} (q[n][k] - z[n][g]) * xq[m][k]
+ * from the logical q, s, z. The integer sum is exact (|.| <= 128*15*127 <
+ * 2^18) and so is the product of the three factors in fp64 (11 + 24 + 18
+ * significant bits); only the fp64 sum over groups, in ascending g, rounds.
+ * absref = sum_g |s * sx * integer sum|. With `rows` (nrows entries), only
+ * those rows, ref/absref [M][nrows]; with rows == NULL all N rows, [M][N]. */
+int or_gemv_a8(int64_t M, int64_t N, int64_t K, const uint8_t* q, const uint16_t* s, const uint8_t* z,
+               const int8_t* xq, const float* sx, const int64_t* rows, int64_t nrows, double* ref,
+               double* absref) {
+  if (M < 0 || !shape_ok(N, K)) return -1;
+  int64_t G = K / OR_GROUP;
+  int64_t R = rows ? nrows : N;
+  for (int64_t r = 0; rows && r < nrows; r++)
+    if (rows[r] < 0 || rows[r] >= N) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t r = 0; r < R; r++) {
+    int64_t n = rows ? rows[r] : r;
+    for (int64_t m = 0; m < M; m++) {
+      double acc = 0.0, aacc = 0.0;
+      for (int64_t g = 0; g < G; g++) {
+        int64_t isum = 0;
+        for (int64_t k = g * OR_GROUP; k < (g + 1) * OR_GROUP; k++) {
+#if OR_PLANT == 12
+          isum += (int64_t)q[n * K + k] * xq[m * K + k]; /* planted: zero point dropped */
+#else
+          isum += ((int64_t)q[n * K + k] - z[n * G + g]) * xq[m * K + k];
+#endif
+        }
+#if OR_PLANT == 11
+        double term = or_f16_to_f64(s[n * G + g]) * (double)sx[g] * (double)isum; /* planted: row 0's scale */
+#else
+        double term = or_f16_to_f64(s[n * G + g]) * (double)sx[m * G + g] * (double)isum;
+#endif
+        acc += term;
+        aacc += fabs(term);
+      }
+      ref[m * R + r] = acc;
+      absref[m * R + r] = aacc;
+    }
+  }
   return 0;
 }

@@ -473,4 +473,143 @@ def pin_swiglu_bound_admits_rounded_reference(o):
     assert np.median(bound / np.abs(ref).mean()) < 0.2
 
 
+
+# ------------------------------------------------------- INT8 activations
+
+def _grid_activations(seed, M=3, K=512, exps=(0, -3, 2, -7)):
+    """Activations already on an int8 grid: each group holds integers in
+    [-127, 127] including one +-127, times a power of two that varies by row
+    and group, so that the group's code scale is exactly that power."""
+    rng = np.random.default_rng(seed)
+    G = K // GROUP
+    c = rng.integers(-127, 128, size=(M, G, GROUP))
+    where = rng.integers(0, GROUP, size=(M, G))
+    sign = rng.choice([-1, 1], size=(M, G))
+    for m in range(M):
+        for g in range(G):
+            c[m, g, where[m, g]] = 127 * sign[m, g]
+    e = np.array([[exps[(m + 2 * g) % len(exps)] for g in range(G)] for m in range(M)], dtype=np.float64)
+    x = c * np.exp2(e)[..., None]
+    return c.reshape(M, K), np.exp2(e), x.reshape(M, K).astype(np.float16).view(np.uint16)
+
+
+def pin_act_quant_on_grid(o):
+    """A group of integers in [-127, 127] holding +-127, times 2^e, has code
+    scale exactly 2^e, codes equal to the integers and a code sum equal to
+    theirs (every step is exact there)."""
+    c, scale, x = _grid_activations(61)
+    xq, sx, xsum = o.act_quant_i8(x)
+    assert np.array_equal(sx.astype(np.float64), scale)
+    assert np.array_equal(xq.astype(np.int64), c)
+    M, K = c.shape
+    assert np.array_equal(xsum.astype(np.int64), c.reshape(M, K // GROUP, GROUP).sum(axis=2))
+
+
+def pin_act_quant_ties_to_even(o):
+    """With code scale 1, halves round to the even neighbour."""
+    x = np.zeros((1, GROUP))
+    x[0, 0] = 127.0
+    vals = [0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 3.5, -3.5, 126.5, -126.5, 0.25, 0.75]
+    want = [0, 0, 2, -2, 2, -2, 4, -4, 126, -126, 0, 1]
+    x[0, 1:1 + len(vals)] = vals
+    xq, sx, xsum = o.act_quant_i8(x.astype(np.float16).view(np.uint16))
+    assert sx[0, 0] == 1.0
+    assert xq[0, 1:1 + len(vals)].tolist() == want
+    assert xsum[0, 0] == 127 + sum(want)
+
+
+def pin_act_quant_nearest_code(o):
+    """Brute force over all 255 codes: every code is a nearest one for the
+    stored scale (to within the fp32 rounding of the decision); the absmax
+    element takes code +-127; the scale is absmax / 127 to within one fp32
+    rounding; an all-zero group has scale 0, codes 0 and sum 0."""
+    x = synthetic.activations(4, 1024, seed=63).view(np.float16).astype(np.float64)
+    x[1, 128:256] = 0.0
+    x[2, 256:384] = -np.abs(x[2, 256:384])
+    x[3, 0:128] *= 2.0 ** -12  # small groups, subnormal fp16 among them
+    x16 = x.astype(np.float16).view(np.uint16)
+    xd = x16.view(np.float16).astype(np.float64)
+    xq, sx, xsum = o.act_quant_i8(x16)
+    M, K = xd.shape
+    sd = np.repeat(sx.astype(np.float64), GROUP, axis=1)
+    codes = np.arange(-127, 128, dtype=np.float64)
+    err = np.abs(xd - xq * sd)
+    best = np.abs(xd[..., None] - codes * sd[..., None]).min(axis=2)
+    assert (err <= best + sd * 2.0 ** -20).all()
+    g = xd.reshape(M, K // GROUP, GROUP)
+    amax = np.abs(g).max(axis=2)
+    assert (np.abs(sx.astype(np.float64) * 127.0 - amax) <= amax * 2.0 ** -23).all()
+    arg = np.abs(g).argmax(axis=2)
+    top = np.take_along_axis(xq.reshape(M, K // GROUP, GROUP).astype(np.int64), arg[..., None], 2)[..., 0]
+    nz = amax > 0
+    assert (np.abs(top[nz]) == 127).all()
+    assert sx[1, 1] == 0 and not xq[1, 128:256].any() and xsum[1, 1] == 0
+    assert np.array_equal(xsum.astype(np.int64), xq.reshape(M, K // GROUP, GROUP).astype(np.int64).sum(axis=2))
+
+
+def pin_act_quant_power_of_two_scaling(o):
+    """Doubling the activations doubles every scale bit-exactly and leaves
+    the codes unchanged (fp32 scaling by 2 is exact, away from overflow)."""
+    x = synthetic.activations(3, 512, seed=65)
+    x2 = (x.view(np.float16).astype(np.float64) * 2.0).astype(np.float16).view(np.uint16)
+    a = o.act_quant_i8(x)
+    b = o.act_quant_i8(x2)
+    assert np.array_equal(b[0], a[0]) and np.array_equal(b[2], a[2])
+    assert np.array_equal(b[1], a[1] * np.float32(2.0))
+
+
+def pin_gemv_a8_tiny_case(o):
+    """Worked by hand: K = 128, q - z = 3 on k = 0..3, s = 0.5, activations
+    (127, -4.4, 2.6, 0.5) with scale 1 give codes (127, -4, 3, 0), so
+    y = 0.5 * 1 * 3 * (127 - 4 + 3 + 0) = 189; a second row with every
+    activation negated gives -189."""
+    q = np.full((1, GROUP), 5, np.uint8)
+    q[0, :4] = 8
+    z = np.full((1, 1), 5, np.uint8)
+    s = np.array([[np.float16(0.5).view(np.uint16)]], np.uint16)
+    x = np.zeros((2, GROUP))
+    x[0, :4] = [127.0, -4.4, 2.6, 0.5]
+    x[1] = -x[0]
+    xq, sx, _ = o.act_quant_i8(x.astype(np.float16).view(np.uint16))
+    ref, absref = o.gemv_a8(q, s, z, xq, sx)
+    assert ref[0, 0] == 189.0 and ref[1, 0] == -189.0 and absref[0, 0] == 189.0
+
+
+def pin_gemv_a8_matches_fp_path_on_grid(o):
+    """When the activations are already on the int8 grid their codes are
+    exact, so the integer-sum product equals the fp16-activation product of
+    the (separately pinned) main oracle, row by row and group scale by group
+    scale."""
+    _, _, x = _grid_activations(67, M=3, K=768)
+    q, s, z = synthetic.weights(40, 768, seed=68)
+    xq, sx, _ = o.act_quant_i8(x)
+    ref8, abs8 = o.gemv_a8(q, s, z, xq, sx)
+    ref, absref = o.gemv(q, s, z, x)
+    assert (abs8 <= absref * (1 + 1e-12)).all()  # |group sums| summed, against |w x| summed
+    assert (np.abs(ref8 - ref) <= 1e-12 * absref).all()
+    rows = np.array([39, 0, 17])
+    r8, _ = o.gemv_a8(q, s, z, xq, sx, rows=rows)
+    assert np.array_equal(r8, ref8[:, rows])
+
+
+def pin_gemv_a8_quantization_error_bound(o):
+    """On the workload's activations the integer-sum product differs from the
+    exact fp16-activation product by no more than the codes' rounding allows,
+    sum_g s * (sx / 2) * sum_k |q - z| (codes never clamp: |x| <= absmax);
+    and, the rounding errors being independent, the root-mean-square
+    difference is a small fraction of the outputs' (about 0.7% here)."""
+    K = 1024
+    q, s, z = synthetic.weights(48, K, seed=69)
+    x = synthetic.activations(5, K, seed=70)
+    xq, sx, _ = o.act_quant_i8(x)
+    ref8, _ = o.gemv_a8(q, s, z, xq, sx)
+    ref, _ = o.gemv(q, s, z, x)
+    G = K // GROUP
+    sd = o.f16_to_f64(s)                                                   # [N][G]
+    wabs = np.abs(q.astype(np.int64) - np.repeat(z, GROUP, axis=1)).reshape(48, G, GROUP).sum(axis=2)
+    allow = (sd * wabs) @ (sx.astype(np.float64).T / 2.0)                  # [N][M]
+    assert (np.abs(ref8 - ref) <= allow.T * (1 + 1e-9) + 1e-12).all()
+    assert np.sqrt(((ref8 - ref) ** 2).mean()) < 0.02 * np.sqrt((ref ** 2).mean())
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -18,6 +18,9 @@ PLANTS = {
     7: "fp16 subnormals decoded with a hidden bit",
     8: "symmetric quantizer scale absmax / 8",
     9: "asymmetric quantizer drops the zero point",
+    10: "activation code scale absmax / 128",
+    11: "activation scale of row 0 used for every row",
+    12: "integer-sum product drops the zero point",
 }
 
 
