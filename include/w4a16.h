@@ -239,6 +239,41 @@ int w4a16_gemm(int M, int N, int K, const void* Wq, const void* scales, const vo
                void* y, void* stream);
 
 /*
+ * INT8 activations, step 1 of 2: the activation quantizer of the alternative
+ * path ("Path A") of "Building an LLM Inference Runtime", Bug #3, which turns
+ * the fp16 activations into 8-bit integers with one scale per group in a
+ * launch of its own before each GEMV. Per activation row m and group g of 128
+ * consecutive columns (the weight groups' column ranges):
+ *     sx[m][g]   = absmax_g / 127            (fp32, correctly rounded)
+ *     xq[m][k]   = clamp(rne(x[m][k] / sx[m][g]), -127, 127)   (fp32 division)
+ *     xsum[m][g] = sum of the group's codes
+ * and a group of zeros gets sx = 0 and codes 0. x: device fp16 [M][K]
+ * (finite values; codes for NaN or infinity are unspecified); xq: device
+ * int8 [M][K]; sx: device fp32 [M][K/128]; xsum: device int32 [M][K/128],
+ * all row-major and 16-byte aligned. Same M and K rules as w4a16_gemv.
+ * Errors: W4A16_EINVAL (shape, NULL, alignment), W4A16_EUNSUPPORTED (M > 8),
+ * W4A16_EHIP.
+ */
+int w4a16_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream);
+
+/*
+ * INT8 activations, step 2 of 2: the GEMV over the codes of
+ * w4a16_act_quant_i8, on the integer matrix cores (the counterpart of the
+ * page's dp4a):
+ *     y[m][n] = sum_g s[n][g] * sx[m][g] * sum_{k in g} (q[n][k] - z[n][g]) * xq[m][k]
+ * Each group's integer sum is exact (computed as sum q xq - z * xsum); the
+ * group terms are scaled and summed in fp32, in a fixed order, and y is
+ * rounded to fp16 (nearest even): within 2e-3 * sum_g |term| + 1e-5 of the
+ * exact value. This approximates w4a16_gemv's y by the activation rounding
+ * (at most sum_g s * sx / 2 * sum_k |q - z| per output); it is provided for
+ * comparison, as on that page. Wq, scales, zeros: layout ID 2; xq, sx, xsum:
+ * the outputs of w4a16_act_quant_i8 for the same M and K; y: device fp16
+ * [M][N]. Rows are bit-identical whatever M. Errors: as w4a16_gemv.
+ */
+int w4a16_gemv_a8(int M, int N, int K, const void* Wq, const void* scales, const void* zeros, const void* xq,
+                  const void* sx, const void* xsum, void* y, void* stream);
+
+/*
  * Standalone dequantization, for paths that want the fp16 matrix itself
  * (a GEMM over many activation rows, for instance): W_out[n][k] =
  * fp16((q - z) * s), the exact product rounded once to nearest even, for

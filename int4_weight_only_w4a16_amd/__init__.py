@@ -26,7 +26,8 @@ MAX_M = 8
 EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_quantize",
            "w4a16_unpack",
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
-           "w4a16_gemv_splitk", "w4a16_gemm", "w4a16_dequant_f16", "w4a16_dequant_f32", "w4a16_strerror")
+           "w4a16_gemv_splitk", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemm", "w4a16_dequant_f16",
+           "w4a16_dequant_f32", "w4a16_strerror")
 
 
 class W4A16Error(RuntimeError):
@@ -73,6 +74,8 @@ def lib():
         L.w4a16_dequant_f32.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_dequant_f16.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_gemm.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
+        L.w4a16_act_quant_i8.argtypes = [_i, _i, _p, _p, _p, _p, _p]
+        L.w4a16_gemv_a8.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]
         L.w4a16_strerror.restype = ctypes.c_char_p
         L.w4a16_strerror.argtypes = [_i]
         _lib = L
@@ -205,6 +208,20 @@ def w4a16_gemv_splitk(M, N, K, splits, Wq, scales, zeros, x, y, workspace, ws_by
     _check(lib().w4a16_gemv_splitk(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x),
                                    _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)),
            "w4a16_gemv_splitk")
+
+
+def w4a16_act_quant_i8(M, K, x, xq, sx, xsum, stream=None):
+    """Device: fp16 x[M][K] -> int8 codes xq[M][K], fp32 scales sx[M][K/128],
+    int32 code sums xsum[M][K/128] (one symmetric scale per group of 128)."""
+    _check(lib().w4a16_act_quant_i8(M, K, _ptr(x), _ptr(xq), _ptr(sx), _ptr(xsum), _stream(stream)),
+           "w4a16_act_quant_i8")
+
+
+def w4a16_gemv_a8(M, N, K, Wq, scales, zeros, xq, sx, xsum, y, stream=None):
+    """Device: y[M][N] (fp16) from the int8 activation codes of
+    w4a16_act_quant_i8 (integer sums per group, then both scales)."""
+    _check(lib().w4a16_gemv_a8(M, N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(xq), _ptr(sx), _ptr(xsum),
+                               _ptr(y), _stream(stream)), "w4a16_gemv_a8")
 
 
 def w4a16_gemm(M, N, K, Wq, scales, zeros, x, y, stream=None):

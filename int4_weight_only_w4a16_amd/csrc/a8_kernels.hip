@@ -1,0 +1,291 @@
+// INT8-activation variant for gfx950: the alternative path of "Building an
+// LLM Inference Runtime ... on NVIDIA H100", Bug #3 (Path A). The fp16
+// activations are first turned into signed 8-bit codes with one fp32 scale
+// per group of 128 (a launch of its own, as on that page); the GEMV then
+// multiplies weight codes by activation codes as integers and brings each
+// group's integer sum back with the weight scale and the activation scale.
+//
+// On CDNA4 the integer products run on the matrix cores
+// (v_mfma_i32_16x16x64_i8, the counterpart of the page's dp4a). The weight
+// codes need no arithmetic at all: q is 0..15, already a valid signed byte,
+// so masking a packed word's low and high nibbles yields four int8 B-operand
+// bytes each. The zero point is applied once per group and row, exactly, in
+// integers: sum_k (q - z) xq = sum_k q xq - z * sum_k xq, with sum_k xq
+// (one number per activation row and group) produced by the quantizer.
+#include "w4a16_device.h"
+
+namespace w4a16 {
+namespace dev {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One wave per (activation row m, group g): lane l holds x[m][128g + 2l] and
+// the next. sx = absmax / 127 (fp32, correctly rounded); code =
+// clamp(rne(x / sx), -127, 127); a group of zeros gets sx = 0 and codes 0.
+// xsum = the sum of the group's codes. Groups are numbered i = m * G + g.
+__global__ __launch_bounds__(256) void act_quant_i8_kernel(const _Float16* __restrict__ x, int8_t* __restrict__ xq,
+                                                          float* __restrict__ sx, int32_t* __restrict__ xsum,
+                                                          int64_t groups_total, int K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (i >= groups_total) return;  // whole waves
+  const int G = K / kGroup;
+  const int64_t m = i / G;
+  const int64_t g = i - m * G;
+  const int64_t base = m * K + g * kGroup + 2 * lane;
+  const half2_t v = *reinterpret_cast<const half2_t*>(x + base);
+  const float a0 = float(v.x), a1 = float(v.y);
+  float amax = fmaxf(fabsf(a0), fabsf(a1));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax / 127.0f;
+  int c0 = 0, c1 = 0;
+  if (scale > 0.0f) {
+    c0 = int(fminf(fmaxf(rintf(a0 / scale), -127.0f), 127.0f));
+    c1 = int(fminf(fmaxf(rintf(a1 / scale), -127.0f), 127.0f));
+  }
+  *reinterpret_cast<uint16_t*>(xq + base) = uint16_t((uint32_t(c0) & 0xFFu) | ((uint32_t(c1) & 0xFFu) << 8));
+  int sum = c0 + c1;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane == 0) {
+    sx[i] = scale;
+    xsum[i] = sum;
+  }
+}
+
+// Activation bytes x0..x7 of 8 consecutive columns -> the two words whose
+// bytes line up with the masked nibbles of one packed weight word: the
+// layout puts weight j of a word at nibble slot {0,4,1,5,2,6,3,7}[j], so
+// (w & 0x0F0F0F0F) holds weights (0, 4, 1, 5) in bytes 0..3 and
+// ((w >> 4) & 0x0F0F0F0F) weights (2, 6, 3, 7).
+__device__ __forceinline__ u32x2 interleave_codes(uint32_t d0, uint32_t d1) {
+  const uint32_t lo = (d0 & 0xFFu) | ((d1 & 0xFFu) << 8) | ((d0 & 0xFF00u) << 8) | ((d1 & 0xFF00u) << 16);
+  const uint32_t hi = ((d0 >> 16) & 0xFFu) | ((d1 >> 8) & 0xFF00u) | ((d0 & 0xFF000000u) >> 8) | (d1 & 0xFF000000u);
+  return {lo, hi};
+}
+
+// GEMV with int8 activation codes: one 16-row tile per workgroup; the WAVES
+// waves take contiguous shares of the groups, in rounds of at most SHARE
+// tiles. Per round a wave stages its activation codes in its private LDS
+// slice, in MFMA operand order, with the groups' sx and xsum; requests all
+// of the round's weight tiles (straight-line, clamped, as the fp16 GEMV
+// does) and then runs, per tile, two integer MFMAs (64 columns each) with
+// the codes as A (row m = lane % 16, rows >= M repeat the last) and the
+// weight nibbles as B (column = tile row). Lane l then holds the integer
+// sums D[4(l/16) + r][l % 16], corrects them by the zero point, and adds
+// float(D - z xsum) * (s * sx) to its fp32 accumulators. The waves' sums
+// meet in LDS and are added in wave order, so results are bit-identical run
+// to run and do not depend on M.
+//
+// LDS: [WAVES][4][rows][16] floats for the reduction, then per wave
+// [M][SHARE][128] code bytes and [SHARE][16] sx and xsum values (activation
+// rows 0..15 of each group, zero past M).
+template <int MR, int WAVES, int SHARE>
+__global__ __launch_bounds__(WAVES * 64) void gemv_a8_kernel(
+    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
+    const int8_t* __restrict__ xq, const float* __restrict__ sx, const int32_t* __restrict__ xsum,
+    _Float16* __restrict__ y, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int kRows = MR < 4 ? MR : 4;                      // D rows of a lane that are activation rows
+  constexpr int kRedWave = 4 * kRows * 16;
+  constexpr int kSlice = MR * SHARE * kGroup + 2 * SHARE * 16 * 4;  // bytes per wave
+  float* red = reinterpret_cast<float*>(smem);
+  const int G = K / kGroup;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int piece = lane >> 4, rlane = lane & 15;
+  const int mm = rlane < MR ? rlane : MR - 1;
+  unsigned char* slice = smem + WAVES * kRedWave * sizeof(float) + wave * kSlice;
+  float* ssx = reinterpret_cast<float*>(slice + MR * SHARE * kGroup);  // [SHARE][16]
+  int32_t* ssum = reinterpret_cast<int32_t*>(ssx + SHARE * 16);      // [SHARE][16]
+  const int share_beg = (wave * G) / WAVES, share_end = ((wave + 1) * G) / WAVES;
+
+  const int64_t t = blockIdx.x;
+  const int64_t q0 = t * G;  // tile (t, 0)
+  const u32x4* wlane = reinterpret_cast<const u32x4*>(wq + q0 * kTileBytes) + lane;
+  const uint32_t* sword = reinterpret_cast<const uint32_t*>(scales) + q0 * (kTileRows / 2) + (rlane >> 1);
+  const uint32_t* zword = reinterpret_cast<const uint32_t*>(zeros) + q0 * (kTileRows / 8) + (rlane >> 3);
+
+  float acc[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
+
+  for (int g0 = share_beg; g0 < share_end; g0 += SHARE) {
+    const int n = min(SHARE, share_end - g0);
+    // Activation codes first (their wait then covers them alone): 16-byte
+    // chunks c = (m, group u, 16 columns h), clamped to the last real chunk.
+    constexpr int kXSteps = (MR * SHARE * 8 + 63) / 64;
+    const int xchunks = n * 8, xtotal = MR * xchunks;
+    u32x4 xv[kXSteps];
+#pragma unroll
+    for (int j = 0; j < kXSteps; ++j) {
+      const int c = min(lane + 64 * j, xtotal - 1);
+      const int m = c / xchunks, cc = c - m * xchunks;
+      xv[j] = *reinterpret_cast<const u32x4*>(xq + int64_t(m) * K + int64_t(g0) * kGroup + cc * 16);
+    }
+    constexpr int kMSteps = (SHARE * 16 + 63) / 64;
+    float mv[kMSteps];
+    int32_t sv[kMSteps];
+#pragma unroll
+    for (int j = 0; j < kMSteps; ++j) {
+      const int c = min(lane + 64 * j, n * 16 - 1);
+      const int u = c >> 4, m = c & 15;
+      const int64_t e = int64_t(m < MR ? m : 0) * G + g0 + u;
+      mv[j] = m < MR ? sx[e] : 0.f;
+      sv[j] = m < MR ? xsum[e] : 0;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 w[SHARE];
+    uint32_t sw[SHARE], zw[SHARE];
+#pragma unroll
+    for (int u = 0; u < SHARE; ++u) {
+      const int gg = g0 + min(u, n - 1);
+      w[u] = __builtin_nontemporal_load(wlane + int64_t(gg) * (kTileBytes / 16));
+      sw[u] = sword[gg * (kTileRows / 2)];
+      zw[u] = zword[gg * (kTileRows / 8)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage: chunk (m, u, h) covers columns 16h .. 16h+15 of group u, i.e.
+    // 8-column blocks b = 2h, 2h+1 with b = 4 kb + piece; block b goes to
+    // byte (kb / 2) * 64 + piece * 16 + (kb % 2) * 8 of the group's 128.
+#pragma unroll
+    for (int j = 0; j < kXSteps; ++j) {
+      const int c = min(lane + 64 * j, xtotal - 1);
+      const int m = c / xchunks, cc = c - m * xchunks;
+      const int u = cc >> 3, h = cc & 7;
+      unsigned char* dst = slice + (m * SHARE + u) * kGroup;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int b = 2 * h + half, kb = b >> 2, pc = b & 3;
+        const u32x2 v = interleave_codes(xv[j][2 * half], xv[j][2 * half + 1]);
+        *reinterpret_cast<u32x2*>(dst + (kb >> 1) * 64 + pc * 16 + (kb & 1) * 8) = v;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMSteps; ++j) {
+      const int c = min(lane + 64 * j, n * 16 - 1);
+      ssx[c] = mv[j];
+      ssum[c] = sv[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+
+    int xoff = mm * SHARE * kGroup + piece * 16;
+    asm volatile("" : "+v"(xoff));
+#pragma unroll
+    for (int u = 0; u < SHARE; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 wt = w[u];
+      uint32_t zt = zw[u], st = sw[u];
+      asm volatile("" : "+v"(wt), "+v"(zt), "+v"(st));
+      const unsigned char* xg = slice + xoff + u * kGroup;
+      const i32x4 a0 = *reinterpret_cast<const i32x4*>(xg);
+      const i32x4 a1 = *reinterpret_cast<const i32x4*>(xg + 64);
+      const i32x4 b0 = {int32_t(wt[0] & 0x0F0F0F0Fu), int32_t((wt[0] >> 4) & 0x0F0F0F0Fu),
+                        int32_t(wt[1] & 0x0F0F0F0Fu), int32_t((wt[1] >> 4) & 0x0F0F0F0Fu)};
+      const i32x4 b1 = {int32_t(wt[2] & 0x0F0F0F0Fu), int32_t((wt[2] >> 4) & 0x0F0F0F0Fu),
+                        int32_t(wt[3] & 0x0F0F0F0Fu), int32_t((wt[3] >> 4) & 0x0F0F0F0Fu)};
+      i32x4 d = {0, 0, 0, 0};
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, d, 0, 0, 0);
+      const int z = int((zt >> ((rlane & 7) * 4)) & 15u);
+      const float s = half_bits_to_float((st >> ((rlane & 1) * 16)) & 0xFFFFu);
+      const f32x4 gsx = *reinterpret_cast<const f32x4*>(ssx + u * 16 + 4 * piece);
+      const i32x4 gsum = *reinterpret_cast<const i32x4*>(ssum + u * 16 + 4 * piece);
+      const bool valid = u < n;
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const float term = float(d[r] - __mul24(z, gsum[r]));  // |xsum| <= 128 * 127 < 2^23
+        acc[r] = valid ? __builtin_fmaf(term, s * gsx[r], acc[r]) : acc[r];
+      }
+    }
+    // The next round restages the slice: every lane's reads are done first.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+
+  // Cross-wave sum in wave order; lane l holds activation rows 4 piece + r.
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) red[wave * kRedWave + (piece * kRows + r) * 16 + rlane] = acc[r];
+  lds_barrier();
+  constexpr int kOut = (MR * 16 + WAVES * 64 - 1) / (WAVES * 64);
+#pragma unroll
+  for (int j = 0; j < kOut; ++j) {
+    const int idx = tid + j * WAVES * 64;
+    const int m = idx >> 4, i = idx & 15;
+    const int64_t nn = t * kTileRows + i;
+    if (idx < MR * 16 && nn < N) {
+      const int slot = ((m >> 2) * kRows + (m & 3)) * 16 + i;
+      float sum = red[slot];
+#pragma unroll
+      for (int w2 = 1; w2 < WAVES; ++w2) sum += red[w2 * kRedWave + slot];
+      y[int64_t(m) * N + nn] = (_Float16)sum;
+    }
+  }
+}
+
+template <int MR, int WAVES, int SHARE>
+hipError_t launch_a8_typed(int N, int K, const void* wq, const void* scales, const void* zeros, const void* xq,
+                           const void* sx, const void* xsum, void* y, hipStream_t stream) {
+  constexpr size_t lds = gemv_a8_lds_bytes(MR, WAVES, SHARE);
+  static_assert(lds <= kMaxLdsBytes, "instantiation beyond the LDS of a workgroup");
+  auto* kernel = &gemv_a8_kernel<MR, WAVES, SHARE>;
+  if constexpr (lds > kDefaultLdsLimit) {
+    static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (raised != hipSuccess) return raised;
+  }
+  const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;
+  return launch_kernel(kernel, dim3(unsigned(row_tiles)), dim3(WAVES * 64), lds, stream,
+                       static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
+                       static_cast<const uint8_t*>(zeros), static_cast<const int8_t*>(xq),
+                       static_cast<const float*>(sx), static_cast<const int32_t*>(xsum), static_cast<_Float16*>(y),
+                       N, K);
+}
+
+template <int MR>
+hipError_t launch_a8_m(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales, const void* zeros,
+                       const void* xq, const void* sx, const void* xsum, void* y, hipStream_t stream) {
+#define W4A16_A8_CASE(W, S)                                                                      \
+  if constexpr (a8_instantiated(MR, W, S)) {                                                     \
+    if (plan.waves == W && plan.share == S)                                                      \
+      return launch_a8_typed<MR, W, S>(N, K, wq, scales, zeros, xq, sx, xsum, y, stream);        \
+  }
+#define W4A16_A8_SHARES(W) W4A16_A8_CASE(W, 4) W4A16_A8_CASE(W, 7) W4A16_A8_CASE(W, 10)
+  W4A16_A8_SHARES(1) W4A16_A8_SHARES(2) W4A16_A8_SHARES(4) W4A16_A8_SHARES(8) W4A16_A8_SHARES(16)
+#undef W4A16_A8_SHARES
+#undef W4A16_A8_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dev
+
+int launch_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream) {
+  const int64_t groups_total = int64_t(M) * (K / kGroup);
+  return int(dev::launch_kernel(&dev::act_quant_i8_kernel, dim3(unsigned((groups_total + 3) / 4)), dim3(256), 0,
+                                static_cast<hipStream_t>(stream), static_cast<const _Float16*>(x),
+                                static_cast<int8_t*>(xq), static_cast<float*>(sx), static_cast<int32_t*>(xsum),
+                                groups_total, K));
+}
+
+int launch_gemv_a8(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
+                   const void* zeros, const void* xq, const void* sx, const void* xsum, void* y, void* stream_ptr) {
+  const hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  switch (M) {
+    case 1: return int(dev::launch_a8_m<1>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 2: return int(dev::launch_a8_m<2>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 3: return int(dev::launch_a8_m<3>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 4: return int(dev::launch_a8_m<4>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 5: return int(dev::launch_a8_m<5>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 6: return int(dev::launch_a8_m<6>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 7: return int(dev::launch_a8_m<7>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 8: return int(dev::launch_a8_m<8>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    default: return int(hipErrorInvalidValue);
+  }
+}
+
+}  // namespace w4a16

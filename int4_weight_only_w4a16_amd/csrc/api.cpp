@@ -111,7 +111,41 @@ w4a16::LaunchPlan plan_swiglu(int K) {
   return plan;
 }
 
+// Plan of the INT8-activation GEMV: as many waves as plan_for gives the
+// same K (so rows are batch invariant: the fp32 order depends on the waves
+// only), each wave's groups in one round of a 4-, 7- or 10-tile share, or
+// in rounds of a smaller share where the workgroup's LDS (codes of all M
+// rows) would not hold the larger one.
+w4a16::LaunchPlan plan_a8(int M, int K) {
+  w4a16::LaunchPlan plan = plan_for(1, 0, K, 1);
+  const int groups = K / W4A16_GROUP;
+  const int per_wave = (groups + plan.waves - 1) / plan.waves;
+  plan.engine = w4a16::kEngineMfma;
+  plan.share = per_wave <= 4 ? 4 : (per_wave <= 7 ? 7 : 10);
+  while (plan.share > 4 && !w4a16::a8_instantiated(M, plan.waves, plan.share)) plan.share = plan.share == 10 ? 7 : 4;
+  return plan;
+}
+
 }  // namespace
+
+extern "C" int w4a16_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream) {
+  const int rc = check_shape(M, 1, K);
+  if (rc != W4A16_OK) return rc == 1 ? W4A16_OK : rc;
+  if (!pointers_ok({x, xq, sx, xsum})) return W4A16_EINVAL;
+  if (w4a16::launch_act_quant_i8(M, K, x, xq, sx, xsum, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
+
+extern "C" int w4a16_gemv_a8(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,
+                             const void* xq, const void* sx, const void* xsum, void* y, void* stream) {
+  const int rc = check_shape(M, N, K);
+  if (rc != W4A16_OK) return rc == 1 ? W4A16_OK : rc;
+  if (!pointers_ok({Wq, scales, zeros, xq, sx, xsum, y})) return W4A16_EINVAL;
+  const w4a16::LaunchPlan plan = plan_a8(M, K);
+  if (!w4a16::a8_instantiated(M, plan.waves, plan.share)) return W4A16_EUNSUPPORTED;
+  if (w4a16::launch_gemv_a8(M, N, K, plan, Wq, scales, zeros, xq, sx, xsum, y, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
 
 extern "C" int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,
                           const void* x, void* y, void* stream) {

@@ -116,6 +116,23 @@ int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, con
 W4A16_DECLARE_M(1) W4A16_DECLARE_M(2) W4A16_DECLARE_M(3) W4A16_DECLARE_M(4)
 W4A16_DECLARE_M(5) W4A16_DECLARE_M(6) W4A16_DECLARE_M(7) W4A16_DECLARE_M(8)
 #undef W4A16_DECLARE_M
+// INT8-activation variant (a8_kernels.hip). LDS of a GEMV workgroup: the
+// reduction buffers [waves][4][min(M, 4)][16] floats, then per wave the
+// activation codes [M][share][128] bytes and [share][16] fp32 scales and
+// int32 code sums.
+constexpr size_t gemv_a8_lds_bytes(int mr, int waves, int share) {
+  return size_t(waves) * 4 * (mr < 4 ? mr : 4) * 16 * sizeof(float) +
+         size_t(waves) * (size_t(mr) * share * kGroup + size_t(share) * 16 * 8);
+}
+// Instantiated (waves, share): waves 1..16 (powers of two), shares 4, 7, 10,
+// within the LDS of a workgroup.
+constexpr bool a8_instantiated(int mr, int waves, int share) {
+  return (waves == 1 || waves == 2 || waves == 4 || waves == 8 || waves == 16) &&
+         (share == 4 || share == 7 || share == 10) && gemv_a8_lds_bytes(mr, waves, share) <= kMaxLdsBytes;
+}
+int launch_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream);
+int launch_gemv_a8(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
+                   const void* zeros, const void* xq, const void* sx, const void* xsum, void* y, void* stream);
 int launch_gemm(int M, int N, int K, const void* wq, const void* scales, const void* zeros, const void* x, void* y,
                 void* stream);
 int launch_dequant_f16(int N, int K, const void* wq, const void* scales, const void* zeros, void* out,

@@ -198,6 +198,18 @@ def test_device_entry_points_reject_before_launch():
     assert L.w4a16_dequant_f16(16, 200, fake, fake, fake, fake, None) == w.W4A16_EINVAL
     assert L.w4a16_dequant_f16(0, 128, None, None, None, None, None) == w.W4A16_OK
     assert L.w4a16_dequant_f16(16, 128, fake, fake, fake, fake + 4, None) == w.W4A16_EINVAL
+    # INT8 activations: quantizer and GEMV
+    assert L.w4a16_act_quant_i8(1, 200, fake, fake, fake, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_act_quant_i8(9, 128, fake, fake, fake, fake, None) == w.W4A16_EUNSUPPORTED
+    assert L.w4a16_act_quant_i8(0, 128, None, None, None, None, None) == w.W4A16_OK
+    assert L.w4a16_act_quant_i8(1, 128, fake, fake, fake + 4, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_act_quant_i8(1, 128, fake, None, fake, fake, None) == w.W4A16_EINVAL
+    a8 = [fake] * 8
+    assert L.w4a16_gemv_a8(1, 16, 200, *a8, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemv_a8(9, 16, 128, *a8, None) == w.W4A16_EUNSUPPORTED
+    assert L.w4a16_gemv_a8(1, 0, 128, *a8, None) == w.W4A16_OK
+    assert L.w4a16_gemv_a8(1, 16, 128, fake, fake, fake, fake, fake, fake + 4, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemv_a8(1, 16, 128, fake, fake, fake, fake, None, fake, fake, None) == w.W4A16_EINVAL
     # dequant hook
     assert L.w4a16_dequant_f32(16, 200, fake, fake, fake, fake, None) == w.W4A16_EINVAL
     assert L.w4a16_dequant_f32(0, 128, None, None, None, None, None) == w.W4A16_OK
