@@ -111,11 +111,18 @@ class Step:
         self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)  # zero once; calls leave it zero
         self.stream = torch.cuda.Stream()
 
-    def launch_all(self, stream, only=None, swiglu=False, torch_act=False):
-        for name, N, K, wq, sc, zp, x, y in self.bufs:
+    def launch_all(self, stream, only=None, swiglu=False, torch_act=False, a8=None):
+        for i, (name, N, K, wq, sc, zp, x, y) in enumerate(self.bufs):
             if only is not None and not name.endswith(only):
                 continue
-            if swiglu and name.endswith("gate_up_proj"):
+            if a8 is not None:
+                # INT8-activation variant: quantize x (a launch of its own,
+                # skipped for a8 == "gemv"), then the integer-MFMA GEMV.
+                xq, sx, xs = self.a8_bufs[i]
+                if a8 != "gemv":
+                    self.w.w4a16_act_quant_i8(1, K, x, xq, sx, xs, stream=stream)
+                self.w.w4a16_gemv_a8(1, N, K, wq, sc, zp, xq, sx, xs, y, stream=stream)
+            elif swiglu and name.endswith("gate_up_proj"):
                 # The same packed bytes read as the 16-row gate/up interleave.
                 self.w.w4a16_gemv_swiglu(1, N // 2, K, wq, sc, zp, x, self.y_act, stream=stream)
             else:
@@ -130,19 +137,27 @@ class Step:
                     h = y.view(self.torch.float16).view(1, 2, N // 2)
                     self.torch.mul(self.torch.nn.functional.silu(h[:, 0]), h[:, 1], out=self.y_act_h)
 
-    def capture(self, only=None, swiglu=False, torch_act=False):
+    def capture(self, only=None, swiglu=False, torch_act=False, a8=None):
         torch = self.torch
         if (swiglu or torch_act) and not hasattr(self, "y_act"):
             _, N, _ = synthetic.QWEN7B_LAYER[2]
             self.y_act = torch.empty((1, N // 2), dtype=torch.int16, device="cuda:0")
             self.y_act_h = self.y_act.view(torch.float16)
+        if a8 is not None and not hasattr(self, "a8_bufs"):
+            dev = torch.device("cuda:0")
+            self.a8_bufs = [(torch.empty((1, K), dtype=torch.int8, device=dev),
+                             torch.empty((1, K // 128), dtype=torch.float32, device=dev),
+                             torch.empty((1, K // 128), dtype=torch.int32, device=dev))
+                            for _, _, K, *_ in self.bufs]
         self.stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(self.stream):
-            self.launch_all(self.stream, only, swiglu, torch_act)  # warm: first launches load code objects
+            # warm: first launches load code objects (and, for the INT8
+            # variant, leave valid codes for a8 == "gemv")
+            self.launch_all(self.stream, only, swiglu, torch_act, None if a8 is None else "both")
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=self.stream):
-                self.launch_all(self.stream, only, swiglu, torch_act)
+                self.launch_all(self.stream, only, swiglu, torch_act, a8)
         torch.cuda.synchronize()
         return g
 
@@ -298,6 +313,16 @@ def main():
     unfused_us = step.time_graph(unfused, reps, 3) / (reps * n_dom) * 1e6
     del fused, fused_step, unfused
 
+    # Variant: INT8 activations (the dp4a path of the H100 runtime page, here
+    # on the integer matrix cores): a quantize launch before each GEMV.
+    a8_gate_up = step.capture(only="gate_up_proj", a8="both")
+    a8_gate_up_us = step.time_graph(a8_gate_up, reps, 3) / (reps * n_dom) * 1e6
+    a8_gemv = step.capture(only="gate_up_proj", a8="gemv")
+    a8_gemv_us = step.time_graph(a8_gemv, reps, 3) / (reps * n_dom) * 1e6
+    a8_step = step.capture(a8="both")
+    a8_step_us = step.time_graph(a8_step, args.steps, args.warmup) / args.steps * 1e6
+    del a8_gate_up, a8_gemv, a8_step
+
     # Prefill (M = 2048) on the gate+up shape: the fused W4A16 GEMM, the
     # standalone fp16 dequantization, and for context the two-step route
     # (that dequantization, then torch's fp16 library GEMM).
@@ -398,6 +423,15 @@ def main():
                 "unfused_gate_up_plus_torch_silu_mul_us": round(unfused_us, 3),
                 "step_us_with_fused_gate_up": round(fused_step_s / args.steps * 1e6, 2),
             },
+        },
+        "int8_activations": {
+            "kernels": "w4a16_act_quant_i8 + w4a16_gemv_a8 (v_mfma_i32_16x16x64_i8), per GEMV",
+            "gate_up_quant_plus_gemv_us": round(a8_gate_up_us, 3),
+            "gate_up_gemv_a8_only_us": round(a8_gemv_us, 3),
+            "gate_up_fp16_activations_us": round(dom_us, 3),
+            "step_us": round(a8_step_us, 2),
+            "step_us_fp16_activations": round(us_step, 2),
+            "launches_per_step": 2 * len(step.shapes),
         },
         "prefill_gemm": prefill,
         "host_quantize": {"shape": f"{Nq}x{Kq} fp16", "GBps_fp16_in": quant,
