@@ -240,12 +240,14 @@ def trace_summary(directory):
                     continue
                 dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3  # us
                 key = (name.split("(")[0][-60:], row.get("Grid_Size_X", row.get("Grid_Size", "?")),
-                       row.get("Workgroup_Size_X", row.get("Workgroup_Size", "?")))
+                       row.get("Workgroup_Size_X", row.get("Workgroup_Size", "?")), row.get("Grid_Size_Y", "1"))
                 groups.setdefault(key, []).append(dur)
-    print(f"{'kernel':60s} {'grid_x':>10s} {'wg_x':>5s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s}")
+    print(f"{'kernel':60s} {'grid_x':>10s} {'wg_x':>5s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s}"
+          f" {'grid_y':>7s}")
     for key, durs in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         d = np.array(durs)
-        print(f"{key[0]:60s} {key[1]:>10s} {key[2]:>5s} {len(d):6d} {d.mean():9.2f} {np.median(d):9.2f} {d.min():9.2f}")
+        print(f"{key[0]:60s} {key[1]:>10s} {key[2]:>5s} {len(d):6d} {d.mean():9.2f} {np.median(d):9.2f} {d.min():9.2f}"
+              f" {key[3]:>7s}")
 
 
 def main():
@@ -323,15 +325,14 @@ def main():
     a8_step_us = step.time_graph(a8_step, args.steps, args.warmup) / args.steps * 1e6
     del a8_gate_up, a8_gemv, a8_step
 
-    # Prefill (M = 2048) on the gate+up shape: the fused W4A16 GEMM, the
-    # standalone fp16 dequantization, and for context the two-step route
-    # (that dequantization, then torch's fp16 library GEMM).
+    # Prefill (M = 2048) on the gate+up and down shapes: the fused W4A16
+    # GEMM, the standalone fp16 dequantization, and for context the two-step
+    # route (that dequantization, then torch's fp16 library GEMM). Matrix-core
+    # runs on this GPU vary by several percent with what ran just before
+    # (power and clock state), so the three are timed in turn, three rounds,
+    # and each reports its median.
     import int4_weight_only_w4a16_amd as wl
     Mp = 2048
-    wq_g, sc_g, zp_g = step.bufs[2][3:6]  # layer 0 gate_up weights
-    xp = synthetic.device_activations(Mp, Kd, args.seed, 9999, torch.device("cuda:0"))
-    yp = torch.empty((Mp, Nd), dtype=torch.int16, device="cuda:0")
-    w16 = torch.empty((Nd, Kd), dtype=torch.float16, device="cuda:0")
 
     def timed(fn, reps=10):
         for _ in range(2):
@@ -345,22 +346,33 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
 
-    gemm_us = timed(lambda: wl.w4a16_gemm(Mp, Nd, Kd, wq_g, sc_g, zp_g, xp, yp))
-    dq_us = timed(lambda: wl.w4a16_dequant_f16(Nd, Kd, wq_g, sc_g, zp_g, w16))
-    lib_us = timed(lambda: torch.matmul(xp.view(torch.float16), w16.t()))
-    flops = 2.0 * Mp * Nd * Kd
-    dq_bytes = algorithmic_bytes(0, Nd, Kd) + 2 * Nd * Kd
-    prefill = {
-        "shape": f"M={Mp} x gate_up {Nd}x{Kd}",
-        "w4a16_gemm_us": round(gemm_us, 1),
-        "w4a16_gemm_TFLOPs": round(flops / (gemm_us * 1e-6) / 1e12, 1),
-        "w4a16_gemm_frac_of_mfma_f16_peak": round(flops / (gemm_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-        "dequant_f16_us": round(dq_us, 1),
-        "dequant_f16_GBps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1),
-        "dequant_f16_frac_of_hbm_peak": round(dq_bytes / (dq_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-        "two_step_dequant_plus_torch_fp16_gemm_us": round(dq_us + lib_us, 1),
-    }
-    del xp, yp, w16
+    prefill = {}
+    for label, layer in (("gate_up", 2), ("down", 3)):
+        _, Np, Kp = synthetic.QWEN7B_LAYER[layer]
+        wq_g, sc_g, zp_g = step.bufs[layer][3:6]  # layer 0 weights of this shape
+        xp = synthetic.device_activations(Mp, Kp, args.seed, 9999, torch.device("cuda:0"))
+        yp = torch.empty((Mp, Np), dtype=torch.int16, device="cuda:0")
+        w16 = torch.empty((Np, Kp), dtype=torch.float16, device="cuda:0")
+        runs = {"gemm": [], "dq": [], "lib": []}
+        for _ in range(3):
+            runs["gemm"].append(timed(lambda: wl.w4a16_gemm(Mp, Np, Kp, wq_g, sc_g, zp_g, xp, yp)))
+            runs["dq"].append(timed(lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16)))
+            runs["lib"].append(timed(lambda: torch.matmul(xp.view(torch.float16), w16.t())))
+        gemm_us, dq_us, lib_us = (float(np.median(runs[k])) for k in ("gemm", "dq", "lib"))
+        flops = 2.0 * Mp * Np * Kp
+        dq_bytes = algorithmic_bytes(0, Np, Kp) + 2 * Np * Kp
+        prefill[label] = {
+            "shape": f"M={Mp} x {label} {Np}x{Kp}",
+            "w4a16_gemm_us": round(gemm_us, 1),
+            "w4a16_gemm_TFLOPs": round(flops / (gemm_us * 1e-6) / 1e12, 1),
+            "w4a16_gemm_frac_of_mfma_f16_peak": round(flops / (gemm_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "dequant_f16_us": round(dq_us, 1),
+            "dequant_f16_GBps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1),
+            "dequant_f16_frac_of_hbm_peak": round(dq_bytes / (dq_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "torch_fp16_gemm_us": round(lib_us, 1),
+            "two_step_dequant_plus_torch_fp16_gemm_us": round(dq_us + lib_us, 1),
+        }
+        del xp, yp, w16
 
     # Host quantizer (w4a16_quantize) on the qkv matrix's shape: fp16 in.
     wlib = wl

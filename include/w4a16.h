@@ -233,7 +233,8 @@ int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq, const voi
  * Deterministic (fixed order), but not bit-equal to w4a16_gemv, whose
  * weights are exact (q - z) scaled per group. The standalone dequant + MFMA
  * GEMM variant the AWQ dequantization page builds in two steps, here in
- * one. Errors: W4A16_EINVAL (shape, NULL, alignment), W4A16_EHIP.
+ * one. Errors: W4A16_EINVAL (shape, NULL, alignment), W4A16_EUNSUPPORTED
+ * (K >= 2^25), W4A16_EHIP.
  */
 int w4a16_gemm(int M, int N, int K, const void* Wq, const void* scales, const void* zeros, const void* x,
                void* y, void* stream);

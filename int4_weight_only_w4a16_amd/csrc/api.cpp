@@ -198,6 +198,7 @@ extern "C" int w4a16_gemm(int M, int N, int K, const void* Wq, const void* scale
                           const void* x, void* y, void* stream) {
   if (K < W4A16_GROUP || K % W4A16_GROUP != 0 || M < 0 || N < 0) return W4A16_EINVAL;
   if (M == 0 || N == 0) return W4A16_OK;
+  if (K >= w4a16::kGemmMaxK) return W4A16_EUNSUPPORTED;
   if (!pointers_ok({Wq, scales, zeros, x, y})) return W4A16_EINVAL;
   if (w4a16::launch_gemm(M, N, K, Wq, scales, zeros, x, y, stream) != 0) return W4A16_EHIP;
   return W4A16_OK;

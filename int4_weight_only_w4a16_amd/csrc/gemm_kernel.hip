@@ -1,19 +1,26 @@
 // W4A16 GEMM for many activation rows (prefill-sized M), on the matrix
 // cores: y[M][N] = x[M][K] W^T with W in layout ID 2, dequantized in
 // registers. A 256-thread workgroup computes a 128 (m) x 128 (n) tile of y
-// as four 64 x 64 wave tiles (2 x 2), each 4 x 4 blocks of
+// as four 128 x 32 wave tiles side by side in n, each 8 x 2 blocks of
 // v_mfma_f32_16x16x32_f16 with fp32 accumulators, over K one 128-column
-// group at a time. (Wave tiles of 128 x 64, which dequantize each weight
-// tile once instead of twice, need 424 registers, one wave per SIMD, and
-// measured 20-50% slower.)
-//  - x[m0 .. m0+127][group] is staged in LDS (double-buffered, rows padded
-//    by 16 bytes against bank conflicts) and read as the A operand;
-//  - each wave streams its four weight tiles (16 rows x 128 columns, 1 KiB
+// group at a time. Every weight tile is dequantized once per workgroup, and
+// each dequantized fragment feeds eight MFMAs: about two VALU instructions
+// per MFMA, where a VALU:MFMA ratio of 4 alone caps gfx950 at about 60% of
+// its MFMA rate (measured). Every wave reads all 128 rows of x from LDS,
+// about 160 bytes per clock per CU at full MFMA rate, within the 256 the
+// LDS delivers (also measured).
+//  - x[m0 .. m0+127][group] is staged in LDS by direct global-to-LDS loads
+//    (double-buffered, 16-byte slots XOR-swizzled by row against bank
+//    conflicts) and read as the A operand;
+//  - each wave streams its two weight tiles (16 rows x 128 columns, 1 KiB
 //    each; a lane's 16 bytes are exactly its B operand for the four 32-column
 //    blocks) and dequantizes them to fp16 (q - z) * s, rounded once to
 //    nearest even -- the values w4a16_dequant_f16 writes;
-//  - the next group's x and weight requests go out before the current group
-//    is multiplied.
+//  - the next group's requests go out before the current group is
+//    multiplied: x into the other LDS buffer, the weights into the other of
+//    two register buffers. (Weights two groups ahead, which needs x staged
+//    through registers, measured 10% slower: the multiply is not waiting
+//    on memory as much as on issue.)
 #include "w4a16_device.h"
 
 namespace w4a16 {
@@ -21,105 +28,112 @@ namespace dev {
 
 constexpr int kGemmBM = 128;                // activation rows per workgroup
 constexpr int kGemmBN = 128;                // weight rows per workgroup (8 row tiles)
-constexpr int kGemmMB = 4;                  // 16-row m blocks per wave (64 rows)
-constexpr int kXStride = kGroup + 8;        // halves per LDS row of x (272 bytes)
-constexpr size_t kGemmLds = size_t(2) * kGemmBM * kXStride * 2;
+constexpr int kGemmMB = 8;                  // 16-row m blocks per wave (all 128 rows)
+constexpr int kGemmNB = 2;                  // 16-row weight tiles per wave (the 4 waves side by side in n)
+constexpr int kXTile = kGemmBM * kGroup;    // halves of one staged x group (32 KiB)
+constexpr size_t kGemmLds = size_t(2) * kXTile * 2;
+constexpr int kOStride = kGemmBN + 8;       // halves per LDS row of the output tile (epilogue)
+static_assert(size_t(kGemmBM) * kOStride * 2 <= kGemmLds, "output tile must fit the x buffers");
+// s_waitcnt operand (gfx9 encoding): vmcnt <= the weight requests of one
+// step (3 per tile), expcnt and lgkmcnt not waited on.
+constexpr int kWeightRequests = 3 * kGemmNB;
+constexpr int kVmcntW = (kWeightRequests & 15) | ((kWeightRequests >> 4) << 14) | (7 << 4) | (15 << 8);
 
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ wq,
+__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict__ wq,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros,
                                                    const _Float16* __restrict__ x, _Float16* __restrict__ y,
                                                    int M, int N, int K) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  _Float16* xs = reinterpret_cast<_Float16*>(smem);  // [2][kGemmBM][kXStride]
+  _Float16* xs = reinterpret_cast<_Float16*>(smem);  // [2][kGemmBM][128], 16-byte slots swizzled
   const int G = K / kGroup;
   const int64_t NT = (int64_t(N) + kTileRows - 1) / kTileRows;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;  // this wave's 64 x 64 quarter
   const int rlane = lane & 15, piece = lane >> 4;
   // m fastest: the workgroups resident at once share weight tiles in L2
   // (making n fastest instead, to share x, measured no faster).
   const int64_t m0 = int64_t(blockIdx.x) * kGemmBM;
-  const int64_t tw = int64_t(blockIdx.y) * (kGemmBN / kTileRows) + wn * 4;  // wave's first row tile
+  const int64_t tw = int64_t(blockIdx.y) * (kGemmBN / kTileRows) + wave * kGemmNB;  // wave's first row tile
 
-  // The wave's four row tiles (clamped past the end: valid memory, never stored).
-  const u32x4* wl[4];
-  const uint32_t* swp[4];
-  const uint32_t* zwp[4];
+  // The wave's row tiles (clamped past the end: valid memory, never
+  // stored). Their bases are wave-uniform, and a lane's part of each
+  // request is one 32-bit offset for every tile and group, so requests take
+  // a scalar base and a single offset register.
+  const uint8_t* wbase[kGemmNB];
+  const uint32_t* sbase[kGemmNB];
+  const uint32_t* zbase[kGemmNB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kGemmNB; ++j) {
     const int64_t t = tw + j < NT ? tw + j : NT - 1;
     const int64_t q0 = t * G;
-    wl[j] = reinterpret_cast<const u32x4*>(wq + q0 * kTileBytes) + lane;
-    swp[j] = reinterpret_cast<const uint32_t*>(scales) + q0 * (kTileRows / 2) + (rlane >> 1);
-    zwp[j] = reinterpret_cast<const uint32_t*>(zeros) + q0 * (kTileRows / 8) + (rlane >> 3);
+    wbase[j] = wq + q0 * kTileBytes;
+    sbase[j] = reinterpret_cast<const uint32_t*>(scales) + q0 * (kTileRows / 2);
+    zbase[j] = reinterpret_cast<const uint32_t*>(zeros) + q0 * (kTileRows / 8);
   }
-  // x chunks of this thread: 8 x 16 bytes of the 128 x 128 group tile (rows
-  // past M read row M - 1: valid memory, never stored).
-  auto load_x = [&](int g, u32x4 (&xv)[8]) {
+  const uint32_t w_off = uint32_t(lane) * 16, s_off = uint32_t(rlane >> 1), z_off = uint32_t(rlane >> 3);
+  // x[m0 .. m0+127][group g] -> LDS buffer buf, straight from global memory
+  // (global_load_lds_dwordx4: lane l of a wave's request writes 16 bytes at
+  // the request's LDS base + 16 l, so a request fills 1 KiB). Row r of the
+  // tile keeps its 16 sixteen-byte chunks c in slots c ^ (r % 16): the A
+  // operand reads of 16 consecutive rows then hit 16 distinct bank groups.
+  // Rows past M read row M - 1 (valid memory, never stored). x_off[i] is
+  // the element offset of request i's chunk from x[m0][0], below 128 K,
+  // which the host keeps under 2^32.
+  uint32_t x_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int req = wave * 8 + i;  // this wave's request i: slots 64 req .. 64 req + 63
+    const int p = req * 64 + lane, row = p >> 4, c = (p & 15) ^ (row & 15);
+    const int64_t mr = m0 + row < M ? row : M - 1 - m0;
+    x_off[i] = uint32_t(mr * K + c * 8);
+  }
+  auto load_x = [&](int g, int buf) {
+    const _Float16* xg = x + m0 * K + int64_t(g) * kGroup;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, row = c >> 4, col = c & 15;
-      const int64_t mr = m0 + row < M ? m0 + row : M - 1;
-      xv[i] = *reinterpret_cast<const u32x4*>(x + mr * K + int64_t(g) * kGroup + col * 8);
-    }
-  };
-  auto store_x = [&](int buf, const u32x4 (&xv)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, row = c >> 4, col = c & 15;
-      *reinterpret_cast<u32x4*>(xs + (buf * kGemmBM + row) * kXStride + col * 8) = xv[i];
+      const int req = wave * 8 + i;
+      __builtin_amdgcn_global_load_lds(xg + x_off[i], xs + buf * kXTile + req * 512, 16, 0, 0);
     }
   };
   struct W {
-    u32x4 w[4];
-    uint32_t s[4], z[4];
+    u32x4 w[kGemmNB];
+    uint32_t s[kGemmNB], z[kGemmNB];
   };
   auto load_w = [&](int g, W& r) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      r.w[j] = __builtin_nontemporal_load(wl[j] + int64_t(g) * (kTileBytes / 16));
-      r.s[j] = swp[j][g * (kTileRows / 2)];
-      r.z[j] = zwp[j][g * (kTileRows / 8)];
+    for (int j = 0; j < kGemmNB; ++j) {
+      r.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wbase[j] + int64_t(g) * kTileBytes + w_off));
+      r.s[j] = sbase[j][g * (kTileRows / 2) + s_off];
+      r.z[j] = zbase[j][g * (kTileRows / 8) + z_off];
     }
   };
 
-  f32x4 acc[kGemmMB][4];
+  f32x4 acc[kGemmMB][kGemmNB];
 #pragma unroll
   for (int a = 0; a < kGemmMB; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < kGemmNB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 xv[8];
-  W cur, nxt;
-  load_x(0, xv);
-  load_w(0, cur);
-  store_x(0, xv);
-  __syncthreads();
   const uint32_t magic = kMagic1024;
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    const bool more = g + 1 < G;
-    if (more) {
-      load_x(g + 1, xv);
-      load_w(g + 1, nxt);
-    }
+  // Multiply group g: x from LDS buffer buf, the wave's weight tiles from
+  // `cur`.
+  auto compute = [&](int buf, const W& cur) {
     // Per tile: the fp16 scale pair and the zero-point pairs of row rlane.
-    half2_t s2[4];
-    ZeroPairs zp[4];
+    half2_t s2[kGemmNB];
+    ZeroPairs zp[kGemmNB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kGemmNB; ++j) {
       const uint16_t sb = uint16_t((cur.s[j] >> ((rlane & 1) * 16)) & 0xFFFFu);
       s2[j] = as_h2(uint32_t(sb) * 0x00010001u);
       zp[j] = zero_pairs((cur.z[j] >> ((rlane & 7) * 4)) & 15u);
     }
-    const _Float16* xa = xs + (buf * kGemmBM + wm * 64 + rlane) * kXStride + piece * 8;
+    const _Float16* xa = xs + buf * kXTile + rlane * kGroup;  // row rlane of each 16-row block
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      half8_t bw[4];
+      half8_t bw[kGemmNB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kGemmNB; ++j) {
         half2_t p[4];
         unpack8(cur.w[j][kb], magic, zp[j], p);
 #pragma unroll
@@ -128,32 +142,82 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w
       }
       half8_t af[kGemmMB];
 #pragma unroll
-      for (int mb = 0; mb < kGemmMB; ++mb) af[mb] = *reinterpret_cast<const half8_t*>(xa + mb * 16 * kXStride + kb * 32);
+      for (int mb = 0; mb < kGemmMB; ++mb)
+        af[mb] = *reinterpret_cast<const half8_t*>(xa + mb * 16 * kGroup + ((kb * 4 + piece) ^ rlane) * 8);
 #pragma unroll
       for (int mb = 0; mb < kGemmMB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bw[nb], acc[mb][nb], 0, 0, 0);
+        for (int nb = 0; nb < kGemmNB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bw[nb], acc[mb][nb], 0, 0, 0);
     }
-    if (more) {
-      store_x(buf ^ 1, xv);  // buffer buf ^ 1 was last read before the previous barrier
-      cur = nxt;
-    }
-    __syncthreads();
-  }
+  };
 
+  // One step per group: request the next group's x (into the other LDS
+  // buffer, last read before the previous barrier) and weights (the last
+  // step re-requests the last group: in bounds, unused), multiply this
+  // group, wait for the x requests only, and meet at an LDS-only barrier.
+  // The requests are unconditional and the two weight buffers alternate
+  // statically (the loop is unrolled by two), so the only wait before the
+  // multiply is for the weights requested one step earlier; a branch around
+  // the requests or a register copy between the buffers let the compiler
+  // wait for all of them, and __syncthreads() would wait for every
+  // outstanding load too.
+  W wa, wb;
+  auto step = [&](int g, const W& cur, W& nxt) {
+    const int gn = g + 1 < G ? g + 1 : G - 1;
+    load_x(gn, (g & 1) ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(gn, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(g & 1, cur);
+    // The x requests were issued before the weight requests (one dwordx4
+    // and two dwords per tile): at most that many outstanding leaves x
+    // complete. (The compiler makes this a full wait, as it does not count
+    // the LDS-bound requests apart; the weights are due next step anyway.)
+    __builtin_amdgcn_s_waitcnt(kVmcntW);
+    lds_barrier();
+  };
+  load_x(0, 0);
+  load_w(0, wa);
+  __builtin_amdgcn_s_waitcnt(kVmcntW);
+  lds_barrier();
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    step(g, wa, wb);
+    step(g + 1, wb, wa);
+  }
+  if (g < G) step(g, wa, wb);
+
+  // Epilogue through LDS (free after the last barrier): the tile's fp16
+  // values go to a [128][136] array (rows padded so the four 16-lane
+  // pieces of a write hit distinct banks), then every thread stores whole
+  // 16-byte runs along n. Stored straight from the MFMA layout, each
+  // instruction would write 32-byte pieces of four rows: a quarter of each
+  // cache line, which cost up to 15% of the kernel when y is not already
+  // in cache.
+  _Float16* ot = xs;
   // D layout: lane l holds D[4 * (l / 16) + r][l % 16] of each 16 x 16 block.
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int64_t t = tw + nb;
-    const int64_t n = t * kTileRows + rlane;
-    if (t >= NT || n >= N) continue;
+  for (int mb = 0; mb < kGemmMB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < kGemmMB; ++mb)
+    for (int nb = 0; nb < kGemmNB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * 64 + mb * 16 + piece * 4 + r;
-        if (m < M) y[m * N + n] = (_Float16)acc[mb][nb][r];
-      }
+      for (int r = 0; r < 4; ++r)
+        ot[(mb * 16 + piece * 4 + r) * kOStride + wave * (kGemmNB * 16) + nb * 16 + rlane] = (_Float16)acc[mb][nb][r];
+  lds_barrier();
+  const int64_t n_wg = int64_t(blockIdx.y) * kGemmBN;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;
+    const int64_t m = m0 + row, n0 = n_wg + col;
+    if (m >= M || n0 >= N) continue;
+    const _Float16* src = ot + row * kOStride + col;
+    _Float16* dst = y + m * N + n0;
+    if ((N & 7) == 0 && n0 + 8 <= N) {
+      *reinterpret_cast<half8_t*>(dst) = *reinterpret_cast<const half8_t*>(src);
+    } else {
+      for (int e = 0; e < 8 && n0 + e < N; ++e) dst[e] = src[e];
+    }
   }
 }
 

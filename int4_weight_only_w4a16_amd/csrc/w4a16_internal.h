@@ -133,6 +133,9 @@ constexpr bool a8_instantiated(int mr, int waves, int share) {
 int launch_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream);
 int launch_gemv_a8(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
                    const void* zeros, const void* xq, const void* sx, const void* xsum, void* y, void* stream);
+// The GEMM addresses a workgroup's 128 rows of x with 32-bit element
+// offsets (below 128 K), so K stays under 2^25.
+constexpr int kGemmMaxK = 1 << 25;
 int launch_gemm(int M, int N, int K, const void* wq, const void* scales, const void* zeros, const void* x, void* y,
                 void* stream);
 int launch_dequant_f16(int N, int K, const void* wq, const void* scales, const void* zeros, void* out,

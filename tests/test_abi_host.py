@@ -193,6 +193,7 @@ def test_device_entry_points_reject_before_launch():
     assert L.w4a16_gemm(64, 16, 200, *ptrs, None) == w.W4A16_EINVAL
     assert L.w4a16_gemm(-1, 16, 128, *ptrs, None) == w.W4A16_EINVAL
     assert L.w4a16_gemm(0, 16, 128, *ptrs, None) == w.W4A16_OK
+    assert L.w4a16_gemm(64, 16, 1 << 25, *ptrs, None) == w.W4A16_EUNSUPPORTED
     assert L.w4a16_gemm(64, 16, 128, fake, fake, fake, fake + 2, fake, None) == w.W4A16_EINVAL
     # dequant to fp16
     assert L.w4a16_dequant_f16(16, 200, fake, fake, fake, fake, None) == w.W4A16_EINVAL

@@ -43,7 +43,7 @@ def check_rounded_weights(p, y, rows=None):
 
 
 @pytest.mark.parametrize("M,N,K", [(9, 37, 384), (16, 896, 896), (130, 200, 640), (128, 128, 128),
-                                   (300, 1000, 1152), (257, 4608, 3584)])
+                                   (300, 1000, 1152), (257, 4608, 3584), (64, 301, 256), (200, 1031, 128)])
 def test_gemm_against_oracle(M, N, K):
     _say("shape", M, N, K)
     p = Problem(M, N, K, seed=M + N)
