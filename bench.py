@@ -243,11 +243,107 @@ def trace_summary(directory):
                        row.get("Workgroup_Size_X", row.get("Workgroup_Size", "?")), row.get("Grid_Size_Y", "1"))
                 groups.setdefault(key, []).append(dur)
     print(f"{'kernel':60s} {'grid_x':>10s} {'wg_x':>5s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s}"
-          f" {'grid_y':>7s}")
+          f" {'grid_y':>7s} {'p90_us':>9s} {'p99_us':>9s}")
     for key, durs in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         d = np.array(durs)
         print(f"{key[0]:60s} {key[1]:>10s} {key[2]:>5s} {len(d):6d} {d.mean():9.2f} {np.median(d):9.2f} {d.min():9.2f}"
-              f" {key[3]:>7s}")
+              f" {key[3]:>7s} {np.percentile(d, 90):9.2f} {np.percentile(d, 99):9.2f}")
+
+
+def run_configs(torch, seed):
+    """Every workload configuration, warm and cold, µs and GB/s per set.
+
+    A set is the configuration's GEMVs launched back to back on one stream,
+    with the library's split choice. Warm: one copy of the weights, the set
+    repeated in one captured graph of at least 64 launches (inputs stay in
+    the 256 MB last-level cache where they fit). Cold: distinct weight copies
+    totalling at least 1 GiB, each set once per graph replay, so every
+    replay streams from HBM.
+    Configuration 4 (the whole 7B step) is the default bench line."""
+    import int4_weight_only_w4a16_amd as w
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    GiB = 1 << 30
+
+    def build(shapes, M, copies, tid0):
+        sets = []
+        for c in range(copies):
+            one = []
+            for i, (name, N, K) in enumerate(shapes):
+                wq, sc, zp = synthetic.device_packed_weights(N, K, seed, tid0 + 1000 * c + i, dev)
+                x = synthetic.device_activations(M, K, seed, tid0 + i, dev)
+                y = torch.empty((M, N), dtype=torch.int16, device=dev)
+                one.append((N, K, wq, sc, zp, x, y, w.w4a16_splitk_choose(M, N, K)))
+            sets.append(one)
+        ws_bytes = max(w.w4a16_splitk_workspace_bytes(M, N, 2) for _, N, K in shapes)
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+        return sets, ws
+
+    def launch(sets, ws, M, reps):
+        for _ in range(reps):
+            for one in sets:
+                for N, K, wq, sc, zp, x, y, splits in one:
+                    if splits > 1:
+                        w.w4a16_gemv_splitk(M, N, K, splits, wq, sc, zp, x, y, ws, stream=stream)
+                    else:
+                        w.w4a16_gemv(M, N, K, wq, sc, zp, x, y, stream=stream)
+
+    def timed_graph(sets, ws, M, reps_in_graph, replays):
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            launch(sets, ws, M, 1)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                launch(sets, ws, M, reps_in_graph)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(replays):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (replays * reps_in_graph * len(sets))  # µs per set
+
+    configs = [
+        ("1: single GEMV 896x896", [("single", 896, 896)], (1,)),
+        ("2: Qwen2.5-0.5B decode linear set, 24 layers x 7", [
+            (f"L{l}.{n}", N, K) for l in range(synthetic.QWEN05B_LAYERS) for n, N, K in synthetic.QWEN05B_LAYER], (1,)),
+        ("2 (variant): the same with q/k/v and gate/up each packed as one matrix, 24 layers x 4", [
+            (f"L{l}.{n}", N, K) for l in range(synthetic.QWEN05B_LAYERS)
+            for n, N, K in (("qkv_proj", 896 + 2 * 128, 896), ("o_proj", 896, 896), ("gate_up_proj", 2 * 4864, 896),
+                            ("down_proj", 896, 4864))], (1,)),
+        ("3: Qwen2.5-7B layer (qkv, o, gate_up, down)", list(synthetic.QWEN7B_LAYER), (1,)),
+        ("5: 27B-class verify pair (up 17408x5120, down 5120x17408)", list(synthetic.VERIFY27B), synthetic.VERIFY_M),
+    ]
+    rows = []
+    for ci, (label, shapes, Ms) in enumerate(configs):
+        for M in Ms:
+            nbytes = sum(algorithmic_bytes(M, N, K) for _, N, K in shapes)
+            launches = len(shapes)
+            out = {"config": label, "M": M, "launches_per_set": launches, "bytes_per_set": nbytes}
+            sets, ws = build(shapes, M, 1, 100 * ci)
+            reps = -(-64 // launches)  # at least 64 launches per replay (a replay has a fixed cost)
+            us = timed_graph(sets, ws, M, reps, 5)
+            out["warm_us"] = round(us, 2)
+            out["warm_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+            del sets, ws
+            copies = -(-GiB // nbytes)
+            sets, ws = build(shapes, M, copies, 100 * ci)
+            us = timed_graph(sets, ws, M, 1, 5)
+            out["cold_copies"] = copies
+            out["cold_us"] = round(us, 2)
+            out["cold_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+            out["cold_frac_of_hbm_peak"] = round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+            del sets, ws
+            torch.cuda.empty_cache()
+            rows.append(out)
+            print(json.dumps(out), flush=True)
+    return rows
 
 
 def main():
@@ -261,6 +357,8 @@ def main():
     ap.add_argument("--trace-summary", metavar="DIR")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device copy kernel (counter scaling)")
+    ap.add_argument("--configs", action="store_true",
+                    help="time every workload configuration warm and cold (one JSON line each) instead")
     args = ap.parse_args()
 
     if args.trace_summary:
@@ -280,6 +378,10 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+        return
+
+    if args.configs:
+        run_configs(torch, args.seed)
         return
 
     t_setup = time.perf_counter()
