@@ -78,6 +78,11 @@ w4a16::LaunchPlan plan_for(int M, int N, int K, int splits) {
 //    not (3584 x 18944: 8.7 us unsplit, 9.4 us at 9 splits in a decode step);
 //  - fewer than 128 row tiles with K of 24 groups or more: about one split
 //    per 12 groups (128 x 18944: 7.3 -> 3.7 us);
+//  - 1024 to 2047 row tiles with K of 40 groups or more: 2 splits. Each
+//    workgroup then stages x of half the K range in LDS, and more of them
+//    stay resident when x has several rows (17408 x 5120: M = 5 16.2 ->
+//    13.5 us, M = 8 22.8 -> 15.3 us, at a cost of 10.6 -> 11.3 us at M = 1
+//    and 11.3 -> 12.1 us at M = 2);
 //  - elsewhere it lost (qkv 4608 x 3584: 4.65 us unsplit, 5.25 us at 2).
 int choose_splits(int N, int K) {
   const int groups = K / W4A16_GROUP;
@@ -87,6 +92,8 @@ int choose_splits(int N, int K) {
     splits = groups / 16;
   else if (row_tiles < 128 && groups >= 24)
     splits = groups / 12 < 2 ? 2 : groups / 12;
+  else if (groups >= 40 && row_tiles >= 1024 && row_tiles < 2048)
+    splits = 2;
   return splits > 16 ? 16 : splits;
 }
 

@@ -173,6 +173,8 @@ def test_device_entry_points_reject_before_launch():
     assert w.w4a16_splitk_choose(1, 37888, 3584) == 1 and w.w4a16_splitk_choose(1, 3584, 7936) == 1
     assert w.w4a16_splitk_choose(1, 3584, 18944) == 1 and w.w4a16_splitk_choose(8, 5120, 17408) == 8
     assert w.w4a16_splitk_choose(1, 896, 4864) == 3 and w.w4a16_splitk_choose(5, 4608, 3584) == 1
+    assert w.w4a16_splitk_choose(5, 17408, 5120) == 2 and w.w4a16_splitk_choose(1, 152064, 5120) == 1
+    assert w.w4a16_splitk_choose(1, 37888, 3584) == 1 and w.w4a16_splitk_choose(8, 16384, 5120) == 2
     assert len({w.w4a16_splitk_choose(m, 5120, 17408) for m in range(1, 9)}) == 1  # never depends on M
     assert w.w4a16_splitk_choose(1, 128, 65536) == 16 and w.w4a16_splitk_choose(1, 8192, 131072) == 16
     assert w.w4a16_splitk_choose(1, 16, 200) == 0 and w.w4a16_splitk_choose(9, 16, 128) == 0
