@@ -180,8 +180,9 @@ size_t w4a16_splitk_workspace_bytes(int M, int N, int splits);
  * measured on MI355X: about one split per 16 groups of 128 when K has at
  * least 96 groups and the matrix 257 to 1023 tiles of 16 rows; about one
  * per 12 groups when it has fewer than 128 tiles and K at least 24 groups;
- * otherwise 1 (do not split). At most 16. It does not depend on M, so rows stay batch invariant
- * for a caller who follows it. Returns 0 for an invalid shape.
+ * 2 when it has 1024 to 2047 tiles and K at least 40 groups; otherwise 1
+ * (do not split). At most 16. It does not depend on M, so rows stay batch
+ * invariant for a caller who follows it. Returns 0 for an invalid shape.
  */
 int w4a16_splitk_choose(int M, int N, int K);
 

@@ -28,11 +28,12 @@ namespace dev {
 // waves [0, WAVES/2) split the K range of the gate tile, the other half the
 // same K range of the up tile (R = 1), and the sums meet in LDS, where
 // y[m][16j + i] = fp16(silu(g) * u), silu(g) = g / (1 + e^-g) in fp32. N is
-// the output width (the matrix has 2 * ceil(N/16) row tiles). Wave w of the
-// gate half stages the x slice that wave w of the up half also reads (one
-// LDS barrier after staging), and every share fits one round: the host
-// launches nothing else, and a workgroup exits at once (all of it) if the
-// shape would need more.
+// the output width (the matrix has 2 * ceil(N/16) row tiles). Every wave
+// stages its own x slice when all slices fit in 64 KiB; otherwise wave w of
+// the gate half stages the slice that wave w of the up half also reads (one
+// LDS barrier after staging). Every share fits one round: the host launches
+// nothing else, and a workgroup exits at once (all of it) if the shape
+// would need more.
 // Writes fp16 y[MR][N] directly when `acc` is null. Otherwise (split-K,
 // gridDim.y splits) each workgroup adds its fp32 partial sums, in the
 // fixed-point word format of splitk_addend(), to acc[MR][N] (one uint64 per
@@ -65,6 +66,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   constexpr bool kPair = EPI == kEpiSwiglu;
   static_assert(!kPair || (R == 1 && WAVES % 2 == 0), "SwiGLU: one gate/up pair, half the waves on each");
   constexpr int kHalf = kPair ? WAVES / 2 : WAVES;  // waves sharing one row tile's K range
+  // SwiGLU halves read one shared x slice per wave pair (staged by the gate
+  // wave, behind an LDS barrier) only when private slices would not fit.
+  constexpr bool kSharedX = kPair && !swiglu_private_x(MR, WAVES, SHARE);
   const int64_t row_tiles = (kPair ? 2 : 1) * ((int64_t(N) + kTileRows - 1) / kTileRows);
   const int split = blockIdx.y, splits = gridDim.y;
   const int g_beg = int(int64_t(split) * G / splits);
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   const int share_end = g_beg + ((wave_in + 1) * ng) / kHalf;
   const int mm = rlane < MR ? rlane : MR - 1;  // activation row feeding A-operand row rlane
   _Float16* xw = reinterpret_cast<_Float16*>(smem + 2 * kRed * sizeof(float)) +
-                 (kGlobalX ? 0 : (kPair ? wave_in : wave) * MR * kXRow);  // x slice [MR][SHARE*128]
+                 (kGlobalX ? 0 : (kSharedX ? wave_in : wave) * MR * kXRow);  // x slice [MR][SHARE*128]
   int parity = 0;
 
   // Copy x[:, 128*g0 : 128*(g0+n)) into this wave's LDS slice (synchronous).
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
         // serves all of this workgroup's row tiles.
         constexpr int kXSteps = (MR * SHARE * 16 + 63) / 64;
         const int xchunks = share_n * (kGroup / 8), xtotal = MR * xchunks;
-        const bool stages_x = !kPair || half == 0;  // wave-uniform
+        const bool stages_x = !kSharedX || half == 0;  // wave-uniform
         u32x4 xv[kXSteps];
         if (stages_x) {
 #pragma unroll
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
             *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) = xv[j];
           }
         }
-        if constexpr (kPair) {
+        if constexpr (kSharedX) {
           lds_barrier();  // the up half reads what the gate half staged; weights stay in flight
         } else {
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");

@@ -78,13 +78,22 @@ constexpr size_t reduction_lds_bytes(int mr, int waves, int engine) {
   return 2 * size_t(waves) * 4 * (engine == kEngineDot2 ? mr : (mr < 4 ? mr : 4)) * 16 * sizeof(float);
 }
 
+// SwiGLU: every wave stages its own x slice when all the slices fit in
+// 64 KiB; otherwise wave w of the gate half stages the slice that wave w of
+// the up half also reads, behind one LDS barrier.
+constexpr bool swiglu_private_x(int mr, int waves, int share) {
+  return size_t(waves) * mr * share * kGroup * 2 <= 64 * 1024;
+}
+
 // Dynamic LDS of a GEMV workgroup: the reduction buffers, then one x slice
-// [M][share * 128] fp16 per wave (per pair of waves for SwiGLU, whose gate
-// and up halves share the slices; none when x is read from global memory).
+// [M][share * 128] fp16 per wave (per pair of waves for SwiGLU when the
+// halves share slices; none when x is read from global memory).
 constexpr size_t gemv_lds_bytes(int mr, int waves, int share, int engine, int epi) {
   return reduction_lds_bytes(mr, waves, engine) +
-         (engine == kEngineMfmaGlobalX ? 0
-                                       : size_t(epi == kEpiSwiglu ? waves / 2 : waves) * mr * share * kGroup * 2);
+         (engine == kEngineMfmaGlobalX
+              ? 0
+              : size_t(epi == kEpiSwiglu && !swiglu_private_x(mr, waves, share) ? waves / 2 : waves) * mr * share *
+                    kGroup * 2);
 }
 
 // Largest dynamic LDS a GEMV workgroup may use: gfx950's 160 KiB per
