@@ -105,7 +105,8 @@ int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, const uint8_t*
  * packed as by w4a16_pack. That interleave is what lets SwiGLU run in
  * registers (the 4-bit matrix-vector kernel of the qengine page, "How it
  * works"). Output buffers: w4a16_packed_sizes(2 * roundup(F, 16), K) bytes.
- * Errors: as w4a16_pack. Host only.
+ * Errors: as w4a16_pack, and W4A16_EINVAL when 2 * roundup(F, 16) exceeds
+ * INT32_MAX. Host only; allocates nothing.
  */
 int w4a16_pack_gate_up(int F, int K, const uint8_t* qg, const uint16_t* sg, const uint8_t* zg,
                        const uint8_t* qu, const uint16_t* su, const uint8_t* zu, void* wq_out, void* s_out,
@@ -126,7 +127,8 @@ int w4a16_pack_gate_up(int F, int K, const uint8_t* qg, const uint16_t* sg, cons
  *     z = clamp(round(-lo / s), 0, 15), q = clamp(round(w / s) + z, 0, 15).
  *   A group whose scale rounds to 0 gets q = z (it dequantizes to 0).
  * Errors: W4A16_EINVAL for a bad shape or mode, a NULL pointer (when N > 0)
- * or a non-finite weight. Runs on host threads (no GPU needed).
+ * or a non-finite weight. Runs on host threads (no GPU needed); where a
+ * thread cannot be started, its rows run on the calling thread.
  */
 int w4a16_quantize(int N, int K, const uint16_t* w, int mode, uint8_t* q, uint16_t* s, uint8_t* z);
 

@@ -17,8 +17,8 @@
 // The 16 scales and 16 zero points of a tile sit next to each other in tile
 // order (32 and 8 bytes), so the scale and zero requests of a wave touch one
 // cache line each instead of one line per row.
+#include <cstdint>
 #include <cstring>
-#include <vector>
 
 #include "w4a16.h"
 #include "w4a16_internal.h"
@@ -54,32 +54,45 @@ extern "C" int w4a16_packed_sizes(int N, int K, size_t* wq_bytes, size_t* s_byte
   return W4A16_OK;
 }
 
-extern "C" int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, const uint8_t* z,
-                          void* wq_out, void* s_out, void* z_out) {
-  if (!shape_ok(N, K)) return W4A16_EINVAL;
-  if (N == 0) return W4A16_OK;
-  if (!q || !s || !z || !wq_out || !s_out || !z_out) return W4A16_EINVAL;
-  const w4a16::Geometry geo(N, K);
+namespace {
+
+// Logical data of one row of the matrix being packed; all null for a row
+// that is zero (padding of the gate/up interleave).
+struct RowData {
+  const uint8_t* q;   // [K]
+  const uint16_t* s;  // [K/128]
+  const uint8_t* z;   // [K/128]
+};
+
+// Packs `rows` rows (rows past the last one up to the 16-row boundary are
+// padding) whose data row_src(r) returns. Returns W4A16_EINVAL if a q or z
+// value exceeds 15 (the outputs are then unspecified). Allocates nothing.
+template <typename RowSrc>
+int pack_rows(int64_t rows, int K, RowSrc row_src, void* wq_out, void* s_out, void* z_out) {
+  const w4a16::Geometry geo(rows, K);
   uint8_t* wq = static_cast<uint8_t*>(wq_out);
   uint8_t* sp = static_cast<uint8_t*>(s_out);
   uint8_t* zp = static_cast<uint8_t*>(z_out);
 
   unsigned bad = 0;  // any bit above the low nibble of a q or z value
   for (int64_t t = 0; t < geo.row_tiles; ++t) {
-    for (int64_t g = 0; g < geo.groups; ++g) {
-      uint8_t* tile = wq + (t * geo.groups + g) * w4a16::kTileBytes;
-      for (int lane = 0; lane < 64; ++lane) {
-        const int64_t row = 16 * t + (lane & 15);
-        for (int kb = 0; kb < 4; ++kb) {
-          uint32_t word = 0;
-          if (row < N) {
-            const uint8_t* src = q + row * int64_t(K) + g * W4A16_GROUP + 32 * kb + 8 * (lane >> 4);
-            for (int j = 0; j < 8; ++j) {
-              bad |= src[j];
-              word |= uint32_t(src[j] & 15u) << kShift[j];
+    for (int lane16 = 0; lane16 < 16; ++lane16) {
+      const int64_t row = 16 * t + lane16;
+      const RowData d = row < rows ? row_src(row) : RowData{nullptr, nullptr, nullptr};
+      for (int64_t g = 0; g < geo.groups; ++g) {
+        uint8_t* tile = wq + (t * geo.groups + g) * w4a16::kTileBytes;
+        for (int lane = lane16; lane < 64; lane += 16) {
+          for (int kb = 0; kb < 4; ++kb) {
+            uint32_t word = 0;
+            if (d.q) {
+              const uint8_t* src = d.q + g * W4A16_GROUP + 32 * kb + 8 * (lane >> 4);
+              for (int j = 0; j < 8; ++j) {
+                bad |= src[j];
+                word |= uint32_t(src[j] & 15u) << kShift[j];
+              }
             }
+            store_le32(tile + lane * 16 + kb * 4, word);
           }
-          store_le32(tile + lane * 16 + kb * 4, word);
         }
       }
     }
@@ -88,18 +101,32 @@ extern "C" int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, con
 
   std::memset(sp, 0, geo.s_bytes());
   std::memset(zp, 0, geo.z_bytes());
-  for (int64_t n = 0; n < N; ++n) {
+  for (int64_t n = 0; n < rows; ++n) {
+    const RowData d = row_src(n);
+    if (!d.q) continue;
     for (int64_t g = 0; g < geo.groups; ++g) {
       const int64_t e = geo.meta_index(n, g);
-      const uint16_t sv = s[n * geo.groups + g];
+      const uint16_t sv = d.s[g];
       sp[2 * e] = uint8_t(sv);
       sp[2 * e + 1] = uint8_t(sv >> 8);
-      const uint8_t zv = z[n * geo.groups + g];
+      const uint8_t zv = d.z[g];
       bad |= zv & ~15u;
       zp[e >> 1] |= uint8_t((zv & 15u) << ((n & 1) * 4));
     }
   }
   return bad ? W4A16_EINVAL : W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, const uint8_t* z,
+                          void* wq_out, void* s_out, void* z_out) {
+  if (!shape_ok(N, K)) return W4A16_EINVAL;
+  if (N == 0) return W4A16_OK;
+  if (!q || !s || !z || !wq_out || !s_out || !z_out) return W4A16_EINVAL;
+  const int64_t G = K / W4A16_GROUP;
+  return pack_rows(
+      N, K, [&](int64_t r) { return RowData{q + r * int64_t(K), s + r * G, z + r * G}; }, wq_out, s_out, z_out);
 }
 
 extern "C" int w4a16_pack_gate_up(int F, int K, const uint8_t* qg, const uint16_t* sg, const uint8_t* zg,
@@ -108,21 +135,21 @@ extern "C" int w4a16_pack_gate_up(int F, int K, const uint8_t* qg, const uint16_
   if (!shape_ok(F, K)) return W4A16_EINVAL;
   if (F == 0) return W4A16_OK;
   if (!qg || !sg || !zg || !qu || !su || !zu || !wq_out || !s_out || !z_out) return W4A16_EINVAL;
-  // Interleave 16-row blocks (gate block j, then up block j; rows past F in
-  // a block are zero) and pack the 2 * roundup(F, 16)-row result.
-  const int64_t G = K / W4A16_GROUP, blocks = (int64_t(F) + 15) / 16, rows = 32 * blocks;
-  std::vector<uint8_t> q(size_t(rows) * K, 0), z(size_t(rows) * G, 0);
-  std::vector<uint16_t> s(size_t(rows) * G, 0);
-  for (int64_t f = 0; f < F; ++f) {
-    const int64_t rg = 32 * (f / 16) + f % 16, ru = rg + 16;
-    std::memcpy(&q[rg * K], qg + f * K, size_t(K));
-    std::memcpy(&q[ru * K], qu + f * K, size_t(K));
-    std::memcpy(&s[rg * G], sg + f * G, size_t(G) * 2);
-    std::memcpy(&s[ru * G], su + f * G, size_t(G) * 2);
-    std::memcpy(&z[rg * G], zg + f * G, size_t(G));
-    std::memcpy(&z[ru * G], zu + f * G, size_t(G));
-  }
-  return w4a16_pack(int(rows), K, q.data(), s.data(), z.data(), wq_out, s_out, z_out);
+  // 16-row blocks interleaved: packed rows 32j .. 32j+15 are gate rows
+  // 16j .. 16j+15, the next 16 the up rows of the same outputs; rows past
+  // F within a block are zero. The result has 2 * roundup(F, 16) rows,
+  // which w4a16_packed_sizes must be able to describe.
+  const int64_t G = K / W4A16_GROUP, rows = 32 * ((int64_t(F) + 15) / 16);
+  if (rows > INT32_MAX) return W4A16_EINVAL;
+  return pack_rows(
+      rows, K,
+      [&](int64_t r) {
+        const int64_t f = 16 * (r / 32) + r % 16;
+        if (f >= F) return RowData{nullptr, nullptr, nullptr};
+        return (r % 32) < 16 ? RowData{qg + f * K, sg + f * G, zg + f * G}
+                             : RowData{qu + f * K, su + f * G, zu + f * G};
+      },
+      wq_out, s_out, z_out);
 }
 
 extern "C" int w4a16_unpack(int N, int K, const void* wq_in, const void* s_packed, const void* z_packed,
@@ -162,7 +189,7 @@ extern "C" const char* w4a16_strerror(int status) {
   switch (status) {
     case W4A16_OK: return "ok";
     case W4A16_EINVAL: return "invalid argument (shape, pointer, alignment or value)";
-    case W4A16_EUNSUPPORTED: return "unsupported: more than 8 activation rows, or a fused shape beyond its limits";
+    case W4A16_EUNSUPPORTED: return "unsupported: more than 8 activation rows, or a shape beyond an entry point's stated limits";
     case W4A16_ELAYOUT: return "packed layout ID mismatch";
     case W4A16_EHIP: return "HIP runtime refused the launch";
     default: return "unknown status";

@@ -78,15 +78,40 @@ extern "C" int w4a16_quantize(int N, int K, const uint16_t* w, int mode, uint8_t
   if (N == 0) return W4A16_OK;
   if (!w || !q || !s || !z) return W4A16_EINVAL;
   const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
-  const int64_t threads = std::min<int64_t>(hw, std::max<int64_t>(1, int64_t(N) * K / (1 << 20)));
-  std::vector<char> ok(size_t(threads), 1);
+  const int64_t chunks = std::min<int64_t>(hw, std::max<int64_t>(1, int64_t(N) * K / (1 << 20)));
+  auto rows_of = [&](int64_t c, int64_t& r0, int64_t& r1) {
+    r0 = int64_t(N) * c / chunks;
+    r1 = int64_t(N) * (c + 1) / chunks;
+  };
+  // Chunks go to host threads. A chunk no thread could be started for (or
+  // every chunk, if the bookkeeping cannot be allocated) runs on the calling
+  // thread, whose rounding mode is restored afterwards; every started
+  // thread is joined. No exception leaves this C entry point.
   std::vector<std::thread> pool;
-  for (int64_t t = 0; t < threads; ++t) {
-    const int64_t r0 = int64_t(N) * t / threads, r1 = int64_t(N) * (t + 1) / threads;
-    pool.emplace_back([=, &ok] { ok[size_t(t)] = quantize_rows(r0, r1, K, w, mode, q, s, z) ? 1 : 0; });
+  std::vector<char> ok;
+  int64_t started = 0;
+  try {
+    ok.assign(size_t(chunks), 1);
+    pool.reserve(size_t(chunks));
+    for (; started < chunks; ++started) {
+      int64_t r0, r1;
+      rows_of(started, r0, r1);
+      char* flag = &ok[size_t(started)];
+      pool.emplace_back([=] { *flag = quantize_rows(r0, r1, K, w, mode, q, s, z) ? 1 : 0; });
+    }
+  } catch (...) {
+  }
+  bool good = true;
+  if (started < chunks) {
+    const int saved = std::fegetround();
+    for (int64_t c = started; c < chunks; ++c) {
+      int64_t r0, r1;
+      rows_of(c, r0, r1);
+      good = quantize_rows(r0, r1, K, w, mode, q, s, z) && good;
+    }
+    std::fesetround(saved);
   }
   for (auto& th : pool) th.join();
-  for (char o : ok)
-    if (!o) return W4A16_EINVAL;
-  return W4A16_OK;
+  for (int64_t c = 0; c < started; ++c) good = good && ok[size_t(c)] != 0;
+  return good ? W4A16_OK : W4A16_EINVAL;
 }
