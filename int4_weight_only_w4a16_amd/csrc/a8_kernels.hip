@@ -24,9 +24,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // the next. sx = absmax / 127 (fp32, correctly rounded); code =
 // clamp(rne(x / sx), -127, 127); a group of zeros gets sx = 0 and codes 0.
 // xsum = the sum of the group's codes. Groups are numbered i = m * G + g.
-__global__ __launch_bounds__(256) void act_quant_i8_kernel(const _Float16* __restrict__ x, int8_t* __restrict__ xq,
-                                                          float* __restrict__ sx, int32_t* __restrict__ xsum,
-                                                          int64_t groups_total, int K) {
+__global__ __launch_bounds__(256) void act_quant_i8_kernel(int64_t groups_total, int K, const _Float16* __restrict__ x,
+                                                          int8_t* __restrict__ xq, float* __restrict__ sx,
+                                                          int32_t* __restrict__ xsum) {
   const int lane = threadIdx.x & 63;
   const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (i >= groups_total) return;  // whole waves
@@ -84,9 +84,9 @@ __device__ __forceinline__ u32x2 interleave_codes(uint32_t d0, uint32_t d1) {
 // rows 0..15 of each group, zero past M).
 template <int MR, int WAVES, int SHARE>
 __global__ __launch_bounds__(WAVES * 64) void gemv_a8_kernel(
-    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
-    const int8_t* __restrict__ xq, const float* __restrict__ sx, const int32_t* __restrict__ xsum,
-    _Float16* __restrict__ y, int N, int K) {
+    int N, int K, const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, const int8_t* __restrict__ xq, const float* __restrict__ sx,
+    const int32_t* __restrict__ xsum, _Float16* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int kRows = MR < 4 ? MR : 4;                      // D rows of a lane that are activation rows
   constexpr int kRedWave = 4 * kRows * 16;
@@ -240,11 +240,10 @@ hipError_t launch_a8_typed(int N, int K, const void* wq, const void* scales, con
     if (raised != hipSuccess) return raised;
   }
   const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;
-  return launch_kernel(kernel, dim3(unsigned(row_tiles)), dim3(WAVES * 64), lds, stream,
+  return launch_kernel(kernel, dim3(unsigned(row_tiles)), dim3(WAVES * 64), lds, stream, N, K,
                        static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
                        static_cast<const uint8_t*>(zeros), static_cast<const int8_t*>(xq),
-                       static_cast<const float*>(sx), static_cast<const int32_t*>(xsum), static_cast<_Float16*>(y),
-                       N, K);
+                       static_cast<const float*>(sx), static_cast<const int32_t*>(xsum), static_cast<_Float16*>(y));
 }
 
 template <int MR>
@@ -267,9 +266,8 @@ hipError_t launch_a8_m(int N, int K, const LaunchPlan& plan, const void* wq, con
 int launch_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream) {
   const int64_t groups_total = int64_t(M) * (K / kGroup);
   return int(dev::launch_kernel(&dev::act_quant_i8_kernel, dim3(unsigned((groups_total + 3) / 4)), dim3(256), 0,
-                                static_cast<hipStream_t>(stream), static_cast<const _Float16*>(x),
-                                static_cast<int8_t*>(xq), static_cast<float*>(sx), static_cast<int32_t*>(xsum),
-                                groups_total, K));
+                                static_cast<hipStream_t>(stream), groups_total, K, static_cast<const _Float16*>(x),
+                                static_cast<int8_t*>(xq), static_cast<float*>(sx), static_cast<int32_t*>(xsum)));
 }
 
 int launch_gemv_a8(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,

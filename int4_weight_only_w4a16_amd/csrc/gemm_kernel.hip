@@ -39,11 +39,10 @@ static_assert(size_t(kGemmBM) * kOStride * 2 <= kGemmLds, "output tile must fit 
 constexpr int kWeightRequests = 3 * kGemmNB;
 constexpr int kVmcntW = (kWeightRequests & 15) | ((kWeightRequests >> 4) << 14) | (7 << 4) | (15 << 8);
 
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict__ wq,
+__global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ wq,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros,
-                                                   const _Float16* __restrict__ x, _Float16* __restrict__ y,
-                                                   int M, int N, int K) {
+                                                   const _Float16* __restrict__ x, _Float16* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16* xs = reinterpret_cast<_Float16*>(smem);  // [2][kGemmBM][128], 16-byte slots swizzled
   const int G = K / kGroup;
@@ -237,10 +236,10 @@ int launch_gemm(int M, int N, int K, const void* wq, const void* scales, const v
   const int64_t NT = (int64_t(N) + kTileRows - 1) / kTileRows;
   const dim3 grid(unsigned((M + dev::kGemmBM - 1) / dev::kGemmBM),
                   unsigned((NT + dev::kGemmBN / kTileRows - 1) / (dev::kGemmBN / kTileRows)));
-  return int(dev::launch_kernel(&dev::gemm_kernel, grid, dim3(256), dev::kGemmLds, static_cast<hipStream_t>(stream),
-                                static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
+  return int(dev::launch_kernel(&dev::gemm_kernel, grid, dim3(256), dev::kGemmLds, static_cast<hipStream_t>(stream), M,
+                                N, K, static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
                                 static_cast<const uint8_t*>(zeros), static_cast<const _Float16*>(x),
-                                static_cast<_Float16*>(y), M, N, K));
+                                static_cast<_Float16*>(y)));
 }
 
 }  // namespace w4a16

@@ -43,11 +43,14 @@ namespace dev {
 // zero for the next call. Integer addition is exact and order-free, so y
 // does not depend on the order in which the splits arrive; and each output
 // lives in one atomic location, so no fence is needed.
+// The sizes and the split count come first among the arguments, and the
+// split count is an argument rather than gridDim.y, so that everything the
+// kernel needs at entry arrives in preloaded SGPRs (no scalar load).
 template <int MR, int WAVES, int SHARE, int ENGINE, int R, int EPI>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
-    const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    int N, int K, int splits, const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint8_t* __restrict__ zeros, const _Float16* __restrict__ x, _Float16* __restrict__ y,
-    unsigned long long* __restrict__ acc, int N, int K) {
+    unsigned long long* __restrict__ acc) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr bool kGlobalX = ENGINE == kEngineMfmaGlobalX;
   // Accumulators per lane: MR for dot2; for MFMA the D rows a lane can hold
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   // wave, behind an LDS barrier) only when private slices would not fit.
   constexpr bool kSharedX = kPair && !swiglu_private_x(MR, WAVES, SHARE);
   const int64_t row_tiles = (kPair ? 2 : 1) * ((int64_t(N) + kTileRows - 1) / kTileRows);
-  const int split = blockIdx.y, splits = gridDim.y;
+  const int split = blockIdx.y;  // splits == gridDim.y, passed as an argument
   const int g_beg = int(int64_t(split) * G / splits);
   const int g_end = int(int64_t(split + 1) * G / splits);
   const int ng = g_end - g_beg;
@@ -420,9 +423,9 @@ hipError_t launch_typed(int N, int K, const LaunchPlan& plan, const void* wq, co
     if (raised != hipSuccess) return raised;
   }
   return launch_kernel(&gemv_kernel<MR, WAVES, SHARE, ENGINE, R, EPI>, dim3(unsigned(grid), unsigned(plan.splits)),
-                       dim3(WAVES * 64), lds, stream, static_cast<const uint8_t*>(wq),
+                       dim3(WAVES * 64), lds, stream, N, K, plan.splits, static_cast<const uint8_t*>(wq),
                        static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
-                       static_cast<const _Float16*>(x), static_cast<_Float16*>(y), acc, N, K);
+                       static_cast<const _Float16*>(x), static_cast<_Float16*>(y), acc);
 }
 
 template <int MR, int ENGINE>

@@ -38,11 +38,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 // the exact (q - z) * s in fp32 and rounds once to fp16: the result is the
 // exact product rounded to nearest even. 2.5 bytes of HBM traffic per weight
 // (0.5 read + 2 written), plus the scales and zeros.
-__global__ __launch_bounds__(256) void dequant_f16_kernel(const uint8_t* __restrict__ wq,
+__global__ __launch_bounds__(256) void dequant_f16_kernel(int N, int K, int64_t tiles,
+                                                          const uint8_t* __restrict__ wq,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint8_t* __restrict__ zeros,
-                                                          _Float16* __restrict__ out, int N, int K,
-                                                          int64_t tiles) {
+                                                          _Float16* __restrict__ out) {
   const int G = K / kGroup;
   const int lane = threadIdx.x & 63;
   const int64_t tile = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -115,9 +115,9 @@ int launch_dequant_f16(int N, int K, const void* wq, const void* scales, const v
                        void* stream_ptr) {
   const int64_t tiles = (int64_t(N) + kTileRows - 1) / kTileRows * (K / kGroup);
   return int(dev::launch_kernel(&dev::dequant_f16_kernel, dim3(unsigned((tiles + 3) / 4)), dim3(256), 0,
-                                static_cast<hipStream_t>(stream_ptr), static_cast<const uint8_t*>(wq),
+                                static_cast<hipStream_t>(stream_ptr), N, K, tiles, static_cast<const uint8_t*>(wq),
                                 static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
-                                static_cast<_Float16*>(out), N, K, tiles));
+                                static_cast<_Float16*>(out)));
 }
 
 int launch_dequant(int N, int K, const void* wq, const void* scales, const void* zeros, float* out,
