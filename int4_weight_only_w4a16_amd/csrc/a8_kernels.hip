@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void act_quant_i8_kernel(int64_t groups_total,
   const int64_t i = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (i >= groups_total) return;  // whole waves
   const int G = K / kGroup;
-  const int64_t m = i / G;
+  const int64_t m = int64_t(unsigned(i) / unsigned(G));  // i < M * G <= 8 * 2^24
   const int64_t g = i - m * G;
   const int64_t base = m * K + g * kGroup + 2 * lane;
   const half2_t v = *reinterpret_cast<const half2_t*>(x + base);
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_a8_kernel(
 #pragma unroll
     for (int j = 0; j < kXSteps; ++j) {
       const int c = min(lane + 64 * j, xtotal - 1);
-      const int m = c / xchunks, cc = c - m * xchunks;
+      const int m = row_of_chunk<MR>(c, xchunks), cc = c - m * xchunks;
       xv[j] = *reinterpret_cast<const u32x4*>(xq + int64_t(m) * K + int64_t(g0) * kGroup + cc * 16);
     }
     constexpr int kMSteps = (SHARE * 16 + 63) / 64;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_a8_kernel(
 #pragma unroll
     for (int j = 0; j < kXSteps; ++j) {
       const int c = min(lane + 64 * j, xtotal - 1);
-      const int m = c / xchunks, cc = c - m * xchunks;
+      const int m = row_of_chunk<MR>(c, xchunks), cc = c - m * xchunks;
       const int u = cc >> 3, h = cc & 7;
       unsigned char* dst = slice + (m * SHARE + u) * kGroup;
 #pragma unroll

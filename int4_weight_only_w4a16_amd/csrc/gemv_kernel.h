@@ -74,8 +74,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   constexpr bool kSharedX = kPair && !swiglu_private_x(MR, WAVES, SHARE);
   const int64_t row_tiles = (kPair ? 2 : 1) * ((int64_t(N) + kTileRows - 1) / kTileRows);
   const int split = blockIdx.y;  // splits == gridDim.y, passed as an argument
-  const int g_beg = int(int64_t(split) * G / splits);
-  const int g_end = int(int64_t(split + 1) * G / splits);
+  // The split's groups. No division for the usual unsplit launch; else a
+  // 32-bit one (split * G < 31 * 2^24): the 64-bit division compiled to
+  // some 130 instructions per wave before the first request.
+  const int g_beg = splits == 1 ? 0 : int(unsigned(split) * unsigned(G) / unsigned(splits));
+  const int g_end = splits == 1 ? G : int(unsigned(split + 1) * unsigned(G) / unsigned(splits));
   const int ng = g_end - g_beg;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps share bounds scalar
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     if constexpr (!kGlobalX) {
       const int xchunks = n * (kGroup / 8), xtotal = MR * xchunks;
       for (int c = lane; c < xtotal; c += 64) {
-        const int m = c / xchunks, cc = c - m * xchunks;
+        const int m = row_of_chunk<MR>(c, xchunks), cc = c - m * xchunks;
         *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) =
             *reinterpret_cast<const u32x4*>(x + int64_t(m) * K + int64_t(g0) * kGroup + cc * 8);
       }
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
 #pragma unroll
           for (int j = 0; j < kXSteps; ++j) {  // clamped: unconditional, in bounds
             const int c = min(lane + 64 * j, xtotal - 1);
-            const int m = c / xchunks, cc = c - m * xchunks;
+            const int m = row_of_chunk<MR>(c, xchunks), cc = c - m * xchunks;
             xv[j] = *reinterpret_cast<const u32x4*>(x + int64_t(m) * K + int64_t(share_beg) * kGroup + cc * 8);
           }
         }
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
 #pragma unroll
           for (int j = 0; j < kXSteps; ++j) {  // clamped steps rewrite the last chunk with its own data
             const int c = min(lane + 64 * j, xtotal - 1);
-            const int m = c / xchunks, cc = c - m * xchunks;
+            const int m = row_of_chunk<MR>(c, xchunks), cc = c - m * xchunks;
             *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) = xv[j];
           }
         }

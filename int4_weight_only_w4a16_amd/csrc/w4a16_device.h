@@ -61,6 +61,18 @@ __device__ __forceinline__ _Float16 splitk_value(unsigned long long word, int sp
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
+// Activation row of staged chunk c, chunks_per_row chunks per row (c below
+// MR * chunks_per_row): 0 without a division for one row, else an unsigned
+// 32-bit division (cheaper than the signed one).
+template <int MR>
+__device__ __forceinline__ int row_of_chunk(int c, int chunks_per_row) {
+  if constexpr (MR == 1) {
+    return 0;
+  } else {
+    return int(unsigned(c) / unsigned(chunks_per_row));
+  }
+}
+
 // fp16 pairs (1024 + z, 1024 + z) and (64 + z, 64 + z) for a zero point z.
 // 1024 + z has bits 0x6400 | z (spacing 1 in [1024, 2048)); 64 + z has bits
 // 0x5400 | (z << 4) (spacing 1/16 in [64, 128)).

@@ -13,7 +13,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
                                                       float* __restrict__ out, int N, int K) {
   const int G = K / kGroup;
   const int64_t tile = blockIdx.x;
-  const int64_t t = tile / G;
+  const int64_t t = int64_t(unsigned(tile) / unsigned(G));  // tile = blockIdx.x < 2^32
   const int g = int(tile - t * G);
   const int lane = threadIdx.x >> 2, kb = threadIdx.x & 3;
   const int64_t row = t * kTileRows + (lane & 15);
@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256) void dequant_f16_kernel(int N, int K, int64_t 
   const int lane = threadIdx.x & 63;
   const int64_t tile = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (tile >= tiles) return;
-  const int64_t t = tile / G;
+  // 32-bit division whenever the tile index fits (always short of 2^32 tiles).
+  const int64_t t = tile < (int64_t(1) << 32) ? int64_t(unsigned(tile) / unsigned(G)) : tile / G;
   const int g = int(tile - t * G);
   const int rlane = lane & 15;
   const int64_t row = t * kTileRows + rlane;
