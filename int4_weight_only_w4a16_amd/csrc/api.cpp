@@ -39,17 +39,22 @@ int share_for(int tiles) {
 // operations in the same order for a given (waves, K range). The fewest
 // waves (a power of two, at most 16) whose shares hold at most 10 tiles: the
 // whole K range is then in flight at once, in as few waves as possible (a
-// sweep of all instantiated plans on the 0.5B, 7B and 27B shapes put this
-// choice first or within 2% of the best). MFMA with x from LDS when the
-// per-wave x slices fit, else from global memory.
+// sweep of all instantiated plans on the 7B and 27B shapes put this choice
+// first or within 2% of the best; small matrices take shorter shares, below).
+// MFMA with x from LDS when the per-wave x slices fit, else from global
+// memory.
 w4a16::LaunchPlan plan_for(int M, int N, int K, int splits) {
-  (void)N;
   const int groups = K / W4A16_GROUP;
+  const int64_t row_tiles = (int64_t(N) + 15) / 16;
   const int range = (groups + splits - 1) / splits;
   // Split-K grids are large already: shorter shares (more waves per
   // workgroup) measured faster there (3584 x 18944 at 8 splits: 4 waves x 5
-  // tiles 8.9 us, 2 waves x 10 tiles 9.6 us).
-  const int target = splits > 1 ? 5 : 10;
+  // tiles 8.9 us, 2 waves x 10 tiles 9.6 us). A matrix too small to fill
+  // the GPU with at most 8 groups (the 0.5B model's 896 columns) waits
+  // mostly on each wave's serial unpack once its few tiles arrive: two tiles
+  // per wave (896 x 896: 4 waves x 2 tiles 2.34 us, 1 wave x 7 tiles 2.53
+  // us or more).
+  const int target = splits > 1 ? 5 : (groups <= 8 && row_tiles < 256 ? 2 : 10);
   w4a16::LaunchPlan plan;
   plan.engine = w4a16::kEngineMfma;
   plan.splits = splits;
@@ -119,12 +124,12 @@ w4a16::LaunchPlan plan_swiglu(int K) {
 }
 
 // Plan of the INT8-activation GEMV: as many waves as plan_for gives the
-// same K (so rows are batch invariant: the fp32 order depends on the waves
-// only), each wave's groups in one round of a 4-, 7- or 10-tile share, or
+// same shape (so rows are batch invariant: the fp32 order depends on the
+// waves only), each wave's groups in one round of a 4-, 7- or 10-tile share, or
 // in rounds of a smaller share where the workgroup's LDS (codes of all M
 // rows) would not hold the larger one.
-w4a16::LaunchPlan plan_a8(int M, int K) {
-  w4a16::LaunchPlan plan = plan_for(1, 0, K, 1);
+w4a16::LaunchPlan plan_a8(int M, int N, int K) {
+  w4a16::LaunchPlan plan = plan_for(1, N, K, 1);
   const int groups = K / W4A16_GROUP;
   const int per_wave = (groups + plan.waves - 1) / plan.waves;
   plan.engine = w4a16::kEngineMfma;
@@ -148,7 +153,7 @@ extern "C" int w4a16_gemv_a8(int M, int N, int K, const void* Wq, const void* sc
   const int rc = check_shape(M, N, K);
   if (rc != W4A16_OK) return rc == 1 ? W4A16_OK : rc;
   if (!pointers_ok({Wq, scales, zeros, xq, sx, xsum, y})) return W4A16_EINVAL;
-  const w4a16::LaunchPlan plan = plan_a8(M, K);
+  const w4a16::LaunchPlan plan = plan_a8(M, N, K);
   if (!w4a16::a8_instantiated(M, plan.waves, plan.share)) return W4A16_EUNSUPPORTED;
   if (w4a16::launch_gemv_a8(M, N, K, plan, Wq, scales, zeros, xq, sx, xsum, y, stream) != 0) return W4A16_EHIP;
   return W4A16_OK;
