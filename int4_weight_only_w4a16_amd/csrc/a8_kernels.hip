@@ -235,9 +235,9 @@ hipError_t launch_a8_typed(int N, int K, const void* wq, const void* scales, con
   static_assert(lds <= kMaxLdsBytes, "instantiation beyond the LDS of a workgroup");
   auto* kernel = &gemv_a8_kernel<MR, WAVES, SHARE>;
   if constexpr (lds > kDefaultLdsLimit) {
-    static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (raised != hipSuccess) return raised;
+    static std::atomic<uint64_t> raised{0};  // devices on which this instantiation's limit is raised
+    const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kernel), lds, raised);
+    if (e != hipSuccess) return e;
   }
   const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;
   return launch_kernel(kernel, dim3(unsigned(row_tiles)), dim3(WAVES * 64), lds, stream, N, K,

@@ -229,10 +229,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, const
 
 int launch_gemm(int M, int N, int K, const void* wq, const void* scales, const void* zeros, const void* x, void* y,
                 void* stream) {
-  static const hipError_t raised = hipFuncSetAttribute(reinterpret_cast<const void*>(&dev::gemm_kernel),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       int(dev::kGemmLds));
-  if (raised != hipSuccess) return int(raised);
+  static std::atomic<uint64_t> raised{0};  // devices on which the kernel's LDS limit is raised
+  const hipError_t e = dev::raise_lds_limit(reinterpret_cast<const void*>(&dev::gemm_kernel), dev::kGemmLds, raised);
+  if (e != hipSuccess) return int(e);
   const int64_t NT = (int64_t(N) + kTileRows - 1) / kTileRows;
   const dim3 grid(unsigned((M + dev::kGemmBM - 1) / dev::kGemmBM),
                   unsigned((NT + dev::kGemmBN / kTileRows - 1) / (dev::kGemmBN / kTileRows)));

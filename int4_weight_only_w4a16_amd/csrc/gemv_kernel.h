@@ -419,11 +419,10 @@ hipError_t launch_typed(int N, int K, const LaunchPlan& plan, const void* wq, co
   const int64_t grid = (row_tiles + R - 1) / R;
   constexpr size_t lds = lds_for<MR, WAVES, SHARE, ENGINE, EPI>();
   if constexpr (lds > kDefaultLdsLimit) {
-    // Raise this instantiation's dynamic-LDS limit once per process.
-    static const hipError_t raised = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemv_kernel<MR, WAVES, SHARE, ENGINE, R, EPI>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (raised != hipSuccess) return raised;
+    static std::atomic<uint64_t> raised{0};  // devices on which this instantiation's limit is raised
+    const hipError_t e = raise_lds_limit(
+        reinterpret_cast<const void*>(&gemv_kernel<MR, WAVES, SHARE, ENGINE, R, EPI>), lds, raised);
+    if (e != hipSuccess) return e;
   }
   return launch_kernel(&gemv_kernel<MR, WAVES, SHARE, ENGINE, R, EPI>, dim3(unsigned(grid), unsigned(plan.splits)),
                        dim3(WAVES * 64), lds, stream, N, K, plan.splits, static_cast<const uint8_t*>(wq),

@@ -5,6 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstdint>
+
 #include "w4a16_internal.h"
 
 namespace w4a16 {
@@ -24,6 +27,21 @@ hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
                          typename same_type<KArgs>::type... args) {
   void* ptrs[] = {static_cast<void*>(&args)...};
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream);
+}
+
+// Raises `kernel`'s dynamic-LDS limit to `bytes` on the current device, once
+// per device: `done` is the caller's per-kernel record, one bit per device
+// (64 devices; beyond that the call is simply repeated). Concurrent first
+// calls may both set the attribute, which is harmless.
+inline hipError_t raise_lds_limit(const void* kernel, size_t bytes, std::atomic<uint64_t>& done) {
+  int device = 0;
+  const hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = device >= 0 && device < 64 ? uint64_t(1) << device : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t r = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+  if (r == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return r;
 }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
