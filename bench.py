@@ -476,6 +476,39 @@ def main():
         }
         del xp, yp, w16
 
+    # Short prefill chunks (M = 64) leave the 128 x 128-tile GEMM with a few
+    # dozen workgroups on 256 compute units: the split-K GEMM at the split
+    # count the library chooses, against the unsplit one and the two-step
+    # route, timed in turn as above.
+    prefill_small = {}
+    Ms = 64
+    for label, layer in (("qkv", 0), ("o", 1), ("down", 3)):
+        _, Np, Kp = synthetic.QWEN7B_LAYER[layer]
+        wq_g, sc_g, zp_g = step.bufs[layer][3:6]
+        xp = synthetic.device_activations(Ms, Kp, args.seed, 9998, torch.device("cuda:0"))
+        yp = torch.empty((Ms, Np), dtype=torch.int16, device="cuda:0")
+        w16 = torch.empty((Np, Kp), dtype=torch.float16, device="cuda:0")
+        splits = wl.w4a16_gemm_splitk_choose(Ms, Np, Kp)
+        ws_g = torch.zeros(wl.w4a16_splitk_workspace_bytes(Ms, Np, splits), dtype=torch.uint8, device="cuda:0")
+        runs = {"gemm": [], "split": [], "dq": [], "lib": []}
+        for _ in range(3):
+            runs["gemm"].append(timed(lambda: wl.w4a16_gemm(Ms, Np, Kp, wq_g, sc_g, zp_g, xp, yp)))
+            runs["split"].append(timed(lambda: wl.w4a16_gemm_splitk(Ms, Np, Kp, splits, wq_g, sc_g, zp_g, xp, yp,
+                                                                    ws_g)))
+            runs["dq"].append(timed(lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16)))
+            runs["lib"].append(timed(lambda: torch.matmul(xp.view(torch.float16), w16.t())))
+        gemm_us, split_us, dq_us, lib_us = (float(np.median(runs[k])) for k in ("gemm", "split", "dq", "lib"))
+        prefill_small[label] = {
+            "shape": f"M={Ms} x {label} {Np}x{Kp}",
+            "splits": splits,
+            "w4a16_gemm_splitk_us": round(split_us, 1),
+            "w4a16_gemm_unsplit_us": round(gemm_us, 1),
+            "two_step_dequant_plus_torch_fp16_gemm_us": round(dq_us + lib_us, 1),
+            "splitk_TFLOPs": round(2.0 * Ms * Np * Kp / (split_us * 1e-6) / 1e12, 1),
+            "splitk_weight_GBps": round(algorithmic_bytes(0, Np, Kp) / (split_us * 1e-6) / 1e9, 1),
+        }
+        del xp, yp, w16, ws_g
+
     # Host quantizer (w4a16_quantize) on the qkv matrix's shape: fp16 in.
     wlib = wl
     _, Nq, Kq = synthetic.QWEN7B_LAYER[0]
@@ -548,6 +581,7 @@ def main():
             "launches_per_step": 2 * len(step.shapes),
         },
         "prefill_gemm": prefill,
+        "prefill_gemm_small_m": prefill_small,
         "host_quantize": {"shape": f"{Nq}x{Kq} fp16", "GBps_fp16_in": quant,
                           "threads": os.cpu_count()},
         "setup_s": round(setup_s, 1),

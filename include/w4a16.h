@@ -278,6 +278,38 @@ int w4a16_gemv_a8(int M, int N, int K, const void* Wq, const void* scales, const
                   const void* sx, const void* xsum, void* y, void* stream);
 
 /*
+ * Split count this library recommends for w4a16_gemm_splitk (1: do not
+ * split), measured on MI355X over the 7B-shaped matrices at M = 16 .. 2048.
+ * With W the number of 128 x 128 output tiles: 1 from 256 tiles on; else
+ * 256 / W, at most 8 where K holds >= 96 groups, and where it holds fewer
+ * at most 6 for M <= 32, 4 for M <= 64, 4 for M <= 128 with W <= 32, else
+ * 1 (each split adds a pass of atomics over its tile, which a short K does
+ * not pay for once the tile holds many rows); never above K/512 or 31. It
+ * depends on M, and the GEMM makes no batch-invariance promise. Returns 0
+ * for an invalid shape or one w4a16_gemm does not support.
+ */
+int w4a16_gemm_splitk_choose(int M, int N, int K);
+
+/*
+ * w4a16_gemm with the K groups divided into `splits` contiguous ranges, so
+ * that a product with few 128 x 128 output tiles (few rows, or a narrow
+ * matrix with a long K) still fills the GPU. Each (tile, range) workgroup
+ * adds its fp32 partial sums to one 64-bit fixed-point word per output, and
+ * the add that completes an output's count writes y, exactly as in
+ * w4a16_gemv_splitk (same format, same error: each partial within 2^-25 of
+ * its fp32 value; results bit-identical run to run, whatever the arrival
+ * order; within the workload's bound). The workspace rules are those of
+ * w4a16_gemv_splitk: device memory, 16-byte aligned, at least
+ * w4a16_splitk_workspace_bytes(M, N, splits) bytes, zero-filled once before
+ * its first use and left zero by every completed call; calls that may
+ * overlap in time need different workspaces. 1 <= splits <= min(K/128, 31);
+ * splits == 1 is w4a16_gemm and does not touch the workspace. Errors: as
+ * w4a16_gemm, plus W4A16_EINVAL for a bad split count or a short workspace.
+ */
+int w4a16_gemm_splitk(int M, int N, int K, int splits, const void* Wq, const void* scales, const void* zeros,
+                      const void* x, void* y, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Standalone dequantization, for paths that want the fp16 matrix itself
  * (a GEMM over many activation rows, for instance): W_out[n][k] =
  * fp16((q - z) * s), the exact product rounded once to nearest even, for

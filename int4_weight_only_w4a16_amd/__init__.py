@@ -26,7 +26,8 @@ MAX_M = 8
 EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_quantize",
            "w4a16_unpack",
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
-           "w4a16_gemv_splitk", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemm", "w4a16_dequant_f16",
+           "w4a16_gemv_splitk", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemm", "w4a16_gemm_splitk_choose",
+           "w4a16_gemm_splitk", "w4a16_dequant_f16",
            "w4a16_dequant_f32", "w4a16_strerror")
 
 
@@ -74,6 +75,9 @@ def lib():
         L.w4a16_dequant_f32.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_dequant_f16.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_gemm.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
+        L.w4a16_gemm_splitk_choose.restype = _i
+        L.w4a16_gemm_splitk_choose.argtypes = [_i, _i, _i]
+        L.w4a16_gemm_splitk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.w4a16_act_quant_i8.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_gemv_a8.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]
         L.w4a16_strerror.restype = ctypes.c_char_p
@@ -228,6 +232,19 @@ def w4a16_gemm(M, N, K, Wq, scales, zeros, x, y, stream=None):
     """Device: y[M][N] (fp16) = x[M][K] W^T for many rows (prefill), MFMA."""
     _check(lib().w4a16_gemm(M, N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y), _stream(stream)),
            "w4a16_gemm")
+
+
+def w4a16_gemm_splitk_choose(M, N, K):
+    return lib().w4a16_gemm_splitk_choose(M, N, K)
+
+
+def w4a16_gemm_splitk(M, N, K, splits, Wq, scales, zeros, x, y, workspace, ws_bytes=None, stream=None):
+    """Device: the GEMM with K split across workgroups, combined exactly
+    through workspace (zero-filled once; every call leaves it zero)."""
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().w4a16_gemm_splitk(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
+                                   _ptr(workspace), ws_bytes, _stream(stream)), "w4a16_gemm_splitk")
 
 
 def w4a16_dequant_f16(N, K, Wq, scales, zeros, W_out, stream=None):

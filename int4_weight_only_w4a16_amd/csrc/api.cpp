@@ -123,6 +123,29 @@ w4a16::LaunchPlan plan_swiglu(int K) {
   return plan;
 }
 
+// Split count for w4a16_gemm_splitk, measured on MI355X (7B-shaped
+// matrices, M = 16 .. 2048). Each split adds a full pass of 64-bit atomics
+// over its output tile, whose cost grows with the tile's rows, against
+// K/128 / splits groups of products: a long K (>= 96 groups) pays for it
+// up to 8 splits or about one workgroup per compute unit; a short K only
+// while the tile holds few rows.
+int choose_gemm_splits(int M, int N, int K) {
+  const int groups = K / W4A16_GROUP;
+  const int64_t wgs = (int64_t(M) + 127) / 128 * ((int64_t(N) + 127) / 128);
+  if (wgs >= 256) return 1;
+  int64_t splits = 256 / wgs;
+  if (groups >= 96) {
+    splits = splits > 8 ? 8 : splits;
+  } else {
+    const int rows = M < 128 ? M : 128;
+    const int64_t cap = rows <= 32 ? 6 : rows <= 64 ? 4 : (wgs <= 32 ? 4 : 1);
+    splits = splits > cap ? cap : splits;
+  }
+  splits = splits > groups / 4 ? groups / 4 : splits;
+  splits = splits > w4a16::kMaxSplits ? w4a16::kMaxSplits : splits;
+  return splits < 1 ? 1 : int(splits);
+}
+
 // Plan of the INT8-activation GEMV: as many waves as plan_for gives the
 // same shape (so rows are batch invariant: the fp32 order depends on the
 // waves only), each wave's groups in one round of a 4-, 7- or 10-tile share, or
@@ -212,7 +235,27 @@ extern "C" int w4a16_gemm(int M, int N, int K, const void* Wq, const void* scale
   if (M == 0 || N == 0) return W4A16_OK;
   if (K >= w4a16::kGemmMaxK) return W4A16_EUNSUPPORTED;
   if (!pointers_ok({Wq, scales, zeros, x, y})) return W4A16_EINVAL;
-  if (w4a16::launch_gemm(M, N, K, Wq, scales, zeros, x, y, stream) != 0) return W4A16_EHIP;
+  if (w4a16::launch_gemm(M, N, K, 1, Wq, scales, zeros, x, y, nullptr, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
+
+extern "C" int w4a16_gemm_splitk_choose(int M, int N, int K) {
+  if (K < W4A16_GROUP || K % W4A16_GROUP != 0 || M < 1 || N < 1 || K >= w4a16::kGemmMaxK) return 0;
+  return choose_gemm_splits(M, N, K);
+}
+
+extern "C" int w4a16_gemm_splitk(int M, int N, int K, int splits, const void* Wq, const void* scales,
+                                 const void* zeros, const void* x, void* y, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  if (K < W4A16_GROUP || K % W4A16_GROUP != 0 || M < 0 || N < 0) return W4A16_EINVAL;
+  if (splits < 1 || splits > K / W4A16_GROUP || splits > w4a16::kMaxSplits) return W4A16_EINVAL;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (K >= w4a16::kGemmMaxK) return W4A16_EUNSUPPORTED;
+  if (splits == 1) return w4a16_gemm(M, N, K, Wq, scales, zeros, x, y, stream);
+  if (!pointers_ok({Wq, scales, zeros, x, y, workspace})) return W4A16_EINVAL;
+  if (ws_bytes < w4a16::splitk_workspace_bytes(M, N)) return W4A16_EINVAL;
+  auto* ws = static_cast<unsigned long long*>(workspace);
+  if (w4a16::launch_gemm(M, N, K, splits, Wq, scales, zeros, x, y, ws, stream) != 0) return W4A16_EHIP;
   return W4A16_OK;
 }
 

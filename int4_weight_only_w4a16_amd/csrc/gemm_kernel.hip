@@ -39,10 +39,17 @@ static_assert(size_t(kGemmBM) * kOStride * 2 <= kGemmLds, "output tile must fit 
 constexpr int kWeightRequests = 3 * kGemmNB;
 constexpr int kVmcntW = (kWeightRequests & 15) | ((kWeightRequests >> 4) << 14) | (7 << 4) | (15 << 8);
 
-__global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, const uint8_t* __restrict__ wq,
+// Split-K (splits > 1, ws non-null): workgroup (.., .., z) multiplies only
+// the z-th of `splits` contiguous group ranges and adds its fp32 partial
+// sums to ws, one uint64 word per output, in the fixed-point format of
+// splitk_addend(); the add that completes an output's count writes y and
+// zeroes the word (exact and order-free, as in the split-K GEMV).
+__global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int splits,
+                                                   const uint8_t* __restrict__ wq,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros,
-                                                   const _Float16* __restrict__ x, _Float16* __restrict__ y) {
+                                                   const _Float16* __restrict__ x, _Float16* __restrict__ y,
+                                                   unsigned long long* __restrict__ ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16* xs = reinterpret_cast<_Float16*>(smem);  // [2][kGemmBM][128], 16-byte slots swizzled
   const int G = K / kGroup;
@@ -53,6 +60,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, const
   // m fastest: the workgroups resident at once share weight tiles in L2
   // (making n fastest instead, to share x, measured no faster).
   const int64_t m0 = int64_t(blockIdx.x) * kGemmBM;
+  // This workgroup's groups [g_beg, g_beg + ng) (all of K unsplit; a 32-bit
+  // division otherwise, split * G < 31 * 2^24).
+  const int g_beg = splits == 1 ? 0 : int(unsigned(blockIdx.z) * unsigned(G) / unsigned(splits));
+  const int ng = (splits == 1 ? G : int(unsigned(blockIdx.z + 1) * unsigned(G) / unsigned(splits))) - g_beg;
   const int64_t tw = int64_t(blockIdx.y) * (kGemmBN / kTileRows) + wave * kGemmNB;  // wave's first row tile
 
   // The wave's row tiles (clamped past the end: valid memory, never
@@ -167,13 +178,13 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, const
   // wait for all of them, and __syncthreads() would wait for every
   // outstanding load too.
   W wa, wb;
-  auto step = [&](int g, const W& cur, W& nxt) {
-    const int gn = g + 1 < G ? g + 1 : G - 1;
-    load_x(gn, (g & 1) ^ 1);
+  auto step = [&](int i, const W& cur, W& nxt) {  // step i multiplies group g_beg + i
+    const int gn = g_beg + (i + 1 < ng ? i + 1 : ng - 1);
+    load_x(gn, (i & 1) ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     load_w(gn, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    compute(g & 1, cur);
+    compute(i & 1, cur);
     // The x requests were issued before the weight requests (one dwordx4
     // and two dwords per tile): at most that many outstanding leaves x
     // complete. (The compiler makes this a full wait, as it does not count
@@ -181,16 +192,77 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, const
     __builtin_amdgcn_s_waitcnt(kVmcntW);
     lds_barrier();
   };
-  load_x(0, 0);
-  load_w(0, wa);
+  load_x(g_beg, 0);
+  load_w(g_beg, wa);
   __builtin_amdgcn_s_waitcnt(kVmcntW);
   lds_barrier();
-  int g = 0;
-  for (; g + 1 < G; g += 2) {
-    step(g, wa, wb);
-    step(g + 1, wb, wa);
+  int i = 0;
+  for (; i + 1 < ng; i += 2) {
+    step(i, wa, wb);
+    step(i + 1, wb, wa);
   }
-  if (g < G) step(g, wa, wb);
+  if (i < ng) step(i, wa, wb);
+
+  if (ws) {
+    // Split-K: one relaxed device-scope atomic add per output. A lane's adds
+    // go out 16 at a time (two row blocks) before their results are
+    // examined: checking each result before the next add made the epilogue
+    // 64 round trips long, and holding all 64 results spills. The adds are
+    // unconditional within a batch (a branch around each made the compiler
+    // serialize them again). Row blocks holding no row below M are skipped
+    // (a workgroup-uniform test); a position past M or N adds 0 to a valid
+    // word, which changes neither its value nor its count and is never
+    // examined. Past M the target is row m0 + ((m - m0) mod p), p the
+    // largest power of two not above the tile's valid rows, which spreads
+    // those adds over the valid rows (zero adds all aimed at one word
+    // serialized the whole epilogue; all aimed at row M - 1 cost 40% at
+    // M = 16). Adds whose results are not read, with one count per tile and
+    // the tile's last workgroup finishing it, measured 5-10% slower from
+    // M = 64 on: that workgroup's pass over the tile is serial.
+    constexpr int kChunk = 2;  // row blocks per batch of adds
+    const int m_left = int(M - m0 < kGemmBM ? M - m0 : kGemmBM);  // rows of this tile below M (>= 1)
+    const int m_pow2 = 1 << (31 - __builtin_clz(unsigned(m_left)));
+#pragma unroll
+    for (int mb0 = 0; mb0 < kGemmMB; mb0 += kChunk) {
+      if (mb0 * 16 >= m_left) break;
+      unsigned long long now[kChunk][kGemmNB][4];
+      bool valid[kChunk][kGemmNB][4];
+#pragma unroll
+      for (int dm = 0; dm < kChunk; ++dm)
+#pragma unroll
+        for (int nb = 0; nb < kGemmNB; ++nb) {
+          const int64_t t = tw + nb;
+          const int64_t n = t * kTileRows + rlane;
+          const int64_t nc = n < N ? n : N - 1;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t m = m0 + (mb0 + dm) * 16 + piece * 4 + r;
+            const int64_t mc = m < M ? m : m0 + ((m - m0) & (m_pow2 - 1));
+            const bool ok = t < NT && n < N && m < M;
+            const unsigned long long add = ok ? splitk_addend(acc[mb0 + dm][nb][r]) : 0ull;
+            valid[dm][nb][r] = ok;
+            now[dm][nb][r] =
+                __hip_atomic_fetch_add(ws + mc * N + nc, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+          }
+        }
+#pragma unroll
+      for (int dm = 0; dm < kChunk; ++dm)
+#pragma unroll
+        for (int nb = 0; nb < kGemmNB; ++nb) {
+          const int64_t n = (tw + nb) * kTileRows + rlane;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (valid[dm][nb][r] && splitk_count(now[dm][nb][r]) == unsigned(splits)) {
+              const int64_t m = m0 + (mb0 + dm) * 16 + piece * 4 + r;
+              y[m * N + n] = splitk_value(now[dm][nb][r], splits);
+              // Every split has added: nothing else touches the word in this call.
+              __hip_atomic_store(ws + m * N + n, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+    }
+    return;
+  }
 
   // Epilogue through LDS (free after the last barrier): the tile's fp16
   // values go to a [128][136] array (rows padded so the four 16-lane
@@ -227,18 +299,18 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, const
 
 }  // namespace dev
 
-int launch_gemm(int M, int N, int K, const void* wq, const void* scales, const void* zeros, const void* x, void* y,
-                void* stream) {
+int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
+                const void* x, void* y, unsigned long long* ws, void* stream) {
   static std::atomic<uint64_t> raised{0};  // devices on which the kernel's LDS limit is raised
   const hipError_t e = dev::raise_lds_limit(reinterpret_cast<const void*>(&dev::gemm_kernel), dev::kGemmLds, raised);
   if (e != hipSuccess) return int(e);
   const int64_t NT = (int64_t(N) + kTileRows - 1) / kTileRows;
   const dim3 grid(unsigned((M + dev::kGemmBM - 1) / dev::kGemmBM),
-                  unsigned((NT + dev::kGemmBN / kTileRows - 1) / (dev::kGemmBN / kTileRows)));
+                  unsigned((NT + dev::kGemmBN / kTileRows - 1) / (dev::kGemmBN / kTileRows)), unsigned(splits));
   return int(dev::launch_kernel(&dev::gemm_kernel, grid, dim3(256), dev::kGemmLds, static_cast<hipStream_t>(stream), M,
-                                N, K, static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
+                                N, K, splits, static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
                                 static_cast<const uint8_t*>(zeros), static_cast<const _Float16*>(x),
-                                static_cast<_Float16*>(y)));
+                                static_cast<_Float16*>(y), splits > 1 ? ws : nullptr));
 }
 
 }  // namespace w4a16

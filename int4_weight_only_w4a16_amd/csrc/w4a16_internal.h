@@ -145,8 +145,9 @@ int launch_gemv_a8(int M, int N, int K, const LaunchPlan& plan, const void* wq, 
 // The GEMM addresses a workgroup's 128 rows of x with 32-bit element
 // offsets (below 128 K), so K stays under 2^25.
 constexpr int kGemmMaxK = 1 << 25;
-int launch_gemm(int M, int N, int K, const void* wq, const void* scales, const void* zeros, const void* x, void* y,
-                void* stream);
+// splits > 1 takes `ws`, the split-K workspace above (all zero); 1 ignores it.
+int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
+                const void* x, void* y, unsigned long long* ws, void* stream);
 int launch_dequant_f16(int N, int K, const void* wq, const void* scales, const void* zeros, void* out,
                        void* stream);
 int launch_dequant(int N, int K, const void* wq, const void* scales, const void* zeros, float* out,

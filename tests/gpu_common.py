@@ -67,6 +67,15 @@ class Problem:
         torch.cuda.synchronize()
         return y.cpu().numpy().view(np.uint16)
 
+    def gemm_splitk(self, splits, ws=None):
+        torch, dev = torch_dev()
+        y = self.new_y()
+        if ws is None:
+            ws = self.splitk_workspace(splits)
+        w.w4a16_gemm_splitk(self.M, self.N, self.K, splits, self.wq_d, self.sp_d, self.zp_d, self.x_d, y, ws)
+        torch.cuda.synchronize()
+        return y.cpu().numpy().view(np.uint16)
+
     def workspace_is_zero(self, ws):
         """Every split-K call leaves its accumulation words at zero."""
         return not ws.cpu().numpy().any()

@@ -69,3 +69,43 @@ def test_gemm_prefill_size_sampled(M, N, K):
     _say(M, N, K, "worst", worst)
     assert ok, worst
     check_rounded_weights(p, y, rows)
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(9, 37, 384, 3), (16, 301, 4864, 8), (64, 1031, 2560, 5),
+                                          (130, 200, 1408, 11), (128, 128, 128 * 31, 31), (70, 300, 640, 2),
+                                          (257, 160, 1024, 4), (1, 16, 256, 2)])
+def test_gemm_splitk_against_oracle(M, N, K, splits):
+    """K split across workgroups: the same bars as the unsplit GEMM (each
+    partial enters the exact fixed-point sum within 2^-25), the workspace
+    left zero, and results bit-identical run to run through one workspace."""
+    _say("splitk", M, N, K, splits)
+    p = Problem(M, N, K, seed=M + N + splits)
+    ws = p.splitk_workspace(splits)
+    y = p.gemm_splitk(splits, ws)
+    _say(M, N, K, splits, "worst", p.check(y))
+    check_rounded_weights(p, y)
+    assert p.workspace_is_zero(ws)
+    assert np.array_equal(y, p.gemm_splitk(splits, ws)), "run-to-run difference"
+    assert p.workspace_is_zero(ws)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 3584, 18944), (64, 4608, 3584), (100, 3584, 3584), (256, 3584, 18944)])
+def test_gemm_splitk_chosen_sampled(M, N, K):
+    """Small-M prefill shapes at the split count the library chooses: a
+    sample of weight rows (tile edges included) against the oracle."""
+    splits = w.w4a16_gemm_splitk_choose(M, N, K)
+    _say("splitk chosen", M, N, K, splits)
+    assert splits > 1
+    rng = np.random.default_rng(M + 1)
+    rows = np.unique(np.concatenate([[0, 15, 16, 127, 128, N - 1], rng.integers(0, N, 42)]))
+    q, s, z = synthetic.weights(N, K, seed=7)
+    p = Problem(M, N, K, q=q, s=s, z=z, x=synthetic.activations(M, K, seed=8))
+    ws = p.splitk_workspace(splits)
+    y = p.gemm_splitk(splits, ws)
+    o = oracle.get()
+    ref, absref = o.gemv_packed(M, N, K, *p.packed, p.x, rows=rows)
+    ok, worst = oracle.bound_report(y[:, rows], ref, absref, o)
+    _say(M, N, K, splits, "worst", worst)
+    assert ok, worst
+    check_rounded_weights(p, y, rows)
+    assert p.workspace_is_zero(ws)

@@ -20,7 +20,8 @@ def _say(*a):
 def test_all_entry_points_in_one_graph():
     torch, dev = torch_dev()
     _say("build inputs")
-    # Plain and split-K GEMV (M = 3), INT8 activations (M = 2), GEMM (M = 70)
+    # Plain and split-K GEMV (M = 3), INT8 activations (M = 2), GEMM (M = 70,
+    # plain and split-K)
     # and dequantization share one 16-byte-aligned set of problems.
     pg = Problem(3, 1000, 4864, seed=31)
     splits = 4
@@ -28,6 +29,7 @@ def test_all_entry_points_in_one_graph():
     pa = Problem(2, 777, 2048, seed=32)
     G = pa.K // 128
     pm = Problem(70, 300, 640, seed=33)
+    ws_m = pm.splitk_workspace(3)
     gate = synthetic.weights(200, 1024, seed=34, tensor_id=1)
     up = synthetic.weights(200, 1024, seed=34, tensor_id=2)
     sw_packed = [upload(a) for a in w.w4a16_pack_gate_up(*gate, *up)]
@@ -41,6 +43,7 @@ def test_all_entry_points_in_one_graph():
         "xsum": torch.empty((2, G), dtype=torch.int32, device=dev),
         "a8": torch.empty((2, 777), dtype=torch.int16, device=dev),
         "gemm": torch.empty((70, 300), dtype=torch.int16, device=dev),
+        "gemm_splitk": torch.empty((70, 300), dtype=torch.int16, device=dev),
         "dequant": torch.empty((300, 640), dtype=torch.float16, device=dev),
         "swiglu": torch.empty((2, 200), dtype=torch.int16, device=dev),
     }
@@ -53,6 +56,8 @@ def test_all_entry_points_in_one_graph():
         w.w4a16_gemv_a8(2, 777, pa.K, pa.wq_d, pa.sp_d, pa.zp_d, outs["xq"], outs["sx"], outs["xsum"],
                         outs["a8"], stream=stream)
         w.w4a16_gemm(70, 300, 640, pm.wq_d, pm.sp_d, pm.zp_d, pm.x_d, outs["gemm"], stream=stream)
+        w.w4a16_gemm_splitk(70, 300, 640, 3, pm.wq_d, pm.sp_d, pm.zp_d, pm.x_d, outs["gemm_splitk"], ws_m,
+                            stream=stream)
         w.w4a16_dequant_f16(300, 640, pm.wq_d, pm.sp_d, pm.zp_d, outs["dequant"], stream=stream)
         w.w4a16_gemv_swiglu(2, 200, 1024, *sw_packed, sw_x, outs["swiglu"], stream=stream)
 
@@ -89,9 +94,10 @@ def test_all_entry_points_in_one_graph():
         got = snapshot()
         for k in outs:
             assert np.array_equal(got[k].view(np.uint8), eager[k].view(np.uint8)), (rep, k)
-        assert pg.workspace_is_zero(ws)
+        assert pg.workspace_is_zero(ws) and pm.workspace_is_zero(ws_m)
         assert np.array_equal(other.cpu().numpy(), eager["splitk"])
     # The eager results themselves are right (each path has its own parity
     # tests; these spot checks tie the graph to them).
     pg.check(eager["gemv"].view(np.uint16))
     pg.check(eager["splitk"].view(np.uint16))
+    pm.check(eager["gemm_splitk"].view(np.uint16))
