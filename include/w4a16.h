@@ -233,7 +233,9 @@ int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq, const voi
  * products are exact, so each output is within fp32 accumulation and fp16
  * output rounding of sum_k fp16w * x -- inside the workload's bound
  * 2e-3 * sum|w x| + 1e-5, the weight rounding taking at most 2^-11 of it.
- * Deterministic (fixed order), but not bit-equal to w4a16_gemv, whose
+ * A workgroup covers 16, 32, 64 or 128 rows of x (the fewest of these that
+ * cover M) and 128 of W. Deterministic (fixed order), but not bit-equal to
+ * w4a16_gemv, whose
  * weights are exact (q - z) scaled per group. The standalone dequant + MFMA
  * GEMM variant the AWQ dequantization page builds in two steps, here in
  * one. Errors: W4A16_EINVAL (shape, NULL, alignment), W4A16_EUNSUPPORTED
@@ -279,21 +281,23 @@ int w4a16_gemv_a8(int M, int N, int K, const void* Wq, const void* scales, const
 
 /*
  * Split count this library recommends for w4a16_gemm_splitk (1: do not
- * split), measured on MI355X over the 7B-shaped matrices at M = 16 .. 2048.
- * With W the number of 128 x 128 output tiles: 1 from 256 tiles on; else
- * 256 / W, at most 8 where K holds >= 96 groups, and where it holds fewer
- * at most 6 for M <= 32, 4 for M <= 64, 4 for M <= 128 with W <= 32, else
- * 1 (each split adds a pass of atomics over its tile, which a short K does
- * not pay for once the tile holds many rows); never above K/512 or 31. It
- * depends on M, and the GEMM makes no batch-invariance promise. Returns 0
- * for an invalid shape or one w4a16_gemm does not support.
+ * split), measured on MI355X over the 7B-shaped matrices at M = 1 .. 2048.
+ * With B the workgroup's rows (16, 32, 64 or 128: the fewest of these that
+ * cover M) and W the number of B x 128 output tiles: 1 from 256 tiles on;
+ * where K holds >= 96 groups, min(8, 256 / W), or min(16, 512 / W) for
+ * B = 16; where it holds fewer, 4 if W <= 40 and M <= 96 (or W <= 32 and
+ * M <= 128), else 1 (each split adds a pass of atomics over its tile, which
+ * a short K does not pay for once the tile holds many rows); never above
+ * K/512 or 31. It depends on M, and the GEMM makes no batch-invariance
+ * promise. Returns 0 for an invalid shape or one w4a16_gemm does not
+ * support.
  */
 int w4a16_gemm_splitk_choose(int M, int N, int K);
 
 /*
  * w4a16_gemm with the K groups divided into `splits` contiguous ranges, so
- * that a product with few 128 x 128 output tiles (few rows, or a narrow
- * matrix with a long K) still fills the GPU. Each (tile, range) workgroup
+ * that a product with few output tiles (few rows, or a narrow matrix with a
+ * long K) still fills the GPU. Each (tile, range) workgroup
  * adds its fp32 partial sums to one 64-bit fixed-point word per output, and
  * the add that completes an output's count writes y, exactly as in
  * w4a16_gemv_splitk (same format, same error: each partial within 2^-25 of

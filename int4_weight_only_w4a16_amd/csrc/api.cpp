@@ -124,22 +124,26 @@ w4a16::LaunchPlan plan_swiglu(int K) {
 }
 
 // Split count for w4a16_gemm_splitk, measured on MI355X (7B-shaped
-// matrices, M = 16 .. 2048). Each split adds a full pass of 64-bit atomics
-// over its output tile, whose cost grows with the tile's rows, against
-// K/128 / splits groups of products: a long K (>= 96 groups) pays for it
-// up to 8 splits or about one workgroup per compute unit; a short K only
-// while the tile holds few rows.
+// matrices, M = 1 .. 2048). Each split adds a pass of 64-bit atomics over
+// its output tile, whose cost grows with the tile's rows, against
+// K/128 / splits groups of products. A long K (>= 96 groups) pays for it up
+// to about one workgroup per compute unit (two for 16-row tiles) and 8
+// splits (16 for 16-row tiles); a short K takes 4 while the grid is small
+// and the tile holds at most 96 rows (128 on a grid of at most 32 tiles).
 int choose_gemm_splits(int M, int N, int K) {
   const int groups = K / W4A16_GROUP;
-  const int64_t wgs = (int64_t(M) + 127) / 128 * ((int64_t(N) + 127) / 128);
+  const int bm = 16 * w4a16::gemm_m_blocks(M);
+  const int64_t wgs = (int64_t(M) + bm - 1) / bm * ((int64_t(N) + 127) / 128);
   if (wgs >= 256) return 1;
-  int64_t splits = 256 / wgs;
+  int64_t splits;
   if (groups >= 96) {
-    splits = splits > 8 ? 8 : splits;
+    splits = (bm == 16 ? 512 : 256) / wgs;
+    const int64_t cap = bm == 16 ? 16 : 8;
+    splits = splits > cap ? cap : splits;
   } else {
     const int rows = M < 128 ? M : 128;
-    const int64_t cap = rows <= 32 ? 6 : rows <= 64 ? 4 : (wgs <= 32 ? 4 : 1);
-    splits = splits > cap ? cap : splits;
+    splits = wgs <= 40 && (rows <= 96 || wgs <= 32) ? 4 : 1;
+    splits = splits > 256 / wgs ? 256 / wgs : splits;
   }
   splits = splits > groups / 4 ? groups / 4 : splits;
   splits = splits > w4a16::kMaxSplits ? w4a16::kMaxSplits : splits;

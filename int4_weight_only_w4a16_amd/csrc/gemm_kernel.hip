@@ -8,8 +8,10 @@
 // per MFMA, where a VALU:MFMA ratio of 4 alone caps gfx950 at about 60% of
 // its MFMA rate (measured). Every wave reads all 128 rows of x from LDS,
 // about 160 bytes per clock per CU at full MFMA rate, within the 256 the
-// LDS delivers (also measured).
-//  - x[m0 .. m0+127][group] is staged in LDS by direct global-to-LDS loads
+// LDS delivers (also measured). For M <= 64 the tile has 16, 32 or 64 rows
+// instead (MB = 1, 2 or 4 m blocks per wave): there the matrix cores are
+// not the limit, and a 128-row tile would mostly multiply padding.
+//  - x[m0 .. m0+16 MB-1][group] is staged in LDS by direct global-to-LDS loads
 //    (double-buffered, 16-byte slots XOR-swizzled by row against bank
 //    conflicts) and read as the A operand;
 //  - each wave streams its two weight tiles (16 rows x 128 columns, 1 KiB
@@ -26,32 +28,32 @@
 namespace w4a16 {
 namespace dev {
 
-constexpr int kGemmBM = 128;                // activation rows per workgroup
 constexpr int kGemmBN = 128;                // weight rows per workgroup (8 row tiles)
-constexpr int kGemmMB = 8;                  // 16-row m blocks per wave (all 128 rows)
 constexpr int kGemmNB = 2;                  // 16-row weight tiles per wave (the 4 waves side by side in n)
-constexpr int kXTile = kGemmBM * kGroup;    // halves of one staged x group (32 KiB)
-constexpr size_t kGemmLds = size_t(2) * kXTile * 2;
 constexpr int kOStride = kGemmBN + 8;       // halves per LDS row of the output tile (epilogue)
-static_assert(size_t(kGemmBM) * kOStride * 2 <= kGemmLds, "output tile must fit the x buffers");
-// s_waitcnt operand (gfx9 encoding): vmcnt <= the weight requests of one
-// step (3 per tile), expcnt and lgkmcnt not waited on.
-constexpr int kWeightRequests = 3 * kGemmNB;
-constexpr int kVmcntW = (kWeightRequests & 15) | ((kWeightRequests >> 4) << 14) | (7 << 4) | (15 << 8);
+// A workgroup covers 16 MB activation rows (MB = 8, 4, 2 or 1 m blocks per
+// wave): two staged x groups of 16 MB x 128 halves.
+constexpr size_t gemm_lds_bytes(int mb) { return size_t(2) * 16 * mb * kGroup * 2; }
+static_assert(size_t(16) * kOStride * 2 <= gemm_lds_bytes(1), "output tile must fit the x buffers");
+// s_waitcnt operand: vmcnt <= the weight requests of one step (3 per tile).
+constexpr int kVmcntW = vmcnt_at_most(3 * kGemmNB);
 
 // Split-K (splits > 1, ws non-null): workgroup (.., .., z) multiplies only
 // the z-th of `splits` contiguous group ranges and adds its fp32 partial
 // sums to ws, one uint64 word per output, in the fixed-point format of
 // splitk_addend(); the add that completes an output's count writes y and
 // zeroes the word (exact and order-free, as in the split-K GEMV).
+template <int MB>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int splits,
                                                    const uint8_t* __restrict__ wq,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros,
                                                    const _Float16* __restrict__ x, _Float16* __restrict__ y,
                                                    unsigned long long* __restrict__ ws) {
+  constexpr int kBM = 16 * MB;           // activation rows per workgroup
+  constexpr int kXTile = kBM * kGroup;   // halves of one staged x group
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  _Float16* xs = reinterpret_cast<_Float16*>(smem);  // [2][kGemmBM][128], 16-byte slots swizzled
+  _Float16* xs = reinterpret_cast<_Float16*>(smem);  // [2][kBM][128], 16-byte slots swizzled
   const int G = K / kGroup;
   const int64_t NT = (int64_t(N) + kTileRows - 1) / kTileRows;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
   const int rlane = lane & 15, piece = lane >> 4;
   // m fastest: the workgroups resident at once share weight tiles in L2
   // (making n fastest instead, to share x, measured no faster).
-  const int64_t m0 = int64_t(blockIdx.x) * kGemmBM;
+  const int64_t m0 = int64_t(blockIdx.x) * kBM;
   // This workgroup's groups [g_beg, g_beg + ng) (all of K unsplit; a 32-bit
   // division otherwise, split * G < 31 * 2^24).
   const int g_beg = splits == 1 ? 0 : int(unsigned(blockIdx.z) * unsigned(G) / unsigned(splits));
@@ -82,18 +84,19 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
     zbase[j] = reinterpret_cast<const uint32_t*>(zeros) + q0 * (kTileRows / 8);
   }
   const uint32_t w_off = uint32_t(lane) * 16, s_off = uint32_t(rlane >> 1), z_off = uint32_t(rlane >> 3);
-  // x[m0 .. m0+127][group g] -> LDS buffer buf, straight from global memory
+  // x[m0 .. m0+kBM-1][group g] -> LDS buffer buf, straight from global memory
   // (global_load_lds_dwordx4: lane l of a wave's request writes 16 bytes at
   // the request's LDS base + 16 l, so a request fills 1 KiB). Row r of the
   // tile keeps its 16 sixteen-byte chunks c in slots c ^ (r % 16): the A
   // operand reads of 16 consecutive rows then hit 16 distinct bank groups.
   // Rows past M read row M - 1 (valid memory, never stored). x_off[i] is
   // the element offset of request i's chunk from x[m0][0], below 128 K,
-  // which the host keeps under 2^32.
-  uint32_t x_off[8];
+  // which the host keeps under 2^32. The 16 kBM slots take 4 MB requests,
+  // MB per wave.
+  uint32_t x_off[MB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int req = wave * 8 + i;  // this wave's request i: slots 64 req .. 64 req + 63
+  for (int i = 0; i < MB; ++i) {
+    const int req = wave * MB + i;  // this wave's request i: slots 64 req .. 64 req + 63
     const int p = req * 64 + lane, row = p >> 4, c = (p & 15) ^ (row & 15);
     const int64_t mr = m0 + row < M ? row : M - 1 - m0;
     x_off[i] = uint32_t(mr * K + c * 8);
@@ -101,9 +104,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
   auto load_x = [&](int g, int buf) {
     const _Float16* xg = x + m0 * K + int64_t(g) * kGroup;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int req = wave * 8 + i;
-      __builtin_amdgcn_global_load_lds(xg + x_off[i], xs + buf * kXTile + req * 512, 16, 0, 0);
+    for (int i = 0; i < MB; ++i) {
+      const int req = wave * MB + i;
+      load_lds16(xg + x_off[i], xs + buf * kXTile + req * 512);
     }
   };
   struct W {
@@ -119,9 +122,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
     }
   };
 
-  f32x4 acc[kGemmMB][kGemmNB];
+  f32x4 acc[MB][kGemmNB];
 #pragma unroll
-  for (int a = 0; a < kGemmMB; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < kGemmNB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -155,12 +158,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
         for (int i = 0; i < 4; ++i) p[i] = p[i] * s2[j];  // (q - z) * s, rounded once
         bw[j] = half8_t{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
       }
-      half8_t af[kGemmMB];
+      half8_t af[MB];
 #pragma unroll
-      for (int mb = 0; mb < kGemmMB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
         af[mb] = *reinterpret_cast<const half8_t*>(xa + mb * 16 * kGroup + ((kb * 4 + piece) ^ rlane) * 8);
 #pragma unroll
-      for (int mb = 0; mb < kGemmMB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < kGemmNB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bw[nb], acc[mb][nb], 0, 0, 0);
@@ -219,11 +222,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
     // M = 16). Adds whose results are not read, with one count per tile and
     // the tile's last workgroup finishing it, measured 5-10% slower from
     // M = 64 on: that workgroup's pass over the tile is serial.
-    constexpr int kChunk = 2;  // row blocks per batch of adds
-    const int m_left = int(M - m0 < kGemmBM ? M - m0 : kGemmBM);  // rows of this tile below M (>= 1)
+    constexpr int kChunk = MB < 2 ? MB : 2;  // row blocks per batch of adds
+    const int m_left = int(M - m0 < kBM ? M - m0 : kBM);  // rows of this tile below M (>= 1)
     const int m_pow2 = 1 << (31 - __builtin_clz(unsigned(m_left)));
 #pragma unroll
-    for (int mb0 = 0; mb0 < kGemmMB; mb0 += kChunk) {
+    for (int mb0 = 0; mb0 < MB; mb0 += kChunk) {
       if (mb0 * 16 >= m_left) break;
       unsigned long long now[kChunk][kGemmNB][4];
       bool valid[kChunk][kGemmNB][4];
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
   _Float16* ot = xs;
   // D layout: lane l holds D[4 * (l / 16) + r][l % 16] of each 16 x 16 block.
 #pragma unroll
-  for (int mb = 0; mb < kGemmMB; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < kGemmNB; ++nb)
 #pragma unroll
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
   lds_barrier();
   const int64_t n_wg = int64_t(blockIdx.y) * kGemmBN;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < MB; ++i) {
     const int c = tid + 256 * i, row = c >> 4, col = (c & 15) * 8;
     const int64_t m = m0 + row, n0 = n_wg + col;
     if (m >= M || n0 >= N) continue;
@@ -299,18 +302,35 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
 
 }  // namespace dev
 
-int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
-                const void* x, void* y, unsigned long long* ws, void* stream) {
+namespace {
+
+template <int MB>
+int launch_gemm_mb(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
+                   const void* x, void* y, unsigned long long* ws, hipStream_t stream) {
   static std::atomic<uint64_t> raised{0};  // devices on which the kernel's LDS limit is raised
-  const hipError_t e = dev::raise_lds_limit(reinterpret_cast<const void*>(&dev::gemm_kernel), dev::kGemmLds, raised);
+  const size_t lds = dev::gemm_lds_bytes(MB);
+  const hipError_t e = dev::raise_lds_limit(reinterpret_cast<const void*>(&dev::gemm_kernel<MB>), lds, raised);
   if (e != hipSuccess) return int(e);
   const int64_t NT = (int64_t(N) + kTileRows - 1) / kTileRows;
-  const dim3 grid(unsigned((M + dev::kGemmBM - 1) / dev::kGemmBM),
+  const dim3 grid(unsigned((M + 16 * MB - 1) / (16 * MB)),
                   unsigned((NT + dev::kGemmBN / kTileRows - 1) / (dev::kGemmBN / kTileRows)), unsigned(splits));
-  return int(dev::launch_kernel(&dev::gemm_kernel, grid, dim3(256), dev::kGemmLds, static_cast<hipStream_t>(stream), M,
-                                N, K, splits, static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
+  return int(dev::launch_kernel(&dev::gemm_kernel<MB>, grid, dim3(256), lds, stream, M, N, K, splits,
+                                static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
                                 static_cast<const uint8_t*>(zeros), static_cast<const _Float16*>(x),
                                 static_cast<_Float16*>(y), splits > 1 ? ws : nullptr));
+}
+
+}  // namespace
+
+int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
+                const void* x, void* y, unsigned long long* ws, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (gemm_m_blocks(M)) {
+    case 1: return launch_gemm_mb<1>(M, N, K, splits, wq, scales, zeros, x, y, ws, s);
+    case 2: return launch_gemm_mb<2>(M, N, K, splits, wq, scales, zeros, x, y, ws, s);
+    case 4: return launch_gemm_mb<4>(M, N, K, splits, wq, scales, zeros, x, y, ws, s);
+    default: return launch_gemm_mb<8>(M, N, K, splits, wq, scales, zeros, x, y, ws, s);
+  }
 }
 
 }  // namespace w4a16

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   // Accumulators per lane: MR for dot2; for MFMA the D rows a lane can hold
   // (4*piece + r) that are activation rows, at most 4.
   constexpr int kAcc = ENGINE == kEngineDot2 ? MR : (MR < 4 ? MR : 4);
-  constexpr int kXRow = SHARE * kGroup;                  // halves per staged x row of a wave
+  constexpr int kXRow = gemv_x_row(MR, SHARE);          // halves per staged x row of a wave (padded)
   // Per-wave partial sums in LDS: every lane writes its kRows accumulators
   // (no lane-dependent branch, which would let the compiler move the whole
   // scale chain, and the scale loads with it, behind the barrier).
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   const int share_end = g_beg + ((wave_in + 1) * ng) / kHalf;
   const int mm = rlane < MR ? rlane : MR - 1;  // activation row feeding A-operand row rlane
   _Float16* xw = reinterpret_cast<_Float16*>(smem + 2 * kRed * sizeof(float)) +
-                 (kGlobalX ? 0 : (kSharedX ? wave_in : wave) * MR * kXRow);  // x slice [MR][SHARE*128]
+                 (kGlobalX ? 0 : (kSharedX ? wave_in : wave) * MR * kXRow);  // x slice [MR][kXRow]
   int parity = 0;
 
   // Copy x[:, 128*g0 : 128*(g0+n)) into this wave's LDS slice (synchronous).
@@ -308,7 +308,45 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     Round rr[2];
     {
       const TilePtrs p = tile_ptrs(tile_of(0));
-      if constexpr (!kGlobalX) {
+      if constexpr (!kGlobalX && MR > 1) {
+        // Several rows: x goes to the slice by direct global-to-LDS requests,
+        // no registers and no LDS stores. Request (m, k) fills chunks
+        // 64 k .. 64 k + 63 of slice row m (lanes past the row's end stay
+        // idle); lane l takes chunk min(64 k + l, last) of the share, the
+        // padding and any groups past a short share receiving a copy of the
+        // row's last chunk. The per-lane offset is the same for every row,
+        // whose base is uniform: no vector arithmetic per request. (Staging
+        // through registers cost some 380 vector instructions per wave at
+        // M = 8, all of them ahead of the first weight request.)
+        constexpr int kRowChunks = kXRow / 8;  // 16-byte chunks per padded slice row
+        constexpr int kRowReqs = (kRowChunks + 63) / 64;
+        const bool stages_x = !kSharedX || half == 0;  // wave-uniform
+        if (stages_x) {
+          const int xlast = share_n * (kGroup / 8) - 1;
+#pragma unroll
+          for (int k = 0; k < kRowReqs; ++k) {
+            const int cc = 64 * k + lane;
+            if (cc < kRowChunks) {
+              const int src = (cc < xlast ? cc : xlast) * 8;
+#pragma unroll
+              for (int m = 0; m < MR; ++m)
+                load_lds16_unordered(x + int64_t(m) * K + int64_t(share_beg) * kGroup + src, xw + m * kXRow + k * 512);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_round(rr[0], p.wlane, p.sword, p.zword, share_beg, share_n);
+        __builtin_amdgcn_sched_barrier(0);
+        // The round's 3 * SHARE requests (weights, scale and zero words) went
+        // out after x: at most that many outstanding leaves x in LDS.
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(3 * SHARE));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kSharedX) {
+          lds_barrier();  // the up half reads what the gate half staged; weights stay in flight
+        } else {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        }
+      } else if constexpr (!kGlobalX) {
         // x requests go out just ahead of the first weight requests, so the
         // wait before the LDS store is for x alone; the staged slice then
         // serves all of this workgroup's row tiles.

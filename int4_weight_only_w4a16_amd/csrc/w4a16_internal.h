@@ -81,19 +81,26 @@ constexpr size_t reduction_lds_bytes(int mr, int waves, int engine) {
 // SwiGLU: every wave stages its own x slice when all the slices fit in
 // 64 KiB; otherwise wave w of the gate half stages the slice that wave w of
 // the up half also reads, behind one LDS barrier.
+// Halves per row of a wave's staged x slice: share * 128, plus 8 when
+// there are several rows. The MFMA A-operand read of 16 lanes takes rows
+// 0 .. M-1 at one column; at an unpadded stride (a multiple of 256 bytes)
+// they all fall in the same LDS banks, an up-to-8-way conflict on every
+// read. One row is a broadcast and needs no padding.
+constexpr int gemv_x_row(int mr, int share) { return share * kGroup + (mr > 1 ? 8 : 0); }
+
 constexpr bool swiglu_private_x(int mr, int waves, int share) {
-  return size_t(waves) * mr * share * kGroup * 2 <= 64 * 1024;
+  return size_t(waves) * mr * gemv_x_row(mr, share) * 2 <= 64 * 1024;
 }
 
 // Dynamic LDS of a GEMV workgroup: the reduction buffers, then one x slice
-// [M][share * 128] fp16 per wave (per pair of waves for SwiGLU when the
+// [M][gemv_x_row] fp16 per wave (per pair of waves for SwiGLU when the
 // halves share slices; none when x is read from global memory).
 constexpr size_t gemv_lds_bytes(int mr, int waves, int share, int engine, int epi) {
   return reduction_lds_bytes(mr, waves, engine) +
          (engine == kEngineMfmaGlobalX
               ? 0
-              : size_t(epi == kEpiSwiglu && !swiglu_private_x(mr, waves, share) ? waves / 2 : waves) * mr * share *
-                    kGroup * 2);
+              : size_t(epi == kEpiSwiglu && !swiglu_private_x(mr, waves, share) ? waves / 2 : waves) * mr *
+                    gemv_x_row(mr, share) * 2);
 }
 
 // Largest dynamic LDS a GEMV workgroup may use: gfx950's 160 KiB per
@@ -142,9 +149,13 @@ constexpr bool a8_instantiated(int mr, int waves, int share) {
 int launch_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream);
 int launch_gemv_a8(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
                    const void* zeros, const void* xq, const void* sx, const void* xsum, void* y, void* stream);
-// The GEMM addresses a workgroup's 128 rows of x with 32-bit element
-// offsets (below 128 K), so K stays under 2^25.
+// The GEMM addresses a workgroup's (at most 128) rows of x with 32-bit
+// element offsets (below 128 K), so K stays under 2^25.
 constexpr int kGemmMaxK = 1 << 25;
+// 16-row m blocks per GEMM wave (the workgroup's rows / 16): the fewest that
+// cover M, up to 8. A 128-row tile at M = 16 spends 7/8 of its matrix-core
+// work on padding rows.
+constexpr int gemm_m_blocks(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
 // splits > 1 takes `ws`, the split-K workspace above (all zero); 1 ignores it.
 int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
                 const void* x, void* y, unsigned long long* ws, void* stream);

@@ -206,11 +206,11 @@ def test_device_entry_points_reject_before_launch():
         assert L.w4a16_gemm_splitk(M, 16, K, splits, *ptrs, fake, wsb, None) == want, (M, K, splits, wsb)
     assert L.w4a16_gemm_splitk(64, 16, 768, 3, fake, fake, fake, fake + 2, fake, fake, wsg, None) == w.W4A16_EINVAL
     assert L.w4a16_gemm_splitk(64, 16, 768, 3, *ptrs, None, wsg, None) == w.W4A16_EINVAL
-    for M, N, K, want in [(16, 3584, 18944, 8), (64, 3584, 18944, 8), (256, 3584, 18944, 4),
-                          (512, 3584, 18944, 2), (1024, 3584, 18944, 1), (16, 37888, 3584, 1),
-                          (16, 4608, 3584, 6), (64, 4608, 3584, 4), (128, 4608, 3584, 1), (128, 3584, 3584, 4),
-                          (256, 3584, 3584, 1), (16, 200, 1024, 2), (1, 16, 128, 1), (16, 16, 200, 0),
-                          (0, 16, 128, 0), (16, 16, 1 << 25, 0)]:
+    for M, N, K, want in [(16, 3584, 18944, 16), (17, 3584, 18944, 8), (64, 3584, 18944, 8),
+                          (256, 3584, 18944, 4), (512, 3584, 18944, 2), (1024, 3584, 18944, 1),
+                          (16, 37888, 3584, 1), (16, 4608, 3584, 4), (64, 4608, 3584, 4), (96, 4608, 3584, 4),
+                          (128, 4608, 3584, 1), (128, 3584, 3584, 4), (256, 3584, 3584, 1), (16, 200, 1024, 2),
+                          (1, 16, 128, 1), (16, 16, 200, 0), (0, 16, 128, 0), (16, 16, 1 << 25, 0)]:
         assert w.w4a16_gemm_splitk_choose(M, N, K) == want, (M, N, K)
     # dequant to fp16
     assert L.w4a16_dequant_f16(16, 200, fake, fake, fake, fake, None) == w.W4A16_EINVAL

@@ -1,5 +1,7 @@
-"""GPU parity of the W4A16 GEMM for many activation rows (w4a16_gemm) and of
-its weights (w4a16_dequant_f16), through the C ABI, against the fp64 oracle.
+"""GPU parity of the W4A16 GEMM for many activation rows (w4a16_gemm, and
+w4a16_gemm_splitk) and of its weights (w4a16_dequant_f16), through the C
+ABI, against the fp64 oracle. The shapes cover each workgroup height (16,
+32, 64 and 128 rows: M <= 16, <= 32, <= 64 and above) with ragged M and N.
 
 Bars: every output within the workload bound 2e-3 * sum|w x| + 1e-5 of the
 oracle's fp64 product; and, tighter, within fp32 accumulation and fp16
@@ -43,7 +45,9 @@ def check_rounded_weights(p, y, rows=None):
 
 
 @pytest.mark.parametrize("M,N,K", [(9, 37, 384), (16, 896, 896), (130, 200, 640), (128, 128, 128),
-                                   (300, 1000, 1152), (257, 4608, 3584), (64, 301, 256), (200, 1031, 128)])
+                                   (300, 1000, 1152), (257, 4608, 3584), (64, 301, 256), (200, 1031, 128),
+                                   (1, 50, 256), (17, 300, 640), (32, 129, 384), (33, 257, 1280), (48, 160, 128),
+                                   (65, 144, 512)])
 def test_gemm_against_oracle(M, N, K):
     _say("shape", M, N, K)
     p = Problem(M, N, K, seed=M + N)
@@ -73,7 +77,8 @@ def test_gemm_prefill_size_sampled(M, N, K):
 
 @pytest.mark.parametrize("M,N,K,splits", [(9, 37, 384, 3), (16, 301, 4864, 8), (64, 1031, 2560, 5),
                                           (130, 200, 1408, 11), (128, 128, 128 * 31, 31), (70, 300, 640, 2),
-                                          (257, 160, 1024, 4), (1, 16, 256, 2)])
+                                          (257, 160, 1024, 4), (1, 16, 256, 2), (30, 515, 2048, 6),
+                                          (40, 200, 1024, 3)])
 def test_gemm_splitk_against_oracle(M, N, K, splits):
     """K split across workgroups: the same bars as the unsplit GEMM (each
     partial enters the exact fixed-point sum within 2^-25), the workspace
@@ -89,7 +94,8 @@ def test_gemm_splitk_against_oracle(M, N, K, splits):
     assert p.workspace_is_zero(ws)
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 3584, 18944), (64, 4608, 3584), (100, 3584, 3584), (256, 3584, 18944)])
+@pytest.mark.parametrize("M,N,K", [(16, 3584, 18944), (64, 4608, 3584), (100, 3584, 3584), (256, 3584, 18944),
+                                   (8, 3584, 18944), (32, 4608, 3584)])
 def test_gemm_splitk_chosen_sampled(M, N, K):
     """Small-M prefill shapes at the split count the library chooses: a
     sample of weight rows (tile edges included) against the oracle."""
