@@ -221,7 +221,23 @@ def cpu_baseline(step, budget_s):
                   f"{', ...' if len(names) > 2 else ''}), {done_bytes / 1e9:.3f} GB of algorithmic bytes, "
                   f"{spent:.1f} s of oracle time",
         "us_per_step_extrapolated": round(spent / done_bytes * step.bytes * 1e6, 1),
+        "host": host_cpu(),
     }, worst, len(names)
+
+
+def host_cpu():
+    """The host's CPU model and logical CPU count, as the oracle's context."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs"
+
 
 
 def trace_summary(directory):
@@ -405,6 +421,27 @@ def main():
     dom_us = dom_s / (reps * n_dom) * 1e6
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
 
+    # Plain-read ceiling of this device: the library's read probe (the GEMV's
+    # own non-temporal 16-byte loads, nothing stored) over 1 GiB at four grid
+    # sizes, the best of all; the kernels are compared with it beside the
+    # peak. (Two to three workgroups per CU read fastest, about 7.1 TB/s;
+    # from 4 on it drops to about 6.)
+    rbuf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda:0")
+    read_ceiling = 0.0
+    for grid in (256, 512, 768, 1024):
+        step.w.w4a16_read_probe(rbuf, grid, sink)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(4):
+                step.w.w4a16_read_probe(rbuf, grid, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            read_ceiling = max(read_ceiling, 4 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del rbuf, sink
+
     # Variant (reported beside, never as `value`): gate+up with the SwiGLU
     # epilogue fused, y = silu(g) * u of width 18944, same weight bytes.
     fused = step.capture(only="gate_up_proj", swiglu=True)
@@ -547,6 +584,7 @@ def main():
             "split_k": {f"{N}x{K}": sp for (N, K), sp in step.splits.items() if sp > 1},
             "eager_us_per_step": round(eager_us, 1),
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+            "frac_of_measured_read_ceiling": round(value / read_ceiling, 4),
         },
         "roofline": {
             "kernel": "w4a16 gemv, gate_up 37888x3584 M=1",
@@ -558,6 +596,8 @@ def main():
             "traffic": load_traffic(),
             "bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_us, 3),
+            "measured_read_ceiling_GBps": round(read_ceiling, 1),
+            "frac_of_measured_read_ceiling": round(achieved / read_ceiling, 4),
         },
         "variants": {
             "gate_up_swiglu_fused": {

@@ -335,6 +335,17 @@ int w4a16_dequant_f16(int N, int K, const void* Wq, const void* scales, const vo
 int w4a16_dequant_f32(int N, int K, const void* Wq, const void* scales, const void* zeros,
                       float* W_out, void* stream);
 
+/*
+ * Measurement hook: reads the `bytes` bytes at `buf` (device memory) once,
+ * with the GEMV's non-temporal 16-byte loads, `grid` workgroups of 256
+ * threads striding over them, and stores nothing but possibly one 32-bit
+ * word of `sink` (device memory, 16 bytes). Its time gives the plain-read
+ * ceiling of the device, the figure the GEMV's bandwidth is compared with
+ * besides the specified peak. buf and sink 16-byte aligned, bytes a
+ * multiple of 16, 1 <= grid <= 65535. Errors: W4A16_EINVAL, W4A16_EHIP.
+ */
+int w4a16_read_probe(const void* buf, size_t bytes, int grid, void* sink, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* w4a16_strerror(int status);
 

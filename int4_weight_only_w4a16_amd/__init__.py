@@ -28,7 +28,7 @@ EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_ga
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
            "w4a16_gemv_splitk", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemm", "w4a16_gemm_splitk_choose",
            "w4a16_gemm_splitk", "w4a16_dequant_f16",
-           "w4a16_dequant_f32", "w4a16_strerror")
+           "w4a16_dequant_f32", "w4a16_read_probe", "w4a16_strerror")
 
 
 class W4A16Error(RuntimeError):
@@ -73,6 +73,7 @@ def lib():
         L.w4a16_splitk_choose.argtypes = [_i, _i, _i]
         L.w4a16_gemv_splitk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.w4a16_dequant_f32.argtypes = [_i, _i, _p, _p, _p, _p, _p]
+        L.w4a16_read_probe.argtypes = [_p, _sz, _i, _p, _p]
         L.w4a16_dequant_f16.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_gemm.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_gemm_splitk_choose.restype = _i
@@ -251,6 +252,14 @@ def w4a16_dequant_f16(N, K, Wq, scales, zeros, W_out, stream=None):
     """Device: W_out[N][K] fp16 = fp16((q - z) * s), rounded once to nearest even."""
     _check(lib().w4a16_dequant_f16(N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(W_out),
                                    _stream(stream)), "w4a16_dequant_f16")
+
+
+def w4a16_read_probe(buf, grid, sink, nbytes=None, stream=None):
+    """Device: read the bytes of `buf` once (measurement hook for the
+    plain-read ceiling); `sink` is a 16-byte device buffer."""
+    if nbytes is None:
+        nbytes = buf.numel() * buf.element_size()
+    _check(lib().w4a16_read_probe(_ptr(buf), nbytes, grid, _ptr(sink), _stream(stream)), "w4a16_read_probe")
 
 
 def w4a16_dequant_f32(N, K, Wq, scales, zeros, W_out, stream=None):

@@ -272,6 +272,14 @@ extern "C" int w4a16_dequant_f16(int N, int K, const void* Wq, const void* scale
   return W4A16_OK;
 }
 
+extern "C" int w4a16_read_probe(const void* buf, size_t bytes, int grid, void* sink, void* stream) {
+  if (bytes % 16 != 0 || grid < 1 || grid > 65535) return W4A16_EINVAL;
+  if (bytes == 0) return W4A16_OK;
+  if (!pointers_ok({buf, sink})) return W4A16_EINVAL;
+  if (w4a16::launch_read_probe(buf, bytes, grid, sink, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
+
 extern "C" int w4a16_dequant_f32(int N, int K, const void* Wq, const void* scales, const void* zeros,
                                  float* W_out, void* stream) {
   if (K < W4A16_GROUP || K % W4A16_GROUP != 0 || N < 0) return W4A16_EINVAL;

@@ -161,6 +161,7 @@ int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* sca
                 const void* x, void* y, unsigned long long* ws, void* stream);
 int launch_dequant_f16(int N, int K, const void* wq, const void* scales, const void* zeros, void* out,
                        void* stream);
+int launch_read_probe(const void* buf, size_t bytes, int grid, void* sink, void* stream);
 int launch_dequant(int N, int K, const void* wq, const void* scales, const void* zeros, float* out,
                    void* stream);
 

@@ -197,6 +197,12 @@ def test_device_entry_points_reject_before_launch():
     assert L.w4a16_gemm(0, 16, 128, *ptrs, None) == w.W4A16_OK
     assert L.w4a16_gemm(64, 16, 1 << 25, *ptrs, None) == w.W4A16_EUNSUPPORTED
     assert L.w4a16_gemm(64, 16, 128, fake, fake, fake, fake + 2, fake, None) == w.W4A16_EINVAL
+    # read probe (measurement hook)
+    assert L.w4a16_read_probe(fake, 100, 8, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_read_probe(fake, 1024, 0, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_read_probe(fake, 1024, 70000, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_read_probe(fake + 4, 1024, 8, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_read_probe(fake, 0, 8, fake, None) == w.W4A16_OK
     # GEMM with split K: split count, workspace, K limit, and the measured choice
     wsg = w.w4a16_splitk_workspace_bytes(64, 16, 3)
     for M, K, splits, wsb, want in [(64, 768, 0, wsg, w.W4A16_EINVAL), (64, 768, 7, wsg, w.W4A16_EINVAL),

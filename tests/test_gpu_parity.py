@@ -336,3 +336,16 @@ def test_misaligned_device_pointer_is_rejected():
     rc = L.w4a16_gemv(1, 64, 256, p.wq_d.data_ptr(), p.sp_d.data_ptr(), p.zp_d.data_ptr(),
                       p.x_d.data_ptr() + 2, p.new_y().data_ptr(), None)
     assert rc == w.W4A16_EINVAL
+
+
+def test_read_probe_stores_nothing():
+    """The read-ceiling probe reads its buffer and leaves the sink alone
+    (the XOR of an all-zero buffer is 0, not the probe's one constant)."""
+    torch, dev = torch_dev()
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    sink = torch.full((16,), 7, dtype=torch.uint8, device=dev)
+    for grid in (1, 3, 1024):
+        w.w4a16_read_probe(buf, grid, sink)
+        w.w4a16_read_probe(buf[:4096 + 16], grid, sink)
+    torch.cuda.synchronize()
+    assert (sink.cpu().numpy() == 7).all()
