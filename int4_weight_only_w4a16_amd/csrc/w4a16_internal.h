@@ -81,12 +81,14 @@ constexpr size_t reduction_lds_bytes(int mr, int waves, int engine) {
 // SwiGLU: every wave stages its own x slice when all the slices fit in
 // 64 KiB; otherwise wave w of the gate half stages the slice that wave w of
 // the up half also reads, behind one LDS barrier.
-// Halves per row of a wave's staged x slice: share * 128, plus 8 when
-// there are several rows. The MFMA A-operand read of 16 lanes takes rows
-// 0 .. M-1 at one column; at an unpadded stride (a multiple of 256 bytes)
-// they all fall in the same LDS banks, an up-to-8-way conflict on every
-// read. One row is a broadcast and needs no padding.
-constexpr int gemv_x_row(int mr, int share) { return share * kGroup + (mr > 1 ? 8 : 0); }
+// Halves per row of a wave's staged x slice: share * 128, plus 32 when
+// there are several rows. An MFMA A-operand read takes rows 0 .. M-1 at
+// four 16-byte column pieces; at an unpadded stride (a multiple of 256
+// bytes, the span of the 64 banks) every row falls in the same banks, an
+// up-to-8-way conflict on every read. A 64-byte pad puts row r's pieces at
+// bank offset 64 r + 16 piece, at most 2-way for 8 rows (512 bytes take
+// two passes anyway). One row is a broadcast and needs no padding.
+constexpr int gemv_x_row(int mr, int share) { return share * kGroup + (mr > 1 ? 32 : 0); }
 
 constexpr bool swiglu_private_x(int mr, int waves, int share) {
   return size_t(waves) * mr * gemv_x_row(mr, share) * 2 <= 64 * 1024;
