@@ -143,10 +143,14 @@ constexpr size_t gemv_a8_lds_bytes(int mr, int waves, int share) {
          size_t(waves) * (size_t(mr) * share * kGroup + size_t(share) * 16 * 8);
 }
 // Instantiated (waves, share): waves 1..16 (powers of two), shares 4, 7, 10,
-// within the LDS of a workgroup.
+// within the LDS of a workgroup; not 16 waves of 10-tile shares for 4 or
+// more rows, whose registers (at most 128 per lane in a 1024-thread
+// workgroup) cannot hold the staged codes of a round without spilling:
+// those take 7-tile shares in two rounds.
 constexpr bool a8_instantiated(int mr, int waves, int share) {
   return (waves == 1 || waves == 2 || waves == 4 || waves == 8 || waves == 16) &&
-         (share == 4 || share == 7 || share == 10) && gemv_a8_lds_bytes(mr, waves, share) <= kMaxLdsBytes;
+         (share == 4 || share == 7 || share == 10) && !(waves == 16 && share == 10 && mr >= 4) &&
+         gemv_a8_lds_bytes(mr, waves, share) <= kMaxLdsBytes;
 }
 int launch_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream);
 int launch_gemv_a8(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,

@@ -74,7 +74,8 @@ def _check_a8(p, y, xq_np, sx_np):
 # group, fewer groups than waves, and K whose codes at M = 8 take several
 # rounds per wave.
 SHAPES = [(1, 37888, 3584), (1, 3584, 18944), (8, 3584, 18944), (5, 17408, 5120), (2, 5120, 17408),
-          (1, 896, 896), (4, 4864, 896), (3, 33, 256), (7, 1, 128), (6, 50, 1408), (8, 64, 7168)]
+          (1, 896, 896), (4, 4864, 896), (3, 33, 256), (7, 1, 128), (6, 50, 1408), (8, 64, 7168),
+          (4, 257, 18944), (5, 3584, 18944), (6, 130, 18944)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -88,16 +89,19 @@ def test_gemv_a8_against_oracle(M, N, K):
     assert np.array_equal(y, _gemv_a8(p, xq, sx, xs)), "run-to-run difference"
 
 
-def test_gemv_a8_codes_from_oracle_and_batch_invariance():
+@pytest.mark.parametrize("M,K", [(8, 3584), (8, 18944), (5, 18944)])
+def test_gemv_a8_codes_from_oracle_and_batch_invariance(M, K):
     """The GEMV alone, fed the oracle's codes (not the GPU quantizer's), and
-    each row of an 8-row call bit-identical to the same row alone."""
-    M, N, K = 8, 200, 3584
+    each row of a multi-row call bit-identical to the same row alone (at
+    K = 18944 the multi-row call takes 7-tile shares in two rounds, the
+    single row one round of 10)."""
+    N = 200
     p = Problem(M, N, K, seed=77)
     rq, rs, rsum = oracle.get().act_quant_i8(p.x)
     xq, sx, xs = upload(rq), upload(rs), upload(rsum)
     y = _gemv_a8(p, xq, sx, xs)
     _check_a8(p, y, rq, rs)
-    for m in (0, 3, 7):
+    for m in (0, 3, M - 1):
         one = Problem(1, N, K, q=p.q, s=p.s, z=p.z, x=p.x[m:m + 1])
         y1 = _gemv_a8(one, upload(rq[m:m + 1]), upload(rs[m:m + 1]), upload(rsum[m:m + 1]))
         assert np.array_equal(y1[0], y[m]), m
