@@ -308,16 +308,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     Round rr[2];
     {
       const TilePtrs p = tile_ptrs(tile_of(0));
-      if constexpr (!kGlobalX && MR > 1) {
-        // Several rows: x goes to the slice by direct global-to-LDS requests,
-        // no registers and no LDS stores. Request (m, k) fills chunks
-        // 64 k .. 64 k + 63 of slice row m (lanes past the row's end stay
-        // idle); lane l takes chunk min(64 k + l, last) of the share, the
-        // padding and any groups past a short share receiving a copy of the
-        // row's last chunk. The per-lane offset is the same for every row,
-        // whose base is uniform: no vector arithmetic per request. (Staging
-        // through registers cost some 380 vector instructions per wave at
-        // M = 8, all of them ahead of the first weight request.)
+      if constexpr (!kGlobalX && MR > 1 && MR <= 5) {
+        // Two to five rows: x goes to the slice by direct global-to-LDS
+        // requests, no registers and no LDS stores. Request (m, k) fills
+        // chunks 64 k .. 64 k + 63 of slice row m (lanes past the row's end
+        // stay idle); lane l takes chunk min(64 k + l, last) of the share,
+        // the padding and any groups past a short share receiving a copy of
+        // the row's last chunk. The per-lane offset is the same for every
+        // row, whose base is uniform: almost no vector arithmetic per
+        // request. Before the first x read the compiler waits for every
+        // outstanding request, the round's weights included (these requests
+        // need not complete in order with ordinary loads). Staging through
+        // registers cost a division per chunk, all ahead of the first weight
+        // request; it still wins from six rows on, where the wait for the
+        // whole round costs more.
         constexpr int kRowChunks = kXRow / 8;  // 16-byte chunks per padded slice row
         constexpr int kRowReqs = (kRowChunks + 63) / 64;
         const bool stages_x = !kSharedX || half == 0;  // wave-uniform
@@ -330,19 +334,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
               const int src = (cc < xlast ? cc : xlast) * 8;
 #pragma unroll
               for (int m = 0; m < MR; ++m)
-                load_lds16_unordered(x + int64_t(m) * K + int64_t(share_beg) * kGroup + src, xw + m * kXRow + k * 512);
+                load_lds16(x + int64_t(m) * K + int64_t(share_beg) * kGroup + src, xw + m * kXRow + k * 512);
             }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
         load_round(rr[0], p.wlane, p.sword, p.zword, share_beg, share_n);
         __builtin_amdgcn_sched_barrier(0);
-        // The round's 3 * SHARE requests (weights, scale and zero words) went
-        // out after x: at most that many outstanding leaves x in LDS.
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(3 * SHARE));
-        __builtin_amdgcn_sched_barrier(0);
         if constexpr (kSharedX) {
-          lds_barrier();  // the up half reads what the gate half staged; weights stay in flight
+          lds_barrier();  // the up half reads what the gate half staged
         } else {
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         }

@@ -83,26 +83,16 @@ __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast
 // vector-memory requests are outstanding, not waiting on expcnt or lgkmcnt.
 constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// One 16-byte global-to-LDS request per active lane: lane l writes l's 16
-// bytes at l + 16 l (l = the wave-uniform LDS address). The compiler does
-// not order later LDS reads after these writes: the caller waits for them
-// (vmcnt) itself. (A plain device function: the host-side instantiation of
-// a kernel template that names the builtin fails, and the kernel's launch
-// stub silently goes missing.)
+// One 16-byte global-to-LDS request per active lane: lane l writes its 16
+// bytes at l + 16 l (l = the wave-uniform LDS address). Before a later LDS
+// read the compiler waits for every outstanding vector-memory request
+// (vmcnt 0): these requests need not complete in order with ordinary loads
+// (counting them exactly, from inline asm, gave run-to-run differences), so
+// that is the only safe wait. (A plain device function: the host-side
+// instantiation of a kernel template that names the builtin fails, and the
+// kernel's launch stub silently goes missing.)
 __device__ __forceinline__ void load_lds16(const _Float16* g, _Float16* l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-
-// The same request, invisible to the compiler's wait counting: through the
-// builtin, any later LDS read waits for every outstanding vector-memory
-// request (vmcnt 0), since the compiler does not tell the LDS-bound loads
-// apart. Here the caller waits for them itself; loads complete in order, so
-// the compiler's own count-based waits for later loads stay correct (they
-// also cover these). M0 is set inside the statement; nothing in the kernels
-// that use it keeps another value in M0.
-__device__ __forceinline__ void load_lds16_unordered(const _Float16* g, const _Float16* l) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(l)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory");
 }
 
 // Activation row of staged chunk c, chunks_per_row chunks per row (c below

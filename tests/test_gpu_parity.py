@@ -85,8 +85,21 @@ def test_qwen7b_shapes(name, N, K):
 @pytest.mark.parametrize("M", synthetic.VERIFY_M)
 @pytest.mark.parametrize("name,N,K", synthetic.VERIFY27B)
 def test_verify27b_shapes(name, N, K, M):
+    """Full size, every output against the oracle, and (many workgroups per
+    CU, x staged by direct LDS requests for 2 to 5 rows) four runs bit for
+    bit equal, plain and with the library's split choice."""
     p = Problem(M, N, K, seed=3)
-    _say(name, M, "worst", p.check(p.gemv()))
+    y = p.gemv()
+    _say(name, M, "worst", p.check(y))
+    for _ in range(3):
+        assert np.array_equal(y, p.gemv()), "run-to-run difference"
+    splits = w.w4a16_splitk_choose(M, N, K)
+    if splits > 1:
+        ws = p.splitk_workspace(splits)
+        ys = p.gemv_splitk(splits, ws)
+        p.check(ys)
+        for _ in range(3):
+            assert np.array_equal(ys, p.gemv_splitk(splits, ws)), "run-to-run difference (split)"
 
 
 # ------------------------------------------------------------ edge cases
