@@ -308,57 +308,33 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     Round rr[2];
     {
       const TilePtrs p = tile_ptrs(tile_of(0));
-      if constexpr (!kGlobalX && MR > 1 && MR <= 5) {
-        // Two to five rows: x goes to the slice by direct global-to-LDS
-        // requests, no registers and no LDS stores. Request (m, k) fills
-        // chunks 64 k .. 64 k + 63 of slice row m (lanes past the row's end
-        // stay idle); lane l takes chunk min(64 k + l, last) of the share,
-        // the padding and any groups past a short share receiving a copy of
-        // the row's last chunk. The per-lane offset is the same for every
-        // row, whose base is uniform: almost no vector arithmetic per
-        // request. Before the first x read the compiler waits for every
-        // outstanding request, the round's weights included (these requests
-        // need not complete in order with ordinary loads). Staging through
-        // registers cost a division per chunk, all ahead of the first weight
-        // request; it still wins from six rows on, where the wait for the
-        // whole round costs more.
-        constexpr int kRowChunks = kXRow / 8;  // 16-byte chunks per padded slice row
-        constexpr int kRowReqs = (kRowChunks + 63) / 64;
-        const bool stages_x = !kSharedX || half == 0;  // wave-uniform
-        if (stages_x) {
-          const int xlast = share_n * (kGroup / 8) - 1;
-#pragma unroll
-          for (int k = 0; k < kRowReqs; ++k) {
-            const int cc = 64 * k + lane;
-            if (cc < kRowChunks) {
-              const int src = (cc < xlast ? cc : xlast) * 8;
-#pragma unroll
-              for (int m = 0; m < MR; ++m)
-                load_lds16(x + int64_t(m) * K + int64_t(share_beg) * kGroup + src, xw + m * kXRow + k * 512);
-            }
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        load_round(rr[0], p.wlane, p.sword, p.zword, share_beg, share_n);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kSharedX) {
-          lds_barrier();  // the up half reads what the gate half staged
-        } else {
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-        }
-      } else if constexpr (!kGlobalX) {
+      if constexpr (!kGlobalX) {
         // x requests go out just ahead of the first weight requests, so the
         // wait before the LDS store is for x alone; the staged slice then
-        // serves all of this workgroup's row tiles.
-        constexpr int kXSteps = (MR * SHARE * 16 + 63) / 64;
-        const int xchunks = share_n * (kGroup / 8), xtotal = MR * xchunks;
+        // serves all of this workgroup's row tiles. Chunk c of the slice is
+        // row c / kRowChunks, a division by a constant (one row: none); in a
+        // short share the chunks past its groups take a copy of the row's
+        // last chunk. (Dividing by the share's own chunk count cost some
+        // 20 vector instructions per chunk, 380 per wave at M = 8, all ahead
+        // of the first weight request. Direct global-to-LDS requests, which
+        // need no registers, measured slower than this from two rows on:
+        // before the first LDS read the compiler waits for every
+        // outstanding load, the whole round of weights included.)
+        constexpr int kRowChunks = SHARE * (kGroup / 8);
+        constexpr int kXSteps = (MR * kRowChunks + 63) / 64;
+        const int xlast = share_n * (kGroup / 8) - 1;
         const bool stages_x = !kSharedX || half == 0;  // wave-uniform
+        auto chunk = [&](int j, int& m, int& cc) {  // clamped: unconditional, in bounds
+          const int c = min(lane + 64 * j, MR * kRowChunks - 1);
+          m = MR == 1 ? 0 : c / kRowChunks;
+          cc = min(c - m * kRowChunks, xlast);
+        };
         u32x4 xv[kXSteps];
         if (stages_x) {
 #pragma unroll
-          for (int j = 0; j < kXSteps; ++j) {  // clamped: unconditional, in bounds
-            const int c = min(lane + 64 * j, xtotal - 1);
-            const int m = row_of_chunk<MR>(c, xchunks), cc = c - m * xchunks;
+          for (int j = 0; j < kXSteps; ++j) {
+            int m, cc;
+            chunk(j, m, cc);
             xv[j] = *reinterpret_cast<const u32x4*>(x + int64_t(m) * K + int64_t(share_beg) * kGroup + cc * 8);
           }
         }
@@ -367,9 +343,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
         __builtin_amdgcn_sched_barrier(0);
         if (stages_x) {
 #pragma unroll
-          for (int j = 0; j < kXSteps; ++j) {  // clamped steps rewrite the last chunk with its own data
-            const int c = min(lane + 64 * j, xtotal - 1);
-            const int m = row_of_chunk<MR>(c, xchunks), cc = c - m * xchunks;
+          for (int j = 0; j < kXSteps; ++j) {  // clamped chunks rewrite a chunk with its own data
+            int m, cc;
+            chunk(j, m, cc);
             *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) = xv[j];
           }
         }
