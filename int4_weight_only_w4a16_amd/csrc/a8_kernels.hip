@@ -116,13 +116,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_a8_kernel(
     const int n = min(SHARE, share_end - g0);
     // Activation codes first (their wait then covers them alone): 16-byte
     // chunks c = (m, group u, 16 columns h), clamped to the last real chunk.
-    constexpr int kXSteps = (MR * SHARE * 8 + 63) / 64;
-    const int xchunks = n * 8, xtotal = MR * xchunks;
+    // Chunk c is row c / (8 SHARE), a division by a constant (a division by
+    // the round's own chunk count costs some 20 vector instructions per
+    // chunk); chunks past a short round's groups take a copy of the row's
+    // last chunk.
+    constexpr int kRowChunks = SHARE * 8;
+    constexpr int kXSteps = (MR * kRowChunks + 63) / 64;
+    const int xlast = n * 8 - 1;
+    auto chunk = [&](int ln, int j, int& m, int& cc) {
+      const int c = min(ln + 64 * j, MR * kRowChunks - 1);
+      m = MR == 1 ? 0 : c / kRowChunks;
+      cc = min(c - m * kRowChunks, xlast);
+    };
     u32x4 xv[kXSteps];
 #pragma unroll
     for (int j = 0; j < kXSteps; ++j) {
-      const int c = min(lane + 64 * j, xtotal - 1);
-      const int m = row_of_chunk<MR>(c, xchunks), cc = c - m * xchunks;
+      int m, cc;
+      chunk(lane, j, m, cc);
       xv[j] = *reinterpret_cast<const u32x4*>(xq + int64_t(m) * K + int64_t(g0) * kGroup + cc * 16);
     }
     constexpr int kMSteps = (SHARE * 16 + 63) / 64;
@@ -150,10 +160,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_a8_kernel(
     // Stage: chunk (m, u, h) covers columns 16h .. 16h+15 of group u, i.e.
     // 8-column blocks b = 2h, 2h+1 with b = 4 kb + piece; block b goes to
     // byte (kb / 2) * 64 + piece * 16 + (kb % 2) * 8 of the group's 128.
+    // The chunk indices again, from an opaque copy of the lane: kept from
+    // the loads instead, they stay live across the weight requests and
+    // spill at 16 waves.
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
 #pragma unroll
     for (int j = 0; j < kXSteps; ++j) {
-      const int c = min(lane + 64 * j, xtotal - 1);
-      const int m = row_of_chunk<MR>(c, xchunks), cc = c - m * xchunks;
+      int m, cc;
+      chunk(lane_o, j, m, cc);
       const int u = cc >> 3, h = cc & 7;
       unsigned char* dst = slice + (m * SHARE + u) * kGroup;
 #pragma unroll
