@@ -115,7 +115,10 @@ class Step:
         for i, (name, N, K, wq, sc, zp, x, y) in enumerate(self.bufs):
             if only is not None and not name.endswith(only):
                 continue
-            if a8 is not None:
+            if a8 == "fused":
+                # INT8 activations quantized inside the GEMV launch.
+                self.w.w4a16_gemv_a8_fused(1, N, K, wq, sc, zp, x, y, stream=stream)
+            elif a8 is not None:
                 # INT8-activation variant: quantize x (a launch of its own,
                 # skipped for a8 == "gemv"), then the integer-MFMA GEMV.
                 xq, sx, xs = self.a8_bufs[i]
@@ -462,7 +465,12 @@ def main():
     a8_gemv_us = step.time_graph(a8_gemv, reps, 3) / (reps * n_dom) * 1e6
     a8_step = step.capture(a8="both")
     a8_step_us = step.time_graph(a8_step, args.steps, args.warmup) / args.steps * 1e6
-    del a8_gate_up, a8_gemv, a8_step
+    # The quantization fused into the GEMV: one launch per GEMV again.
+    a8f_gate_up = step.capture(only="gate_up_proj", a8="fused")
+    a8f_gate_up_us = step.time_graph(a8f_gate_up, reps, 3) / (reps * n_dom) * 1e6
+    a8f_step = step.capture(a8="fused")
+    a8f_step_us = step.time_graph(a8f_step, args.steps, args.warmup) / args.steps * 1e6
+    del a8_gate_up, a8_gemv, a8_step, a8f_gate_up, a8f_step
 
     # Prefill (M = 2048) on the gate+up and down shapes: the fused W4A16
     # GEMM, the standalone fp16 dequantization, and for context the two-step
@@ -619,6 +627,12 @@ def main():
             "step_us": round(a8_step_us, 2),
             "step_us_fp16_activations": round(us_step, 2),
             "launches_per_step": 2 * len(step.shapes),
+            "fused": {
+                "kernel": "w4a16_gemv_a8_fused (quantization inside the GEMV launch, bit-identical)",
+                "gate_up_us": round(a8f_gate_up_us, 3),
+                "step_us": round(a8f_step_us, 2),
+                "launches_per_step": len(step.shapes),
+            },
         },
         "prefill_gemm": prefill,
         "prefill_gemm_small_m": prefill_small,

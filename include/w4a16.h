@@ -280,6 +280,19 @@ int w4a16_gemv_a8(int M, int N, int K, const void* Wq, const void* scales, const
                   const void* sx, const void* xsum, void* y, void* stream);
 
 /*
+ * w4a16_act_quant_i8 and w4a16_gemv_a8 in one launch: x is fp16 [M][K] as
+ * for w4a16_gemv, and each workgroup quantizes the activation groups it
+ * multiplies (per group of 128: sx = absmax / 127, codes rne(x / sx)
+ * clamped to +-127, their sum) with the same fp32 operations as
+ * w4a16_act_quant_i8, so y equals that two-launch path bit for bit, with no
+ * code buffers and one dependent launch fewer per GEMV. Same M limit, same
+ * bound and batch invariance as w4a16_gemv_a8. Errors: W4A16_EINVAL (shape,
+ * NULL, alignment), W4A16_EUNSUPPORTED (M > 8), W4A16_EHIP.
+ */
+int w4a16_gemv_a8_fused(int M, int N, int K, const void* Wq, const void* scales, const void* zeros, const void* x,
+                        void* y, void* stream);
+
+/*
  * Split count this library recommends for w4a16_gemm_splitk (1: do not
  * split), measured on MI355X over the 7B-shaped matrices at M = 1 .. 2048.
  * With B the workgroup's rows (16, 32, 64 or 128: the fewest of these that

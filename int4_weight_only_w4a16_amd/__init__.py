@@ -26,7 +26,7 @@ MAX_M = 8
 EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_quantize",
            "w4a16_unpack",
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
-           "w4a16_gemv_splitk", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemm", "w4a16_gemm_splitk_choose",
+           "w4a16_gemv_splitk", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemv_a8_fused", "w4a16_gemm", "w4a16_gemm_splitk_choose",
            "w4a16_gemm_splitk", "w4a16_dequant_f16",
            "w4a16_dequant_f32", "w4a16_read_probe", "w4a16_strerror")
 
@@ -81,6 +81,7 @@ def lib():
         L.w4a16_gemm_splitk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.w4a16_act_quant_i8.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_gemv_a8.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]
+        L.w4a16_gemv_a8_fused.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_strerror.restype = ctypes.c_char_p
         L.w4a16_strerror.argtypes = [_i]
         _lib = L
@@ -227,6 +228,13 @@ def w4a16_gemv_a8(M, N, K, Wq, scales, zeros, xq, sx, xsum, y, stream=None):
     w4a16_act_quant_i8 (integer sums per group, then both scales)."""
     _check(lib().w4a16_gemv_a8(M, N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(xq), _ptr(sx), _ptr(xsum),
                                _ptr(y), _stream(stream)), "w4a16_gemv_a8")
+
+
+def w4a16_gemv_a8_fused(M, N, K, Wq, scales, zeros, x, y, stream=None):
+    """Device: w4a16_act_quant_i8 + w4a16_gemv_a8 in one launch (x fp16),
+    bit-identical to the two launches."""
+    _check(lib().w4a16_gemv_a8_fused(M, N, K, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
+                                     _stream(stream)), "w4a16_gemv_a8_fused")
 
 
 def w4a16_gemm(M, N, K, Wq, scales, zeros, x, y, stream=None):

@@ -55,6 +55,23 @@ __global__ __launch_bounds__(256) void act_quant_i8_kernel(int64_t groups_total,
   }
 }
 
+// Codes of 8 activations with a group scale computed as in
+// act_quant_i8_kernel (the same fp32 operations, so the same bits): packed
+// little-endian into two words, four codes each, and their sum.
+__device__ __forceinline__ void quantize8(const float (&a)[8], float scale, uint32_t& d0, uint32_t& d1, int& sum) {
+  d0 = d1 = 0u;
+  sum = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = scale > 0.0f ? int(fminf(fmaxf(rintf(a[k] / scale), -127.0f), 127.0f)) : 0;
+    sum += c;
+    if (k < 4)
+      d0 |= (uint32_t(c) & 0xFFu) << (8 * k);
+    else
+      d1 |= (uint32_t(c) & 0xFFu) << (8 * (k - 4));
+  }
+}
+
 // Activation bytes x0..x7 of 8 consecutive columns -> the two words whose
 // bytes line up with the masked nibbles of one packed weight word: the
 // layout puts weight j of a word at nibble slot {0,4,1,5,2,6,3,7}[j], so
@@ -82,11 +99,19 @@ __device__ __forceinline__ u32x2 interleave_codes(uint32_t d0, uint32_t d1) {
 // LDS: [WAVES][4][rows][16] floats for the reduction, then per wave
 // [M][SHARE][128] code bytes and [SHARE][16] sx and xsum values (activation
 // rows 0..15 of each group, zero past M).
-template <int MR, int WAVES, int SHARE>
+//
+// FQ (fused quantization): x is the fp16 activations, and each round
+// quantizes its own slice while the weights are in flight, 16 lanes per
+// group of 128, with the arithmetic of act_quant_i8_kernel: the codes, sx
+// and xsum are those the separate launch would have produced, bit for bit,
+// and so is y. sx and xsum are then unused.
+template <int MR, int WAVES, int SHARE, bool FQ>
 __global__ __launch_bounds__(WAVES * 64) void gemv_a8_kernel(
     int N, int K, const uint8_t* __restrict__ wq, const uint16_t* __restrict__ scales,
-    const uint8_t* __restrict__ zeros, const int8_t* __restrict__ xq, const float* __restrict__ sx,
+    const uint8_t* __restrict__ zeros, const void* __restrict__ xin, const float* __restrict__ sx,
     const int32_t* __restrict__ xsum, _Float16* __restrict__ y) {
+  const int8_t* xq = static_cast<const int8_t*>(xin);
+  const _Float16* xf = static_cast<const _Float16*>(xin);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int kRows = MR < 4 ? MR : 4;                      // D rows of a lane that are activation rows
   constexpr int kRedWave = 4 * kRows * 16;
@@ -114,75 +139,142 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_a8_kernel(
 
   for (int g0 = share_beg; g0 < share_end; g0 += SHARE) {
     const int n = min(SHARE, share_end - g0);
-    // Activation codes first (their wait then covers them alone): 16-byte
-    // chunks c = (m, group u, 16 columns h), clamped to the last real chunk.
-    // Chunk c is row c / (8 SHARE), a division by a constant (a division by
-    // the round's own chunk count costs some 20 vector instructions per
-    // chunk); chunks past a short round's groups take a copy of the row's
-    // last chunk.
-    constexpr int kRowChunks = SHARE * 8;
-    constexpr int kXSteps = (MR * kRowChunks + 63) / 64;
-    const int xlast = n * 8 - 1;
-    auto chunk = [&](int ln, int j, int& m, int& cc) {
-      const int c = min(ln + 64 * j, MR * kRowChunks - 1);
-      m = MR == 1 ? 0 : c / kRowChunks;
-      cc = min(c - m * kRowChunks, xlast);
-    };
-    u32x4 xv[kXSteps];
-#pragma unroll
-    for (int j = 0; j < kXSteps; ++j) {
-      int m, cc;
-      chunk(lane, j, m, cc);
-      xv[j] = *reinterpret_cast<const u32x4*>(xq + int64_t(m) * K + int64_t(g0) * kGroup + cc * 16);
-    }
-    constexpr int kMSteps = (SHARE * 16 + 63) / 64;
-    float mv[kMSteps];
-    int32_t sv[kMSteps];
-#pragma unroll
-    for (int j = 0; j < kMSteps; ++j) {
-      const int c = min(lane + 64 * j, n * 16 - 1);
-      const int u = c >> 4, m = c & 15;
-      const int64_t e = int64_t(m < MR ? m : 0) * G + g0 + u;
-      mv[j] = m < MR ? sx[e] : 0.f;
-      sv[j] = m < MR ? xsum[e] : 0;
-    }
-    __builtin_amdgcn_sched_barrier(0);
     u32x4 w[SHARE];
     uint32_t sw[SHARE], zw[SHARE];
+    auto request_weights = [&]() {
 #pragma unroll
-    for (int u = 0; u < SHARE; ++u) {
-      const int gg = g0 + min(u, n - 1);
-      w[u] = __builtin_nontemporal_load(wlane + int64_t(gg) * (kTileBytes / 16));
-      sw[u] = sword[gg * (kTileRows / 2)];
-      zw[u] = zword[gg * (kTileRows / 8)];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // Stage: chunk (m, u, h) covers columns 16h .. 16h+15 of group u, i.e.
-    // 8-column blocks b = 2h, 2h+1 with b = 4 kb + piece; block b goes to
-    // byte (kb / 2) * 64 + piece * 16 + (kb % 2) * 8 of the group's 128.
-    // The chunk indices again, from an opaque copy of the lane: kept from
-    // the loads instead, they stay live across the weight requests and
-    // spill at 16 waves.
-    int lane_o = lane;
-    asm volatile("" : "+v"(lane_o));
-#pragma unroll
-    for (int j = 0; j < kXSteps; ++j) {
-      int m, cc;
-      chunk(lane_o, j, m, cc);
-      const int u = cc >> 3, h = cc & 7;
-      unsigned char* dst = slice + (m * SHARE + u) * kGroup;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int b = 2 * h + half, kb = b >> 2, pc = b & 3;
-        const u32x2 v = interleave_codes(xv[j][2 * half], xv[j][2 * half + 1]);
-        *reinterpret_cast<u32x2*>(dst + (kb >> 1) * 64 + pc * 16 + (kb & 1) * 8) = v;
+      for (int u = 0; u < SHARE; ++u) {
+        const int gg = g0 + min(u, n - 1);
+        w[u] = __builtin_nontemporal_load(wlane + int64_t(gg) * (kTileBytes / 16));
+        sw[u] = sword[gg * (kTileRows / 2)];
+        zw[u] = zword[gg * (kTileRows / 8)];
       }
-    }
+    };
+    if constexpr (!FQ) {
+      // Activation codes first (their wait then covers them alone): 16-byte
+      // chunks c = (m, group u, 16 columns h), clamped to the last real chunk.
+      // Chunk c is row c / (8 SHARE), a division by a constant (a division by
+      // the round's own chunk count costs some 20 vector instructions per
+      // chunk); chunks past a short round's groups take a copy of the row's
+      // last chunk.
+      constexpr int kRowChunks = SHARE * 8;
+      constexpr int kXSteps = (MR * kRowChunks + 63) / 64;
+      const int xlast = n * 8 - 1;
+      auto chunk = [&](int ln, int j, int& m, int& cc) {
+        const int c = min(ln + 64 * j, MR * kRowChunks - 1);
+        m = MR == 1 ? 0 : c / kRowChunks;
+        cc = min(c - m * kRowChunks, xlast);
+      };
+      u32x4 xv[kXSteps];
 #pragma unroll
-    for (int j = 0; j < kMSteps; ++j) {
-      const int c = min(lane + 64 * j, n * 16 - 1);
-      ssx[c] = mv[j];
-      ssum[c] = sv[j];
+      for (int j = 0; j < kXSteps; ++j) {
+        int m, cc;
+        chunk(lane, j, m, cc);
+        xv[j] = *reinterpret_cast<const u32x4*>(xq + int64_t(m) * K + int64_t(g0) * kGroup + cc * 16);
+      }
+      constexpr int kMSteps = (SHARE * 16 + 63) / 64;
+      float mv[kMSteps];
+      int32_t sv[kMSteps];
+#pragma unroll
+      for (int j = 0; j < kMSteps; ++j) {
+        const int c = min(lane + 64 * j, n * 16 - 1);
+        const int u = c >> 4, m = c & 15;
+        const int64_t e = int64_t(m < MR ? m : 0) * G + g0 + u;
+        mv[j] = m < MR ? sx[e] : 0.f;
+        sv[j] = m < MR ? xsum[e] : 0;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      request_weights();
+      __builtin_amdgcn_sched_barrier(0);
+      // Stage: chunk (m, u, h) covers columns 16h .. 16h+15 of group u, i.e.
+      // 8-column blocks b = 2h, 2h+1 with b = 4 kb + piece; block b goes to
+      // byte (kb / 2) * 64 + piece * 16 + (kb % 2) * 8 of the group's 128.
+      // The chunk indices again, from an opaque copy of the lane: kept from
+      // the loads instead, they stay live across the weight requests and
+      // spill at 16 waves.
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+#pragma unroll
+      for (int j = 0; j < kXSteps; ++j) {
+        int m, cc;
+        chunk(lane_o, j, m, cc);
+        const int u = cc >> 3, h = cc & 7;
+        unsigned char* dst = slice + (m * SHARE + u) * kGroup;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int b = 2 * h + half, kb = b >> 2, pc = b & 3;
+          const u32x2 v = interleave_codes(xv[j][2 * half], xv[j][2 * half + 1]);
+          *reinterpret_cast<u32x2*>(dst + (kb >> 1) * 64 + pc * 16 + (kb & 1) * 8) = v;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kMSteps; ++j) {
+        const int c = min(lane + 64 * j, n * 16 - 1);
+        ssx[c] = mv[j];
+        ssum[c] = sv[j];
+      }
+    } else {
+      // fp16 x of the round first: pass j, lane l takes 8 halves (l % 16)
+      // of group 4 j + l / 16 of the [MR][SHARE] slice, row gi / SHARE,
+      // group gi % SHARE (clamped to the round's last group and to the last
+      // row: duplicates recompute the same values).
+      constexpr int kPasses = (MR * SHARE + 3) / 4;
+      auto group_of = [&](int ln, int j, int& m, int& u) {
+        const int gi = min(4 * j + (ln >> 4), MR * SHARE - 1);
+        m = MR == 1 ? 0 : gi / SHARE;
+        u = min(gi - m * SHARE, n - 1);
+      };
+      u32x4 xh[kPasses];
+#pragma unroll
+      for (int j = 0; j < kPasses; ++j) {
+        int m, u;
+        group_of(lane, j, m, u);
+        xh[j] = *reinterpret_cast<const u32x4*>(xf + int64_t(m) * K + int64_t(g0 + u) * kGroup + (lane & 15) * 8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      request_weights();
+      __builtin_amdgcn_sched_barrier(0);
+      // Rows past M: scale and code sum 0.
+#pragma unroll
+      for (int jj = 0; jj < (SHARE * 16 + 63) / 64; ++jj) {
+        const int c = lane + 64 * jj;
+        if (c < SHARE * 16 && (c & 15) >= MR) {
+          ssx[c] = 0.f;
+          ssum[c] = 0;
+        }
+      }
+      int lane_o = lane;
+      asm volatile("" : "+v"(lane_o));
+      const int h8 = lane & 15;  // 8-column block of the group
+#pragma unroll
+      for (int j = 0; j < kPasses; ++j) {
+        int m, u;
+        group_of(lane_o, j, m, u);
+        float a[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const half2_t h2 = as_h2(xh[j][k]);
+          a[2 * k] = float(h2.x);
+          a[2 * k + 1] = float(h2.y);
+          amax = fmaxf(amax, fmaxf(fabsf(a[2 * k]), fabsf(a[2 * k + 1])));
+        }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        const float scale = amax / 127.0f;
+        uint32_t d0, d1;
+        int sum;
+        quantize8(a, scale, d0, d1, sum);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+        const int kb = h8 >> 2, pc = h8 & 3;
+        *reinterpret_cast<u32x2*>(slice + (m * SHARE + u) * kGroup + (kb >> 1) * 64 + pc * 16 + (kb & 1) * 8) =
+            interleave_codes(d0, d1);
+        if (h8 == 0) {
+          ssx[u * 16 + m] = scale;
+          ssum[u * 16 + m] = sum;
+        }
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
@@ -243,12 +335,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_a8_kernel(
   }
 }
 
-template <int MR, int WAVES, int SHARE>
+template <int MR, int WAVES, int SHARE, bool FQ>
 hipError_t launch_a8_typed(int N, int K, const void* wq, const void* scales, const void* zeros, const void* xq,
                            const void* sx, const void* xsum, void* y, hipStream_t stream) {
   constexpr size_t lds = gemv_a8_lds_bytes(MR, WAVES, SHARE);
   static_assert(lds <= kMaxLdsBytes, "instantiation beyond the LDS of a workgroup");
-  auto* kernel = &gemv_a8_kernel<MR, WAVES, SHARE>;
+  auto* kernel = &gemv_a8_kernel<MR, WAVES, SHARE, FQ>;
   if constexpr (lds > kDefaultLdsLimit) {
     static std::atomic<uint64_t> raised{0};  // devices on which this instantiation's limit is raised
     const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(kernel), lds, raised);
@@ -257,17 +349,17 @@ hipError_t launch_a8_typed(int N, int K, const void* wq, const void* scales, con
   const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;
   return launch_kernel(kernel, dim3(unsigned(row_tiles)), dim3(WAVES * 64), lds, stream, N, K,
                        static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
-                       static_cast<const uint8_t*>(zeros), static_cast<const int8_t*>(xq),
+                       static_cast<const uint8_t*>(zeros), xq,
                        static_cast<const float*>(sx), static_cast<const int32_t*>(xsum), static_cast<_Float16*>(y));
 }
 
-template <int MR>
+template <int MR, bool FQ>
 hipError_t launch_a8_m(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales, const void* zeros,
                        const void* xq, const void* sx, const void* xsum, void* y, hipStream_t stream) {
 #define W4A16_A8_CASE(W, S)                                                                      \
-  if constexpr (a8_instantiated(MR, W, S)) {                                                     \
+  if constexpr (FQ ? a8_fused_instantiated(MR, W, S) : a8_instantiated(MR, W, S)) {              \
     if (plan.waves == W && plan.share == S)                                                      \
-      return launch_a8_typed<MR, W, S>(N, K, wq, scales, zeros, xq, sx, xsum, y, stream);        \
+      return launch_a8_typed<MR, W, S, FQ>(N, K, wq, scales, zeros, xq, sx, xsum, y, stream);    \
   }
 #define W4A16_A8_SHARES(W) W4A16_A8_CASE(W, 4) W4A16_A8_CASE(W, 7) W4A16_A8_CASE(W, 10)
   W4A16_A8_SHARES(1) W4A16_A8_SHARES(2) W4A16_A8_SHARES(4) W4A16_A8_SHARES(8) W4A16_A8_SHARES(16)
@@ -289,14 +381,30 @@ int launch_gemv_a8(int M, int N, int K, const LaunchPlan& plan, const void* wq, 
                    const void* zeros, const void* xq, const void* sx, const void* xsum, void* y, void* stream_ptr) {
   const hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   switch (M) {
-    case 1: return int(dev::launch_a8_m<1>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
-    case 2: return int(dev::launch_a8_m<2>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
-    case 3: return int(dev::launch_a8_m<3>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
-    case 4: return int(dev::launch_a8_m<4>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
-    case 5: return int(dev::launch_a8_m<5>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
-    case 6: return int(dev::launch_a8_m<6>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
-    case 7: return int(dev::launch_a8_m<7>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
-    case 8: return int(dev::launch_a8_m<8>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 1: return int(dev::launch_a8_m<1, false>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 2: return int(dev::launch_a8_m<2, false>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 3: return int(dev::launch_a8_m<3, false>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 4: return int(dev::launch_a8_m<4, false>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 5: return int(dev::launch_a8_m<5, false>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 6: return int(dev::launch_a8_m<6, false>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 7: return int(dev::launch_a8_m<7, false>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    case 8: return int(dev::launch_a8_m<8, false>(N, K, plan, wq, scales, zeros, xq, sx, xsum, y, stream));
+    default: return int(hipErrorInvalidValue);
+  }
+}
+
+int launch_gemv_a8_fused(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
+                         const void* zeros, const void* x, void* y, void* stream_ptr) {
+  const hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  switch (M) {
+    case 1: return int(dev::launch_a8_m<1, true>(N, K, plan, wq, scales, zeros, x, nullptr, nullptr, y, stream));
+    case 2: return int(dev::launch_a8_m<2, true>(N, K, plan, wq, scales, zeros, x, nullptr, nullptr, y, stream));
+    case 3: return int(dev::launch_a8_m<3, true>(N, K, plan, wq, scales, zeros, x, nullptr, nullptr, y, stream));
+    case 4: return int(dev::launch_a8_m<4, true>(N, K, plan, wq, scales, zeros, x, nullptr, nullptr, y, stream));
+    case 5: return int(dev::launch_a8_m<5, true>(N, K, plan, wq, scales, zeros, x, nullptr, nullptr, y, stream));
+    case 6: return int(dev::launch_a8_m<6, true>(N, K, plan, wq, scales, zeros, x, nullptr, nullptr, y, stream));
+    case 7: return int(dev::launch_a8_m<7, true>(N, K, plan, wq, scales, zeros, x, nullptr, nullptr, y, stream));
+    case 8: return int(dev::launch_a8_m<8, true>(N, K, plan, wq, scales, zeros, x, nullptr, nullptr, y, stream));
     default: return int(hipErrorInvalidValue);
   }
 }

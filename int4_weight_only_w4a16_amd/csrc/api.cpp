@@ -186,6 +186,21 @@ extern "C" int w4a16_gemv_a8(int M, int N, int K, const void* Wq, const void* sc
   return W4A16_OK;
 }
 
+extern "C" int w4a16_gemv_a8_fused(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,
+                                   const void* x, void* y, void* stream) {
+  const int rc = check_shape(M, N, K);
+  if (rc != W4A16_OK) return rc == 1 ? W4A16_OK : rc;
+  if (!pointers_ok({Wq, scales, zeros, x, y})) return W4A16_EINVAL;
+  // The separate path's waves (so the same sums in the same order), in
+  // shares short enough for the round's x to sit in registers.
+  w4a16::LaunchPlan plan = plan_a8(M, N, K);
+  while (plan.share > 4 && !w4a16::a8_fused_instantiated(M, plan.waves, plan.share))
+    plan.share = plan.share == 10 ? 7 : 4;
+  if (!w4a16::a8_fused_instantiated(M, plan.waves, plan.share)) return W4A16_EUNSUPPORTED;
+  if (w4a16::launch_gemv_a8_fused(M, N, K, plan, Wq, scales, zeros, x, y, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
+
 extern "C" int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,
                           const void* x, void* y, void* stream) {
   const int rc = check_shape(M, N, K);

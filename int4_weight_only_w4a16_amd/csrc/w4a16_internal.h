@@ -152,9 +152,20 @@ constexpr bool a8_instantiated(int mr, int waves, int share) {
          (share == 4 || share == 7 || share == 10) && !(waves == 16 && share == 10 && mr >= 4) &&
          gemv_a8_lds_bytes(mr, waves, share) <= kMaxLdsBytes;
 }
+// The fused-quantization variant holds a round's fp16 x in registers (one
+// 16-byte load per lane per 4 groups of the [M][share] slice): built where
+// M * share <= 40; in 1024-thread workgroups (128 registers per lane), for
+// two or more rows, with 4-tile shares, or 7-tile shares up to 3 rows
+// (beyond that the compiler spills).
+constexpr bool a8_fused_instantiated(int mr, int waves, int share) {
+  return a8_instantiated(mr, waves, share) && mr * share <= 40 &&
+         !(waves == 16 && mr >= 2 && (share == 10 || (share == 7 && mr >= 4)));
+}
 int launch_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream);
 int launch_gemv_a8(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
                    const void* zeros, const void* xq, const void* sx, const void* xsum, void* y, void* stream);
+int launch_gemv_a8_fused(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
+                         const void* zeros, const void* x, void* y, void* stream);
 // The GEMM addresses a workgroup's (at most 128) rows of x with 32-bit
 // element offsets (below 128 K), so K stays under 2^25.
 constexpr int kGemmMaxK = 1 << 25;

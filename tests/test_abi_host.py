@@ -234,6 +234,12 @@ def test_device_entry_points_reject_before_launch():
     assert L.w4a16_gemv_a8(1, 0, 128, *a8, None) == w.W4A16_OK
     assert L.w4a16_gemv_a8(1, 16, 128, fake, fake, fake, fake, fake, fake + 4, fake, None) == w.W4A16_EINVAL
     assert L.w4a16_gemv_a8(1, 16, 128, fake, fake, fake, fake, None, fake, fake, None) == w.W4A16_EINVAL
+    # the same with the quantization fused (fp16 x)
+    assert L.w4a16_gemv_a8_fused(1, 16, 200, *ptrs, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemv_a8_fused(9, 16, 128, *ptrs, None) == w.W4A16_EUNSUPPORTED
+    assert L.w4a16_gemv_a8_fused(0, 16, 128, *ptrs, None) == w.W4A16_OK
+    assert L.w4a16_gemv_a8_fused(1, 16, 128, fake, fake, fake, fake + 2, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemv_a8_fused(1, 16, 128, fake, fake, None, fake, fake, None) == w.W4A16_EINVAL
     # dequant hook
     assert L.w4a16_dequant_f32(16, 200, fake, fake, fake, fake, None) == w.W4A16_EINVAL
     assert L.w4a16_dequant_f32(0, 128, None, None, None, None, None) == w.W4A16_OK

@@ -2,7 +2,9 @@
 w4a16_gemv_a8) through the C ABI against the oracle: the codes, scales and
 code sums bit for bit (the rounding decision is taken in fp32 on both
 sides), and y within the workload's bound around the oracle's integer-sum
-product, 2e-3 * sum_g |term| + 1e-5."""
+product, 2e-3 * sum_g |term| + 1e-5. The fused variant (w4a16_gemv_a8_fused,
+quantization inside the GEMV launch) must equal the two launches bit for
+bit."""
 import numpy as np
 import pytest
 
@@ -117,3 +119,22 @@ def test_gemv_a8_close_to_fp16_path():
     ya8 = _gemv_a8(p, xq, sx, xs).view(np.float16).astype(np.float64)
     yfp = p.gemv().view(np.float16).astype(np.float64)
     assert np.sqrt(((ya8 - yfp) ** 2).mean()) < 0.02 * np.sqrt((yfp ** 2).mean())
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES + [(3, 3584, 18944), (8, 5120, 17408)])
+def test_gemv_a8_fused_equals_two_launches(M, N, K):
+    """One launch, fp16 x in: y bit-identical to act_quant_i8 + gemv_a8 (same
+    codes from the same fp32 operations, same sums in the same order), on
+    the workload's activations and on the awkward groups."""
+    torch, dev = torch_dev()
+    for special in (False, True):
+        _say("fused", M, N, K, "special" if special else "")
+        x = _special_activations(M, K, seed=M + K) if special else None
+        p = Problem(M, N, K, seed=M + 2 * N + K, x=x)
+        xq, sx, xs = _quantize_on_gpu(M, K, p.x_d)
+        y2 = _gemv_a8(p, xq, sx, xs)
+        y1 = p.new_y()
+        w.w4a16_gemv_a8_fused(M, N, K, p.wq_d, p.sp_d, p.zp_d, p.x_d, y1)
+        torch.cuda.synchronize()
+        y1 = y1.cpu().numpy().view(np.uint16)
+        assert np.array_equal(y1, y2), (M, N, K, special, int((y1 != y2).sum()))

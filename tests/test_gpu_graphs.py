@@ -42,6 +42,7 @@ def test_all_entry_points_in_one_graph():
         "sx": torch.empty((2, G), dtype=torch.float32, device=dev),
         "xsum": torch.empty((2, G), dtype=torch.int32, device=dev),
         "a8": torch.empty((2, 777), dtype=torch.int16, device=dev),
+        "a8_fused": torch.empty((2, 777), dtype=torch.int16, device=dev),
         "gemm": torch.empty((70, 300), dtype=torch.int16, device=dev),
         "gemm_splitk": torch.empty((70, 300), dtype=torch.int16, device=dev),
         "dequant": torch.empty((300, 640), dtype=torch.float16, device=dev),
@@ -55,6 +56,7 @@ def test_all_entry_points_in_one_graph():
         w.w4a16_act_quant_i8(2, pa.K, pa.x_d, outs["xq"], outs["sx"], outs["xsum"], stream=stream)
         w.w4a16_gemv_a8(2, 777, pa.K, pa.wq_d, pa.sp_d, pa.zp_d, outs["xq"], outs["sx"], outs["xsum"],
                         outs["a8"], stream=stream)
+        w.w4a16_gemv_a8_fused(2, 777, pa.K, pa.wq_d, pa.sp_d, pa.zp_d, pa.x_d, outs["a8_fused"], stream=stream)
         w.w4a16_gemm(70, 300, 640, pm.wq_d, pm.sp_d, pm.zp_d, pm.x_d, outs["gemm"], stream=stream)
         w.w4a16_gemm_splitk(70, 300, 640, 3, pm.wq_d, pm.sp_d, pm.zp_d, pm.x_d, outs["gemm_splitk"], ws_m,
                             stream=stream)
@@ -101,3 +103,4 @@ def test_all_entry_points_in_one_graph():
     pg.check(eager["gemv"].view(np.uint16))
     pg.check(eager["splitk"].view(np.uint16))
     pm.check(eager["gemm_splitk"].view(np.uint16))
+    assert np.array_equal(eager["a8_fused"], eager["a8"])
