@@ -1,7 +1,10 @@
 /*
  * w4a16.h -- C ABI of libw4a16.so: batch-1 (M <= 8) matrix-vector product
  * y = W x with 4-bit weights, dequantized inside the kernel (W4A16 GEMV),
- * for AMD Instinct MI355X (gfx950).
+ * for AMD Instinct MI355X (gfx950); with it the host packer and quantizer,
+ * a split-K GEMV, the fused gate/up + SwiGLU GEMV, an INT8-activation
+ * variant, a matrix-core GEMM for many activation rows (prefill) and
+ * standalone dequantization.
  *
  * The operation. W is N x K (N output features, K input features, row-major
  * like the matrix of the row-per-output GEMV of "CodeAlign-Runtime", Level 1).
@@ -47,7 +50,8 @@ extern "C" {
 
 #define W4A16_OK 0
 #define W4A16_EINVAL (-1)      /* bad shape, null or misaligned pointer, bad value */
-#define W4A16_EUNSUPPORTED (-2) /* M > 8: prefill-sized batches are not served */
+#define W4A16_EUNSUPPORTED (-2) /* M > 8 for a GEMV (w4a16_gemm serves more rows), or a shape
+                                   outside what an entry point documents it supports */
 #define W4A16_ELAYOUT (-3)     /* layout ID mismatch (see w4a16_layout_id) */
 #define W4A16_EHIP (-4)        /* the HIP runtime refused a launch */
 
