@@ -277,7 +277,10 @@ def run_configs(torch, seed):
     repeated in one captured graph of at least 64 launches (inputs stay in
     the 256 MB last-level cache where they fit). Cold: distinct weight copies
     totalling at least 1 GiB, each set once per graph replay, so every
-    replay streams from HBM.
+    replay streams from HBM. Every graph is timed in 5 rounds (5 replays
+    each), the measurements in a seeded random order within each round; a
+    row reports the median and the mean of its rounds and flags a mean more
+    than 15% away from the median.
     Configuration 4 (the whole 7B step) is the default bench line."""
     import int4_weight_only_w4a16_amd as w
     dev = torch.device("cuda:0")
@@ -307,7 +310,7 @@ def run_configs(torch, seed):
                     else:
                         w.w4a16_gemv(M, N, K, wq, sc, zp, x, y, stream=stream)
 
-    def timed_graph(sets, ws, M, reps_in_graph, replays):
+    def capture(sets, ws, M, reps_in_graph):
         stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(stream):
             launch(sets, ws, M, 1)
@@ -316,6 +319,9 @@ def run_configs(torch, seed):
             with torch.cuda.graph(g, stream=stream):
                 launch(sets, ws, M, reps_in_graph)
         torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, launches_per_replay_in_sets, replays):
         for _ in range(2):
             g.replay()
         torch.cuda.synchronize()
@@ -326,7 +332,7 @@ def run_configs(torch, seed):
                 g.replay()
             e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (replays * reps_in_graph * len(sets))  # µs per set
+        return e0.elapsed_time(e1) * 1e3 / (replays * launches_per_replay_in_sets)  # µs per set
 
     configs = [
         ("1: single GEMV 896x896", [("single", 896, 896)], (1,)),
@@ -339,29 +345,42 @@ def run_configs(torch, seed):
         ("3: Qwen2.5-7B layer (qkv, o, gate_up, down)", list(synthetic.QWEN7B_LAYER), (1,)),
         ("5: 27B-class verify pair (up 17408x5120, down 5120x17408)", list(synthetic.VERIFY27B), synthetic.VERIFY_M),
     ]
-    rows = []
+    import random
+    rows, items = [], []  # items: (row index, "warm"/"cold", graph, sets per replay, kept buffers)
     for ci, (label, shapes, Ms) in enumerate(configs):
         for M in Ms:
             nbytes = sum(algorithmic_bytes(M, N, K) for _, N, K in shapes)
             launches = len(shapes)
-            out = {"config": label, "M": M, "launches_per_set": launches, "bytes_per_set": nbytes}
+            rows.append({"config": label, "M": M, "launches_per_set": launches, "bytes_per_set": nbytes})
             sets, ws = build(shapes, M, 1, 100 * ci)
             reps = -(-64 // launches)  # at least 64 launches per replay (a replay has a fixed cost)
-            us = timed_graph(sets, ws, M, reps, 5)
-            out["warm_us"] = round(us, 2)
-            out["warm_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
-            del sets, ws
+            items.append((len(rows) - 1, "warm", capture(sets, ws, M, reps), reps, (sets, ws)))
             copies = -(-GiB // nbytes)
+            rows[-1]["cold_copies"] = copies
             sets, ws = build(shapes, M, copies, 100 * ci)
-            us = timed_graph(sets, ws, M, 1, 5)
-            out["cold_copies"] = copies
-            out["cold_us"] = round(us, 2)
-            out["cold_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
-            out["cold_frac_of_hbm_peak"] = round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
-            del sets, ws
-            torch.cuda.empty_cache()
-            rows.append(out)
-            print(json.dumps(out), flush=True)
+            items.append((len(rows) - 1, "cold", capture(sets, ws, M, 1), copies, (sets, ws)))
+    rng = random.Random(seed)
+    times = {}
+    for rnd in range(5):
+        order = list(range(len(items)))
+        rng.shuffle(order)
+        for k in order:
+            r, kind, g, per, _ = items[k]
+            times.setdefault((r, kind), []).append(time_graph(g, per, 5))
+    for r, out in enumerate(rows):
+        nbytes = out["bytes_per_set"]
+        for kind in ("warm", "cold"):
+            t = sorted(times[(r, kind)])
+            med, mean = t[len(t) // 2], sum(t) / len(t)
+            out[f"{kind}_us"] = round(med, 2)
+            out[f"{kind}_us_mean"] = round(mean, 2)
+            out[f"{kind}_GBps"] = round(nbytes / (med * 1e-6) / 1e9, 1)
+            out[f"{kind}_mean_median_divergence_over_15pct"] = abs(mean - med) > 0.15 * med
+        out["cold_frac_of_hbm_peak"] = round(nbytes / (out["cold_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        out["rounds"] = 5
+        print(json.dumps(out), flush=True)
+    del items
+    torch.cuda.empty_cache()
     return rows
 
 
