@@ -1,7 +1,9 @@
 """GPU parity of the W4A16 GEMM for many activation rows (w4a16_gemm, and
 w4a16_gemm_splitk) and of its weights (w4a16_dequant_f16), through the C
 ABI, against the fp64 oracle. The shapes cover each workgroup height (16,
-32, 64 and 128 rows: M <= 16, <= 32, <= 64 and above) with ragged M and N.
+32, 64 and 128 rows: M <= 16, <= 32, <= 64 and above) with ragged M and N,
+and both tile orders (the XCD band order needs 4k m blocks and 8k tiles:
+500x250 and 1000x300 here, and the prefill-sized calls).
 
 Bars: every output within the workload bound 2e-3 * sum|w x| + 1e-5 of the
 oracle's fp64 product; and, tighter, within fp32 accumulation and fp16
@@ -47,7 +49,7 @@ def check_rounded_weights(p, y, rows=None):
 @pytest.mark.parametrize("M,N,K", [(9, 37, 384), (16, 896, 896), (130, 200, 640), (128, 128, 128),
                                    (300, 1000, 1152), (257, 4608, 3584), (64, 301, 256), (200, 1031, 128),
                                    (1, 50, 256), (17, 300, 640), (32, 129, 384), (33, 257, 1280), (48, 160, 128),
-                                   (65, 144, 512)])
+                                   (65, 144, 512), (500, 250, 384), (1000, 300, 256)])
 def test_gemm_against_oracle(M, N, K):
     _say("shape", M, N, K)
     p = Problem(M, N, K, seed=M + N)
