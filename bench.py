@@ -432,11 +432,20 @@ def main():
     value = step.bytes * args.steps / elapsed / 1e9
     eager_us = step.time_eager(max(3, args.steps // 10)) / max(3, args.steps // 10) * 1e6
 
+    def median_rounds(g, reps, rounds=5):
+        """Median over `rounds` timings of `reps` replays, after one untimed
+        pass of as many, so that no single round (the first after the eager
+        timing, which leaves the device idle between launches, say) sets the
+        figure. Returns (median, fastest, slowest) in seconds."""
+        step.time_graph(g, reps, 3)
+        t = sorted(step.time_graph(g, reps, 3) for _ in range(rounds))
+        return t[len(t) // 2], t[0], t[-1]
+
     # Dominant kernel: the gate+up GEMV (58% of the step's bytes), 28 distinct
     # weight sets back to back in one graph.
     dom = step.capture(only="gate_up_proj")
     reps = args.roofline_reps
-    dom_s = step.time_graph(dom, reps, 3)
+    dom_s, dom_fast_s, dom_slow_s = median_rounds(dom, reps)
     n_dom = synthetic.QWEN7B_LAYERS
     _, Nd, Kd = synthetic.QWEN7B_LAYER[2]
     dom_bytes = algorithmic_bytes(1, Nd, Kd)
@@ -467,26 +476,26 @@ def main():
     # Variant (reported beside, never as `value`): gate+up with the SwiGLU
     # epilogue fused, y = silu(g) * u of width 18944, same weight bytes.
     fused = step.capture(only="gate_up_proj", swiglu=True)
-    fused_s = step.time_graph(fused, reps, 3)
+    fused_s = median_rounds(fused, reps)[0]
     fused_us = fused_s / (reps * n_dom) * 1e6
     fused_bytes = dom_bytes - 2 * Nd + 2 * (Nd // 2)
     fused_step = step.capture(swiglu=True)
     fused_step_s = step.time_graph(fused_step, args.steps, args.warmup)
     unfused = step.capture(only="gate_up_proj", torch_act=True)
-    unfused_us = step.time_graph(unfused, reps, 3) / (reps * n_dom) * 1e6
+    unfused_us = median_rounds(unfused, reps)[0] / (reps * n_dom) * 1e6
     del fused, fused_step, unfused
 
     # Variant: INT8 activations (the dp4a path of the H100 runtime page, here
     # on the integer matrix cores): a quantize launch before each GEMV.
     a8_gate_up = step.capture(only="gate_up_proj", a8="both")
-    a8_gate_up_us = step.time_graph(a8_gate_up, reps, 3) / (reps * n_dom) * 1e6
+    a8_gate_up_us = median_rounds(a8_gate_up, reps)[0] / (reps * n_dom) * 1e6
     a8_gemv = step.capture(only="gate_up_proj", a8="gemv")
-    a8_gemv_us = step.time_graph(a8_gemv, reps, 3) / (reps * n_dom) * 1e6
+    a8_gemv_us = median_rounds(a8_gemv, reps)[0] / (reps * n_dom) * 1e6
     a8_step = step.capture(a8="both")
     a8_step_us = step.time_graph(a8_step, args.steps, args.warmup) / args.steps * 1e6
     # The quantization fused into the GEMV: one launch per GEMV again.
     a8f_gate_up = step.capture(only="gate_up_proj", a8="fused")
-    a8f_gate_up_us = step.time_graph(a8f_gate_up, reps, 3) / (reps * n_dom) * 1e6
+    a8f_gate_up_us = median_rounds(a8f_gate_up, reps)[0] / (reps * n_dom) * 1e6
     a8f_step = step.capture(a8="fused")
     a8f_step_us = step.time_graph(a8f_step, args.steps, args.warmup) / args.steps * 1e6
     del a8_gate_up, a8_gemv, a8_step, a8f_gate_up, a8f_step
@@ -623,6 +632,8 @@ def main():
             "traffic": load_traffic(),
             "bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_us, 3),
+            "avg_launch_us_fastest_slowest_round": [round(dom_fast_s / (reps * n_dom) * 1e6, 3),
+                                                    round(dom_slow_s / (reps * n_dom) * 1e6, 3)],
             "measured_read_ceiling_GBps": round(read_ceiling, 1),
             "frac_of_measured_read_ceiling": round(achieved / read_ceiling, 4),
         },
