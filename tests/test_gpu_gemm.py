@@ -2,8 +2,9 @@
 w4a16_gemm_splitk) and of its weights (w4a16_dequant_f16), through the C
 ABI, against the fp64 oracle. The shapes cover each workgroup height (16,
 32, 64 and 128 rows: M <= 16, <= 32, <= 64 and above) with ragged M and N,
-and both tile orders (the XCD band order needs 4k m blocks and 8k tiles:
-500x250 and 1000x300 here, and the prefill-sized calls).
+and both tile orders (the XCD band order needs 4k m blocks and 8k tiles per
+split: 500x250 and 1000x300 here, split in 3 at 500x250, the chosen split
+at M = 512 on 3584x18944, and the prefill-sized calls).
 
 Bars: every output within the workload bound 2e-3 * sum|w x| + 1e-5 of the
 oracle's fp64 product; and, tighter, within fp32 accumulation and fp16
@@ -80,7 +81,7 @@ def test_gemm_prefill_size_sampled(M, N, K):
 @pytest.mark.parametrize("M,N,K,splits", [(9, 37, 384, 3), (16, 301, 4864, 8), (64, 1031, 2560, 5),
                                           (130, 200, 1408, 11), (128, 128, 128 * 31, 31), (70, 300, 640, 2),
                                           (257, 160, 1024, 4), (1, 16, 256, 2), (30, 515, 2048, 6),
-                                          (40, 200, 1024, 3)])
+                                          (40, 200, 1024, 3), (500, 250, 1536, 3)])
 def test_gemm_splitk_against_oracle(M, N, K, splits):
     """K split across workgroups: the same bars as the unsplit GEMM (each
     partial enters the exact fixed-point sum within 2^-25), the workspace
@@ -97,7 +98,7 @@ def test_gemm_splitk_against_oracle(M, N, K, splits):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 3584, 18944), (64, 4608, 3584), (100, 3584, 3584), (256, 3584, 18944),
-                                   (8, 3584, 18944), (32, 4608, 3584)])
+                                   (8, 3584, 18944), (32, 4608, 3584), (512, 3584, 18944)])
 def test_gemm_splitk_chosen_sampled(M, N, K):
     """Small-M prefill shapes at the split count the library chooses: a
     sample of weight rows (tile edges included) against the oracle."""
