@@ -302,7 +302,7 @@ int w4a16_gemv_a8_fused(int M, int N, int K, const void* Wq, const void* scales,
  * With B the workgroup's rows (16, 32, 64 or 128: the fewest of these that
  * cover M) and W the number of B x 128 output tiles: 1 from 256 tiles on;
  * where K holds >= 96 groups, min(8, 256 / W), or min(16, 512 / W) for
- * B = 16; where it holds fewer, 4 if W <= 40 and M <= 96 (or W <= 32 and
+ * B = 16, and 3 where that gives 1 and 3 W <= 512; where it holds fewer, 4 if W <= 40 and M <= 96 (or W <= 32 and
  * M <= 128), else 1 (each split adds a pass of atomics over its tile, which
  * a short K does not pay for once the tile holds many rows); never above
  * K/512 or 31. It depends on M, and the GEMM makes no batch-invariance

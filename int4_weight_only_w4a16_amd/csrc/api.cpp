@@ -128,8 +128,10 @@ w4a16::LaunchPlan plan_swiglu(int K) {
 // its output tile, whose cost grows with the tile's rows, against
 // K/128 / splits groups of products. A long K (>= 96 groups) pays for it up
 // to about one workgroup per compute unit (two for 16-row tiles) and 8
-// splits (16 for 16-row tiles); a short K takes 4 while the grid is small
-// and the tile holds at most 96 rows (128 on a grid of at most 32 tiles).
+// splits (16 for 16-row tiles), or 3 splits for two per CU where one split
+// per CU would leave the grid unsplit; a short K takes 4 while the grid is
+// small and the tile holds at most 96 rows (128 on a grid of at most 32
+// tiles).
 int choose_gemm_splits(int M, int N, int K) {
   const int groups = K / W4A16_GROUP;
   const int bm = 16 * w4a16::gemm_m_blocks(M);
@@ -140,6 +142,10 @@ int choose_gemm_splits(int M, int N, int K) {
     splits = (bm == 16 ? 512 : 256) / wgs;
     const int64_t cap = bm == 16 ? 16 : 8;
     splits = splits > cap ? cap : splits;
+    // 129 to 170 tiles: 3 splits give about two workgroups per CU, where 2
+    // leave some CUs one (3584x18944 at M = 768: 141 us, against 164 us
+    // unsplit and 164 us in 2).
+    if (splits == 1 && 3 * wgs <= 512) splits = 3;
   } else {
     const int rows = M < 128 ? M : 128;
     splits = wgs <= 40 && (rows <= 96 || wgs <= 32) ? 4 : 1;

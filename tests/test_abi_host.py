@@ -213,7 +213,8 @@ def test_device_entry_points_reject_before_launch():
     assert L.w4a16_gemm_splitk(64, 16, 768, 3, fake, fake, fake, fake + 2, fake, fake, wsg, None) == w.W4A16_EINVAL
     assert L.w4a16_gemm_splitk(64, 16, 768, 3, *ptrs, None, wsg, None) == w.W4A16_EINVAL
     for M, N, K, want in [(16, 3584, 18944, 16), (17, 3584, 18944, 8), (64, 3584, 18944, 8),
-                          (256, 3584, 18944, 4), (512, 3584, 18944, 2), (1024, 3584, 18944, 1),
+                          (256, 3584, 18944, 4), (512, 3584, 18944, 2), (640, 3584, 18944, 3),
+                          (768, 3584, 18944, 3), (1024, 3584, 18944, 1),
                           (16, 37888, 3584, 1), (16, 4608, 3584, 4), (64, 4608, 3584, 4), (96, 4608, 3584, 4),
                           (128, 4608, 3584, 1), (128, 3584, 3584, 4), (256, 3584, 3584, 1), (16, 200, 1024, 2),
                           (1, 16, 128, 1), (16, 16, 200, 0), (0, 16, 128, 0), (16, 16, 1 << 25, 0)]:

@@ -98,7 +98,7 @@ def test_gemm_splitk_against_oracle(M, N, K, splits):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 3584, 18944), (64, 4608, 3584), (100, 3584, 3584), (256, 3584, 18944),
-                                   (8, 3584, 18944), (32, 4608, 3584), (512, 3584, 18944)])
+                                   (8, 3584, 18944), (32, 4608, 3584), (512, 3584, 18944), (768, 3584, 18944)])
 def test_gemm_splitk_chosen_sampled(M, N, K):
     """Small-M prefill shapes at the split count the library chooses: a
     sample of weight rows (tile edges included) against the oracle."""
