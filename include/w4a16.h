@@ -228,6 +228,35 @@ int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq, const voi
                       void* stream);
 
 /*
+ * Bytes of the device array behind w4a16_gemv_splitk_noalloc: 2 MiB per GPU,
+ * one uint64 accumulation word per output, so M * N <= 262144.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (2u << 20)
+
+/*
+ * w4a16_gemv_splitk for callers that cannot allocate device memory (code
+ * under graph capture, serving loops or harnesses that forbid hipMalloc):
+ * the same split-K GEMV, with the same plan and kernel and so the same bits,
+ * but its accumulation words live in a file-scope device array of the
+ * library (W4A16_NOALLOC_SCRATCH_BYTES per GPU, held by each GPU the library
+ * runs on until the process ends) instead of a caller workspace. The caller
+ * still passes the inputs and the output. The call allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine. The first call on a
+ * device looks the array up (hipGetSymbolAddress, with that device current)
+ * and clears it with a fill kernel on `stream`; every completed call leaves
+ * it zero again. Calls on one GPU share that GPU's array: calls that overlap
+ * in time on one GPU (different streams, or different host threads without
+ * ordering) race and give wrong results; order them on one stream.
+ *   M, N, K, splits, Wq, scales, zeros, x, y: as w4a16_gemv_splitk;
+ *   splits == 1 is w4a16_gemv and does not touch the array.
+ * Errors: as w4a16_gemv_splitk; W4A16_EUNSUPPORTED when M * N exceeds
+ * W4A16_NOALLOC_SCRATCH_BYTES / 8 (use w4a16_gemv_splitk with a workspace);
+ * W4A16_EHIP when the array cannot be looked up or cleared.
+ */
+int w4a16_gemv_splitk_noalloc(int M, int N, int K, int splits, const void* Wq, const void* scales,
+                              const void* zeros, const void* x, void* y, void* stream);
+
+/*
  * W4A16 GEMM for many activation rows (prefill, M > 8), on the matrix cores:
  * y[M][N] = x[M][K] W^T. Wq, scales, zeros: device buffers in layout ID 2;
  * x: device fp16 [M][K]; y: device fp16 [M][N]; any M >= 1 (for M <= 8

@@ -26,7 +26,7 @@ MAX_M = 8
 EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_quantize",
            "w4a16_unpack",
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
-           "w4a16_gemv_splitk", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemv_a8_fused", "w4a16_gemm", "w4a16_gemm_splitk_choose",
+           "w4a16_gemv_splitk", "w4a16_gemv_splitk_noalloc", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemv_a8_fused", "w4a16_gemm", "w4a16_gemm_splitk_choose",
            "w4a16_gemm_splitk", "w4a16_dequant_f16",
            "w4a16_dequant_f32", "w4a16_read_probe", "w4a16_strerror")
 
@@ -72,6 +72,7 @@ def lib():
         L.w4a16_splitk_choose.restype = _i
         L.w4a16_splitk_choose.argtypes = [_i, _i, _i]
         L.w4a16_gemv_splitk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+        L.w4a16_gemv_splitk_noalloc.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_dequant_f32.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_read_probe.argtypes = [_p, _sz, _i, _p, _p]
         L.w4a16_dequant_f16.argtypes = [_i, _i, _p, _p, _p, _p, _p]
@@ -214,6 +215,17 @@ def w4a16_gemv_splitk(M, N, K, splits, Wq, scales, zeros, x, y, workspace, ws_by
     _check(lib().w4a16_gemv_splitk(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x),
                                    _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)),
            "w4a16_gemv_splitk")
+
+
+NOALLOC_SCRATCH_BYTES = 2 << 20
+
+
+def w4a16_gemv_splitk_noalloc(M, N, K, splits, Wq, scales, zeros, x, y, stream=None):
+    """Device: w4a16_gemv_splitk with the library's own per-GPU accumulation
+    array (no workspace argument, nothing allocated; calls on one GPU must
+    not overlap in time)."""
+    _check(lib().w4a16_gemv_splitk_noalloc(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x),
+                                           _ptr(y), _stream(stream)), "w4a16_gemv_splitk_noalloc")
 
 
 def w4a16_act_quant_i8(M, K, x, xq, sx, xsum, stream=None):

@@ -173,6 +173,17 @@ w4a16::LaunchPlan plan_a8(int M, int N, int K) {
 
 }  // namespace
 
+namespace w4a16 {
+
+int gemv_splitk_status(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
+                       const void* x, void* y, unsigned long long* acc, void* stream) {
+  const LaunchPlan plan = plan_for(M, N, K, splits);
+  if (launch_gemv(M, N, K, plan, wq, scales, zeros, x, y, acc, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
+
+}  // namespace w4a16
+
 extern "C" int w4a16_act_quant_i8(int M, int K, const void* x, void* xq, void* sx, void* xsum, void* stream) {
   const int rc = check_shape(M, 1, K);
   if (rc != W4A16_OK) return rc == 1 ? W4A16_OK : rc;
@@ -248,10 +259,8 @@ extern "C" int w4a16_gemv_splitk(int M, int N, int K, int splits, const void* Wq
   if (splits == 1) return w4a16_gemv(M, N, K, Wq, scales, zeros, x, y, stream);
   if (!pointers_ok({Wq, scales, zeros, x, y, workspace})) return W4A16_EINVAL;
   if (ws_bytes < w4a16::splitk_workspace_bytes(M, N)) return W4A16_EINVAL;
-  const w4a16::LaunchPlan plan = plan_for(M, N, K, splits);
-  auto* acc = static_cast<unsigned long long*>(workspace);
-  if (w4a16::launch_gemv(M, N, K, plan, Wq, scales, zeros, x, y, acc, stream) != 0) return W4A16_EHIP;
-  return W4A16_OK;
+  return w4a16::gemv_splitk_status(M, N, K, splits, Wq, scales, zeros, x, y,
+                                   static_cast<unsigned long long*>(workspace), stream);
 }
 
 extern "C" int w4a16_gemm(int M, int N, int K, const void* Wq, const void* scales, const void* zeros,

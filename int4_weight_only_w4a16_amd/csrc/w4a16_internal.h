@@ -124,6 +124,12 @@ constexpr size_t splitk_workspace_bytes(int M, int N) {
   return (size_t(8) * size_t(M) * size_t(N) + 15) / 16 * 16;
 }
 
+// Plans and launches a split-K GEMV (splits > 1) with accumulation words
+// `acc` (all zero; left zero). Arguments already checked. Returns a W4A16
+// status (api.cpp).
+int gemv_splitk_status(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
+                       const void* x, void* y, unsigned long long* acc, void* stream);
+
 // Kernel launchers (w4a16_kernels.hip). They return a hipError_t value as int.
 // `acc` non-null selects split-K: it is the workspace above, all zero.
 int launch_gemv(int M, int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,

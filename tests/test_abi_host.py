@@ -186,6 +186,18 @@ def test_device_entry_points_reject_before_launch():
     assert L.w4a16_gemv_splitk(9, 16, 768, 2, *ptrs, fake, 10 ** 9, None) == w.W4A16_EUNSUPPORTED
     assert L.w4a16_gemv_splitk(1, 16, 128 * 40, 32, *ptrs, fake, 10 ** 9, None) == w.W4A16_EINVAL  # > 31 splits
     assert L.w4a16_gemv_splitk(2, 0, 768, 2, *ptrs, fake, 0, None) == w.W4A16_OK
+    # split-K with the library's own accumulation array: the same checks, and
+    # outputs beyond the array (8 bytes each) are refused before any GPU call
+    cap = w.NOALLOC_SCRATCH_BYTES // 8
+    for M, N, K, splits, want in [(1, 16, 200, 2, w.W4A16_EINVAL), (1, 16, 768, 0, w.W4A16_EINVAL),
+                                  (1, 16, 768, 7, w.W4A16_EINVAL), (1, 16, 128 * 40, 32, w.W4A16_EINVAL),
+                                  (9, 16, 768, 2, w.W4A16_EUNSUPPORTED), (-1, 16, 768, 2, w.W4A16_EINVAL),
+                                  (0, 16, 768, 2, w.W4A16_OK), (2, 0, 768, 2, w.W4A16_OK),
+                                  (1, cap + 1, 768, 2, w.W4A16_EUNSUPPORTED),
+                                  (8, cap // 8 + 16, 768, 2, w.W4A16_EUNSUPPORTED)]:
+        assert L.w4a16_gemv_splitk_noalloc(M, N, K, splits, *ptrs, None) == want, (M, N, K, splits)
+    assert L.w4a16_gemv_splitk_noalloc(1, 16, 768, 2, fake, fake, fake, fake + 2, fake, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemv_splitk_noalloc(1, 16, 768, 2, fake, None, fake, fake, fake, None) == w.W4A16_EINVAL
     # fused SwiGLU
     assert L.w4a16_gemv_swiglu(1, 16, 200, *ptrs, None) == w.W4A16_EINVAL
     assert L.w4a16_gemv_swiglu(9, 16, 128, *ptrs, None) == w.W4A16_EUNSUPPORTED
