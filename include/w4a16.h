@@ -392,6 +392,85 @@ int w4a16_dequant_f32(int N, int K, const void* Wq, const void* scales, const vo
  */
 int w4a16_read_probe(const void* buf, size_t bytes, int grid, void* sink, void* stream);
 
+/*
+ * A chain of dependent GEMVs in one launch -- a whole decode step's linear
+ * layers, each reading an earlier GEMV's output -- so that no launch
+ * boundary stops the weight stream between them. The qengine page runs its
+ * matrix kernels at 94.9% of bandwidth inside its decode loop by starting
+ * each kernel's loads before the previous kernel finishes ("Why speed is a
+ * byte count", "How it works"); here every workgroup requests the weights
+ * of its next work items before it waits for their input.
+ *
+ * One GEMV of the chain:
+ *   kind   W4A16_CHAIN_GEMV: y = W x as w4a16_gemv / w4a16_gemv_splitk;
+ *          W4A16_CHAIN_SWIGLU: y = silu(gate x) * (up x) as
+ *          w4a16_gemv_swiglu (W from w4a16_pack_gate_up, N = F, the output
+ *          width; K at most 3584 and splits 1).
+ *   N, K   output and input features (K a multiple of 128).
+ *   splits K ranges combined by the split-K fixed-point atomics (1..31).
+ *          Each wave takes at most 7 tiles of a range (5 when split): K/128
+ *          / splits must be at most 56 (40 when split), else
+ *          W4A16_EUNSUPPORTED.
+ *   x_src  -1: the input is `x`, fp16 [M][K] on the device; otherwise the
+ *          index of an earlier GEMV of the chain whose output has at least K
+ *          columns: the input is its first K columns, times 2^-x_shift
+ *          (0 <= x_shift <= 24; an exact power-of-two rescale, then fp16
+ *          rounding to nearest even).
+ *   wq, scales, zeros: layout ID 2 on the device; y: fp16 [M][N] on the
+ *          device, written for every GEMV. 16-byte aligned.
+ */
+#define W4A16_CHAIN_GEMV 0
+#define W4A16_CHAIN_SWIGLU 1
+typedef struct w4a16_chain_op {
+  int kind, N, K, splits, x_src, x_shift;
+  const void* wq;
+  const void* scales;
+  const void* zeros;
+  const void* x;
+  void* y;
+} w4a16_chain_op;
+
+/*
+ * Host: checks a chain of n_ops GEMVs for M activation rows and writes its
+ * plan -- a byte image the caller copies to device memory unchanged -- into
+ * `plan` (host memory, plan_bytes bytes; NULL to only ask for sizes).
+ * *plan_bytes_needed and *ws_bytes_needed (either may be NULL) receive the
+ * plan's size and the workspace size w4a16_chain_run needs. The plan holds
+ * the device pointers of `ops`: it is valid as long as those buffers are.
+ * Errors: W4A16_EINVAL (a bad kind, shape, split count, pointer, x_src or
+ * x_shift, or plan_bytes too small), W4A16_EUNSUPPORTED (M > 8, or a GEMV
+ * whose waves' shares would exceed 7 tiles). Host only; allocates nothing
+ * the caller sees.
+ */
+int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, void* plan, size_t plan_bytes,
+                     size_t* plan_bytes_needed, size_t* ws_bytes_needed);
+
+/*
+ * Runs a chain in one persistent launch on `stream`.
+ *   plan_dev: the plan of w4a16_chain_plan, copied to device memory
+ *     (16-byte aligned), for the same M.
+ *   workspace: device memory of at least the plan's ws_bytes_needed,
+ *     16-byte aligned, zero-filled once before its first use. It holds the
+ *     launch counter, the error word, the split-K words (left zero by a
+ *     completed run) and the tagged outputs the GEMVs hand each other.
+ *     One workspace serves every later run of any plan that fits it, on
+ *     one stream; runs that may overlap in time need different workspaces.
+ *   Every GEMV's y is written. Each output has the arithmetic of the
+ *   standalone entry points with the same waves and shares (bit-identical to
+ *   w4a16_gemv for K = 3584 unsplit, to w4a16_gemv_swiglu, and to
+ *   w4a16_gemv_splitk with 4 splits of K = 18944, given the same input).
+ * The launch has one workgroup per compute unit and needs all of them
+ * resident at once: nothing else may occupy the device's compute units while
+ * it runs. The uint32 at byte 8 of the workspace is 0 after a completed run;
+ * 1 if a wait ran out (1 s without progress: residency was lost), 2 if the
+ * plan does not match M or the workspace. A nonzero word is sticky: later
+ * runs return at once until the caller zero-fills the workspace again.
+ * Errors (returned): W4A16_EINVAL (NULL or misaligned pointer, ws_bytes
+ * below 256), W4A16_EUNSUPPORTED (M other than 1, or the device cannot keep
+ * one workgroup per compute unit resident), W4A16_EHIP.
+ */
+int w4a16_chain_run(int M, const void* plan_dev, void* workspace, size_t ws_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* w4a16_strerror(int status);
 

@@ -28,7 +28,21 @@ EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_ga
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
            "w4a16_gemv_splitk", "w4a16_gemv_splitk_noalloc", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemv_a8_fused", "w4a16_gemm", "w4a16_gemm_splitk_choose",
            "w4a16_gemm_splitk", "w4a16_dequant_f16",
-           "w4a16_dequant_f32", "w4a16_read_probe", "w4a16_strerror")
+           "w4a16_dequant_f32", "w4a16_read_probe", "w4a16_chain_plan", "w4a16_chain_run", "w4a16_strerror")
+
+
+CHAIN_GEMV = 0
+CHAIN_SWIGLU = 1
+# Byte offset of the chain workspace's error word (0: the last run completed).
+CHAIN_ERROR_OFFSET = 8
+
+
+class ChainOp(ctypes.Structure):
+    """struct w4a16_chain_op of the header."""
+    _fields_ = [("kind", ctypes.c_int), ("N", ctypes.c_int), ("K", ctypes.c_int), ("splits", ctypes.c_int),
+                ("x_src", ctypes.c_int), ("x_shift", ctypes.c_int), ("wq", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p)]
 
 
 class W4A16Error(RuntimeError):
@@ -83,6 +97,9 @@ def lib():
         L.w4a16_act_quant_i8.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_gemv_a8.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]
         L.w4a16_gemv_a8_fused.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
+        L.w4a16_chain_plan.argtypes = [_i, _i, ctypes.POINTER(ChainOp), _p, _sz, ctypes.POINTER(_sz),
+                                       ctypes.POINTER(_sz)]
+        L.w4a16_chain_run.argtypes = [_i, _p, _p, _sz, _p]
         L.w4a16_strerror.restype = ctypes.c_char_p
         L.w4a16_strerror.argtypes = [_i]
         _lib = L
@@ -280,6 +297,32 @@ def w4a16_read_probe(buf, grid, sink, nbytes=None, stream=None):
     if nbytes is None:
         nbytes = buf.numel() * buf.element_size()
     _check(lib().w4a16_read_probe(_ptr(buf), nbytes, grid, _ptr(sink), _stream(stream)), "w4a16_read_probe")
+
+
+def w4a16_chain_plan(M, ops):
+    """Host: plan of a chain of GEMVs. `ops` is a sequence of dicts with keys
+    kind, N, K, splits, x_src, x_shift, wq, scales, zeros, x, y (device
+    tensors or integer pointers; x may be None when x_src >= 0). Returns
+    (plan bytes as a uint8 numpy array, workspace bytes)."""
+    arr = (ChainOp * len(ops))()
+    for i, o in enumerate(ops):
+        arr[i] = ChainOp(int(o["kind"]), int(o["N"]), int(o["K"]), int(o.get("splits", 1)), int(o.get("x_src", -1)),
+                         int(o.get("x_shift", 0)), _ptr(o["wq"]), _ptr(o["scales"]), _ptr(o["zeros"]),
+                         _ptr(o.get("x")), _ptr(o["y"]))
+    pb, wb = _sz(), _sz()
+    _check(lib().w4a16_chain_plan(M, len(ops), arr, None, 0, ctypes.byref(pb), ctypes.byref(wb)), "w4a16_chain_plan")
+    plan = np.zeros(pb.value, np.uint8)
+    _check(lib().w4a16_chain_plan(M, len(ops), arr, plan.ctypes.data, pb.value, None, None), "w4a16_chain_plan")
+    return plan, wb.value
+
+
+def w4a16_chain_run(M, plan_dev, workspace, ws_bytes=None, stream=None):
+    """Device: the whole chain in one launch. plan_dev: the plan copied to
+    device memory; workspace: zero-filled once (its uint32 at byte 8 is the
+    error word)."""
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().w4a16_chain_run(M, _ptr(plan_dev), _ptr(workspace), ws_bytes, _stream(stream)), "w4a16_chain_run")
 
 
 def w4a16_dequant_f32(N, K, Wq, scales, zeros, W_out, stream=None):

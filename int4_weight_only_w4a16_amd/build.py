@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.cpp", "pack.cpp", "quantize.cpp", "w4a16_kernels.hip", "gemm_kernel.hip", "a8_kernels.hip", "noalloc.hip"] + [f"gemv_m{m}.hip" for m in range(1, 9)]
+SOURCES = ["api.cpp", "pack.cpp", "quantize.cpp", "w4a16_kernels.hip", "gemm_kernel.hip", "a8_kernels.hip", "noalloc.hip", "chain.hip"] + [f"gemv_m{m}.hip" for m in range(1, 9)]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -1,0 +1,779 @@
+// A chain of dependent W4A16 GEMVs in one persistent launch (w4a16_chain_plan,
+// w4a16_chain_run): a whole decode step of GEMVs, each reading its input from
+// an earlier GEMV's output, without a launch boundary between them.
+//
+// Why: between two dependent GEMV launches the GPU streams no weights. The
+// qengine page gets its matrix kernels to 94.9% of bandwidth inside the
+// decode loop by letting each kernel start loading while the previous one
+// finishes ("Why speed is a byte count", "How it works": programmatic
+// dependent launch, the DeltaNet kernel started ahead of its wait). Here a
+// workgroup requests the weights of its next work items before it waits for
+// their input, so the weight stream goes on across every dependency.
+//
+// Structure. One workgroup per compute unit, all resident at once (checked
+// at launch): 8 compute waves and 1 control wave. The chain's work items --
+// (GEMV, 16-row tile or tile pair, K range) -- are numbered in chain order,
+// and workgroup w takes items w, w + P, w + 2P, ... (P workgroups).
+//  - A compute wave takes a fixed share of every item's K range (as the
+//    standalone kernels' waves do). For item k it (1) waits until the
+//    control wave has seen the item's producer finish, (2) requests its x
+//    slice, (3) requests the weights of item k + (NBUF-1) P, (4) checks and
+//    converts x into its private LDS slice, (5) multiplies item k, whose
+//    weights were requested NBUF-1 items ago, and (6) hands its fp32 partial
+//    sums to the control wave through an LDS slot. When the input is not
+//    ready yet, (3) goes before (1), so the wave waits with NBUF items of
+//    weights in flight.
+//  - The control wave adds each item's partial sums in wave order and does
+//    the epilogue (fp16 store, SwiGLU, or the split-K fixed-point atomics),
+//    and polls one word of each producer its workgroup will need, publishing
+//    readiness in LDS. It never waits for another workgroup, so a workgroup
+//    never waits for itself.
+//
+// Handoff between GEMVs. A GEMV whose output feeds another also writes each
+// output as a 32-bit word (fp16 bits | tag << 16) with device-scope stores,
+// tag = a 16-bit number of this launch, never 0 (it comes from the
+// workspace and the last workgroup to finish advances it). A consumer
+// accepts a word only when its tag is this launch's: no word from an
+// earlier launch or an unfinished producer is ever used, whatever order the
+// stores become visible in, and no fence or counter is needed. Stale words
+// are requested again with device-scope loads until they carry the tag.
+//
+// Progress. Item k waits only for GEMVs of smaller item numbers, every
+// workgroup takes its items in increasing order, and all workgroups are
+// resident, so the smallest unfinished item can always finish. Every wait
+// is bounded (kWaitTicks of the 100 MHz real-time counter); a wait that
+// runs out sets the workspace error word and every workgroup leaves.
+//
+// The arithmetic of an item is that of the standalone kernels with the same
+// waves and shares (w4a16_gemv: 4 waves per tile at 28 groups; SwiGLU: 4 +
+// 4 waves; w4a16_gemv_splitk: 8 waves of the split's range), so each output
+// equals theirs bit for bit where the plans coincide.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <vector>
+
+#include "w4a16.h"
+#include "w4a16_device.h"
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+namespace chain {
+
+using dev::f32x4;
+using dev::u32x4;
+
+constexpr int kComputeWaves = 8;
+constexpr int kThreads = (kComputeWaves + 1) * 64;
+constexpr int kShare = 7;   // tiles per wave and item, at most
+constexpr int kSlots = 4;   // partial-sum slots between compute waves and control wave
+constexpr uint32_t kMagic = 0x57344348u;  // "W4CH"
+constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz counter
+
+// Workspace control words (uint32, first 256 bytes): launch number, finished
+// workgroups, error.
+enum : int { kWsEpoch = 0, kWsFinished = 1, kWsError = 2 };
+constexpr size_t kWsHeader = 256;
+
+// Device addresses are kept as integers and read back as global-memory
+// pointers: a pointer loaded from memory would otherwise be a generic (flat)
+// one, and flat loads also count against the LDS wait counter.
+#define W4A16_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ W4A16_GLOBAL T* gptr(uint64_t a) {
+  return reinterpret_cast<W4A16_GLOBAL T*>(a);
+}
+
+struct alignas(16) OpDev {
+  uint64_t wq;
+  uint64_t sw;           // scales, as 32-bit words
+  uint64_t zw;           // zero points, as 32-bit words
+  uint64_t x_ext;        // external fp16 input [M][K] when x_src < 0
+  uint64_t y;            // fp16 output [M][N]
+  uint64_t yt_off;       // workspace offset of this GEMV's tagged output [M][N] (0: nobody reads it)
+  uint64_t xt_off;       // workspace offset of the producer's tagged output (x_src >= 0)
+  uint64_t acc_off;      // workspace offset of the split-K words [M][N] (splits > 1)
+  int32_t N, K, G, kind;
+  int32_t splits, tp, wpt, row_tiles;       // tiles per item, waves per tile, output row tiles
+  int32_t per_split, items, item_begin, x_shift;
+  int32_t x_stride;   // producer's N: row stride of its tagged output, in words
+  int32_t sentinel;   // word of the producer's tagged output the control wave polls
+  int32_t x_src;
+  int32_t reserved;
+};
+static_assert(sizeof(OpDev) == 128, "descriptor size");
+
+struct alignas(16) Header {
+  uint32_t magic;
+  int32_t M, n_ops, total_items;
+  uint64_t plan_bytes, ws_bytes;
+  int32_t reserved[8];
+};
+static_assert(sizeof(Header) == 64, "header size");
+
+// LDS control block.
+struct LdsCtl {
+  int ready;             // highest GEMV index whose producer the control wave has seen finish
+  int abort;             // nonzero: leave
+  int cnt[kSlots];       // compute waves that have written the slot's partial sums
+  int gen[kSlots];       // times the slot has been consumed
+  int pad[6];
+};
+
+__device__ __forceinline__ uint32_t ld_dev(const W4A16_GLOBAL uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(W4A16_GLOBAL uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int lds_ld(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local"); }
+__device__ __forceinline__ void lds_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local"); }
+
+// The GEMV of item k, found by walking the descriptors forward from `op`
+// (items are visited in increasing order).
+__device__ __forceinline__ int op_of(const OpDev* ops, int op, int k) {
+  while (k >= ops[op].item_begin + ops[op].items) ++op;
+  return op;
+}
+
+// Where a compute wave works in an item: the matrix row tile it reads and
+// its share of the item's K range.
+struct Share {
+  int64_t tile;
+  int beg, n;
+};
+
+__device__ __forceinline__ Share share_of(const OpDev& d, int i, int wave) {
+  const int split = i / d.per_split, tg = i - split * d.per_split;
+  const int lt = wave / d.wpt, wi = wave - lt * d.wpt;
+  int64_t tile;
+  if (d.kind == W4A16_CHAIN_SWIGLU) {
+    tile = 2 * int64_t(tg) + lt;  // gate tile 2 tg, up tile 2 tg + 1
+  } else {
+    tile = int64_t(tg) * d.tp + lt;
+    if (tile >= d.row_tiles) tile = d.row_tiles - 1;  // a pair's missing second tile: valid, never stored
+  }
+  const int g_beg = d.splits == 1 ? 0 : int(unsigned(split) * unsigned(d.G) / unsigned(d.splits));
+  const int g_end = d.splits == 1 ? d.G : int(unsigned(split + 1) * unsigned(d.G) / unsigned(d.splits));
+  const int ng = g_end - g_beg;
+  const int beg = g_beg + int(unsigned(wi * ng) / unsigned(d.wpt));
+  const int end = g_beg + int(unsigned((wi + 1) * ng) / unsigned(d.wpt));
+  return Share{tile, beg, end - beg};
+}
+
+template <int MR>
+struct Geo {
+  static constexpr int kRows = MR < 4 ? MR : 4;          // accumulators per lane (MFMA D rows used)
+  static constexpr int kRedWave = 4 * kRows * 16;        // floats of one wave's partial sums
+  static constexpr int kXRow = kShare * kGroup + (MR > 1 ? 32 : 0);  // halves per x slice row
+  static constexpr size_t kCtlBytes = sizeof(LdsCtl);
+  static constexpr size_t kPartBytes = size_t(kSlots) * kComputeWaves * kRedWave * 4;
+  static constexpr size_t kXBytes = size_t(kComputeWaves) * MR * kXRow * 2;
+  static constexpr size_t kLds = kCtlBytes + kPartBytes + kXBytes;
+};
+
+struct Buf {
+  u32x4 w[kShare];
+  uint32_t sw[kShare], zw[kShare];
+};
+
+template <int MR, int NBUF>
+__global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restrict__ plan, uint8_t* __restrict__ ws,
+                                                          uint64_t ws_bytes) {
+  using GG = Geo<MR>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  LdsCtl* lc = reinterpret_cast<LdsCtl*>(smem);
+  float* part = reinterpret_cast<float*>(smem + GG::kCtlBytes);  // [kSlots][waves][kRedWave]
+  _Float16* xs = reinterpret_cast<_Float16*>(smem + GG::kCtlBytes + GG::kPartBytes);
+  const uint64_t wsa = reinterpret_cast<uint64_t>(ws);
+  W4A16_GLOBAL uint32_t* ctl = gptr<uint32_t>(wsa);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = gridDim.x, wg = blockIdx.x;
+  if (tid == 0) {
+    lc->ready = -1;
+    lc->abort = 0;
+    for (int s = 0; s < kSlots; ++s) lc->cnt[s] = 0, lc->gen[s] = 0;
+  }
+  const bool plan_ok = plan->magic == kMagic && plan->M == MR && plan->ws_bytes <= ws_bytes;
+  const uint32_t err0 = ld_dev(ctl + kWsError);
+  const uint32_t epoch = ld_dev(ctl + kWsEpoch);
+  __syncthreads();
+  if (!plan_ok) {
+    if (tid == 0) st_dev(ctl + kWsError, 2u);
+    return;
+  }
+  if (err0 != 0) return;  // a failed earlier run: the caller clears the workspace first
+  const uint32_t tag = epoch % 65535u + 1u;
+  const int total = plan->total_items;
+  const OpDev* ops = reinterpret_cast<const OpDev*>(plan + 1);
+  const uint64_t t_start = wall_clock64();
+
+  if (wave == kComputeWaves) {
+    // ---------------------------------------------------------------- control wave
+    int op_ep = 0, o_ep = 0;       // next item to finish: ordinal o_ep, item wg + o_ep P
+    int op_need = 0, k_need = wg;  // next item whose producer must be seen
+    uint64_t last_progress = t_start;
+    bool failed = false;
+    while (true) {
+      bool progressed = false;
+      const int k_ep = wg + o_ep * P;
+      if (k_ep >= total) break;
+      // epilogue of the next item, once all compute waves have handed in
+      const int slot = o_ep % kSlots;
+      if (lds_ld(&lc->cnt[slot]) == kComputeWaves) {
+        lds_acquire();
+        op_ep = op_of(ops, op_ep, k_ep);
+        const OpDev& d = ops[op_ep];
+        const int i = k_ep - d.item_begin;
+        const int split = i / d.per_split, tg = i - split * d.per_split;
+        const float* pb = part + size_t(slot) * kComputeWaves * GG::kRedWave;
+        W4A16_GLOBAL uint32_t* yt = gptr<uint32_t>(wsa + d.yt_off);
+        W4A16_GLOBAL uint16_t* yd = gptr<uint16_t>(d.y);
+        const bool pair = d.kind == W4A16_CHAIN_SWIGLU;
+        const int tiles_out = pair ? 1 : d.tp;
+        const int n_out = tiles_out * MR * 16;
+        for (int idx = lane; idx < ((n_out + 63) & ~63); idx += 64) {
+          const int id = idx < n_out ? idx : n_out - 1;
+          const int lt = id / (MR * 16), rem = id - lt * MR * 16, m = rem >> 4, r = rem & 15;
+          const int sl = ((m >> 2) * GG::kRows + (m & 3)) * 16 + r;
+          const int w0 = pair ? 0 : lt * d.wpt;
+          float sum = pb[w0 * GG::kRedWave + sl];
+          for (int w2 = 1; w2 < (pair ? 4 : d.wpt); ++w2) sum += pb[(w0 + w2) * GG::kRedWave + sl];
+          if (pair) {
+            float up = pb[4 * GG::kRedWave + sl];
+            for (int w2 = 5; w2 < 8; ++w2) up += pb[w2 * GG::kRedWave + sl];
+            sum = sum / (1.f + expf(-sum)) * up;  // silu(gate) * up
+          }
+          const int64_t t = pair ? tg : int64_t(tg) * d.tp + lt;
+          const int64_t n = t * kTileRows + r;
+          if (idx < n_out && t < d.row_tiles && n < d.N) {
+            const int64_t o = int64_t(m) * d.N + n;
+            bool write = true;
+            _Float16 v;
+            if (d.splits > 1) {
+              W4A16_GLOBAL unsigned long long* word = gptr<unsigned long long>(wsa + d.acc_off) + o;
+              const unsigned long long add = dev::splitk_addend(sum);
+              const unsigned long long now =
+                  __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+              write = dev::splitk_count(now) == unsigned(d.splits);
+              v = dev::splitk_value(now, d.splits);
+              if (write) __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+              v = (_Float16)sum;
+            }
+            if (write) {
+              const uint16_t bits = __builtin_bit_cast(uint16_t, v);
+              yd[o] = bits;
+              if (d.yt_off) st_dev(yt + o, (tag << 16) | bits);
+            }
+          }
+        }
+        lds_st(&lc->cnt[slot], 0);
+        lds_release();
+        lds_st(&lc->gen[slot], o_ep / kSlots + 1);
+        ++o_ep;
+        progressed = true;
+      }
+      // readiness of the next GEMV this workgroup reads from a producer
+      while (k_need < total) {
+        op_need = op_of(ops, op_need, k_need);
+        const OpDev& d = ops[op_need];
+        if (d.x_src >= 0 && lds_ld(&lc->ready) < op_need) break;
+        // no producer, or already published: on to this workgroup's first item of a later GEMV
+        const int next_begin = d.item_begin + d.items;
+        k_need = next_begin <= wg ? wg : wg + ((next_begin - wg + P - 1) / P) * P;
+      }
+      if (k_need < total) {
+        const OpDev& d = ops[op_need];
+        if ((ld_dev(gptr<uint32_t>(wsa + d.xt_off) + d.sentinel) >> 16) == tag) {
+          lds_st(&lc->ready, op_need);
+          progressed = true;
+        }
+      }
+      const uint64_t now = wall_clock64();
+      if (progressed) {
+        last_progress = now;
+      } else {
+        if (lds_ld(&lc->abort) || ld_dev(ctl + kWsError)) {
+          failed = true;
+        } else if (now - last_progress > kWaitTicks) {
+          st_dev(ctl + kWsError, 1u);
+          failed = true;
+        }
+        if (failed) {
+          lds_st(&lc->abort, 1);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    if (lane == 0) {
+      const uint32_t done = __hip_atomic_fetch_add(ctl + kWsFinished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done == uint32_t(P) - 1) {
+        __hip_atomic_store(ctl + kWsFinished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(ctl + kWsEpoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------------ compute waves
+  const int piece = lane >> 4, rlane = lane & 15;
+  const int mm = rlane < MR ? rlane : MR - 1;
+  _Float16* xw = xs + size_t(wave) * MR * GG::kXRow;
+  const uint32_t magic = dev::kMagic1024;
+  bool failed = false;
+
+  auto fail = [&](uint32_t code) {
+    st_dev(ctl + kWsError, code);
+    lds_st(&lc->abort, 1);
+    failed = true;
+  };
+  // Bounded wait helper: true while the wait may go on.
+  auto may_wait = [&](uint64_t t0) {
+    if (lds_ld(&lc->abort)) {
+      failed = true;
+      return false;
+    }
+    if (wall_clock64() - t0 > kWaitTicks) {
+      fail(1u);
+      return false;
+    }
+    return true;
+  };
+
+  // A share's weight tiles, scales and zero words as buffer loads: the row
+  // tile's base goes into the (scalar) resource, the group into the scalar
+  // offset, and the lane's constant offset is the only vector operand, so
+  // no 64-bit addresses occupy vector registers. Indices past the share are
+  // clamped to its last tile (in bounds, discarded in compute()). `live`
+  // false gives the resources 0 records: the same requests go out and come
+  // back as zeros without touching memory, so every path issues the same
+  // number of requests and every wait count stays exact.
+  const int w_voff = lane * 16, s_voff = (rlane >> 1) * 4, z_voff = (rlane >> 3) * 4;
+  auto load = [&](Buf& b, const OpDev& d, const Share& s, bool live) {
+    const uint64_t q0 = uint64_t(s.tile) * uint64_t(d.G);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(d.wq + q0 * kTileBytes), (short)0, live ? d.G * kTileBytes : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(d.sw + q0 * 32), (short)0, live ? d.G * 32 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(d.zw + q0 * 8), (short)0, live ? d.G * 8 : 0, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < kShare; ++u) {
+      const int gg = max(s.beg + min(u, s.n - 1), 0);
+      b.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff, gg * kTileBytes, 2 /* nt */);
+      b.sw[u] = __builtin_amdgcn_raw_buffer_load_b32(rsc, s_voff, gg * 32, 0);
+      b.zw[u] = __builtin_amdgcn_raw_buffer_load_b32(rz, z_voff, gg * 8, 0);
+    }
+  };
+
+  // x of a share: tagged words (4 per 16-byte chunk, tag checked) or the
+  // external fp16 input (8 per chunk). Chunks past the share are clamped
+  // copies of its last chunk: every request is in bounds and unconditional.
+  constexpr int kTChunksRow = kShare * kGroup / 4, kTSteps = (MR * kTChunksRow + 63) / 64;
+  constexpr int kEChunksRow = kShare * kGroup / 8, kESteps = (MR * kEChunksRow + 63) / 64;
+  auto tchunk = [&](int j, int n, int& m, int& cc) {
+    const int c = min(lane + 64 * j, MR * kTChunksRow - 1);
+    m = MR == 1 ? 0 : c / kTChunksRow;
+    cc = min(c - m * kTChunksRow, n * (kGroup / 4) - 1);
+  };
+  auto echunk = [&](int j, int n, int& m, int& cc) {
+    const int c = min(lane + 64 * j, MR * kEChunksRow - 1);
+    m = MR == 1 ? 0 : c / kEChunksRow;
+    cc = min(c - m * kEChunksRow, n * (kGroup / 8) - 1);
+  };
+  // Requests of the share's x: a resource based at the share's first column
+  // (uniform), the lane's chunk offset as the vector operand. sc1 == false:
+  // plain loads (an L2 hit serves the other compute units of the same chip
+  // die); true: device scope, for chunks found stale.
+  auto t_request = [&](u32x4 (&tv)[kTSteps], const OpDev& d, const Share& s, bool sc1) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        ws + d.xt_off + uint64_t(s.beg) * kGroup * 4, (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kTSteps; ++j) {
+      int m, cc;
+      tchunk(j, s.n, m, cc);
+      const int off = (m * d.x_stride + cc * 4) * 4;
+      if (sc1)
+        tv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16);
+      else
+        tv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    }
+  };
+  // Every word of the wave's chunks carries this launch's tag?
+  auto t_fresh = [&](const u32x4 (&tv)[kTSteps]) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < kTSteps; ++j)
+      ok &= (tv[j].x >> 16) == tag && (tv[j].y >> 16) == tag && (tv[j].z >> 16) == tag && (tv[j].w >> 16) == tag;
+    return __builtin_amdgcn_read_exec() == __ballot(ok);
+  };
+  auto t_store = [&](const u32x4 (&tv)[kTSteps], const OpDev& d, const Share& s) {
+    const float scale = __builtin_ldexpf(1.0f, -d.x_shift);  // exact power of two
+#pragma unroll
+    for (int j = 0; j < kTSteps; ++j) {
+      int m, cc;
+      tchunk(j, s.n, m, cc);
+      const u32x4 v = tv[j];
+      const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v.x & 0xFFFFu) * scale));
+      const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v.y & 0xFFFFu) * scale));
+      const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v.z & 0xFFFFu) * scale));
+      const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v.w & 0xFFFFu) * scale));
+      uint2 packed;
+      packed.x = h0 | (h1 << 16);
+      packed.y = h2 | (h3 << 16);
+      *reinterpret_cast<uint2*>(xw + m * GG::kXRow + cc * 4) = packed;
+    }
+  };
+  static_assert(kESteps <= kTSteps, "external x chunks fit the tagged registers");
+  auto e_request = [&](u32x4 (&ev)[kTSteps], const OpDev& d, const Share& s) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(d.x_ext + uint64_t(s.beg) * kGroup * 2), (short)0, 0x7fffffff, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < kESteps; ++j) {
+      int m, cc;
+      echunk(j, s.n, m, cc);
+      ev[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (m * d.K + cc * 8) * 2, 0, 0);
+    }
+  };
+  auto e_store = [&](const u32x4 (&ev)[kTSteps], const Share& s) {
+#pragma unroll
+    for (int j = 0; j < kESteps; ++j) {
+      int m, cc;
+      echunk(j, s.n, m, cc);
+      *reinterpret_cast<u32x4*>(xw + m * GG::kXRow + cc * 8) = ev[j];
+    }
+  };
+  auto slice_done = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  };
+
+  auto compute = [&](const Buf& b, const Share& s, float (&acc)[GG::kRows]) {
+#pragma unroll
+    for (int r = 0; r < GG::kRows; ++r) acc[r] = 0.f;
+    if (s.n <= 0) return;
+    int xoff = 8 * piece;
+    asm volatile("" : "+v"(xoff));
+    const _Float16* xbase = xw + xoff;
+    f32x4 dsave[kShare];
+    float ssave[kShare];
+#pragma unroll
+    for (int u = 0; u < kShare; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 wt = b.w[u];
+      uint32_t zt = b.zw[u], st = b.sw[u];
+      asm volatile("" : "+v"(wt), "+v"(zt), "+v"(st));
+      const dev::ZeroPairs zp = dev::zero_pairs((zt >> ((rlane & 7) * 4)) & 15u);
+      const float sc = dev::half_bits_to_float((st >> ((rlane & 1) * 16)) & 0xFFFFu);
+      const _Float16* xg = xbase + u * kGroup;
+      f32x4 dd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        dev::half2_t p[4];
+        dev::unpack8(wt[kb], magic, zp, p);
+        const dev::half8_t bw = {p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
+        const dev::half8_t ax = *reinterpret_cast<const dev::half8_t*>(xg + mm * GG::kXRow + 32 * kb);
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, dd, 0, 0, 0);
+      }
+      dsave[u] = dd;
+      ssave[u] = sc;
+    }
+#pragma unroll
+    for (int u = 0; u < kShare; ++u) {
+      const bool valid = u < s.n;
+#pragma unroll
+      for (int r2 = 0; r2 < GG::kRows; ++r2) acc[r2] = valid ? __builtin_fmaf(dsave[u][r2], ssave[u], acc[r2]) : acc[r2];
+    }
+  };
+
+  auto hand_in = [&](int o, const float (&acc)[GG::kRows]) {
+    const int slot = o % kSlots, gen = o / kSlots;
+    const uint64_t t0 = wall_clock64();
+    while (lds_ld(&lc->gen[slot]) != gen) {
+      if (!may_wait(t0)) return;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    lds_acquire();
+    float* pw = part + (size_t(slot) * kComputeWaves + wave) * GG::kRedWave;
+#pragma unroll
+    for (int r = 0; r < GG::kRows; ++r) pw[(piece * GG::kRows + r) * 16 + rlane] = acc[r];
+    lds_release();
+    if (lane == 0) __hip_atomic_fetch_add(&lc->cnt[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+
+  // One item: ordinal o (item wg + o P) with weights in `cur`; the weights of
+  // ordinal o + NBUF - 1 go into `nxt`.
+  int op_c = 0, op_p = 0;
+  auto step = [&](int o, const Buf& cur, Buf& nxt) {
+    const int k = wg + o * P;
+    op_c = op_of(ops, op_c, k);
+    const OpDev& d = ops[op_c];
+    const Share s = share_of(d, k - d.item_begin, wave);
+    const int kp = k + (NBUF - 1) * P;
+    // The next weights (dead requests past the chain's end or for an empty
+    // share: see load()).
+    auto prefetch = [&]() {
+      const bool valid = kp < total;
+      if (valid) op_p = op_of(ops, op_p, kp);
+      const OpDev& dp = ops[valid ? op_p : op_c];
+      const Share sp = share_of(dp, (valid ? kp : k) - dp.item_begin, wave);
+      load(nxt, dp, sp, valid && sp.n > 0);
+    };
+    // One request site for the next weights (a single definition of their
+    // registers: no copies, so no waits for them). The x requests go ahead
+    // of it when the input is ready -- then the wait for x counts exactly
+    // the weight requests behind it (requests complete in order) -- and
+    // after it otherwise, so that the wave waits with the next weights in
+    // flight.
+    const bool tagged = d.x_src >= 0, have = s.n > 0;
+    const bool early = !tagged || lds_ld(&lc->ready) >= op_c;
+    u32x4 tv[kTSteps];
+    if (have && early) {
+      if (tagged)
+        t_request(tv, d, s, false);
+      else
+        e_request(tv, d, s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch();
+    __builtin_amdgcn_sched_barrier(0);
+    if (have && !early) {
+      const uint64_t t0 = wall_clock64();
+      while (lds_ld(&lc->ready) < op_c) {
+        if (!may_wait(t0)) return;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      t_request(tv, d, s, false);
+    }
+    if (have) {
+      if (tagged) {
+        if (!t_fresh(tv)) {
+          const uint64_t t0 = wall_clock64();
+          do {
+            if (!may_wait(t0)) return;
+            __builtin_amdgcn_s_sleep(2);
+            t_request(tv, d, s, true);
+          } while (!t_fresh(tv));
+        }
+        t_store(tv, d, s);
+      } else {
+        e_store(tv, s);
+      }
+      slice_done();
+    }
+    float acc[GG::kRows];
+    compute(cur, s, acc);
+    hand_in(o, acc);
+  };
+
+  Buf bufs[NBUF];
+#pragma unroll
+  for (int i = 0; i + 1 < NBUF; ++i) {
+    const int k = wg + i * P;
+    if (k < total) {
+      op_p = op_of(ops, op_p, k);
+      const OpDev& dp = ops[op_p];
+      const Share sp = share_of(dp, k - dp.item_begin, wave);
+      load(bufs[i], dp, sp, sp.n > 0);
+    }
+  }
+  bool more = true;
+  for (int o0 = 0; more; o0 += NBUF) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (!more || failed || wg + (o0 + j) * P >= total) {
+        more = false;
+        break;
+      }
+      step(o0 + j, bufs[j], bufs[(j + NBUF - 1) % NBUF]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------ host side
+
+constexpr size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+template <int MR, int NBUF>
+hipError_t launch_typed(const void* plan, void* ws, size_t ws_bytes, hipStream_t stream, int grid) {
+  constexpr size_t lds = Geo<MR>::kLds;
+  static std::atomic<uint64_t> raised{0};
+  if (lds > kDefaultLdsLimit) {
+    const hipError_t e = dev::raise_lds_limit(reinterpret_cast<const void*>(&chain_kernel<MR, NBUF>), lds, raised);
+    if (e != hipSuccess) return e;
+  }
+  return dev::launch_kernel(&chain_kernel<MR, NBUF>, dim3(unsigned(grid)), dim3(kThreads), lds, stream,
+                            static_cast<const Header*>(plan), static_cast<uint8_t*>(ws), uint64_t(ws_bytes));
+}
+
+// Workgroups of one launch: one per compute unit, if that many can be
+// resident at once (0 otherwise).
+template <int MR, int NBUF>
+int resident_grid() {
+  int device = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&device) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
+  constexpr size_t lds = Geo<MR>::kLds;
+  static std::atomic<uint64_t> raised{0};
+  if (lds > kDefaultLdsLimit &&
+      dev::raise_lds_limit(reinterpret_cast<const void*>(&chain_kernel<MR, NBUF>), lds, raised) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&chain_kernel<MR, NBUF>),
+                                                   kThreads, lds) != hipSuccess)
+    return 0;
+  return per_cu >= 1 ? cus : 0;
+}
+
+}  // namespace chain
+}  // namespace w4a16
+
+using w4a16::chain::Header;
+using w4a16::chain::OpDev;
+
+namespace {
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Waves per tile and tiles per item for one GEMV of the chain: 4 waves per
+// 16-row tile (two tiles per item) while each wave's share of the K range
+// holds at most 7 tiles (5 with split K, as the standalone split-K plan),
+// else 8 (one tile per item); 0 if 8 waves cannot hold it.
+void chain_geometry(int kind, int G, int splits, int* wpt, int* tp) {
+  const int range = (G + splits - 1) / splits;
+  const int cap4 = splits > 1 ? 5 : w4a16::chain::kShare;
+  if (kind == W4A16_CHAIN_SWIGLU) {
+    *wpt = (range + 3) / 4 <= w4a16::chain::kShare ? 4 : 0;
+    *tp = 1;
+  } else if ((range + 3) / 4 <= cap4) {
+    *wpt = 4, *tp = 2;
+  } else if ((range + 7) / 8 <= w4a16::chain::kShare) {
+    *wpt = 8, *tp = 1;
+  } else {
+    *wpt = 0, *tp = 0;
+  }
+}
+
+}  // namespace
+
+extern "C" int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, void* plan, size_t plan_bytes,
+                                size_t* plan_bytes_needed, size_t* ws_bytes_needed) {
+  using namespace w4a16::chain;
+  if (M < 1 || n_ops < 1 || !ops) return W4A16_EINVAL;
+  if (M > W4A16_MAX_M) return W4A16_EUNSUPPORTED;
+  const size_t need_plan = sizeof(Header) + size_t(n_ops) * sizeof(OpDev);
+  size_t ws = kWsHeader;
+  int64_t total = 0;
+  // First pass: check every GEMV and size the workspace.
+  for (int j = 0; j < n_ops; ++j) {
+    const w4a16_chain_op& o = ops[j];
+    if (o.kind != W4A16_CHAIN_GEMV && o.kind != W4A16_CHAIN_SWIGLU) return W4A16_EINVAL;
+    if (o.N < 1 || o.K < W4A16_GROUP || o.K % W4A16_GROUP != 0) return W4A16_EINVAL;
+    const int G = o.K / W4A16_GROUP;
+    if (o.splits < 1 || o.splits > G || o.splits > w4a16::kMaxSplits) return W4A16_EINVAL;
+    if (o.kind == W4A16_CHAIN_SWIGLU && o.splits != 1) return W4A16_EINVAL;
+    if (!aligned16(o.wq) || !aligned16(o.scales) || !aligned16(o.zeros) || !aligned16(o.y)) return W4A16_EINVAL;
+    if (o.x_src < -1 || o.x_src >= j) return W4A16_EINVAL;
+    if (o.x_src < 0 && !aligned16(o.x)) return W4A16_EINVAL;
+    if (o.x_src >= 0 && (ops[o.x_src].N < o.K || o.x_shift < 0 || o.x_shift > 24)) return W4A16_EINVAL;
+    int wpt, tp;
+    chain_geometry(o.kind, G, o.splits, &wpt, &tp);
+    if (wpt == 0) return W4A16_EUNSUPPORTED;  // a wave's share would exceed 7 tiles: more splits needed
+    const int64_t row_tiles = (int64_t(o.N) + 15) / 16;
+    const int64_t items = (row_tiles + tp - 1) / tp * o.splits;
+    total += items;
+    if (total >= (int64_t(1) << 30) || row_tiles >= (int64_t(1) << 26)) return W4A16_EUNSUPPORTED;
+    if (o.splits > 1) ws = align_up(ws, 256) + align_up(size_t(8) * M * o.N, 256);
+  }
+  std::vector<char> consumed(size_t(n_ops), 0);
+  for (int j = 0; j < n_ops; ++j)
+    if (ops[j].x_src >= 0) consumed[size_t(ops[j].x_src)] = 1;
+  for (int j = 0; j < n_ops; ++j)
+    if (consumed[size_t(j)]) ws = align_up(ws, 256) + align_up(size_t(4) * M * ops[j].N, 256);
+  if (plan_bytes_needed) *plan_bytes_needed = need_plan;
+  if (ws_bytes_needed) *ws_bytes_needed = ws;
+  if (!plan) return W4A16_OK;
+  if (plan_bytes < need_plan) return W4A16_EINVAL;
+  // Second pass: the descriptors.
+  Header h;
+  std::memset(&h, 0, sizeof(h));
+  h.magic = kMagic;
+  h.M = M;
+  h.n_ops = n_ops;
+  h.total_items = int32_t(total);
+  h.plan_bytes = need_plan;
+  h.ws_bytes = ws;
+  std::vector<OpDev> d(static_cast<size_t>(n_ops));
+  std::memset(d.data(), 0, d.size() * sizeof(OpDev));
+  size_t off = kWsHeader;
+  std::vector<uint64_t> yt_off(size_t(n_ops), 0);
+  int begin = 0;
+  for (int j = 0; j < n_ops; ++j) {
+    const w4a16_chain_op& o = ops[j];
+    OpDev& e = d[size_t(j)];
+    e.wq = reinterpret_cast<uintptr_t>(o.wq);
+    e.sw = reinterpret_cast<uintptr_t>(o.scales);
+    e.zw = reinterpret_cast<uintptr_t>(o.zeros);
+    e.x_ext = o.x_src < 0 ? reinterpret_cast<uintptr_t>(o.x) : 0;
+    e.y = reinterpret_cast<uintptr_t>(o.y);
+    e.N = o.N;
+    e.K = o.K;
+    e.G = o.K / W4A16_GROUP;
+    e.kind = o.kind;
+    e.splits = o.splits;
+    chain_geometry(o.kind, e.G, o.splits, &e.wpt, &e.tp);
+    e.row_tiles = int32_t((int64_t(o.N) + 15) / 16);
+    e.per_split = (e.row_tiles + e.tp - 1) / e.tp;
+    e.items = e.per_split * o.splits;
+    e.item_begin = begin;
+    begin += e.items;
+    e.x_src = o.x_src;
+    e.x_shift = o.x_src >= 0 ? o.x_shift : 0;
+    if (o.splits > 1) {
+      off = align_up(off, 256);
+      e.acc_off = off;
+      off += align_up(size_t(8) * M * o.N, 256);
+    }
+  }
+  for (int j = 0; j < n_ops; ++j) {
+    if (!consumed[size_t(j)]) continue;
+    off = align_up(off, 256);
+    yt_off[size_t(j)] = off;
+    d[size_t(j)].yt_off = off;
+    off += align_up(size_t(4) * M * ops[j].N, 256);
+  }
+  for (int j = 0; j < n_ops; ++j) {
+    OpDev& e = d[size_t(j)];
+    if (e.x_src < 0) continue;
+    const int p = e.x_src;
+    e.xt_off = yt_off[size_t(p)];
+    e.x_stride = ops[p].N;
+    e.sentinel = int32_t((M - 1) * ops[p].N + ops[p].N - 1);
+  }
+  std::memcpy(plan, &h, sizeof(h));
+  std::memcpy(static_cast<char*>(plan) + sizeof(h), d.data(), d.size() * sizeof(OpDev));
+  return W4A16_OK;
+}
+
+extern "C" int w4a16_chain_run(int M, const void* plan_dev, void* workspace, size_t ws_bytes, void* stream) {
+  using namespace w4a16::chain;
+  if (M < 1 || !aligned16(plan_dev) || !aligned16(workspace) || ws_bytes < kWsHeader) return W4A16_EINVAL;
+  if (M > W4A16_MAX_M) return W4A16_EUNSUPPORTED;
+  if (M != 1) return W4A16_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int grid = resident_grid<1, 2>();
+  if (grid <= 0) return W4A16_EUNSUPPORTED;
+  if (launch_typed<1, 2>(plan_dev, workspace, ws_bytes, s, grid) != hipSuccess) return W4A16_EHIP;
+  return W4A16_OK;
+}

@@ -238,6 +238,12 @@ def gemv_swiglu(oracle, qg, sg, zg, qu, su, zu, x):
     most 2^-10 |y| more (plus ABS for underflow). Returns (ref, bound)."""
     g, ag = oracle.gemv(qg, sg, zg, x)
     u, au = oracle.gemv(qu, su, zu, x)
+    return swiglu_bound(g, ag, u, au)
+
+
+def swiglu_bound(g, ag, u, au):
+    """SwiGLU reference and bound from the gate and up GEMVs' fp64 results
+    (g, u) and their sums of |w x| (ag, au); see gemv_swiglu."""
     ref = silu(g) * u
     dg = BOUND_REL * ag + BOUND_ABS
     du = BOUND_REL * au + BOUND_ABS
