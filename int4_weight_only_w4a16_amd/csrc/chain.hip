@@ -100,7 +100,7 @@ struct alignas(16) OpDev {
   int32_t x_stride;   // producer's N: row stride of its tagged output, in words
   int32_t sentinel;   // word of the producer's tagged output the control wave polls
   int32_t x_src;
-  int32_t reserved;
+  int32_t split_q;    // G / splits
 };
 static_assert(sizeof(OpDev) == 128, "descriptor size");
 
@@ -118,7 +118,9 @@ struct LdsCtl {
   int abort;             // nonzero: leave
   int cnt[kSlots];       // compute waves that have written the slot's partial sums
   int gen[kSlots];       // times the slot has been consumed
-  int pad[6];
+  int xstaged[2];        // compute waves that have staged their part of x buffer b, over all its uses
+  int xfreed[2];         // compute waves that are done with x buffer b, over all its uses
+  int pad[2];
 };
 
 __device__ __forceinline__ uint32_t ld_dev(const W4A16_GLOBAL uint32_t* p) {
@@ -143,45 +145,102 @@ __device__ __forceinline__ int op_of(const OpDev* ops, int op, int k) {
   return op;
 }
 
+// A workgroup's walk over its items (every P-th item of the chain), kept in
+// scalar registers: the item, its GEMV's fields, and its split and tile
+// group. Advancing by P costs no division: a split boundary is crossed by
+// subtraction, and the split's groups [floor(s G / S), floor((s+1) G / S))
+// are tracked incrementally as s grows. Divisions happen only when the walk
+// enters a new GEMV.
+struct Walk {
+  int k, op, end;          // item, its GEMV, first item past that GEMV
+  int split, tg;           // split and tile group of item k
+  int g_beg, g_end, r_end; // the split's groups; r_end = (split + 1) G mod S
+  int G, kind, splits, tp, wpt, row_tiles, per_split, sq, sr;
+};
+
+__device__ __forceinline__ void walk_enter(Walk& w, const OpDev* ops) {
+  while (w.k >= ops[w.op].item_begin + ops[w.op].items) ++w.op;
+  const OpDev& d = ops[w.op];
+  w.end = d.item_begin + d.items;
+  w.G = d.G, w.kind = d.kind, w.splits = d.splits, w.tp = d.tp, w.wpt = d.wpt;
+  w.row_tiles = d.row_tiles, w.per_split = d.per_split, w.sq = d.split_q, w.sr = d.G - d.split_q * d.splits;
+  const int i = w.k - d.item_begin;
+  w.split = i / w.per_split;
+  w.tg = i - w.split * w.per_split;
+  w.g_beg = w.split * w.G / w.splits;
+  const int next = (w.split + 1) * w.G;
+  w.g_end = next / w.splits;
+  w.r_end = next - w.g_end * w.splits;
+}
+
+// Moves the walk P items on (within `total`).
+__device__ __forceinline__ void walk_advance(Walk& w, const OpDev* ops, int P, int total) {
+  w.k += P;
+  if (w.k >= total) return;
+  if (w.k >= w.end) {
+    walk_enter(w, ops);
+    return;
+  }
+  w.tg += P;
+  while (w.tg >= w.per_split) {
+    w.tg -= w.per_split;
+    ++w.split;
+    w.g_beg = w.g_end;
+    w.g_end += w.sq;
+    w.r_end += w.sr;
+    if (w.r_end >= w.splits) {
+      ++w.g_end;
+      w.r_end -= w.splits;
+    }
+  }
+}
+
 // Where a compute wave works in an item: the matrix row tile it reads and
-// its share of the item's K range.
+// its share of the item's K range (waves per tile: 4 or 8).
 struct Share {
   int64_t tile;
   int beg, n;
 };
 
-__device__ __forceinline__ Share share_of(const OpDev& d, int i, int wave) {
-  const int split = i / d.per_split, tg = i - split * d.per_split;
-  const int lt = wave / d.wpt, wi = wave - lt * d.wpt;
+__device__ __forceinline__ Share share_of(const Walk& w, int wave) {
+  const int sh = w.wpt == 8 ? 3 : 2;
+  const int lt = wave >> sh, wi = wave & (w.wpt - 1);
   int64_t tile;
-  if (d.kind == W4A16_CHAIN_SWIGLU) {
-    tile = 2 * int64_t(tg) + lt;  // gate tile 2 tg, up tile 2 tg + 1
+  if (w.kind == W4A16_CHAIN_SWIGLU) {
+    tile = 2 * int64_t(w.tg) + lt;  // gate tile 2 tg, up tile 2 tg + 1
   } else {
-    tile = int64_t(tg) * d.tp + lt;
-    if (tile >= d.row_tiles) tile = d.row_tiles - 1;  // a pair's missing second tile: valid, never stored
+    tile = int64_t(w.tg) * w.tp + lt;
+    if (tile >= w.row_tiles) tile = w.row_tiles - 1;  // a pair's missing second tile: valid, never stored
   }
-  const int g_beg = d.splits == 1 ? 0 : int(unsigned(split) * unsigned(d.G) / unsigned(d.splits));
-  const int g_end = d.splits == 1 ? d.G : int(unsigned(split + 1) * unsigned(d.G) / unsigned(d.splits));
-  const int ng = g_end - g_beg;
-  const int beg = g_beg + int(unsigned(wi * ng) / unsigned(d.wpt));
-  const int end = g_beg + int(unsigned((wi + 1) * ng) / unsigned(d.wpt));
+  const int ng = w.g_end - w.g_beg;
+  const int beg = w.g_beg + ((wi * ng) >> sh);
+  const int end = w.g_beg + (((wi + 1) * ng) >> sh);
   return Share{tile, beg, end - beg};
 }
+
+// The longest K a GEMV of the chain may have: each workgroup keeps a GEMV's
+// whole input in LDS (two buffers of kMaxK halves per activation row).
+constexpr int kMaxK = 20480;
 
 template <int MR>
 struct Geo {
   static constexpr int kRows = MR < 4 ? MR : 4;          // accumulators per lane (MFMA D rows used)
   static constexpr int kRedWave = 4 * kRows * 16;        // floats of one wave's partial sums
-  static constexpr int kXRow = kShare * kGroup + (MR > 1 ? 32 : 0);  // halves per x slice row
+  static constexpr int kXRow = kMaxK + (MR > 1 ? 32 : 0);  // halves per x row of a buffer
   static constexpr size_t kCtlBytes = sizeof(LdsCtl);
   static constexpr size_t kPartBytes = size_t(kSlots) * kComputeWaves * kRedWave * 4;
-  static constexpr size_t kXBytes = size_t(kComputeWaves) * MR * kXRow * 2;
+  static constexpr size_t kXBytes = size_t(2) * MR * kXRow * 2;
   static constexpr size_t kLds = kCtlBytes + kPartBytes + kXBytes;
 };
 
+// One share's requests: the weight tiles (16 bytes per lane each), and the
+// share's scale and zero words gathered one per lane -- lane 8u + i holds the
+// scale word i of tile u (rows 2i, 2i + 1), lane 2u + i its zero word i
+// (rows 8i .. 8i + 7) -- handed to the lanes that need them by a cross-lane
+// read at use.
 struct Buf {
   u32x4 w[kShare];
-  uint32_t sw[kShare], zw[kShare];
+  uint32_t sw, zw;
 };
 
 template <int MR, int NBUF>
@@ -202,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
     lc->ready = -1;
     lc->abort = 0;
     for (int s = 0; s < kSlots; ++s) lc->cnt[s] = 0, lc->gen[s] = 0;
+    lc->xstaged[0] = lc->xstaged[1] = lc->xfreed[0] = lc->xfreed[1] = 0;
   }
   const bool plan_ok = plan->magic == kMagic && plan->M == MR && plan->ws_bytes <= ws_bytes;
   const uint32_t err0 = ld_dev(ctl + kWsError);
@@ -219,7 +279,10 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
 
   if (wave == kComputeWaves) {
     // ---------------------------------------------------------------- control wave
-    int op_ep = 0, o_ep = 0;       // next item to finish: ordinal o_ep, item wg + o_ep P
+    int o_ep = 0;                  // next item to finish: ordinal o_ep, item wg + o_ep P
+    Walk we;                       // its position
+    we.k = wg, we.op = 0;
+    if (wg < total) walk_enter(we, ops);
     int op_need = 0, k_need = wg;  // next item whose producer must be seen
     uint64_t last_progress = t_start;
     bool failed = false;
@@ -231,10 +294,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
       const int slot = o_ep % kSlots;
       if (lds_ld(&lc->cnt[slot]) == kComputeWaves) {
         lds_acquire();
-        op_ep = op_of(ops, op_ep, k_ep);
-        const OpDev& d = ops[op_ep];
-        const int i = k_ep - d.item_begin;
-        const int split = i / d.per_split, tg = i - split * d.per_split;
+        const OpDev& d = ops[we.op];
+        const int tg = we.tg;
         const float* pb = part + size_t(slot) * kComputeWaves * GG::kRedWave;
         W4A16_GLOBAL uint32_t* yt = gptr<uint32_t>(wsa + d.yt_off);
         W4A16_GLOBAL uint16_t* yd = gptr<uint16_t>(d.y);
@@ -281,6 +342,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
         lds_release();
         lds_st(&lc->gen[slot], o_ep / kSlots + 1);
         ++o_ep;
+        walk_advance(we, ops, P, total);
         progressed = true;
       }
       // readiness of the next GEMV this workgroup reads from a producer
@@ -329,7 +391,6 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
   // ------------------------------------------------------------------ compute waves
   const int piece = lane >> 4, rlane = lane & 15;
   const int mm = rlane < MR ? rlane : MR - 1;
-  _Float16* xw = xs + size_t(wave) * MR * GG::kXRow;
   const uint32_t magic = dev::kMagic1024;
   bool failed = false;
 
@@ -350,6 +411,16 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
     }
     return true;
   };
+  // Waits until the LDS word reaches `target`; false if the wait gave up.
+  auto wait_lds = [&](int* word, int target) {
+    const uint64_t t0 = wall_clock64();
+    while (lds_ld(word) < target) {
+      if (!may_wait(t0)) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    lds_acquire();
+    return true;
+  };
 
   // A share's weight tiles, scales and zero words as buffer loads: the row
   // tile's base goes into the (scalar) resource, the group into the scalar
@@ -359,7 +430,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
   // false gives the resources 0 records: the same requests go out and come
   // back as zeros without touching memory, so every path issues the same
   // number of requests and every wait count stays exact.
-  const int w_voff = lane * 16, s_voff = (rlane >> 1) * 4, z_voff = (rlane >> 3) * 4;
+  const int w_voff = lane * 16;
+  const int s_tile = min(lane >> 3, kShare - 1), s_word = lane & 7;  // scale word gathered by this lane
+  const int z_tile = min(lane >> 1, kShare - 1), z_word = lane & 1;  // zero word gathered by this lane
   auto load = [&](Buf& b, const OpDev& d, const Share& s, bool live) {
     const uint64_t q0 = uint64_t(s.tile) * uint64_t(d.G);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -372,112 +445,98 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
     for (int u = 0; u < kShare; ++u) {
       const int gg = max(s.beg + min(u, s.n - 1), 0);
       b.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_voff, gg * kTileBytes, 2 /* nt */);
-      b.sw[u] = __builtin_amdgcn_raw_buffer_load_b32(rsc, s_voff, gg * 32, 0);
-      b.zw[u] = __builtin_amdgcn_raw_buffer_load_b32(rz, z_voff, gg * 8, 0);
     }
+    const int gs = max(s.beg + min(s_tile, s.n - 1), 0), gz = max(s.beg + min(z_tile, s.n - 1), 0);
+    b.sw = __builtin_amdgcn_raw_buffer_load_b32(rsc, gs * 32 + s_word * 4, 0, 0);
+    b.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, gz * 8 + z_word * 4, 0, 0);
   };
 
-  // x of a share: tagged words (4 per 16-byte chunk, tag checked) or the
-  // external fp16 input (8 per chunk). Chunks past the share are clamped
-  // copies of its last chunk: every request is in bounds and unconditional.
-  constexpr int kTChunksRow = kShare * kGroup / 4, kTSteps = (MR * kTChunksRow + 63) / 64;
-  constexpr int kEChunksRow = kShare * kGroup / 8, kESteps = (MR * kEChunksRow + 63) / 64;
-  auto tchunk = [&](int j, int n, int& m, int& cc) {
-    const int c = min(lane + 64 * j, MR * kTChunksRow - 1);
-    m = MR == 1 ? 0 : c / kTChunksRow;
-    cc = min(c - m * kTChunksRow, n * (kGroup / 4) - 1);
-  };
-  auto echunk = [&](int j, int n, int& m, int& cc) {
-    const int c = min(lane + 64 * j, MR * kEChunksRow - 1);
-    m = MR == 1 ? 0 : c / kEChunksRow;
-    cc = min(c - m * kEChunksRow, n * (kGroup / 8) - 1);
-  };
-  // Requests of the share's x: a resource based at the share's first column
-  // (uniform), the lane's chunk offset as the vector operand. sc1 == false:
-  // plain loads (an L2 hit serves the other compute units of the same chip
-  // die); true: device scope, for chunks found stale.
-  auto t_request = [&](u32x4 (&tv)[kTSteps], const OpDev& d, const Share& s, bool sc1) {
+  // Staging of a GEMV's whole input (all M rows, all K) into x buffer xb,
+  // the eight compute waves taking 64-chunk blocks in turn: this wave's
+  // blocks are wave, wave + 8, ... A chunk is 16 bytes: four tagged words
+  // (x from a producer: tag checked, fp16 value scaled by 2^-x_shift and
+  // rounded to fp16) or eight fp16 values (external x). Requests go out in
+  // batches of kBatch chunks per lane; chunks past the end repeat the last
+  // one (in bounds; they rewrite the same values). Stale words are requested
+  // again with device-scope loads until they carry the launch's tag.
+  constexpr int kBatch = 4;
+  auto stage_part = [&](const OpDev& d, _Float16* xb) -> bool {
+    const bool tagged = d.x_src >= 0;
+    const int per_row = tagged ? d.K / 4 : d.K / 8;  // chunks per activation row
+    const int total_chunks = MR * per_row;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        ws + d.xt_off + uint64_t(s.beg) * kGroup * 4, (short)0, 0x7fffffff, 0x00020000);
-#pragma unroll
-    for (int j = 0; j < kTSteps; ++j) {
-      int m, cc;
-      tchunk(j, s.n, m, cc);
-      const int off = (m * d.x_stride + cc * 4) * 4;
-      if (sc1)
-        tv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16);
-      else
-        tv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-    }
-  };
-  // Every word of the wave's chunks carries this launch's tag?
-  auto t_fresh = [&](const u32x4 (&tv)[kTSteps]) {
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < kTSteps; ++j)
-      ok &= (tv[j].x >> 16) == tag && (tv[j].y >> 16) == tag && (tv[j].z >> 16) == tag && (tv[j].w >> 16) == tag;
-    return __builtin_amdgcn_read_exec() == __ballot(ok);
-  };
-  auto t_store = [&](const u32x4 (&tv)[kTSteps], const OpDev& d, const Share& s) {
+        tagged ? reinterpret_cast<void*>(ws + d.xt_off) : reinterpret_cast<void*>(d.x_ext), (short)0, 0x7fffffff,
+        0x00020000);
     const float scale = __builtin_ldexpf(1.0f, -d.x_shift);  // exact power of two
+    for (int j0 = 0; (j0 * kComputeWaves + wave) * 64 < total_chunks; j0 += kBatch) {
+      int m[kBatch], cw[kBatch];
+      u32x4 v[kBatch];
 #pragma unroll
-    for (int j = 0; j < kTSteps; ++j) {
-      int m, cc;
-      tchunk(j, s.n, m, cc);
-      const u32x4 v = tv[j];
-      const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v.x & 0xFFFFu) * scale));
-      const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v.y & 0xFFFFu) * scale));
-      const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v.z & 0xFFFFu) * scale));
-      const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v.w & 0xFFFFu) * scale));
-      uint2 packed;
-      packed.x = h0 | (h1 << 16);
-      packed.y = h2 | (h3 << 16);
-      *reinterpret_cast<uint2*>(xw + m * GG::kXRow + cc * 4) = packed;
-    }
-  };
-  static_assert(kESteps <= kTSteps, "external x chunks fit the tagged registers");
-  auto e_request = [&](u32x4 (&ev)[kTSteps], const OpDev& d, const Share& s) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>(d.x_ext + uint64_t(s.beg) * kGroup * 2), (short)0, 0x7fffffff, 0x00020000);
+      for (int j = 0; j < kBatch; ++j) {
+        const int c = min(((j0 + j) * kComputeWaves + wave) * 64 + lane, total_chunks - 1);
+        m[j] = MR == 1 ? 0 : c / per_row;
+        cw[j] = c - m[j] * per_row;
+        const int off = tagged ? (m[j] * d.x_stride + cw[j] * 4) * 4 : (m[j] * d.K + cw[j] * 8) * 2;
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      }
+      if (tagged) {
+        auto fresh = [&]() {
+          bool ok = true;
 #pragma unroll
-    for (int j = 0; j < kESteps; ++j) {
-      int m, cc;
-      echunk(j, s.n, m, cc);
-      ev[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (m * d.K + cc * 8) * 2, 0, 0);
-    }
-  };
-  auto e_store = [&](const u32x4 (&ev)[kTSteps], const Share& s) {
+          for (int j = 0; j < kBatch; ++j)
+            ok &= (v[j].x >> 16) == tag && (v[j].y >> 16) == tag && (v[j].z >> 16) == tag && (v[j].w >> 16) == tag;
+          return __builtin_amdgcn_read_exec() == __ballot(ok);
+        };
+        if (!fresh()) {
+          const uint64_t t0 = wall_clock64();
+          do {
+            if (!may_wait(t0)) return false;
+            __builtin_amdgcn_s_sleep(2);
 #pragma unroll
-    for (int j = 0; j < kESteps; ++j) {
-      int m, cc;
-      echunk(j, s.n, m, cc);
-      *reinterpret_cast<u32x4*>(xw + m * GG::kXRow + cc * 8) = ev[j];
+            for (int j = 0; j < kBatch; ++j)
+              v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (m[j] * d.x_stride + cw[j] * 4) * 4, 0, 16 /* sc1 */);
+          } while (!fresh());
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v[j].x & 0xFFFFu) * scale));
+          const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v[j].y & 0xFFFFu) * scale));
+          const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v[j].z & 0xFFFFu) * scale));
+          const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)(dev::half_bits_to_float(v[j].w & 0xFFFFu) * scale));
+          uint2 packed;
+          packed.x = h0 | (h1 << 16);
+          packed.y = h2 | (h3 << 16);
+          *reinterpret_cast<uint2*>(xb + m[j] * GG::kXRow + cw[j] * 4) = packed;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) *reinterpret_cast<u32x4*>(xb + m[j] * GG::kXRow + cw[j] * 8) = v[j];
+      }
     }
-  };
-  auto slice_done = [&]() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    return true;
   };
 
-  auto compute = [&](const Buf& b, const Share& s, float (&acc)[GG::kRows]) {
+  // The item's products: per tile, four MFMAs over the unpacked weights
+  // (x from the LDS buffer as the A operand), the group sum scaled by its
+  // fp16 scale and added in tile order -- the fp32 operations of the
+  // standalone kernel, in the same order. Tiles past the share (clamped
+  // duplicates) are computed and discarded by a select. Every request of
+  // the buffer has arrived (the wait for it is exact), so the tiles are left
+  // to the compiler's scheduling.
+  auto compute = [&](const Buf& b, const Share& s, const _Float16* xb, float (&acc)[GG::kRows]) {
 #pragma unroll
     for (int r = 0; r < GG::kRows; ++r) acc[r] = 0.f;
     if (s.n <= 0) return;
-    int xoff = 8 * piece;
-    asm volatile("" : "+v"(xoff));
-    const _Float16* xbase = xw + xoff;
-    f32x4 dsave[kShare];
-    float ssave[kShare];
+    const _Float16* xbase = xb + s.beg * kGroup + 8 * piece;
 #pragma unroll
     for (int u = 0; u < kShare; ++u) {
-      __builtin_amdgcn_sched_barrier(0);
-      u32x4 wt = b.w[u];
-      uint32_t zt = b.zw[u], st = b.sw[u];
-      asm volatile("" : "+v"(wt), "+v"(zt), "+v"(st));
+      const u32x4 wt = b.w[u];
+      // this lane's scale and zero words of tile u, from the lanes that hold them
+      const uint32_t st = uint32_t(__builtin_amdgcn_ds_bpermute((u * 8 + (rlane >> 1)) * 4, int(b.sw)));
+      const uint32_t zt = uint32_t(__builtin_amdgcn_ds_bpermute((u * 2 + (rlane >> 3)) * 4, int(b.zw)));
       const dev::ZeroPairs zp = dev::zero_pairs((zt >> ((rlane & 7) * 4)) & 15u);
       const float sc = dev::half_bits_to_float((st >> ((rlane & 1) * 16)) & 0xFFFFu);
-      const _Float16* xg = xbase + u * kGroup;
+      const _Float16* xg = xbase + min(u, s.n - 1) * kGroup;  // clamped tiles read the last tile's x
       f32x4 dd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -487,14 +546,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
         const dev::half8_t ax = *reinterpret_cast<const dev::half8_t*>(xg + mm * GG::kXRow + 32 * kb);
         dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, dd, 0, 0, 0);
       }
-      dsave[u] = dd;
-      ssave[u] = sc;
-    }
-#pragma unroll
-    for (int u = 0; u < kShare; ++u) {
       const bool valid = u < s.n;
 #pragma unroll
-      for (int r2 = 0; r2 < GG::kRows; ++r2) acc[r2] = valid ? __builtin_fmaf(dsave[u][r2], ssave[u], acc[r2]) : acc[r2];
+      for (int r2 = 0; r2 < GG::kRows; ++r2) acc[r2] = valid ? __builtin_fmaf(dd[r2], sc, acc[r2]) : acc[r2];
     }
   };
 
@@ -514,90 +568,66 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
   };
 
   // One item: ordinal o (item wg + o P) with weights in `cur`; the weights of
-  // ordinal o + NBUF - 1 go into `nxt`.
-  int op_c = 0, op_p = 0;
-  auto step = [&](int o, const Buf& cur, Buf& nxt) {
-    const int k = wg + o * P;
-    op_c = op_of(ops, op_c, k);
-    const OpDev& d = ops[op_c];
-    const Share s = share_of(d, k - d.item_begin, wave);
-    const int kp = k + (NBUF - 1) * P;
-    // The next weights (dead requests past the chain's end or for an empty
-    // share: see load()).
-    auto prefetch = [&]() {
-      const bool valid = kp < total;
-      if (valid) op_p = op_of(ops, op_p, kp);
-      const OpDev& dp = ops[valid ? op_p : op_c];
-      const Share sp = share_of(dp, (valid ? kp : k) - dp.item_begin, wave);
-      load(nxt, dp, sp, valid && sp.n > 0);
-    };
-    // One request site for the next weights (a single definition of their
-    // registers: no copies, so no waits for them). The x requests go ahead
-    // of it when the input is ready -- then the wait for x counts exactly
-    // the weight requests behind it (requests complete in order) -- and
-    // after it otherwise, so that the wave waits with the next weights in
-    // flight.
-    const bool tagged = d.x_src >= 0, have = s.n > 0;
-    const bool early = !tagged || lds_ld(&lc->ready) >= op_c;
-    u32x4 tv[kTSteps];
-    if (have && early) {
-      if (tagged)
-        t_request(tv, d, s, false);
-      else
-        e_request(tv, d, s);
+  // ordinal o + NBUF - 1 go into `nxt` first (one request site, so their
+  // registers have a single definition and are never copied). At the first
+  // item of a GEMV the waves stage its input into the next x buffer (those
+  // requests follow the weights' and wait for them: this happens once per
+  // GEMV, mostly while the input is not there yet anyway).
+  int cur_op = -1, nchg = 0;
+  Walk wc, wp;  // the item being computed, and the one whose weights are requested
+  wc.k = wg, wc.op = 0;
+  if (wg < total) walk_enter(wc, ops);
+  wp = wc;
+  auto step = [&](const Buf& cur, Buf& nxt, int o) {
+    const Share s = share_of(wc, wave);
+    {
+      const bool valid = wp.k < total;
+      const Share sp = valid ? share_of(wp, wave) : s;
+      load(nxt, ops[valid ? wp.op : wc.op], sp, valid && sp.n > 0);
+      walk_advance(wp, ops, P, total);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    prefetch();
-    __builtin_amdgcn_sched_barrier(0);
-    if (have && !early) {
-      const uint64_t t0 = wall_clock64();
-      while (lds_ld(&lc->ready) < op_c) {
-        if (!may_wait(t0)) return;
-        __builtin_amdgcn_s_sleep(1);
+    if (wc.op != cur_op) {
+      const OpDev& d = ops[wc.op];
+      const int b = nchg & 1, g = nchg >> 1;
+      if (cur_op >= 0) {  // done with the previous GEMV's buffer
+        lds_release();
+        if (lane == 0)
+          __hip_atomic_fetch_add(&lc->xfreed[b ^ 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-      t_request(tv, d, s, false);
-    }
-    if (have) {
-      if (tagged) {
-        if (!t_fresh(tv)) {
-          const uint64_t t0 = wall_clock64();
-          do {
-            if (!may_wait(t0)) return;
-            __builtin_amdgcn_s_sleep(2);
-            t_request(tv, d, s, true);
-          } while (!t_fresh(tv));
-        }
-        t_store(tv, d, s);
-      } else {
-        e_store(tv, s);
-      }
-      slice_done();
+      if (!wait_lds(&lc->xfreed[b], kComputeWaves * g)) return;  // its use before last is over
+      if (d.x_src >= 0 && !wait_lds(&lc->ready, wc.op)) return;  // producer seen finishing
+      if (!stage_part(d, xs + size_t(b) * MR * GG::kXRow)) return;
+      lds_release();
+      if (lane == 0)
+        __hip_atomic_fetch_add(&lc->xstaged[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (!wait_lds(&lc->xstaged[b], kComputeWaves * (g + 1))) return;  // every part staged
+      cur_op = wc.op;
+      ++nchg;
     }
     float acc[GG::kRows];
-    compute(cur, s, acc);
+    compute(cur, s, xs + size_t((nchg - 1) & 1) * MR * GG::kXRow, acc);
     hand_in(o, acc);
+    walk_advance(wc, ops, P, total);
   };
 
   Buf bufs[NBUF];
 #pragma unroll
   for (int i = 0; i + 1 < NBUF; ++i) {
-    const int k = wg + i * P;
-    if (k < total) {
-      op_p = op_of(ops, op_p, k);
-      const OpDev& dp = ops[op_p];
-      const Share sp = share_of(dp, k - dp.item_begin, wave);
-      load(bufs[i], dp, sp, sp.n > 0);
+    if (wp.k < total) {
+      const Share sp = share_of(wp, wave);
+      load(bufs[i], ops[wp.op], sp, sp.n > 0);
     }
+    walk_advance(wp, ops, P, total);
   }
   bool more = true;
   for (int o0 = 0; more; o0 += NBUF) {
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
-      if (!more || failed || wg + (o0 + j) * P >= total) {
+      if (!more || failed || wc.k >= total) {
         more = false;
         break;
       }
-      step(o0 + j, bufs[j], bufs[(j + NBUF - 1) % NBUF]);
+      step(bufs[j], bufs[(j + NBUF - 1) % NBUF], o0 + j);
     }
   }
 }
@@ -683,6 +713,7 @@ extern "C" int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, voi
     const int G = o.K / W4A16_GROUP;
     if (o.splits < 1 || o.splits > G || o.splits > w4a16::kMaxSplits) return W4A16_EINVAL;
     if (o.kind == W4A16_CHAIN_SWIGLU && o.splits != 1) return W4A16_EINVAL;
+    if (o.K > kMaxK) return W4A16_EUNSUPPORTED;  // a workgroup keeps the whole input in LDS
     if (!aligned16(o.wq) || !aligned16(o.scales) || !aligned16(o.zeros) || !aligned16(o.y)) return W4A16_EINVAL;
     if (o.x_src < -1 || o.x_src >= j) return W4A16_EINVAL;
     if (o.x_src < 0 && !aligned16(o.x)) return W4A16_EINVAL;
@@ -740,6 +771,7 @@ extern "C" int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, voi
     begin += e.items;
     e.x_src = o.x_src;
     e.x_shift = o.x_src >= 0 ? o.x_shift : 0;
+    e.split_q = e.G / o.splits;
     if (o.splits > 1) {
       off = align_up(off, 256);
       e.acc_off = off;
@@ -772,8 +804,8 @@ extern "C" int w4a16_chain_run(int M, const void* plan_dev, void* workspace, siz
   if (M > W4A16_MAX_M) return W4A16_EUNSUPPORTED;
   if (M != 1) return W4A16_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int grid = resident_grid<1, 2>();
+  const int grid = resident_grid<1, 3>();
   if (grid <= 0) return W4A16_EUNSUPPORTED;
-  if (launch_typed<1, 2>(plan_dev, workspace, ws_bytes, s, grid) != hipSuccess) return W4A16_EHIP;
+  if (launch_typed<1, 3>(plan_dev, workspace, ws_bytes, s, grid) != hipSuccess) return W4A16_EHIP;
   return W4A16_OK;
 }

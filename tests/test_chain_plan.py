@@ -21,7 +21,7 @@ OPDEV = np.dtype([("wq", "<u8"), ("sw", "<u8"), ("zw", "<u8"), ("x_ext", "<u8"),
                   ("xt_off", "<u8"), ("acc_off", "<u8"), ("N", "<i4"), ("K", "<i4"), ("G", "<i4"), ("kind", "<i4"),
                   ("splits", "<i4"), ("tp", "<i4"), ("wpt", "<i4"), ("row_tiles", "<i4"), ("per_split", "<i4"),
                   ("items", "<i4"), ("item_begin", "<i4"), ("x_shift", "<i4"), ("x_stride", "<i4"),
-                  ("sentinel", "<i4"), ("x_src", "<i4"), ("reserved", "<i4")])
+                  ("sentinel", "<i4"), ("x_src", "<i4"), ("split_q", "<i4")])
 WAVES, SHARE, LANES = 8, 7, 64
 
 
@@ -104,6 +104,19 @@ def walk(plan, ops, sizes, M):
             assert d[p]["item_begin"] + d[p]["items"] <= e["item_begin"]
         if e["splits"] > 1:
             assert e["acc_off"] >= 256 and e["acc_off"] + 8 * M * N <= ws_bytes and e["acc_off"] % 256 == 0
+        # staging of the whole input: 16-byte chunks of tagged words (4 per
+        # chunk) or of external fp16 values (8 per chunk), all rows
+        K = int(e["K"])
+        if e["x_src"] >= 0:
+            c = np.arange(M * K // 4)
+            m, cw = c // (K // 4), c % (K // 4)
+            word = m * int(e["x_stride"]) + cw * 4
+            assert (word + 4 <= M * int(e["x_stride"])).all() and (cw * 4 + 4 <= K).all()
+        else:
+            c = np.arange(M * K // 8)
+            m, cw = c // (K // 8), c % (K // 8)
+            assert ((m * K + cw * 8) * 2 + 16 <= sizes[int(e["x_ext"])]).all()
+        assert K <= 20480  # the LDS x buffer
         for i in range(int(e["items"])):
             for wave in range(WAVES):
                 tile, beg, n = share_of(e, i, wave)
@@ -121,23 +134,6 @@ def walk(plan, ops, sizes, M):
                 assert ((q0 + gg) * 1024 + 1024 <= wb).all() and (gg * 1024 + lanes.max() * 16 + 16 <= G * 1024).all()
                 assert ((q0 + gg) * 32 + (rlane.max() >> 1) * 4 + 4 <= sb).all()
                 assert ((q0 + gg) * 8 + (rlane.max() >> 3) * 4 + 4 <= zb).all()
-                # x slice: chunks clamped to the share
-                if e["x_src"] >= 0:
-                    t_row = SHARE * 128 // 4
-                    c = np.minimum(lanes[:, None] + 64 * np.arange((M * t_row + 63) // 64)[None, :], M * t_row - 1)
-                    m = c // t_row
-                    cc = np.minimum(c - m * t_row, n * 32 - 1)
-                    word = m * int(e["x_stride"]) + beg * 128 + cc * 4
-                    assert word.min() >= 0 and (word + 4 <= M * int(e["x_stride"])).all()
-                    assert (cc * 4 + 4 <= n * 128).all() and (beg * 128 + cc * 4 + 4 <= int(e["K"])).all()
-                else:
-                    e_row = SHARE * 128 // 8
-                    c = np.minimum(lanes[:, None] + 64 * np.arange((M * e_row + 63) // 64)[None, :], M * e_row - 1)
-                    m = c // e_row
-                    cc = np.minimum(c - m * e_row, n * 16 - 1)
-                    half = m * int(e["K"]) + beg * 128 + cc * 8
-                    assert (half + 8 <= M * int(e["K"])).all()
-                    assert sizes[int(e["x_ext"])] == 2 * M * int(e["K"])
             # outputs of the item (control wave)
             split, tg = i // int(e["per_split"]), i % int(e["per_split"])
             tiles_out = 1 if e["kind"] == w.CHAIN_SWIGLU else int(e["tp"])
@@ -230,3 +226,72 @@ def test_chain_plan_rejects():
     assert L.w4a16_chain_run(1, 1 << 20, (1 << 20) + 8, 4096, None) == w.W4A16_EINVAL
     assert L.w4a16_chain_run(1, 1 << 20, 1 << 20, 100, None) == w.W4A16_EINVAL
     assert L.w4a16_chain_run(9, 1 << 20, 1 << 20, 4096, None) == w.W4A16_EUNSUPPORTED
+
+
+class Walk:
+    """The kernel's incremental walk (walk_enter / walk_advance), field for field."""
+
+    def __init__(self, d, k):
+        self.d, self.k, self.op = d, k, 0
+        self.enter()
+
+    def enter(self):
+        d = self.d
+        while self.k >= d[self.op]["item_begin"] + d[self.op]["items"]:
+            self.op += 1
+        e = d[self.op]
+        self.end = int(e["item_begin"] + e["items"])
+        self.G, self.S, self.per_split = int(e["G"]), int(e["splits"]), int(e["per_split"])
+        self.sq = int(e["split_q"])
+        self.sr = self.G - self.sq * self.S
+        i = self.k - int(e["item_begin"])
+        self.split, self.tg = i // self.per_split, i % self.per_split
+        self.g_beg = self.split * self.G // self.S
+        nxt = (self.split + 1) * self.G
+        self.g_end, self.r_end = nxt // self.S, nxt % self.S
+
+    def advance(self, P, total):
+        self.k += P
+        if self.k >= total:
+            return
+        if self.k >= self.end:
+            self.enter()
+            return
+        self.tg += P
+        while self.tg >= self.per_split:
+            self.tg -= self.per_split
+            self.split += 1
+            self.g_beg = self.g_end
+            self.g_end += self.sq
+            self.r_end += self.sr
+            if self.r_end >= self.S:
+                self.g_end += 1
+                self.r_end -= self.S
+
+
+@pytest.mark.parametrize("P", [1, 7, 100, 256, 300])
+def test_incremental_walk_matches_division(P):
+    """Every workgroup's walk, advanced P items at a time, gives the GEMV,
+    split, tile group and split range that direct division gives."""
+    M = 1
+    spec = [(w.CHAIN_GEMV, 520, 1024, 1, -1, 0), (w.CHAIN_GEMV, 300, 512, 2, 0, 3),
+            (w.CHAIN_SWIGLU, 200, 256, 1, 1, 2), (w.CHAIN_GEMV, 96, 128, 1, 2, 0),
+            (w.CHAIN_GEMV, 64, 7168, 1, -1, 0), (w.CHAIN_GEMV, 33, 4864, 4, -1, 0),
+            (w.CHAIN_GEMV, 3584, 18944, 4, -1, 0), (w.CHAIN_GEMV, 2000, 3968, 31, -1, 0),
+            (w.CHAIN_GEMV, 17, 1280, 7, -1, 0)]
+    ops, _ = make_ops(M, spec)
+    plan, _ = w.w4a16_chain_plan(M, ops)
+    h, d = parse(plan)
+    total = int(h["total"])
+    begins = np.asarray(d["item_begin"], dtype=np.int64)
+    for wg in range(min(P, total)):
+        wk = Walk(d, wg)
+        while wk.k < total:
+            j = int(np.searchsorted(begins, wk.k, side="right") - 1)
+            e = d[j]
+            i = wk.k - int(e["item_begin"])
+            split, tg = i // int(e["per_split"]), i % int(e["per_split"])
+            G, S = int(e["G"]), int(e["splits"])
+            assert (wk.op, wk.split, wk.tg) == (j, split, tg)
+            assert (wk.g_beg, wk.g_end) == (split * G // S, (split + 1) * G // S)
+            wk.advance(P, total)
