@@ -405,12 +405,12 @@ int w4a16_read_probe(const void* buf, size_t bytes, int grid, void* sink, void* 
  *   kind   W4A16_CHAIN_GEMV: y = W x as w4a16_gemv / w4a16_gemv_splitk;
  *          W4A16_CHAIN_SWIGLU: y = silu(gate x) * (up x) as
  *          w4a16_gemv_swiglu (W from w4a16_pack_gate_up, N = F, the output
- *          width; K at most 3584 and splits 1).
- *   N, K   output and input features (K a multiple of 128).
+ *          width; splits 1).
+ *   N, K   output and input features (K a multiple of 128, at most 32768:
+ *          each workgroup holds a GEMV's whole input in LDS).
  *   splits K ranges combined by the split-K fixed-point atomics (1..31).
- *          Each wave takes at most 7 tiles of a range (5 when split): K/128
- *          / splits must be at most 56 (40 when split), else
- *          W4A16_EUNSUPPORTED.
+ *          A wave takes its share of a range in rounds of at most 7 tiles
+ *          (16 x 128 weights each).
  *   x_src  -1: the input is `x`, fp16 [M][K] on the device; otherwise the
  *          index of an earlier GEMV of the chain whose output has at least K
  *          columns: the input is its first K columns, times 2^-x_shift
@@ -438,9 +438,8 @@ typedef struct w4a16_chain_op {
  * plan's size and the workspace size w4a16_chain_run needs. The plan holds
  * the device pointers of `ops`: it is valid as long as those buffers are.
  * Errors: W4A16_EINVAL (a bad kind, shape, split count, pointer, x_src or
- * x_shift, or plan_bytes too small), W4A16_EUNSUPPORTED (M > 8, or a GEMV
- * whose waves' shares would exceed 7 tiles). Host only; allocates nothing
- * the caller sees.
+ * x_shift, or plan_bytes too small), W4A16_EUNSUPPORTED (M > 8, or K above
+ * 32768). Host only; allocates nothing the caller sees.
  */
 int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, void* plan, size_t plan_bytes,
                      size_t* plan_bytes_needed, size_t* ws_bytes_needed);
@@ -457,9 +456,10 @@ int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, void* plan, si
  *     one stream; runs that may overlap in time need different workspaces.
  *   Every GEMV's y is written. Each output has the arithmetic of the
  *   standalone entry points with the same waves and shares (bit-identical to
- *   w4a16_gemv for K = 3584 unsplit, to w4a16_gemv_swiglu, and to
- *   w4a16_gemv_splitk with 4 splits of K = 18944, given the same input).
- * The launch has one workgroup per compute unit and needs all of them
+ *   w4a16_gemv for K = 3584 unsplit, to w4a16_gemv_swiglu for K = 3584, and
+ *   to w4a16_gemv_splitk with 4 splits of K = 18944, given the same input);
+ *   every output is within the bound of the plain matrix-vector product.
+ * The launch has two workgroups per compute unit and needs all of them
  * resident at once: nothing else may occupy the device's compute units while
  * it runs. The uint32 at byte 8 of the workspace is 0 after a completed run;
  * 1 if a wait ran out (1 s without progress: residency was lost), 2 if the

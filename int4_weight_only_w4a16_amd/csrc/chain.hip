@@ -10,24 +10,23 @@
 // workgroup requests the weights of its next work items before it waits for
 // their input, so the weight stream goes on across every dependency.
 //
-// Structure. One workgroup per compute unit, all resident at once (checked
-// at launch): 8 compute waves and 1 control wave. The chain's work items --
-// (GEMV, 16-row tile or tile pair, K range) -- are numbered in chain order,
-// and workgroup w takes items w, w + P, w + 2P, ... (P workgroups).
-//  - A compute wave takes a fixed share of every item's K range (as the
-//    standalone kernels' waves do). For item k it (1) waits until the
-//    control wave has seen the item's producer finish, (2) requests its x
-//    slice, (3) requests the weights of item k + (NBUF-1) P, (4) checks and
-//    converts x into its private LDS slice, (5) multiplies item k, whose
-//    weights were requested NBUF-1 items ago, and (6) hands its fp32 partial
-//    sums to the control wave through an LDS slot. When the input is not
-//    ready yet, (3) goes before (1), so the wave waits with NBUF items of
-//    weights in flight.
-//  - The control wave adds each item's partial sums in wave order and does
-//    the epilogue (fp16 store, SwiGLU, or the split-K fixed-point atomics),
-//    and polls one word of each producer its workgroup will need, publishing
-//    readiness in LDS. It never waits for another workgroup, so a workgroup
-//    never waits for itself.
+// Structure. Two workgroups of 8 waves per compute unit, all resident at
+// once (checked at launch). The chain's work items -- (GEMV, 16-row tile or
+// tile pair, K range) -- are numbered in chain order, and workgroup w takes
+// items w, w + P, w + 2P, ... (P workgroups). A wave takes a fixed share of
+// every item's K range (as the standalone kernels' waves do), in rounds of
+// at most 7 tiles when the share is longer. Per round it (1) requests the
+// weights of the round NBUF - 1 rounds on, (2) multiplies the round whose
+// weights were requested a round ago, with x from LDS, and, at an item's last
+// round, (3) hands its fp32 partial sums in through an LDS slot. At the
+// first round of a GEMV the waves first stage the GEMV's whole input into
+// LDS -- wave 0 polls the producer's last output word, the others wait in
+// LDS -- while that round's weights are already in flight.
+// The epilogue of an item (its partial sums added in wave order, then the
+// fp16 store, SwiGLU, or the split-K fixed-point atomics) rotates over the
+// waves: wave o % 8 does item o's one item later, when every wave has
+// almost always handed it in, or at once for the workgroup's last item of a
+// GEMV, whose consumers wait for it.
 //
 // Handoff between GEMVs. A GEMV whose output feeds another also writes each
 // output as a 32-bit word (fp16 bits | tag << 16) with device-scope stores,
@@ -40,8 +39,11 @@
 //
 // Progress. Item k waits only for GEMVs of smaller item numbers, every
 // workgroup takes its items in increasing order, and all workgroups are
-// resident, so the smallest unfinished item can always finish. Every wait
-// is bounded (kWaitTicks of the 100 MHz real-time counter); a wait that
+// resident, so the smallest unfinished item can always finish. Inside a
+// workgroup every wait is for an earlier item (a slot is reused once the
+// epilogue of the item 4 before has run; an epilogue waits for the item's
+// hand-ins; a deferred epilogue never crosses into the next GEMV). Every
+// wait is bounded (kWaitTicks of the 100 MHz real-time counter); a wait that
 // runs out sets the workspace error word and every workgroup leaves.
 //
 // The arithmetic of an item is that of the standalone kernels with the same
@@ -64,10 +66,10 @@ namespace chain {
 using dev::f32x4;
 using dev::u32x4;
 
-constexpr int kComputeWaves = 8;
-constexpr int kThreads = (kComputeWaves + 1) * 64;
-constexpr int kShare = 7;   // tiles per wave and item, at most
-constexpr int kSlots = 4;   // partial-sum slots between compute waves and control wave
+constexpr int kWaves = 8;   // waves per workgroup, all computing
+constexpr int kThreads = kWaves * 64;
+constexpr int kShare = 7;   // tiles per wave and round, at most
+constexpr int kSlots = 4;   // partial-sum slots of a workgroup (items a wave may run ahead)
 constexpr uint32_t kMagic = 0x57344348u;  // "W4CH"
 constexpr uint64_t kWaitTicks = 100000000ull;  // 1 s of the 100 MHz counter
 
@@ -98,11 +100,13 @@ struct alignas(16) OpDev {
   int32_t splits, tp, wpt, row_tiles;       // tiles per item, waves per tile, output row tiles
   int32_t per_split, items, item_begin, x_shift;
   int32_t x_stride;   // producer's N: row stride of its tagged output, in words
-  int32_t sentinel;   // word of the producer's tagged output the control wave polls
+  int32_t sentinel;   // word of the producer's tagged output polled before staging
   int32_t x_src;
   int32_t split_q;    // G / splits
+  int32_t rounds;     // rounds of at most kShare tiles per wave and item
+  int32_t pad[3];
 };
-static_assert(sizeof(OpDev) == 128, "descriptor size");
+static_assert(sizeof(OpDev) == 144, "descriptor size");
 
 struct alignas(16) Header {
   uint32_t magic;
@@ -114,23 +118,27 @@ static_assert(sizeof(Header) == 64, "header size");
 
 // LDS control block.
 struct LdsCtl {
-  int ready;             // highest GEMV index whose producer the control wave has seen finish
+  int ready;             // highest GEMV index whose producer wave 0 has seen finish
   int abort;             // nonzero: leave
-  int cnt[kSlots];       // compute waves that have written the slot's partial sums
+  int cnt[kSlots];       // waves that have written the slot's partial sums
   int gen[kSlots];       // times the slot has been consumed
-  int xstaged[2];        // compute waves that have staged their part of x buffer b, over all its uses
-  int xfreed[2];         // compute waves that are done with x buffer b, over all its uses
-  int pad[2];
+  int xstaged;           // waves that have staged their part of the x buffer, over all its uses
+  int xfreed;            // waves that are done with the x buffer, over all its uses
+  int pad[4];
 };
+static_assert(sizeof(LdsCtl) == 64, "LDS control block");
 
+// Control words are read the same by every lane: reading the value back from
+// the first lane tells the compiler so, and keeps every decision made on it
+// (and all the walk state behind it) in scalar registers.
 __device__ __forceinline__ uint32_t ld_dev(const W4A16_GLOBAL uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 __device__ __forceinline__ void st_dev(W4A16_GLOBAL uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int lds_ld(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
 __device__ __forceinline__ void lds_st(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -138,43 +146,84 @@ __device__ __forceinline__ void lds_st(int* p, int v) {
 __device__ __forceinline__ void lds_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local"); }
 __device__ __forceinline__ void lds_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local"); }
 
-// The GEMV of item k, found by walking the descriptors forward from `op`
-// (items are visited in increasing order).
-__device__ __forceinline__ int op_of(const OpDev* ops, int op, int k) {
-  while (k >= ops[op].item_begin + ops[op].items) ++op;
-  return op;
-}
+// Bounded waiting: a wait gives up after kWaitTicks without progress
+// (setting the workspace error word and the workgroup's abort flag), or at
+// once when another wave of the workgroup has given up; a wait for another
+// workgroup also gives up when some workgroup has reported an error.
+struct Waiter {
+  LdsCtl* lc;
+  W4A16_GLOBAL uint32_t* ctl;
+  bool failed = false;
 
-// A workgroup's walk over its items (every P-th item of the chain), kept in
-// scalar registers: the item, its GEMV's fields, and its split and tile
-// group. Advancing by P costs no division: a split boundary is crossed by
-// subtraction, and the split's groups [floor(s G / S), floor((s+1) G / S))
-// are tracked incrementally as s grows. Divisions happen only when the walk
-// enters a new GEMV.
+  __device__ __forceinline__ void fail(uint32_t code) {
+    st_dev(ctl + kWsError, code);
+    lds_st(&lc->abort, 1);
+    failed = true;
+  }
+  // True while the wait that began at t0 may go on.
+  __device__ __forceinline__ bool may_wait(uint64_t t0, bool global) {
+    if (lds_ld(&lc->abort) || (global && ld_dev(ctl + kWsError))) {
+      lds_st(&lc->abort, 1);
+      failed = true;
+      return false;
+    }
+    if (wall_clock64() - t0 > kWaitTicks) {
+      fail(1u);
+      return false;
+    }
+    return true;
+  }
+  // Waits until the LDS word reaches `target`; false if the wait gave up.
+  __device__ __forceinline__ bool wait_lds(int* word, int target) {
+    const uint64_t t0 = wall_clock64();
+    while (lds_ld(word) < target) {
+      if (!may_wait(t0, false)) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    lds_acquire();
+    return true;
+  }
+};
+
+// A workgroup's walk over its items (every P-th item of the chain) and over
+// each item's rounds, kept in scalar registers: the item, its GEMV's
+// fields, its split and tile group, and the round. Advancing by P costs no
+// division: a split boundary is crossed by subtraction, and the split's
+// groups [floor(s G / S), floor((s+1) G / S)) are tracked incrementally as s
+// grows. Divisions happen only when the walk enters a new GEMV.
 struct Walk {
-  int k, op, end;          // item, its GEMV, first item past that GEMV
+  int k, op, end, rd;      // item, its GEMV, first item past that GEMV, round
   int split, tg;           // split and tile group of item k
   int g_beg, g_end, r_end; // the split's groups; r_end = (split + 1) G mod S
-  int G, kind, splits, tp, wpt, row_tiles, per_split, sq, sr;
+  int splits, per_split, row_tiles;
+  int shape;               // kind | log2(waves per tile) << 1 | tiles per item << 3 | rounds << 6
+  __device__ int kind() const { return shape & 1; }
+  __device__ int wpt_log2() const { return (shape >> 1) & 3; }
+  __device__ int tp() const { return (shape >> 3) & 7; }
+  __device__ int rounds() const { return shape >> 6; }
 };
 
 __device__ __forceinline__ void walk_enter(Walk& w, const OpDev* ops) {
   while (w.k >= ops[w.op].item_begin + ops[w.op].items) ++w.op;
   const OpDev& d = ops[w.op];
   w.end = d.item_begin + d.items;
-  w.G = d.G, w.kind = d.kind, w.splits = d.splits, w.tp = d.tp, w.wpt = d.wpt;
-  w.row_tiles = d.row_tiles, w.per_split = d.per_split, w.sq = d.split_q, w.sr = d.G - d.split_q * d.splits;
+  w.rd = 0;
+  w.splits = d.splits, w.per_split = d.per_split, w.row_tiles = d.row_tiles;
+  w.shape = d.kind | (d.wpt == 8 ? 3 : 2) << 1 | d.tp << 3 | d.rounds << 6;
   const int i = w.k - d.item_begin;
   w.split = i / w.per_split;
   w.tg = i - w.split * w.per_split;
-  w.g_beg = w.split * w.G / w.splits;
-  const int next = (w.split + 1) * w.G;
+  w.g_beg = w.split * d.G / w.splits;
+  const int next = (w.split + 1) * d.G;
   w.g_end = next / w.splits;
   w.r_end = next - w.g_end * w.splits;
 }
 
-// Moves the walk P items on (within `total`).
+// Moves the walk one round on: to the item's next round, or P items on
+// (within `total`).
 __device__ __forceinline__ void walk_advance(Walk& w, const OpDev* ops, int P, int total) {
+  if (++w.rd < w.rounds()) return;
+  w.rd = 0;
   w.k += P;
   if (w.k >= total) return;
   if (w.k >= w.end) {
@@ -183,11 +232,12 @@ __device__ __forceinline__ void walk_advance(Walk& w, const OpDev* ops, int P, i
   }
   w.tg += P;
   while (w.tg >= w.per_split) {
+    const OpDev& d = ops[w.op];
     w.tg -= w.per_split;
     ++w.split;
     w.g_beg = w.g_end;
-    w.g_end += w.sq;
-    w.r_end += w.sr;
+    w.g_end += d.split_q;
+    w.r_end += d.G - d.split_q * w.splits;
     if (w.r_end >= w.splits) {
       ++w.g_end;
       w.r_end -= w.splits;
@@ -195,47 +245,48 @@ __device__ __forceinline__ void walk_advance(Walk& w, const OpDev* ops, int P, i
   }
 }
 
-// Where a compute wave works in an item: the matrix row tile it reads and
-// its share of the item's K range (waves per tile: 4 or 8).
+// Where a wave works in a round of an item: the matrix row tile it reads and
+// the round's part of its share of the item's K range (waves per tile: 4 or
+// 8; up to kShare tiles per round, possibly none).
 struct Share {
   int64_t tile;
   int beg, n;
 };
 
 __device__ __forceinline__ Share share_of(const Walk& w, int wave) {
-  const int sh = w.wpt == 8 ? 3 : 2;
-  const int lt = wave >> sh, wi = wave & (w.wpt - 1);
+  const int sh = w.wpt_log2();
+  const int lt = wave >> sh, wi = wave & ((1 << sh) - 1);
   int64_t tile;
-  if (w.kind == W4A16_CHAIN_SWIGLU) {
+  if (w.kind() == W4A16_CHAIN_SWIGLU) {
     tile = 2 * int64_t(w.tg) + lt;  // gate tile 2 tg, up tile 2 tg + 1
   } else {
-    tile = int64_t(w.tg) * w.tp + lt;
+    tile = int64_t(w.tg) * w.tp() + lt;
     if (tile >= w.row_tiles) tile = w.row_tiles - 1;  // a pair's missing second tile: valid, never stored
   }
   const int ng = w.g_end - w.g_beg;
-  const int beg = w.g_beg + ((wi * ng) >> sh);
+  const int beg = w.g_beg + ((wi * ng) >> sh) + w.rd * kShare;
   const int end = w.g_beg + (((wi + 1) * ng) >> sh);
-  return Share{tile, beg, end - beg};
+  return Share{tile, beg, min(end - beg, kShare)};
 }
 
 // The longest K a GEMV of the chain may have: each workgroup keeps a GEMV's
-// whole input in LDS (two buffers of kMaxK halves per activation row).
-constexpr int kMaxK = 20480;
+// whole input in LDS (kMaxK halves per activation row).
+constexpr int kMaxK = 32768;
 
 template <int MR>
 struct Geo {
   static constexpr int kRows = MR < 4 ? MR : 4;          // accumulators per lane (MFMA D rows used)
   static constexpr int kRedWave = 4 * kRows * 16;        // floats of one wave's partial sums
-  static constexpr int kXRow = kMaxK + (MR > 1 ? 32 : 0);  // halves per x row of a buffer
+  static constexpr int kXRow = kMaxK + (MR > 1 ? 32 : 0);  // halves per x row
   static constexpr size_t kCtlBytes = sizeof(LdsCtl);
-  static constexpr size_t kPartBytes = size_t(kSlots) * kComputeWaves * kRedWave * 4;
-  static constexpr size_t kXBytes = size_t(2) * MR * kXRow * 2;
+  static constexpr size_t kPartBytes = size_t(kSlots) * kWaves * kRedWave * 4;
+  static constexpr size_t kXBytes = size_t(MR) * kXRow * 2;
   static constexpr size_t kLds = kCtlBytes + kPartBytes + kXBytes;
 };
 
-// One share's requests: the weight tiles (16 bytes per lane each), and the
-// share's scale and zero words gathered one per lane -- lane 8u + i holds the
-// scale word i of tile u (rows 2i, 2i + 1), lane 2u + i its zero word i
+// One round's requests: the weight tiles (16 bytes per lane each), and the
+// round's scale and zero words gathered one per lane -- lane 8u + i holds
+// the scale word i of tile u (rows 2i, 2i + 1), lane 2u + i its zero word i
 // (rows 8i .. 8i + 7) -- handed to the lanes that need them by a cross-lane
 // read at use.
 struct Buf {
@@ -244,8 +295,8 @@ struct Buf {
 };
 
 template <int MR, int NBUF>
-__global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restrict__ plan, uint8_t* __restrict__ ws,
-                                                          uint64_t ws_bytes) {
+__global__ __launch_bounds__(kThreads, 4) void chain_kernel(const Header* __restrict__ plan, uint8_t* __restrict__ ws,
+                                                             uint64_t ws_bytes) {
   using GG = Geo<MR>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   LdsCtl* lc = reinterpret_cast<LdsCtl*>(smem);
@@ -261,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
     lc->ready = -1;
     lc->abort = 0;
     for (int s = 0; s < kSlots; ++s) lc->cnt[s] = 0, lc->gen[s] = 0;
-    lc->xstaged[0] = lc->xstaged[1] = lc->xfreed[0] = lc->xfreed[1] = 0;
+    lc->xstaged = lc->xfreed = 0;
   }
   const bool plan_ok = plan->magic == kMagic && plan->M == MR && plan->ws_bytes <= ws_bytes;
   const uint32_t err0 = ld_dev(ctl + kWsError);
@@ -275,157 +326,17 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
   const uint32_t tag = epoch % 65535u + 1u;
   const int total = plan->total_items;
   const OpDev* ops = reinterpret_cast<const OpDev*>(plan + 1);
-  const uint64_t t_start = wall_clock64();
 
-  if (wave == kComputeWaves) {
-    // ---------------------------------------------------------------- control wave
-    int o_ep = 0;                  // next item to finish: ordinal o_ep, item wg + o_ep P
-    Walk we;                       // its position
-    we.k = wg, we.op = 0;
-    if (wg < total) walk_enter(we, ops);
-    int op_need = 0, k_need = wg;  // next item whose producer must be seen
-    uint64_t last_progress = t_start;
-    bool failed = false;
-    while (true) {
-      bool progressed = false;
-      const int k_ep = wg + o_ep * P;
-      if (k_ep >= total) break;
-      // epilogue of the next item, once all compute waves have handed in
-      const int slot = o_ep % kSlots;
-      if (lds_ld(&lc->cnt[slot]) == kComputeWaves) {
-        lds_acquire();
-        const OpDev& d = ops[we.op];
-        const int tg = we.tg;
-        const float* pb = part + size_t(slot) * kComputeWaves * GG::kRedWave;
-        W4A16_GLOBAL uint32_t* yt = gptr<uint32_t>(wsa + d.yt_off);
-        W4A16_GLOBAL uint16_t* yd = gptr<uint16_t>(d.y);
-        const bool pair = d.kind == W4A16_CHAIN_SWIGLU;
-        const int tiles_out = pair ? 1 : d.tp;
-        const int n_out = tiles_out * MR * 16;
-        for (int idx = lane; idx < ((n_out + 63) & ~63); idx += 64) {
-          const int id = idx < n_out ? idx : n_out - 1;
-          const int lt = id / (MR * 16), rem = id - lt * MR * 16, m = rem >> 4, r = rem & 15;
-          const int sl = ((m >> 2) * GG::kRows + (m & 3)) * 16 + r;
-          const int w0 = pair ? 0 : lt * d.wpt;
-          float sum = pb[w0 * GG::kRedWave + sl];
-          for (int w2 = 1; w2 < (pair ? 4 : d.wpt); ++w2) sum += pb[(w0 + w2) * GG::kRedWave + sl];
-          if (pair) {
-            float up = pb[4 * GG::kRedWave + sl];
-            for (int w2 = 5; w2 < 8; ++w2) up += pb[w2 * GG::kRedWave + sl];
-            sum = sum / (1.f + expf(-sum)) * up;  // silu(gate) * up
-          }
-          const int64_t t = pair ? tg : int64_t(tg) * d.tp + lt;
-          const int64_t n = t * kTileRows + r;
-          if (idx < n_out && t < d.row_tiles && n < d.N) {
-            const int64_t o = int64_t(m) * d.N + n;
-            bool write = true;
-            _Float16 v;
-            if (d.splits > 1) {
-              W4A16_GLOBAL unsigned long long* word = gptr<unsigned long long>(wsa + d.acc_off) + o;
-              const unsigned long long add = dev::splitk_addend(sum);
-              const unsigned long long now =
-                  __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
-              write = dev::splitk_count(now) == unsigned(d.splits);
-              v = dev::splitk_value(now, d.splits);
-              if (write) __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-              v = (_Float16)sum;
-            }
-            if (write) {
-              const uint16_t bits = __builtin_bit_cast(uint16_t, v);
-              yd[o] = bits;
-              if (d.yt_off) st_dev(yt + o, (tag << 16) | bits);
-            }
-          }
-        }
-        lds_st(&lc->cnt[slot], 0);
-        lds_release();
-        lds_st(&lc->gen[slot], o_ep / kSlots + 1);
-        ++o_ep;
-        walk_advance(we, ops, P, total);
-        progressed = true;
-      }
-      // readiness of the next GEMV this workgroup reads from a producer
-      while (k_need < total) {
-        op_need = op_of(ops, op_need, k_need);
-        const OpDev& d = ops[op_need];
-        if (d.x_src >= 0 && lds_ld(&lc->ready) < op_need) break;
-        // no producer, or already published: on to this workgroup's first item of a later GEMV
-        const int next_begin = d.item_begin + d.items;
-        k_need = next_begin <= wg ? wg : wg + ((next_begin - wg + P - 1) / P) * P;
-      }
-      if (k_need < total) {
-        const OpDev& d = ops[op_need];
-        if ((ld_dev(gptr<uint32_t>(wsa + d.xt_off) + d.sentinel) >> 16) == tag) {
-          lds_st(&lc->ready, op_need);
-          progressed = true;
-        }
-      }
-      const uint64_t now = wall_clock64();
-      if (progressed) {
-        last_progress = now;
-      } else {
-        if (lds_ld(&lc->abort) || ld_dev(ctl + kWsError)) {
-          failed = true;
-        } else if (now - last_progress > kWaitTicks) {
-          st_dev(ctl + kWsError, 1u);
-          failed = true;
-        }
-        if (failed) {
-          lds_st(&lc->abort, 1);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    if (lane == 0) {
-      const uint32_t done = __hip_atomic_fetch_add(ctl + kWsFinished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (done == uint32_t(P) - 1) {
-        __hip_atomic_store(ctl + kWsFinished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(ctl + kWsEpoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    return;
-  }
-
-  // ------------------------------------------------------------------ compute waves
   const int piece = lane >> 4, rlane = lane & 15;
   const int mm = rlane < MR ? rlane : MR - 1;
   const uint32_t magic = dev::kMagic1024;
-  bool failed = false;
+  Waiter wt{lc, ctl};
+  bool& failed = wt.failed;
 
-  auto fail = [&](uint32_t code) {
-    st_dev(ctl + kWsError, code);
-    lds_st(&lc->abort, 1);
-    failed = true;
-  };
-  // Bounded wait helper: true while the wait may go on.
-  auto may_wait = [&](uint64_t t0) {
-    if (lds_ld(&lc->abort)) {
-      failed = true;
-      return false;
-    }
-    if (wall_clock64() - t0 > kWaitTicks) {
-      fail(1u);
-      return false;
-    }
-    return true;
-  };
-  // Waits until the LDS word reaches `target`; false if the wait gave up.
-  auto wait_lds = [&](int* word, int target) {
-    const uint64_t t0 = wall_clock64();
-    while (lds_ld(word) < target) {
-      if (!may_wait(t0)) return false;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    lds_acquire();
-    return true;
-  };
-
-  // A share's weight tiles, scales and zero words as buffer loads: the row
+  // A round's weight tiles, scales and zero words as buffer loads: the row
   // tile's base goes into the (scalar) resource, the group into the scalar
   // offset, and the lane's constant offset is the only vector operand, so
-  // no 64-bit addresses occupy vector registers. Indices past the share are
+  // no 64-bit addresses occupy vector registers. Indices past the round are
   // clamped to its last tile (in bounds, discarded in compute()). `live`
   // false gives the resources 0 records: the same requests go out and come
   // back as zeros without touching memory, so every path issues the same
@@ -451,16 +362,16 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
     b.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, gz * 8 + z_word * 4, 0, 0);
   };
 
-  // Staging of a GEMV's whole input (all M rows, all K) into x buffer xb,
-  // the eight compute waves taking 64-chunk blocks in turn: this wave's
-  // blocks are wave, wave + 8, ... A chunk is 16 bytes: four tagged words
-  // (x from a producer: tag checked, fp16 value scaled by 2^-x_shift and
-  // rounded to fp16) or eight fp16 values (external x). Requests go out in
-  // batches of kBatch chunks per lane; chunks past the end repeat the last
-  // one (in bounds; they rewrite the same values). Stale words are requested
-  // again with device-scope loads until they carry the launch's tag.
+  // Staging of a GEMV's whole input (all M rows, all K) into the x buffer,
+  // the waves taking 64-chunk blocks in turn: this wave's blocks are wave,
+  // wave + 8, ... A chunk is 16 bytes: four tagged words (x from a producer:
+  // tag checked, fp16 value scaled by 2^-x_shift and rounded to fp16) or
+  // eight fp16 values (external x). Requests go out in batches of kBatch
+  // chunks per lane; chunks past the end repeat the last one (in bounds;
+  // they rewrite the same values). Stale words are requested again with
+  // device-scope loads until they carry the launch's tag.
   constexpr int kBatch = 4;
-  auto stage_part = [&](const OpDev& d, _Float16* xb) -> bool {
+  auto stage_part = [&](const OpDev& d) -> bool {
     const bool tagged = d.x_src >= 0;
     const int per_row = tagged ? d.K / 4 : d.K / 8;  // chunks per activation row
     const int total_chunks = MR * per_row;
@@ -468,12 +379,12 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
         tagged ? reinterpret_cast<void*>(ws + d.xt_off) : reinterpret_cast<void*>(d.x_ext), (short)0, 0x7fffffff,
         0x00020000);
     const float scale = __builtin_ldexpf(1.0f, -d.x_shift);  // exact power of two
-    for (int j0 = 0; (j0 * kComputeWaves + wave) * 64 < total_chunks; j0 += kBatch) {
+    for (int j0 = 0; (j0 * kWaves + wave) * 64 < total_chunks; j0 += kBatch) {
       int m[kBatch], cw[kBatch];
       u32x4 v[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const int c = min(((j0 + j) * kComputeWaves + wave) * 64 + lane, total_chunks - 1);
+        const int c = min(((j0 + j) * kWaves + wave) * 64 + lane, total_chunks - 1);
         m[j] = MR == 1 ? 0 : c / per_row;
         cw[j] = c - m[j] * per_row;
         const int off = tagged ? (m[j] * d.x_stride + cw[j] * 4) * 4 : (m[j] * d.K + cw[j] * 8) * 2;
@@ -490,11 +401,12 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
         if (!fresh()) {
           const uint64_t t0 = wall_clock64();
           do {
-            if (!may_wait(t0)) return false;
+            if (!wt.may_wait(t0, true)) return false;
             __builtin_amdgcn_s_sleep(2);
 #pragma unroll
             for (int j = 0; j < kBatch; ++j)
               v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (m[j] * d.x_stride + cw[j] * 4) * 4, 0, 16 /* sc1 */);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the check below reads them all
           } while (!fresh());
         }
 #pragma unroll
@@ -506,28 +418,26 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
           uint2 packed;
           packed.x = h0 | (h1 << 16);
           packed.y = h2 | (h3 << 16);
-          *reinterpret_cast<uint2*>(xb + m[j] * GG::kXRow + cw[j] * 4) = packed;
+          *reinterpret_cast<uint2*>(xs + m[j] * GG::kXRow + cw[j] * 4) = packed;
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) *reinterpret_cast<u32x4*>(xb + m[j] * GG::kXRow + cw[j] * 8) = v[j];
+        for (int j = 0; j < kBatch; ++j) *reinterpret_cast<u32x4*>(xs + m[j] * GG::kXRow + cw[j] * 8) = v[j];
       }
     }
     return true;
   };
 
-  // The item's products: per tile, four MFMAs over the unpacked weights
-  // (x from the LDS buffer as the A operand), the group sum scaled by its
-  // fp16 scale and added in tile order -- the fp32 operations of the
-  // standalone kernel, in the same order. Tiles past the share (clamped
-  // duplicates) are computed and discarded by a select. Every request of
-  // the buffer has arrived (the wait for it is exact), so the tiles are left
-  // to the compiler's scheduling.
-  auto compute = [&](const Buf& b, const Share& s, const _Float16* xb, float (&acc)[GG::kRows]) {
-#pragma unroll
-    for (int r = 0; r < GG::kRows; ++r) acc[r] = 0.f;
+  // A round's products: per tile, four MFMAs over the unpacked weights (x
+  // from the LDS buffer as the A operand), the group sum scaled by its fp16
+  // scale and added to the accumulators in tile order -- the fp32 operations
+  // of the standalone kernels, in the same order, carried across rounds.
+  // Tiles past the round (clamped duplicates) are computed and discarded by
+  // a select. Every request of the buffer has arrived (the wait for it is
+  // exact), so the tiles are left to the compiler's scheduling.
+  auto compute = [&](const Buf& b, const Share& s, float (&acc)[GG::kRows]) {
     if (s.n <= 0) return;
-    const _Float16* xbase = xb + s.beg * kGroup + 8 * piece;
+    const _Float16* xbase = xs + s.beg * kGroup + 8 * piece;
 #pragma unroll
     for (int u = 0; u < kShare; ++u) {
       const u32x4 wt = b.w[u];
@@ -552,33 +462,132 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
     }
   };
 
+  // Hands the item's partial sums in through its slot, once the slot's
+  // previous item has had its epilogue.
   auto hand_in = [&](int o, const float (&acc)[GG::kRows]) {
     const int slot = o % kSlots, gen = o / kSlots;
     const uint64_t t0 = wall_clock64();
     while (lds_ld(&lc->gen[slot]) != gen) {
-      if (!may_wait(t0)) return;
+      if (!wt.may_wait(t0, false)) return;
       __builtin_amdgcn_s_sleep(1);
     }
     lds_acquire();
-    float* pw = part + (size_t(slot) * kComputeWaves + wave) * GG::kRedWave;
+    float* pw = part + (size_t(slot) * kWaves + wave) * GG::kRedWave;
 #pragma unroll
     for (int r = 0; r < GG::kRows; ++r) pw[(piece * GG::kRows + r) * 16 + rlane] = acc[r];
     lds_release();
     if (lane == 0) __hip_atomic_fetch_add(&lc->cnt[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   };
 
-  // One item: ordinal o (item wg + o P) with weights in `cur`; the weights of
-  // ordinal o + NBUF - 1 go into `nxt` first (one request site, so their
-  // registers have a single definition and are never copied). At the first
-  // item of a GEMV the waves stage its input into the next x buffer (those
-  // requests follow the weights' and wait for them: this happens once per
-  // GEMV, mostly while the input is not there yet anyway).
-  int cur_op = -1, nchg = 0;
-  Walk wc, wp;  // the item being computed, and the one whose weights are requested
+  // The epilogue of item ordinal o (GEMV op, tile group tg), once every wave
+  // has handed the item in: adds the waves' partial sums in wave order and
+  // stores the outputs (fp16, SwiGLU, or the split-K fixed-point atomics),
+  // then frees the slot.
+  auto epilogue = [&](int o, int op, int tg) {
+    const int slot = o % kSlots;
+    if (!wt.wait_lds(&lc->cnt[slot], kWaves)) return;
+    const OpDev& d = ops[op];
+    const float* pb = part + size_t(slot) * kWaves * GG::kRedWave;
+    W4A16_GLOBAL uint32_t* yt = gptr<uint32_t>(wsa + d.yt_off);
+    W4A16_GLOBAL uint16_t* yd = gptr<uint16_t>(d.y);
+    const bool pair = d.kind == W4A16_CHAIN_SWIGLU;
+    const int tiles_out = pair ? 1 : d.tp;
+    const int n_out = tiles_out * MR * 16;
+    for (int idx = lane; idx < ((n_out + 63) & ~63); idx += 64) {
+      const int id = idx < n_out ? idx : n_out - 1;
+      const int lt = id / (MR * 16), rem = id - lt * MR * 16, m = rem >> 4, r = rem & 15;
+      const int sl = ((m >> 2) * GG::kRows + (m & 3)) * 16 + r;
+      const int w0 = pair ? 0 : lt * d.wpt;
+      float sum = pb[w0 * GG::kRedWave + sl];
+      for (int w2 = 1; w2 < (pair ? 4 : d.wpt); ++w2) sum += pb[(w0 + w2) * GG::kRedWave + sl];
+      if (pair) {
+        float up = pb[4 * GG::kRedWave + sl];
+        for (int w2 = 5; w2 < 8; ++w2) up += pb[w2 * GG::kRedWave + sl];
+        sum = sum / (1.f + expf(-sum)) * up;  // silu(gate) * up
+      }
+      const int64_t t = pair ? tg : int64_t(tg) * d.tp + lt;
+      const int64_t n = t * kTileRows + r;
+      if (idx < n_out && t < d.row_tiles && n < d.N) {
+        const int64_t oi = int64_t(m) * d.N + n;
+        bool write = true;
+        _Float16 v;
+        if (d.splits > 1) {
+          W4A16_GLOBAL unsigned long long* word = gptr<unsigned long long>(wsa + d.acc_off) + oi;
+          const unsigned long long add = dev::splitk_addend(sum);
+          const unsigned long long now =
+              __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+          write = dev::splitk_count(now) == unsigned(d.splits);
+          v = dev::splitk_value(now, d.splits);
+          if (write) __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          v = (_Float16)sum;
+        }
+        if (write) {
+          const uint16_t bits = __builtin_bit_cast(uint16_t, v);
+          yd[oi] = bits;
+          if (d.yt_off) st_dev(yt + oi, (tag << 16) | bits);
+        }
+      }
+    }
+    // the partial sums have been read: the slot is free for its next use
+    lds_st(&lc->cnt[slot], 0);
+    lds_release();
+    lds_st(&lc->gen[slot], o / kSlots + 1);
+  };
+
+  // Wave 0 waits until the producer's sentinel word carries the launch's tag
+  // and publishes that in LDS; the other waves wait for the LDS word.
+  auto wait_ready = [&](const OpDev& d, int op) -> bool {
+    if (wave != 0) return wt.wait_lds(&lc->ready, op);
+    const W4A16_GLOBAL uint32_t* sent = gptr<uint32_t>(wsa + d.xt_off) + d.sentinel;
+    const uint64_t t0 = wall_clock64();
+    while ((ld_dev(sent) >> 16) != tag) {
+      if (!wt.may_wait(t0, true)) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    lds_st(&lc->ready, op);
+    return true;
+  };
+
+  // The input of the GEMV at walk position wc: once every wave is done with
+  // the previous GEMV's x buffer and the producer has been seen finishing,
+  // the waves stage it into the x buffer. Meanwhile the weights of the
+  // GEMV's first round are in flight (requested a round ago).
+  int cur_op = -1, nchg = 0, o = 0;
+  Walk wc, wp;
   wc.k = wg, wc.op = 0;
   if (wg < total) walk_enter(wc, ops);
   wp = wc;
-  auto step = [&](const Buf& cur, Buf& nxt, int o) {
+  auto enter_gemv = [&]() -> bool {
+    const OpDev& d = ops[wc.op];
+    if (cur_op >= 0) {  // done with the previous GEMV's input
+      lds_release();
+      if (lane == 0) __hip_atomic_fetch_add(&lc->xfreed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (!wt.wait_lds(&lc->xfreed, kWaves * nchg)) return false;  // every wave done with it
+    if (d.x_src >= 0 && !wait_ready(d, wc.op)) return false;
+    if (!stage_part(d)) return false;
+    lds_release();
+    if (lane == 0) __hip_atomic_fetch_add(&lc->xstaged, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (!wt.wait_lds(&lc->xstaged, kWaves * (nchg + 1))) return false;  // every part staged
+    cur_op = wc.op;
+    ++nchg;
+    return true;
+  };
+
+  // One round: the round at walk position wc with weights in `cur`; the
+  // weights of the round NBUF - 1 rounds on (walk wp) go into `nxt` first
+  // (one request site, so their registers have a single definition and are
+  // never copied), and stay in flight while this round computes and hands
+  // in. The staging of a GEMV's input happens outside the round, so that
+  // the wait for the round's weights is exact: it never waits for the next
+  // round's.
+  float acc[GG::kRows];
+#pragma unroll
+  for (int r = 0; r < GG::kRows; ++r) acc[r] = 0.f;
+  bool pend = false;         // the previous item's epilogue is still owed
+  int pend_op = 0, pend_tg = 0;
+  auto step = [&](const Buf& cur, Buf& nxt) {
     const Share s = share_of(wc, wave);
     {
       const bool valid = wp.k < total;
@@ -586,27 +595,21 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
       load(nxt, ops[valid ? wp.op : wc.op], sp, valid && sp.n > 0);
       walk_advance(wp, ops, P, total);
     }
-    if (wc.op != cur_op) {
-      const OpDev& d = ops[wc.op];
-      const int b = nchg & 1, g = nchg >> 1;
-      if (cur_op >= 0) {  // done with the previous GEMV's buffer
-        lds_release();
-        if (lane == 0)
-          __hip_atomic_fetch_add(&lc->xfreed[b ^ 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-      if (!wait_lds(&lc->xfreed[b], kComputeWaves * g)) return;  // its use before last is over
-      if (d.x_src >= 0 && !wait_lds(&lc->ready, wc.op)) return;  // producer seen finishing
-      if (!stage_part(d, xs + size_t(b) * MR * GG::kXRow)) return;
-      lds_release();
-      if (lane == 0)
-        __hip_atomic_fetch_add(&lc->xstaged[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (!wait_lds(&lc->xstaged[b], kComputeWaves * (g + 1))) return;  // every part staged
-      cur_op = wc.op;
-      ++nchg;
+    compute(cur, s, acc);
+    if (wc.rd == wc.rounds() - 1) {
+      hand_in(o, acc);
+      if (failed) return;
+      // Epilogues rotate over the waves: wave o % 8 does item o's, one item
+      // later (when every wave has most likely handed it in), or at once
+      // for the workgroup's last item of a GEMV, whose consumers wait for it.
+      if (pend && wave == ((o - 1) & (kWaves - 1))) epilogue(o - 1, pend_op, pend_tg);
+      pend = wc.k + P < wc.end;
+      if (!pend && wave == (o & (kWaves - 1))) epilogue(o, wc.op, wc.tg);
+      pend_op = wc.op, pend_tg = wc.tg;
+      ++o;
+#pragma unroll
+      for (int r = 0; r < GG::kRows; ++r) acc[r] = 0.f;
     }
-    float acc[GG::kRows];
-    compute(cur, s, xs + size_t((nchg - 1) & 1) * MR * GG::kXRow, acc);
-    hand_in(o, acc);
     walk_advance(wc, ops, P, total);
   };
 
@@ -620,14 +623,25 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const Header* __restric
     walk_advance(wp, ops, P, total);
   }
   bool more = true;
-  for (int o0 = 0; more; o0 += NBUF) {
+  while (more) {
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
-      if (!more || failed || wc.k >= total) {
+      if (!more || failed || wc.k >= total || (wc.op != cur_op && !enter_gemv())) {
         more = false;
         break;
       }
-      step(bufs[j], bufs[(j + NBUF - 1) % NBUF], o0 + j);
+      step(bufs[j], bufs[(j + NBUF - 1) % NBUF]);
+    }
+  }
+
+  // Every wave is past its last item (or has left on an error): the last
+  // workgroup to get here advances the launch number.
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(ctl + kWsFinished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == uint32_t(P) - 1) {
+      __hip_atomic_store(ctl + kWsFinished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(ctl + kWsEpoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -648,8 +662,8 @@ hipError_t launch_typed(const void* plan, void* ws, size_t ws_bytes, hipStream_t
                             static_cast<const Header*>(plan), static_cast<uint8_t*>(ws), uint64_t(ws_bytes));
 }
 
-// Workgroups of one launch: one per compute unit, if that many can be
-// resident at once (0 otherwise).
+// Workgroups of one launch: as many per compute unit as can be resident at
+// once (at most 2; 0 if none can).
 template <int MR, int NBUF>
 int resident_grid() {
   int device = 0, cus = 0, per_cu = 0;
@@ -663,7 +677,7 @@ int resident_grid() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&chain_kernel<MR, NBUF>),
                                                    kThreads, lds) != hipSuccess)
     return 0;
-  return per_cu >= 1 ? cus : 0;
+  return min(per_cu, 2) * cus;
 }
 
 }  // namespace chain
@@ -676,22 +690,26 @@ namespace {
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Waves per tile and tiles per item for one GEMV of the chain: 4 waves per
-// 16-row tile (two tiles per item) while each wave's share of the K range
-// holds at most 7 tiles (5 with split K, as the standalone split-K plan),
-// else 8 (one tile per item); 0 if 8 waves cannot hold it.
-void chain_geometry(int kind, int G, int splits, int* wpt, int* tp) {
+// Waves per tile, tiles per item and rounds per item for one GEMV: 4 waves
+// per 16-row tile (two tiles per item) while each wave's share of the K
+// range fits one round of 7 tiles (5 with split K, as the standalone split-K
+// plan), else 8 waves per tile (one tile per item), each taking its share
+// in rounds of at most 7 tiles. (8 waves per tile for the narrow GEMVs of a
+// 7B step -- shorter shares, more items -- measured slower: 1329 against
+// 1246 us per step.) A SwiGLU item is a gate tile and its up tile, 4 waves
+// each.
+void chain_geometry(int kind, int G, int splits, int* wpt, int* tp, int* rounds) {
+  constexpr int share = w4a16::chain::kShare;
   const int range = (G + splits - 1) / splits;
-  const int cap4 = splits > 1 ? 5 : w4a16::chain::kShare;
+  const int cap4 = splits > 1 ? 5 : share;
   if (kind == W4A16_CHAIN_SWIGLU) {
-    *wpt = (range + 3) / 4 <= w4a16::chain::kShare ? 4 : 0;
-    *tp = 1;
+    *wpt = 4, *tp = 1;
+    *rounds = ((range + 3) / 4 + share - 1) / share;
   } else if ((range + 3) / 4 <= cap4) {
-    *wpt = 4, *tp = 2;
-  } else if ((range + 7) / 8 <= w4a16::chain::kShare) {
-    *wpt = 8, *tp = 1;
+    *wpt = 4, *tp = 2, *rounds = 1;
   } else {
-    *wpt = 0, *tp = 0;
+    *wpt = 8, *tp = 1;
+    *rounds = ((range + 7) / 8 + share - 1) / share;
   }
 }
 
@@ -718,10 +736,9 @@ extern "C" int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, voi
     if (o.x_src < -1 || o.x_src >= j) return W4A16_EINVAL;
     if (o.x_src < 0 && !aligned16(o.x)) return W4A16_EINVAL;
     if (o.x_src >= 0 && (ops[o.x_src].N < o.K || o.x_shift < 0 || o.x_shift > 24)) return W4A16_EINVAL;
-    int wpt, tp;
-    chain_geometry(o.kind, G, o.splits, &wpt, &tp);
-    if (wpt == 0) return W4A16_EUNSUPPORTED;  // a wave's share would exceed 7 tiles: more splits needed
     const int64_t row_tiles = (int64_t(o.N) + 15) / 16;
+    int wpt, tp, rounds;
+    chain_geometry(o.kind, G, o.splits, &wpt, &tp, &rounds);
     const int64_t items = (row_tiles + tp - 1) / tp * o.splits;
     total += items;
     if (total >= (int64_t(1) << 30) || row_tiles >= (int64_t(1) << 26)) return W4A16_EUNSUPPORTED;
@@ -763,8 +780,8 @@ extern "C" int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, voi
     e.G = o.K / W4A16_GROUP;
     e.kind = o.kind;
     e.splits = o.splits;
-    chain_geometry(o.kind, e.G, o.splits, &e.wpt, &e.tp);
     e.row_tiles = int32_t((int64_t(o.N) + 15) / 16);
+    chain_geometry(o.kind, e.G, o.splits, &e.wpt, &e.tp, &e.rounds);
     e.per_split = (e.row_tiles + e.tp - 1) / e.tp;
     e.items = e.per_split * o.splits;
     e.item_begin = begin;
@@ -804,8 +821,8 @@ extern "C" int w4a16_chain_run(int M, const void* plan_dev, void* workspace, siz
   if (M > W4A16_MAX_M) return W4A16_EUNSUPPORTED;
   if (M != 1) return W4A16_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int grid = resident_grid<1, 3>();
+  const int grid = resident_grid<1, 2>();
   if (grid <= 0) return W4A16_EUNSUPPORTED;
-  if (launch_typed<1, 3>(plan_dev, workspace, ws_bytes, s, grid) != hipSuccess) return W4A16_EHIP;
+  if (launch_typed<1, 2>(plan_dev, workspace, ws_bytes, s, grid) != hipSuccess) return W4A16_EHIP;
   return W4A16_OK;
 }

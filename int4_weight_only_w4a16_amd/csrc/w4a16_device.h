@@ -118,13 +118,18 @@ __device__ __forceinline__ ZeroPairs zero_pairs(uint32_t z) {
   return {as_h2((0x6400u | z) * 0x00010001u), as_h2((0x5400u | (z << 4)) * 0x00010001u)};
 }
 
-// (w & mask) | magic in one VALU op. gfx9 VOP3 has no literal operand, so the
-// compiler splits this into v_and_b32 + v_or_b32 with literals; with the mask
-// in an SGPR and the magic in a VGPR a single v_and_or_b32 does it.
+// (w & mask) | magic in one VALU op. gfx9 VOP3 has no literal operand, so
+// with literal operands the compiler splits this into v_and_b32 + v_or_b32;
+// with the mask in an SGPR and the magic in a VGPR (each made opaque by an
+// empty asm, which emits no instruction) it selects a single v_and_or_b32
+// itself. The instruction is the compiler's own, not inline asm: the
+// compiler then knows which VGPR it writes and keeps that write clear of the
+// destination of an MFMA still in flight (a VGPR written by an inline asm
+// instruction is invisible to its hazard checks).
 __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
-  return r;
+  asm("" : "+s"(mask));
+  asm("" : "+v"(magic));
+  return (w & mask) | magic;
 }
 
 // Eight weights of one ValueShuffle word -> (q - z) as four fp16 pairs in

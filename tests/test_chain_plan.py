@@ -4,7 +4,7 @@ persistent kernel makes over it, without a GPU.
 The plan is a byte image of descriptors. The test parses it and replays, in
 numpy, the index arithmetic each wave of the kernel performs for every work
 item: which row tile and groups a compute wave requests, where its x slice
-comes from, and which outputs the control wave writes. It checks that every
+comes from, and which outputs the item's epilogue writes. It checks that every
 request stays inside its buffer, that the waves' shares cover every K range
 exactly once, that every output is written exactly once, and that each item
 depends only on items with smaller numbers (the progress argument of the
@@ -21,7 +21,7 @@ OPDEV = np.dtype([("wq", "<u8"), ("sw", "<u8"), ("zw", "<u8"), ("x_ext", "<u8"),
                   ("xt_off", "<u8"), ("acc_off", "<u8"), ("N", "<i4"), ("K", "<i4"), ("G", "<i4"), ("kind", "<i4"),
                   ("splits", "<i4"), ("tp", "<i4"), ("wpt", "<i4"), ("row_tiles", "<i4"), ("per_split", "<i4"),
                   ("items", "<i4"), ("item_begin", "<i4"), ("x_shift", "<i4"), ("x_stride", "<i4"),
-                  ("sentinel", "<i4"), ("x_src", "<i4"), ("split_q", "<i4")])
+                  ("sentinel", "<i4"), ("x_src", "<i4"), ("split_q", "<i4"), ("rounds", "<i4"), ("pad", "<i4", 3)])
 WAVES, SHARE, LANES = 8, 7, 64
 
 
@@ -58,8 +58,8 @@ def parse(plan):
     return h, d
 
 
-def share_of(d, i, wave):
-    """The kernel's share_of(), element for element."""
+def share_of(d, i, wave, rd=0):
+    """The kernel's share_of(), element for element, for round rd."""
     per_split = int(d["per_split"])
     split, tg = i // per_split, i % per_split
     lt, wi = wave // int(d["wpt"]), wave % int(d["wpt"])
@@ -71,9 +71,9 @@ def share_of(d, i, wave):
     g_beg = 0 if S == 1 else split * G // S
     g_end = G if S == 1 else (split + 1) * G // S
     ng = g_end - g_beg
-    beg = g_beg + wi * ng // wpt
+    beg = g_beg + wi * ng // wpt + rd * SHARE
     end = g_beg + (wi + 1) * ng // wpt
-    return tile, beg, end - beg
+    return tile, beg, min(end - beg, SHARE)
 
 
 def walk(plan, ops, sizes, M):
@@ -116,10 +116,10 @@ def walk(plan, ops, sizes, M):
             c = np.arange(M * K // 8)
             m, cw = c // (K // 8), c % (K // 8)
             assert ((m * K + cw * 8) * 2 + 16 <= sizes[int(e["x_ext"])]).all()
-        assert K <= 20480  # the LDS x buffer
+        assert K <= 32768  # the LDS x buffer
         for i in range(int(e["items"])):
-            for wave in range(WAVES):
-                tile, beg, n = share_of(e, i, wave)
+            for wave, rd in ((wv, r) for wv in range(WAVES) for r in range(int(e["rounds"]))):
+                tile, beg, n = share_of(e, i, wave, rd)
                 assert n <= SHARE, (j, i, wave, n)
                 if n <= 0:
                     continue
@@ -134,7 +134,7 @@ def walk(plan, ops, sizes, M):
                 assert ((q0 + gg) * 1024 + 1024 <= wb).all() and (gg * 1024 + lanes.max() * 16 + 16 <= G * 1024).all()
                 assert ((q0 + gg) * 32 + (rlane.max() >> 1) * 4 + 4 <= sb).all()
                 assert ((q0 + gg) * 8 + (rlane.max() >> 3) * 4 + 4 <= zb).all()
-            # outputs of the item (control wave)
+            # outputs of the item (its epilogue)
             split, tg = i // int(e["per_split"]), i % int(e["per_split"])
             tiles_out = 1 if e["kind"] == w.CHAIN_SWIGLU else int(e["tp"])
             for lt in range(tiles_out):
@@ -158,11 +158,15 @@ def test_mixed_chain_plan_walk(M):
             (w.CHAIN_SWIGLU, 200, 256, 1, 1, 2),      # gate/up pair from the split GEMV's output
             (w.CHAIN_GEMV, 96, 128, 1, 2, 0),         # one group: empty shares
             (w.CHAIN_GEMV, 64, 7168, 1, -1, 0),       # 8 waves per tile
-            (w.CHAIN_GEMV, 33, 4864, 4, -1, 0)]       # split, 8 waves, ragged
+            (w.CHAIN_GEMV, 33, 4864, 4, -1, 0),       # split, 8 waves, ragged
+            (w.CHAIN_GEMV, 40, 128 * 57, 1, -1, 0),   # 8 waves, two rounds (7 + 1 tiles at most)
+            (w.CHAIN_SWIGLU, 48, 5120, 1, -1, 0),     # gate/up pairs in two rounds
+            (w.CHAIN_GEMV, 3584, 18944, 1, -1, 0)]    # unsplit down projection: three rounds
     ops, sizes = make_ops(M, spec)
     plan, ws = w.w4a16_chain_plan(M, ops)
     h, d = walk(plan, ops, sizes, M)
-    assert list(d["wpt"]) == [4, 4, 4, 4, 8, 4] and list(d["tp"]) == [2, 2, 1, 2, 1, 2]
+    assert list(d["wpt"]) == [4, 4, 4, 4, 8, 4, 8, 4, 8] and list(d["tp"]) == [2, 2, 1, 2, 1, 2, 1, 1, 1]
+    assert list(d["rounds"]) == [1, 1, 1, 1, 1, 1, 2, 2, 3]
     assert ws == h["ws_bytes"]
 
 
@@ -187,7 +191,7 @@ def test_7b_step_plan_walk():
     assert h["n_ops"] == 113
     # 4 waves x 7 groups at K = 3584 (two tiles per item), 8 waves x 5 at 37-group splits
     assert set(d["wpt"][d["K"] == 3584]) == {4} and set(d["wpt"][d["K"] == 18944]) == {8}
-    assert set(d["splits"][d["K"] == 18944]) == {4}
+    assert set(d["splits"][d["K"] == 18944]) == {4} and set(d["rounds"]) == {1}
     # the workspace holds the tagged handoff words and the split-K words
     assert ws == h["ws_bytes"] and ws < 8 << 20
 
@@ -211,12 +215,12 @@ def test_chain_plan_rejects():
         with pytest.raises(w.W4A16Error) as e:
             w.w4a16_chain_plan(M, [two[0], o1])
         assert e.value.status == want
-    # SwiGLU takes at most 28 groups and no split; a wave share of more than 7 tiles is unsupported
+    # SwiGLU takes no split; K beyond the LDS input buffer is unsupported
     sw, _ = make_ops(M, [(w.CHAIN_SWIGLU, 64, 5120, 1, -1, 0)])
     with pytest.raises(w.W4A16Error) as e:
-        w.w4a16_chain_plan(M, sw)
-    assert e.value.status == w.W4A16_EUNSUPPORTED
-    big, _ = make_ops(M, [(w.CHAIN_GEMV, 64, 128 * 57, 1, -1, 0)])
+        w.w4a16_chain_plan(M, [dict(sw[0], splits=2)])
+    assert e.value.status == w.W4A16_EINVAL
+    big, _ = make_ops(M, [(w.CHAIN_GEMV, 64, 32768 + 128, 1, -1, 0)])
     with pytest.raises(w.W4A16Error) as e:
         w.w4a16_chain_plan(M, big)
     assert e.value.status == w.W4A16_EUNSUPPORTED
@@ -229,7 +233,8 @@ def test_chain_plan_rejects():
 
 
 class Walk:
-    """The kernel's incremental walk (walk_enter / walk_advance), field for field."""
+    """The kernel's incremental walk (walk_enter / walk_advance, one round per
+    advance), field for field."""
 
     def __init__(self, d, k):
         self.d, self.k, self.op = d, k, 0
@@ -241,6 +246,7 @@ class Walk:
             self.op += 1
         e = d[self.op]
         self.end = int(e["item_begin"] + e["items"])
+        self.rd, self.rounds = 0, int(e["rounds"])
         self.G, self.S, self.per_split = int(e["G"]), int(e["splits"]), int(e["per_split"])
         self.sq = int(e["split_q"])
         self.sr = self.G - self.sq * self.S
@@ -251,6 +257,10 @@ class Walk:
         self.g_end, self.r_end = nxt // self.S, nxt % self.S
 
     def advance(self, P, total):
+        self.rd += 1
+        if self.rd < self.rounds:
+            return
+        self.rd = 0
         self.k += P
         if self.k >= total:
             return
@@ -271,14 +281,16 @@ class Walk:
 
 @pytest.mark.parametrize("P", [1, 7, 100, 256, 300])
 def test_incremental_walk_matches_division(P):
-    """Every workgroup's walk, advanced P items at a time, gives the GEMV,
-    split, tile group and split range that direct division gives."""
+    """Every workgroup's walk, advanced a round at a time and P items at a
+    time, gives the GEMV, split, tile group, split range and round that
+    direct division gives."""
     M = 1
     spec = [(w.CHAIN_GEMV, 520, 1024, 1, -1, 0), (w.CHAIN_GEMV, 300, 512, 2, 0, 3),
             (w.CHAIN_SWIGLU, 200, 256, 1, 1, 2), (w.CHAIN_GEMV, 96, 128, 1, 2, 0),
             (w.CHAIN_GEMV, 64, 7168, 1, -1, 0), (w.CHAIN_GEMV, 33, 4864, 4, -1, 0),
             (w.CHAIN_GEMV, 3584, 18944, 4, -1, 0), (w.CHAIN_GEMV, 2000, 3968, 31, -1, 0),
-            (w.CHAIN_GEMV, 17, 1280, 7, -1, 0)]
+            (w.CHAIN_GEMV, 17, 1280, 7, -1, 0), (w.CHAIN_GEMV, 3584, 18944, 1, -1, 0),
+            (w.CHAIN_SWIGLU, 48, 5120, 1, -1, 0)]
     ops, _ = make_ops(M, spec)
     plan, _ = w.w4a16_chain_plan(M, ops)
     h, d = parse(plan)
@@ -294,4 +306,6 @@ def test_incremental_walk_matches_division(P):
             G, S = int(e["G"]), int(e["splits"])
             assert (wk.op, wk.split, wk.tg) == (j, split, tg)
             assert (wk.g_beg, wk.g_end) == (split * G // S, (split + 1) * G // S)
-            wk.advance(P, total)
+            for rd in range(int(e["rounds"])):  # every round of the item, in order
+                assert (wk.k, wk.rd) == (int(e["item_begin"]) + i, rd)
+                wk.advance(P, total)

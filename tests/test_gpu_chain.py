@@ -130,7 +130,11 @@ MIXED = [(w.CHAIN_GEMV, 520, 1024, 1, -1, 0),     # external x, tile pairs, ragg
          (w.CHAIN_GEMV, 96, 128, 1, 2, 0),        # one group (empty shares), fed by the SwiGLU output
          (w.CHAIN_GEMV, 64, 7168, 1, -1, 0),      # 8 waves per tile
          (w.CHAIN_GEMV, 33, 4864, 4, -1, 0),      # split, ragged
-         (w.CHAIN_GEMV, 1000, 512, 1, 0, 3)]      # a second consumer of GEMV 0
+         (w.CHAIN_GEMV, 1000, 512, 1, 0, 3),      # a second consumer of GEMV 0
+         (w.CHAIN_GEMV, 7296, 256, 1, -1, 0),     # a wide producer
+         (w.CHAIN_GEMV, 40, 7296, 1, 7, 2),       # 8 waves, shares in two rounds, fed by GEMV 7
+         (w.CHAIN_SWIGLU, 48, 5120, 1, -1, 0),    # gate/up pairs in two rounds
+         (w.CHAIN_GEMV, 200, 18944, 1, -1, 0)]    # three rounds
 
 
 def test_chain_mixed_kinds_against_oracle_and_repeat():
@@ -142,7 +146,7 @@ def test_chain_mixed_kinds_against_oracle_and_repeat():
         assert np.array_equal(a, b)
 
 
-def layer_spec(layers, lm_head):
+def layer_spec(layers, lm_head, down_splits=4):
     spec = []
     for layer in range(layers):
         base = len(spec)
@@ -150,7 +154,7 @@ def layer_spec(layers, lm_head):
         spec.append((w.CHAIN_GEMV, 4608, 3584, 1, src, 10 if src >= 0 else 0))  # qkv, from the previous down
         spec.append((w.CHAIN_GEMV, 3584, 3584, 1, base, 3))                    # o, from qkv (stands for attention)
         spec.append((w.CHAIN_SWIGLU, 18944, 3584, 1, base + 1, 3))             # gate/up + SwiGLU, from o
-        spec.append((w.CHAIN_GEMV, 3584, 18944, 4, base + 2, 0))               # down, from the SwiGLU output
+        spec.append((w.CHAIN_GEMV, 3584, 18944, down_splits, base + 2, 0))     # down, from the SwiGLU output
     if lm_head:
         spec.append((w.CHAIN_GEMV, 152064, 3584, 1, len(spec) - 1, 10))
     return spec
@@ -164,6 +168,22 @@ def test_chain_7b_layers_bit_identical_to_standalone():
         ref = standalone(o, xs[i], 1)
         assert np.array_equal(ys[i], ref), (i, o["N"], o["K"])
     check_oracle(chain, ys, xs)
+
+
+def test_chain_7b_layers_unsplit_down_in_rounds():
+    """The down projection unsplit: 8 waves per tile, each taking its 18 or 19
+    groups in three rounds. Every other GEMV still equals its standalone
+    entry point; every GEMV is within the oracle's bound."""
+    chain = Chain(1, layer_spec(2, lm_head=False, down_splits=1), seed=24, device_weights=True)
+    ys = chain.run()
+    xs = chain.inputs(ys)
+    check_oracle(chain, ys, xs)
+    for i, o in enumerate(chain.ops):
+        if o["K"] != 18944:
+            assert np.array_equal(ys[i], standalone(o, xs[i], 1)), i
+    again = chain.run()
+    for a, b in zip(ys, again):
+        assert np.array_equal(a, b)
 
 
 def test_chain_full_7b_step_oracle_sampled_and_repeat():
