@@ -17,7 +17,11 @@ Prints one JSON line:
   roofline   = the dominant kernel (the gate+up GEMV launch) timed with HIP
                events over back-to-back launches,
   cpu_baseline = the fp64 oracle on the host cores over a bounded sample of
-               the same step (also used to check sampled outputs).
+               the same step (also used to check sampled outputs),
+  chain      = the same 113 GEMVs as one persistent launch
+               (w4a16_chain_run), each fed by its producer's output: us per
+               step beside the graph's, and (in the cpu_baseline leg) every
+               one of its 113 outputs against the oracle's bound.
 
   python bench.py [--steps K] [--warmup W]
   python bench.py --trace-summary DIR   # summarize a rocprofv3 kernel trace
@@ -193,6 +197,97 @@ class Step:
         return e0.elapsed_time(e1) * 1e-3
 
 
+class ChainStep:
+    """The same 113 GEMVs as one persistent launch (w4a16_chain_run), each
+    reading the previous GEMV's output as its input: qkv the previous layer's
+    down projection (the first one the step's external x), o the qkv output
+    (standing for attention), gate/up + SwiGLU the o output, down the SwiGLU
+    output, lm_head the last down output. Inputs are rescaled by 2^-shift
+    on the way (an exact power of two) to keep fp16 in range. The down
+    projection runs unsplit (three rounds per wave), the fastest measured."""
+
+    SHIFTS = {"qkv_proj": 10, "o_proj": 3, "gate_up_proj": 3, "down_proj": 0, "lm_head": 10}
+
+    def __init__(self, step, torch):
+        w = step.w
+        self.w, self.torch = w, torch
+        dev = torch.device("cuda:0")
+        self.ops = []
+        last_down = -1
+        for i, (name, N, K, wq, sc, zp, x, _) in enumerate(step.bufs):
+            kind, n_out, src = w.CHAIN_GEMV, N, i - 1
+            if name == "lm_head":
+                src = last_down
+            elif name.endswith("qkv_proj"):
+                src = last_down
+            elif name.endswith("gate_up_proj"):
+                kind, n_out = w.CHAIN_SWIGLU, N // 2
+            short = name.split(".")[-1]
+            shift = self.SHIFTS[short] if src >= 0 else 0
+            y = torch.full((1, n_out), -1, dtype=torch.int16, device=dev)
+            self.ops.append(dict(kind=kind, N=n_out, K=K, splits=1, x_src=src, x_shift=shift, wq=wq, scales=sc,
+                                 zeros=zp, x=x if src < 0 else None, y=y))
+            if short == "down_proj":
+                last_down = i
+        plan, ws_bytes = w.w4a16_chain_plan(1, self.ops)
+        self.plan = torch.from_numpy(plan).to(dev)
+        self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.Stream()
+
+    def run(self):
+        self.w.w4a16_chain_run(1, self.plan, self.ws, stream=self.stream)
+
+    def time(self, reps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.run()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(reps):
+            self.run()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    def error_word(self):
+        off = self.w.CHAIN_ERROR_OFFSET
+        return int(self.ws[off:off + 4].cpu().numpy().view(np.uint32)[0])
+
+    def outputs(self):
+        return [o["y"].cpu().numpy().view(np.uint16).copy() for o in self.ops]
+
+
+def check_chain(chain, ys):
+    """Every output of the chain against the oracle's bound, each GEMV's
+    input being its producer's GPU output (first K columns) times 2^-shift,
+    rounded to fp16 on the host (the chain's own input rule)."""
+    import oracle
+    orc = oracle.get()
+    worst = 0.0
+    for i, o in enumerate(chain.ops):
+        M, N, K = 1, o["N"], o["K"]
+        if o["x_src"] < 0:
+            x_h = o["x"].cpu().numpy().view(np.uint16)
+        else:
+            y = np.ascontiguousarray(ys[o["x_src"]][:, :K]).view(np.float16).astype(np.float32)
+            x_h = (y * np.float32(2.0 ** -o["x_shift"])).astype(np.float16).view(np.uint16)
+        host = [t.cpu().numpy() for t in (o["wq"], o["scales"], o["zeros"])]
+        wq_h, sc_h, zp_h = host[0], host[1].view(np.uint8), host[2]
+        if o["kind"] == chain.w.CHAIN_SWIGLU:
+            NP = (N + 15) // 16 * 16
+            r2, a2 = orc.gemv_packed(M, 2 * NP, K, wq_h, sc_h, zp_h, x_h)
+            half = lambda a, h: a.reshape(M, NP // 16, 2, 16)[:, :, h, :].reshape(M, NP)[:, :N]
+            ref, bound = oracle.swiglu_bound(half(r2, 0), half(a2, 0), half(r2, 1), half(a2, 1))
+            _, r = oracle.swiglu_report(ys[i], ref, bound, orc)
+        else:
+            ref, absref = orc.gemv_packed(M, N, K, wq_h, sc_h, zp_h, x_h)
+            _, r = oracle.bound_report(ys[i], ref, absref, orc)
+        worst = max(worst, r)
+    return worst, len(chain.ops)
+
+
 def cpu_baseline(step, budget_s):
     """The fp64 oracle, as it stands, over whole GEMVs of the same step in
     step order (lm_head first, then layers 0, 1, ...) until about budget_s
@@ -269,7 +364,210 @@ def trace_summary(directory):
               f" {key[3]:>7s} {np.percentile(d, 90):9.2f} {np.percentile(d, 99):9.2f}")
 
 
-def run_configs(torch, seed):
+# Shapes of the counter pass, each launched COUNTER_REPS times in this order
+# (with the library's split choice), so that a counter run's w4a16
+# dispatches, in dispatch order, come in groups of COUNTER_REPS per shape.
+COUNTER_REPS = 3
+COUNTER_SHAPES = (
+    [("7B qkv 4608x3584", 1, 4608, 3584, "gemv"), ("7B o 3584x3584", 1, 3584, 3584, "gemv"),
+     ("7B gate_up 37888x3584", 1, 37888, 3584, "gemv"), ("7B gate_up+SwiGLU 37888x3584", 1, 18944, 3584, "swiglu"),
+     ("7B down 3584x18944", 1, 3584, 18944, "gemv"), ("7B lm_head 152064x3584", 1, 152064, 3584, "gemv")]
+    + [(f"27B {name} M={M}", M, N, K, "gemv") for M in synthetic.VERIFY_M if M in (1, 5, 8)
+       for name, N, K in synthetic.VERIFY27B])
+
+
+def counter_pass(torch, seed):
+    """Launches every COUNTER_SHAPES entry COUNTER_REPS times, synchronously,
+    for a rocprofv3 counter run (program directly after --)."""
+    import int4_weight_only_w4a16_amd as w
+    dev = torch.device("cuda:0")
+    for i, (label, M, N, K, kind) in enumerate(COUNTER_SHAPES):
+        rows = 2 * ((N + 15) // 16 * 16) if kind == "swiglu" else N
+        wq, sc, zp = synthetic.device_packed_weights(rows, K, seed, 7000 + i, dev)
+        x = synthetic.device_activations(M, K, seed, 7000 + i, dev)
+        y = torch.empty((M, N), dtype=torch.int16, device=dev)
+        splits = w.w4a16_splitk_choose(M, N, K) if kind == "gemv" else 1
+        ws = torch.zeros(w.w4a16_splitk_workspace_bytes(M, N, max(splits, 2)), dtype=torch.uint8, device=dev)
+        for _ in range(COUNTER_REPS):
+            if kind == "swiglu":
+                w.w4a16_gemv_swiglu(M, N, K, wq, sc, zp, x, y)
+            elif splits > 1:
+                w.w4a16_gemv_splitk(M, N, K, splits, wq, sc, zp, x, y, ws)
+            else:
+                w.w4a16_gemv(M, N, K, wq, sc, zp, x, y)
+            torch.cuda.synchronize()
+        print(f"counter pass: {label} M={M} splits={splits} x{COUNTER_REPS}", flush=True)
+        del wq, sc, zp, x, y, ws
+
+
+def _counter_rows(directory):
+    import csv
+    paths = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no *counter_collection.csv under {directory}")
+    per = {}
+    for path in paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                d = per.setdefault(int(row["Dispatch_Id"]), {"name": row["Kernel_Name"],
+                                                              "grid": row.get("Grid_Size", "?"),
+                                                              "wg": row.get("Workgroup_Size", "?")})
+                d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def counter_summary(dirs):
+    """Per-shape counters of the counter pass, one rocprofv3 run per directory
+    (each with its own counters; a directory whose dispatches include the
+    plain copy kernel of --copy-calibration gives the FETCH_SIZE and
+    WRITE_SIZE scale factors instead)."""
+    merged = [dict(label=l, M=M, N=N, K=K, kind=k) for l, M, N, K, k in COUNTER_SHAPES]
+    scale = {}
+    for directory in dirs:
+        rows = _counter_rows(directory)
+        w4 = [r for r in rows if "w4a16" in r["name"]]
+        if not w4:
+            # the copy kernel reads and writes 512 MiB (the fill before it reads nothing)
+            for key in ("FETCH_SIZE", "WRITE_SIZE"):
+                vals = [r[key] for r in rows if key in r]
+                if vals:
+                    scale[key] = (512 << 20) / (max(vals) * 1024)
+            continue
+        if len(w4) != COUNTER_REPS * len(COUNTER_SHAPES):
+            raise SystemExit(f"{directory}: {len(w4)} w4a16 dispatches, expected {COUNTER_REPS * len(COUNTER_SHAPES)}")
+        for i, m in enumerate(merged):
+            group = w4[i * COUNTER_REPS:(i + 1) * COUNTER_REPS]
+            m["grid"], m["wg"], m["kernel"] = group[0]["grid"], group[0]["wg"], group[0]["name"].split("(")[0][-70:]
+            for key in group[0]:
+                if key not in ("name", "grid", "wg"):
+                    m[key] = sum(g[key] for g in group) / len(group)
+    print(f"# scale factors from the plain copy kernel: {json.dumps({k: round(v, 4) for k, v in scale.items()})}")
+    cols = ["label", "grid", "wg", "alg_MB", "fetch/alg", "write_KB", "tcc_hit%", "VALUBusy%", "lds_conf%",
+            "wait/wave_cyc", "valu/wave", "mfma/wave"]
+    print(" | ".join(cols))
+    for m in merged:
+        M, N, K = m["M"], m["N"], m["K"]
+        rows = 2 * ((N + 15) // 16 * 16) if m["kind"] == "swiglu" else N
+        alg = algorithmic_bytes(M, rows, K) if m["kind"] != "swiglu" else algorithmic_bytes(M, rows, K) - 2 * M * rows + 2 * M * N
+        out = [m["label"], str(m.get("grid", "?")), str(m.get("wg", "?")), f"{alg / 1e6:.2f}"]
+        f = m.get("FETCH_SIZE")
+        out.append(f"{f * 1024 * scale.get('FETCH_SIZE', 1.0) / alg:.4f}" if f is not None else "-")
+        wr = m.get("WRITE_SIZE")
+        out.append(f"{wr * scale.get('WRITE_SIZE', 1.0):.1f}" if wr is not None else "-")
+        hit, miss = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
+        out.append(f"{100 * hit / (hit + miss):.1f}" if hit is not None and miss is not None and hit + miss > 0 else "-")
+        out.append(f"{m['VALUBusy']:.1f}" if "VALUBusy" in m else "-")
+        bc, lds = m.get("SQ_LDS_BANK_CONFLICT"), m.get("SQ_ACTIVE_INST_LDS")
+        out.append(f"{100 * bc / lds:.1f}" if bc is not None and lds else "-")
+        wt, wc = m.get("SQ_WAIT_INST_ANY"), m.get("SQ_WAVE_CYCLES")
+        out.append(f"{wt / wc:.3f}" if wt is not None and wc else "-")
+        waves = m.get("SQ_WAVES")
+        out.append(f"{m['SQ_INSTS_VALU'] / waves:.0f}" if waves and "SQ_INSTS_VALU" in m else "-")
+        out.append(f"{m['SQ_INSTS_MFMA'] / waves:.0f}" if waves and "SQ_INSTS_MFMA" in m else "-")
+        print(" | ".join(out))
+
+
+def read_ceiling_gbps(torch):
+    """Plain-read ceiling of this device: the library's read probe (the
+    GEMV's own non-temporal 16-byte loads, nothing stored) over 1 GiB at four
+    grid sizes, the best of all; the kernels are compared with it beside the
+    peak. (Two to three workgroups per CU read fastest, about 7.1 TB/s; from
+    4 on it drops to about 6.)"""
+    import int4_weight_only_w4a16_amd as w
+    rbuf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda:0")
+    best = 0.0
+    for grid in (256, 512, 768, 1024):
+        w.w4a16_read_probe(rbuf, grid, sink)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(4):
+                w.w4a16_read_probe(rbuf, grid, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, 4 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del rbuf, sink
+    return best
+
+
+def decompose_pass(torch, seed, steps):
+    """`steps` graph replays of the 7B step, then `steps` eager steps (the
+    same 113 launches from the host), for a rocprofv3 --kernel-trace run;
+    then both timed with HIP events without the profiler's help, and the
+    plain-read ceiling, printed as one JSON line."""
+    step = Step(seed, torch)
+    graph = step.capture()
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(step.stream):
+        for _ in range(steps):
+            step.launch_all(step.stream)
+    torch.cuda.synchronize()
+    g_s = step.time_graph(graph, 50, 5) / 50
+    e_s = step.time_eager(50) / 50
+    print(json.dumps({"graph_us_per_step": round(g_s * 1e6, 2), "eager_us_per_step": round(e_s * 1e6, 2),
+                      "bytes_per_step": step.bytes, "read_ceiling_GBps": round(read_ceiling_gbps(torch), 1),
+                      "launches_per_step": len(step.shapes), "steps_traced_each": steps}), flush=True)
+
+
+def decompose_summary(directory, steps, launches=113):
+    """Step decomposition from a kernel trace of decompose_pass: per step,
+    the wall span, the sum of kernel durations and the gaps between
+    consecutive kernels, for the graph steps and the eager steps."""
+    import csv
+    paths = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no *kernel_trace.csv under {directory}")
+    ev = []
+    for path in paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if "w4a16" in row.get("Kernel_Name", ""):
+                    ev.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
+    ev.sort()
+    # The capture's eager warm-up step comes first, then the traced graph and
+    # eager steps; the timed runs (and the read probe) follow them.
+    ev = ev[launches:launches + 2 * steps * launches]
+    for label, part in (("graph", ev[:steps * launches]), ("eager", ev[steps * launches:])):
+        spans, busy, gaps = [], [], []
+        for s0 in range(0, len(part), launches):
+            st = part[s0:s0 + launches]
+            spans.append((st[-1][1] - st[0][0]) * 1e-3)
+            busy.append(sum(e - b for b, e in st) * 1e-3)
+            gaps.extend((st[i][0] - st[i - 1][1]) * 1e-3 for i in range(1, len(st)))
+        g = np.array(gaps)
+        print(f"{label}: steps {len(spans)}, span us median {np.median(spans):.1f}, kernel busy us median "
+              f"{np.median(busy):.1f}, gaps per step us median {np.median(spans) - np.median(busy):.1f}; "
+              f"gap between kernels us: median {np.median(g):.2f} p10 {np.percentile(g, 10):.2f} "
+              f"p90 {np.percentile(g, 90):.2f} min {g.min():.2f}")
+
+
+def oracle_set(one, M, budget_s):
+    """The oracle over whole GEMVs of one set (in set order) until about
+    budget_s seconds of oracle time: (seconds, algorithmic bytes, GEMVs,
+    worst GPU error over the bound)."""
+    import oracle
+    orc = oracle.get()
+    spent, done_bytes, n, worst = 0.0, 0, 0, 0.0
+    for N, K, wq, sc, zp, x, y, _ in one:
+        wq_h, sc_h, zp_h, x_h, y_h = (t.cpu().numpy() for t in (wq, sc, zp, x, y))
+        t0 = time.perf_counter()
+        ref, absref = orc.gemv_packed(M, N, K, wq_h, sc_h.view(np.uint8), zp_h, x_h.view(np.uint16))
+        spent += time.perf_counter() - t0
+        done_bytes += algorithmic_bytes(M, N, K)
+        n += 1
+        _, r = oracle.bound_report(y_h.view(np.uint16), ref, absref, orc)
+        worst = max(worst, r)
+        if spent >= budget_s:
+            break
+    return spent, done_bytes, n, worst, orc.num_threads()
+
+
+def run_configs(torch, seed, oracle_budget_s=3.0):
     """Every workload configuration, warm and cold, µs and GB/s per set.
 
     A set is the configuration's GEMVs launched back to back on one stream,
@@ -280,7 +578,10 @@ def run_configs(torch, seed):
     replay streams from HBM. Every graph is timed in 5 rounds (5 replays
     each), the measurements in a seeded random order within each round; a
     row reports the median and the mean of its rounds and flags a mean more
-    than 15% away from the median.
+    than 15% away from the median. Each row also carries the fp64 oracle
+    timed on the host cores over the set's GEMVs (whole GEMVs, up to about
+    oracle_budget_s seconds, extrapolated to the set) and checks those
+    GEMVs' GPU outputs against the oracle's bound.
     Configuration 4 (the whole 7B step) is the default bench line."""
     import int4_weight_only_w4a16_amd as w
     dev = torch.device("cuda:0")
@@ -378,6 +679,16 @@ def run_configs(torch, seed):
             out[f"{kind}_mean_median_divergence_over_15pct"] = abs(mean - med) > 0.15 * med
         out["cold_frac_of_hbm_peak"] = round(nbytes / (out["cold_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
         out["rounds"] = 5
+        if oracle_budget_s > 0:
+            warm_sets = next(it[4][0] for it in items if it[0] == r and it[1] == "warm")
+            spent, done, n, worst, cores = oracle_set(warm_sets[0], out["M"], oracle_budget_s)
+            oracle_us = spent / done * nbytes * 1e6
+            out["cpu_baseline"] = {
+                "kind": "oracle", "us_per_set": round(oracle_us, 1), "GBps": round(done / spent / 1e9, 4),
+                "cores": cores, "sample": f"{n} of {out['launches_per_set']} GEMVs, whole, {spent:.2f} s",
+                "gpu_speedup_cold": round(oracle_us / out["cold_us"], 1), "host": host_cpu()}
+            out["parity_sample"] = {"gemvs_checked": n, "worst_err_over_bound": round(worst, 4),
+                                    "ok": bool(worst <= 1.0)}
         print(json.dumps(out), flush=True)
     del items
     torch.cuda.empty_cache()
@@ -397,10 +708,23 @@ def main():
                     help="run only a plain 512 MiB device copy kernel (counter scaling)")
     ap.add_argument("--configs", action="store_true",
                     help="time every workload configuration warm and cold (one JSON line each) instead")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="launch each counter-pass shape a few times (for a rocprofv3 --pmc run)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="summarize counter-pass rocprofv3 runs (one directory per counter set)")
+    ap.add_argument("--decompose", type=int, metavar="STEPS",
+                    help="trace STEPS graph and STEPS eager steps (for rocprofv3 --kernel-trace), then time both")
+    ap.add_argument("--decompose-summary", metavar="DIR", help="step decomposition from a --decompose trace")
     args = ap.parse_args()
 
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
+    if args.decompose_summary:
+        decompose_summary(args.decompose_summary, args.decompose or 20)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the W4A16 GEMV path here is single-GPU "
@@ -420,6 +744,12 @@ def main():
 
     if args.configs:
         run_configs(torch, args.seed)
+        return
+    if args.counter_pass:
+        counter_pass(torch, args.seed)
+        return
+    if args.decompose:
+        decompose_pass(torch, args.seed, args.decompose)
         return
 
     t_setup = time.perf_counter()
@@ -452,26 +782,7 @@ def main():
     dom_us = dom_s / (reps * n_dom) * 1e6
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
 
-    # Plain-read ceiling of this device: the library's read probe (the GEMV's
-    # own non-temporal 16-byte loads, nothing stored) over 1 GiB at four grid
-    # sizes, the best of all; the kernels are compared with it beside the
-    # peak. (Two to three workgroups per CU read fastest, about 7.1 TB/s;
-    # from 4 on it drops to about 6.)
-    rbuf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
-    sink = torch.zeros(16, dtype=torch.uint8, device="cuda:0")
-    read_ceiling = 0.0
-    for grid in (256, 512, 768, 1024):
-        step.w.w4a16_read_probe(rbuf, grid, sink)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(4):
-                step.w.w4a16_read_probe(rbuf, grid, sink)
-            e1.record()
-            torch.cuda.synchronize()
-            read_ceiling = max(read_ceiling, 4 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    del rbuf, sink
+    read_ceiling = read_ceiling_gbps(torch)
 
     # Variant (reported beside, never as `value`): gate+up with the SwiGLU
     # epilogue fused, y = silu(g) * u of width 18944, same weight bytes.
@@ -593,6 +904,23 @@ def main():
         wlib.w4a16_quantize(wq16, mode)
         quant[label] = round(wq16.nbytes / (time.perf_counter() - t0) / 1e9, 3)
 
+    # The whole step as one persistent launch, beside the graph of 113.
+    chain = ChainStep(step, torch)
+    chain_s = chain.time(args.steps, args.warmup)
+    chain_err = chain.error_word()  # sticky: nonzero would mean every timed run returned at once
+    chain_ys = chain.outputs()
+    chain_out = {
+        "kernel": "w4a16_chain_run: the step's 113 GEMVs in one persistent launch, each fed by its producer "
+                  "(tagged handoff words), two resident 8-wave workgroups per CU",
+        "us_per_step": round(chain_s * 1e6, 2),
+        "graph_us_per_step": round(us_step, 2),
+        "ratio_to_graph": round(chain_s * 1e6 / us_step, 3),
+        "GBps": round(step.bytes / chain_s / 1e9, 1),
+        "launches_per_step": 1,
+        "down_splits": 1,
+        "error_word": chain_err,
+    }
+
     # Outputs of the last full replay, for the sampled check.
     graph.replay()
     torch.cuda.synchronize()
@@ -664,6 +992,7 @@ def main():
                 "launches_per_step": len(step.shapes),
             },
         },
+        "chain": chain_out,
         "prefill_gemm": prefill,
         "prefill_gemm_small_m": prefill_small,
         "host_quantize": {"shape": f"{Nq}x{Kq} fp16", "GBps_fp16_in": quant,
@@ -675,6 +1004,9 @@ def main():
         out["cpu_baseline"] = cpu
         out["parity_sample"] = {"gemvs_checked": n_checked, "worst_err_over_bound": round(worst, 4),
                                 "ok": bool(worst <= 1.0)}
+        c_worst, c_checked = check_chain(chain, chain_ys)
+        out["chain"]["parity"] = {"gemvs_checked": c_checked, "worst_err_over_bound": round(c_worst, 4),
+                                  "ok": bool(c_worst <= 1.0)}
     print(json.dumps(out))
 
 

@@ -81,6 +81,16 @@ extern "C" {
 int w4a16_layout_id(void);
 
 /*
+ * Host: the loader's check of the layout ID stored with a set of packed
+ * weights (for example in its weight file's header), refusing any layout
+ * but this library's as the runtime of "Building an LLM Inference Runtime"
+ * does (Bug #3). Returns W4A16_OK for layout_id == w4a16_layout_id(), else
+ * W4A16_ELAYOUT. Packed buffers themselves carry no tag: their sizes are
+ * exactly those of w4a16_packed_sizes.
+ */
+int w4a16_check_layout(int layout_id);
+
+/*
  * Sizes in bytes of the three packed buffers for an N x K matrix.
  * N >= 0; K a multiple of 128 and >= 128. Any of the size pointers may be
  * NULL. Errors: W4A16_EINVAL for a bad shape.

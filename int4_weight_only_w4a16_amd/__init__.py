@@ -23,7 +23,7 @@ GROUP = 128
 MAX_M = 8
 
 # Every symbol the header declares.
-EXPORTS = ("w4a16_layout_id", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_quantize",
+EXPORTS = ("w4a16_layout_id", "w4a16_check_layout", "w4a16_packed_sizes", "w4a16_pack", "w4a16_pack_gate_up", "w4a16_quantize",
            "w4a16_unpack",
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
            "w4a16_gemv_splitk", "w4a16_gemv_splitk_noalloc", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemv_a8_fused", "w4a16_gemm", "w4a16_gemm_splitk_choose",
@@ -74,6 +74,8 @@ def lib():
         L = ctypes.CDLL(LIBRARY)
         L.w4a16_layout_id.restype = _i
         L.w4a16_layout_id.argtypes = []
+        L.w4a16_check_layout.restype = _i
+        L.w4a16_check_layout.argtypes = [_i]
         L.w4a16_packed_sizes.argtypes = [_i, _i, _p, _p, _p]
         L.w4a16_pack.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p]
         L.w4a16_pack_gate_up.argtypes = [_i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
@@ -135,6 +137,11 @@ def w4a16_strerror(status):
 
 def w4a16_layout_id():
     return lib().w4a16_layout_id()
+
+
+def w4a16_check_layout(layout_id):
+    """Raises W4A16Error(W4A16_ELAYOUT) unless layout_id is this library's."""
+    _check(lib().w4a16_check_layout(int(layout_id)), "w4a16_check_layout")
 
 
 def w4a16_packed_sizes(N, K):

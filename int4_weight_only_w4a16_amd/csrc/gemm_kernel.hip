@@ -35,8 +35,6 @@ constexpr int kOStride = kGemmBN + 8;       // halves per LDS row of the output 
 // wave): two staged x groups of 16 MB x 128 halves.
 constexpr size_t gemm_lds_bytes(int mb) { return size_t(2) * 16 * mb * kGroup * 2; }
 static_assert(size_t(16) * kOStride * 2 <= gemm_lds_bytes(1), "output tile must fit the x buffers");
-// s_waitcnt operand: vmcnt <= the weight requests of one step (3 per tile).
-constexpr int kVmcntW = vmcnt_at_most(3 * kGemmNB);
 
 // Split-K (splits > 1, ws non-null): workgroup (.., .., z) multiplies only
 // the z-th of `splits` contiguous group ranges and adds its fp32 partial
@@ -207,16 +205,17 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
     load_w(gn, nxt);
     __builtin_amdgcn_sched_barrier(0);
     compute(i & 1, cur);
-    // The x requests were issued before the weight requests (one dwordx4
-    // and two dwords per tile): at most that many outstanding leaves x
-    // complete. (The compiler makes this a full wait, as it does not count
-    // the LDS-bound requests apart; the weights are due next step anyway.)
-    __builtin_amdgcn_s_waitcnt(kVmcntW);
+    // The x requests are global-to-LDS requests, which need not complete in
+    // order with the weight loads issued after them (see load_lds16), so the
+    // only wait that guarantees the next x buffer is complete before the
+    // barrier is a full one. It also waits for the weights requested this
+    // step, which the next step needs first anyway.
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     lds_barrier();
   };
   load_x(g_beg, 0);
   load_w(g_beg, wa);
-  __builtin_amdgcn_s_waitcnt(kVmcntW);
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
   lds_barrier();
   int i = 0;
   for (; i + 1 < ng; i += 2) {

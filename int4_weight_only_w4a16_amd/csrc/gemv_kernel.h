@@ -53,14 +53,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     unsigned long long* __restrict__ acc) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr bool kGlobalX = ENGINE == kEngineMfmaGlobalX;
-  // Accumulators per lane: MR for dot2; for MFMA the D rows a lane can hold
-  // (4*piece + r) that are activation rows, at most 4.
-  constexpr int kAcc = ENGINE == kEngineDot2 ? MR : (MR < 4 ? MR : 4);
+  // Accumulators per lane: the MFMA D rows a lane can hold (4*piece + r)
+  // that are activation rows, at most 4.
+  constexpr int kAcc = MR < 4 ? MR : 4;
   constexpr int kXRow = gemv_x_row(MR, SHARE);          // halves per staged x row of a wave (padded)
   // Per-wave partial sums in LDS: every lane writes its kRows accumulators
   // (no lane-dependent branch, which would let the compiler move the whole
   // scale chain, and the scale loads with it, behind the barrier).
-  constexpr int kRows = ENGINE == kEngineDot2 ? MR : (MR < 4 ? MR : 4);
+  constexpr int kRows = kAcc;
   constexpr int kRedWave = 4 * kRows * 16;               // floats per wave: [piece][kRows][16]
   constexpr int kRed = WAVES * kRedWave;                 // floats per reduction buffer
   float* red = reinterpret_cast<float*>(smem);           // [2][WAVES][4][kRows][16]
@@ -159,8 +159,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     // MFMA: each tile's group sums stay in their own registers and are scaled
     // after the last tile, so a tile's unpack never waits for the previous
     // tile's MFMA chain to finish (same fp32 operations, same order).
-    f32x4 dsave[ENGINE == kEngineDot2 ? 1 : SHARE];
-    float ssave[ENGINE == kEngineDot2 ? 1 : SHARE];
+    f32x4 dsave[SHARE];
+    float ssave[SHARE];
 #pragma unroll
     for (int u = 0; u < SHARE; ++u) {
       const bool valid = u < n;
@@ -177,51 +177,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
       const ZeroPairs zp = zero_pairs((zt >> ((rlane & 7) * 4)) & 15u);
       const float s = half_bits_to_float((st >> ((rlane & 1) * 16)) & 0xFFFFu);
       const _Float16* xg = xbase + u * kGroup;
-      if constexpr (ENGINE == kEngineDot2) {
-        float dot[MR];
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < MR; ++m) dot[m] = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          half2_t p[4];
-          unpack8(wt[kb], magic, zp, p);
-#pragma unroll
-          for (int m = 0; m < MR; ++m) {
-            const u32x4 xq = *reinterpret_cast<const u32x4*>(xg + m * kXRow + 32 * kb);
-            dot[m] = __builtin_amdgcn_fdot2(p[0], as_h2(xq.x), dot[m], false);
-            dot[m] = __builtin_amdgcn_fdot2(p[1], as_h2(xq.y), dot[m], false);
-            dot[m] = __builtin_amdgcn_fdot2(p[2], as_h2(xq.z), dot[m], false);
-            dot[m] = __builtin_amdgcn_fdot2(p[3], as_h2(xq.w), dot[m], false);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MR; ++m) acc[m] = valid ? __builtin_fmaf(dot[m], s, acc[m]) : acc[m];
-      } else {
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          half2_t p[4];
-          unpack8(wt[kb], magic, zp, p);
-          const half8_t bw = {p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
-          half8_t ax;
-          if constexpr (kGlobalX)
-            ax = r.xa[u][kb];
-          else
-            ax = *reinterpret_cast<const half8_t*>(xg + mm * kXRow + 32 * kb);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, d, 0, 0, 0);
-        }
-        dsave[u] = d;
-        ssave[u] = s;
+      for (int kb = 0; kb < 4; ++kb) {
+        half2_t p[4];
+        unpack8(wt[kb], magic, zp, p);
+        const half8_t bw = {p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
+        half8_t ax;
+        if constexpr (kGlobalX)
+          ax = r.xa[u][kb];
+        else
+          ax = *reinterpret_cast<const half8_t*>(xg + mm * kXRow + 32 * kb);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax, bw, d, 0, 0, 0);
       }
+      dsave[u] = d;
+      ssave[u] = s;
     }
-    if constexpr (ENGINE != kEngineDot2) {
 #pragma unroll
-      for (int u = 0; u < SHARE; ++u) {
-        const bool valid = u < n;
+    for (int u = 0; u < SHARE; ++u) {
+      const bool valid = u < n;
 #pragma unroll
-        for (int r2 = 0; r2 < kAcc; ++r2)
-          acc[r2] = valid ? __builtin_fmaf(dsave[u][r2], ssave[u], acc[r2]) : acc[r2];
-      }
+      for (int r2 = 0; r2 < kAcc; ++r2) acc[r2] = valid ? __builtin_fmaf(dsave[u][r2], ssave[u], acc[r2]) : acc[r2];
     }
   };
 
@@ -236,18 +212,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   constexpr int kOut = (MR * 16 + WAVES * 64 - 1) / (WAVES * 64);  // outputs per thread per tile
   auto reduce_tile = [&](float (&acc)[kAcc], float (&out)[kOut]) {
     float* rb = red + parity * kRed;
-    if constexpr (ENGINE == kEngineDot2) {
-      // Lanes l, l^16, l^32, l^48 hold the same row: fold them.
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        float v = acc[m];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[m] = v;
-      }
-    }
-    // MFMA: lane l holds D[4*(l/16) + r][l%16], i.e. activation row
-    // 4*piece + r of weight row rlane. Dot2: every piece holds the full sums.
+    // Lane l holds D[4*(l/16) + r][l%16], i.e. activation row 4*piece + r of
+    // weight row rlane.
 #pragma unroll
     for (int r = 0; r < kRows; ++r) rb[wave * kRedWave + (piece * kRows + r) * 16 + rlane] = acc[r];
     lds_barrier();
@@ -255,7 +221,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     for (int j = 0; j < kOut; ++j) {
       const int idx = min(tid + j * WAVES * 64, MR * 16 - 1);  // one wave has fewer lanes than 8 x 16 outputs
       const int m = idx >> 4, i = idx & 15;
-      const int slot = ENGINE == kEngineDot2 ? m * 16 + i : ((m >> 2) * kRows + (m & 3)) * 16 + i;
+      const int slot = ((m >> 2) * kRows + (m & 3)) * 16 + i;
       float sum = rb[slot];
 #pragma unroll
       for (int w2 = 1; w2 < kHalf; ++w2) sum += rb[w2 * kRedWave + slot];
@@ -457,7 +423,6 @@ hipError_t launch_shape(int N, int K, const LaunchPlan& plan, const void* wq, co
   W4A16_CASE(W, 5, RR, kEpiStore) W4A16_CASE(W, 7, RR, kEpiStore) W4A16_CASE(W, 8, RR, kEpiStore)        \
   W4A16_CASE(W, 10, RR, kEpiStore)
   W4A16_SHARES(1, 1) W4A16_SHARES(2, 1) W4A16_SHARES(4, 1) W4A16_SHARES(8, 1) W4A16_SHARES(16, 1)
-  W4A16_SHARES(4, 2) W4A16_SHARES(8, 2) W4A16_SHARES(4, 3) W4A16_SHARES(8, 3)
 #define W4A16_PAIR(W) W4A16_CASE(W, 4, 1, kEpiSwiglu) W4A16_CASE(W, 5, 1, kEpiSwiglu) W4A16_CASE(W, 7, 1, kEpiSwiglu)
   W4A16_PAIR(2) W4A16_PAIR(4) W4A16_PAIR(8) W4A16_PAIR(16)
 #undef W4A16_PAIR
@@ -474,10 +439,6 @@ hipError_t launch_engine(int N, int K, const LaunchPlan& plan, const void* wq, c
       return launch_shape<MR, kEngineMfma>(N, K, plan, wq, scales, zeros, x, y, acc, stream);
     case kEngineMfmaGlobalX:
       return launch_shape<MR, kEngineMfmaGlobalX>(N, K, plan, wq, scales, zeros, x, y, acc, stream);
-    case kEngineDot2:
-      if constexpr (MR == 1)
-        return launch_shape<MR, kEngineDot2>(N, K, plan, wq, scales, zeros, x, y, acc, stream);
-      return hipErrorInvalidValue;
     default:
       return hipErrorInvalidValue;
   }

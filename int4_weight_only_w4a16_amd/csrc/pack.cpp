@@ -45,6 +45,10 @@ inline uint32_t load_le32(const uint8_t* p) {
 
 extern "C" int w4a16_layout_id(void) { return w4a16::kLayoutId; }
 
+extern "C" int w4a16_check_layout(int layout_id) {
+  return layout_id == w4a16::kLayoutId ? W4A16_OK : W4A16_ELAYOUT;
+}
+
 extern "C" int w4a16_packed_sizes(int N, int K, size_t* wq_bytes, size_t* s_bytes, size_t* z_bytes) {
   if (!shape_ok(N, K)) return W4A16_EINVAL;
   const w4a16::Geometry geo(N, K);

@@ -161,8 +161,7 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
-// Inner-product engines. kEngineDot2: v_dot2_f32_f16 on the VALU, lane-private
-// partial sums over 8-column pieces. kEngineMfma*: v_mfma_f32_16x16x32_f16
+// Inner-product engines. kEngineMfma*: v_mfma_f32_16x16x32_f16
 // with the activations as the A operand (row m of A = x[m]; rows >= M repeat
 // the last x row and are ignored) and the unpacked weights as the B operand
 // (column j of B = weight row j of the tile), so D[m][j] = sum_k x[m][k]

@@ -31,7 +31,6 @@ struct Geometry {
 
 // Inner-product engine of the GEMV kernel.
 enum Engine : int {
-  kEngineDot2 = 0,      // v_dot2_f32_f16 on the VALU (M = 1), x staged in LDS
   kEngineMfma = 1,      // v_mfma_f32_16x16x32_f16, x staged in LDS
   kEngineMfmaGlobalX = 2  // v_mfma_f32_16x16x32_f16, x read straight from global memory
 };
@@ -48,34 +47,32 @@ struct LaunchPlan {
   int waves;   // waves per workgroup: 1, 2, 4, 8 or 16
   int share;   // tiles a wave requests at once (2 .. 10); longer shares take several rounds
   int splits;  // K ranges (gridDim.y); 1 for the plain GEMV
-  int tiles_per_wg;  // row tiles per workgroup, 1..3 (gridDim.x = ceil(row tiles / this))
+  int tiles_per_wg;  // row tiles per workgroup: 1 (gridDim.x = row tiles)
   int epilogue;      // Epilogue (kEpiSwiglu: tiles_per_wg 1, waves = 2 x the waves per row tile)
 };
 
-// Instantiated (waves, share, row tiles per workgroup) per engine and M:
-// those that fit in registers without spilling. Several row tiles per
-// workgroup (R > 1, software-pipelined) only for the MFMA engine with x in
-// LDS; the VALU dot2 engine only for M = 1. The SwiGLU epilogue: MFMA, one
-// gate/up pair per workgroup (2, 4, 8 or 16 waves in two halves), shares of
-// 4, 5 or 7, within the register rule of the plain kernel of as many waves.
+// Instantiated (waves, share) per engine and M: those that fit in registers
+// without spilling, one row tile per workgroup. The SwiGLU epilogue: MFMA,
+// one gate/up pair per workgroup (2, 4, 8 or 16 waves in two halves),
+// shares of 4, 5 or 7, within the register rule of the plain kernel of as
+// many waves. (Several row tiles per workgroup and a VALU dot2 engine were
+// measured and dropped: the plans never chose them.)
 constexpr bool instantiated(int mr, int waves, int share, int engine, int r, int epi = kEpiStore) {
+  if (r != 1) return false;
   if (epi == kEpiSwiglu)
-    return r == 1 && engine == kEngineMfma && (waves == 2 || waves == 4 || waves == 8 || waves == 16) &&
+    return engine == kEngineMfma && (waves == 2 || waves == 4 || waves == 8 || waves == 16) &&
            (share == 4 || share == 5 || share == 7) && instantiated(mr, waves, share, engine, 1);
-  if (r > 1)
-    return engine == kEngineMfma && (waves == 4 || waves == 8) &&
-           (share == 4 || share == 5 || share == 7 || share == 8) && !(waves == 8 && share == 8) &&
-           !(mr >= 3 && share >= 7);
   if (engine == kEngineMfmaGlobalX) return waves == 16 ? share <= 3 : share <= 4;
-  if (engine == kEngineDot2) return mr == 1 && !(waves == 16 && share >= 4) && !(waves == 8 && share >= 10);
+  if (engine != kEngineMfma) return false;
   if (waves == 16) return mr <= 2 ? share <= 10 : share <= 5;
   return !(waves == 8 && mr >= 3 && share >= 8);
 }
 
 // LDS of the cross-wave reduction: two buffers of [waves][4 pieces][rows][16]
-// floats, rows = accumulators per lane (M for dot2, min(M, 4) for MFMA).
+// floats, rows = the MFMA D rows a lane holds that are activation rows.
 constexpr size_t reduction_lds_bytes(int mr, int waves, int engine) {
-  return 2 * size_t(waves) * 4 * (engine == kEngineDot2 ? mr : (mr < 4 ? mr : 4)) * 16 * sizeof(float);
+  (void)engine;
+  return 2 * size_t(waves) * 4 * (mr < 4 ? mr : 4) * 16 * sizeof(float);
 }
 
 // SwiGLU: every wave stages its own x slice when all the slices fit in

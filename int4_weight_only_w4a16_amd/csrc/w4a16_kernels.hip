@@ -109,8 +109,8 @@ size_t lds_bytes(int M, int K, const LaunchPlan& plan) {
 
 bool plan_supported(int M, int K, const LaunchPlan& plan) {
   if (M < 1 || M > 8 || plan.splits < 1 || plan.splits > K / kGroup || plan.splits > kMaxSplits) return false;
-  if (plan.tiles_per_wg < 1 || plan.tiles_per_wg > 3) return false;
-  if (plan.engine < kEngineDot2 || plan.engine > kEngineMfmaGlobalX) return false;
+  if (plan.tiles_per_wg != 1) return false;
+  if (plan.engine != kEngineMfma && plan.engine != kEngineMfmaGlobalX) return false;
   const int w = plan.waves, sh = plan.share;
   if (!(w == 1 || w == 2 || w == 4 || w == 8 || w == 16)) return false;
   if (!(sh == 2 || sh == 3 || sh == 4 || sh == 5 || sh == 7 || sh == 8 || sh == 10)) return false;

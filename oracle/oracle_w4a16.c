@@ -182,6 +182,11 @@ static int weight_at(const uint8_t* wq, int64_t n, int64_t k, int64_t G) {
 /* Element index of (n, g) in the scale buffer; the zero buffer holds half
  * as many bytes per tile (two nibbles per byte). */
 static int64_t scale_index(int64_t n, int64_t g, int64_t G) {
+#if OR_PLANT == 13
+  /* planted: rows of a block reversed past the first row tile (a permutation:
+     round trips and first-tile checks cannot see it) */
+  if (n >= 16) return ((n / 16) * G + g) * 16 + 15 - n % 16;
+#endif
   return ((n / 16) * G + g) * 16 + n % 16;
 }
 

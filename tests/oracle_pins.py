@@ -112,6 +112,31 @@ def pin_layout_tile_locality(o):
         assert lane // 16 == (k % 32) // 8
 
 
+def pin_layout_scale_zero_locality(o):
+    """Layout statement for scales and zeros: the block of tile (t, g) holds
+    the 16 fp16 scales of rows 16t..16t+15 for group g in row order (32
+    bytes at ((t G + g) 16) * 2), and their 16 zero nibbles in 8 bytes at
+    (t G + g) * 8, the even row of each pair in the low nibble. Checked by
+    lighting one scale and one zero at a time, mostly in row tiles t > 0 and
+    in the ragged last tile."""
+    N, K = 53, 640
+    G = K // GROUP
+    rng = np.random.default_rng(5)
+    picks = [(int(rng.integers(16, N)), int(rng.integers(G))) for _ in range(40)] + [(N - 1, G - 1), (16, 0), (0, 0)]
+    for n, g in picks:
+        s = np.zeros((N, G), np.uint16)
+        s[n, g] = 0x3C00
+        z = np.zeros((N, G), np.uint8)
+        z[n, g] = 9
+        _, sp, zp = o.pack(np.zeros((N, K), np.uint8), s, z)
+        t, i = n // 16, n % 16
+        nz = np.flatnonzero(sp)
+        assert nz.size == 1 and int(nz[0]) == ((t * G + g) * 16 + i) * 2 + 1, (n, g, nz)  # 0x3C00 little-endian
+        nz = np.flatnonzero(zp)
+        assert nz.size == 1 and int(nz[0]) == (t * G + g) * 8 + i // 2, (n, g, nz)
+        assert int(zp[nz[0]]) == (9 << 4 if i % 2 else 9), (n, g, int(zp[nz[0]]))
+
+
 def pin_layout_roundtrip(o):
     """unpack(pack(q, s, z)) == (q, s, z) bit for bit, on random data, ragged
     N, G not a multiple of 8, and the all-0 / all-15 / walking-nibble cases."""

@@ -36,6 +36,11 @@ def test_library_exports_every_declared_symbol():
 
 def test_layout_id_and_status_text():
     assert w.w4a16_layout_id() == 2
+    w.w4a16_check_layout(2)
+    for other in (0, 1, 3, -1):
+        with pytest.raises(w.W4A16Error) as e:
+            w.w4a16_check_layout(other)
+        assert e.value.status == w.W4A16_ELAYOUT
     for code in (0, -1, -2, -3, -4):
         assert w.w4a16_strerror(code)
     assert w.w4a16_strerror(-99) == "unknown status"

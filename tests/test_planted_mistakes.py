@@ -21,6 +21,7 @@ PLANTS = {
     10: "activation code scale absmax / 128",
     11: "activation scale of row 0 used for every row",
     12: "integer-sum product drops the zero point",
+    13: "scale and zero rows reversed past the first row tile",
 }
 
 
