@@ -259,6 +259,60 @@ class ChainStep:
         return [o["y"].cpu().numpy().view(np.uint16).copy() for o in self.ops]
 
 
+def handoff_costs(torch, seed, n=64, reps=20):
+    """Cost of one dependency: n tiny GEMVs (128 x 128, 8 row tiles, one
+    group), each reading the previous one's output, as one chain launch and
+    as n launches in one graph; us per GEMV of each (almost no bytes: the
+    time is the handoff and the fixed cost of a GEMV)."""
+    import int4_weight_only_w4a16_amd as w
+    dev = torch.device("cuda:0")
+    N = K = 128
+    wq, sc, zp = synthetic.device_packed_weights(N, K, seed, 8000, dev)
+    xs = [synthetic.device_activations(1, K, seed, 8000, dev)]
+    ys = [torch.empty((1, N), dtype=torch.int16, device=dev) for _ in range(n)]
+    ops = [dict(kind=w.CHAIN_GEMV, N=N, K=K, splits=1, x_src=i - 1, x_shift=4 if i else 0, wq=wq, scales=sc,
+                zeros=zp, x=xs[0] if i == 0 else None, y=ys[i]) for i in range(n)]
+    plan, ws_bytes = w.w4a16_chain_plan(1, ops)
+    plan_d = torch.from_numpy(plan).to(dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    for _ in range(3):
+        w.w4a16_chain_run(1, plan_d, ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        w.w4a16_chain_run(1, plan_d, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    chain_us = e0.elapsed_time(e1) * 1e3 / reps
+    off = w.CHAIN_ERROR_OFFSET
+    err = int(ws[off:off + 4].cpu().numpy().view(np.uint32)[0])
+    # the same n GEMVs, each its own launch, in one graph (inputs chained through y as fp16)
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            w.w4a16_gemv(1, N, K, wq, sc, zp, xs[0] if i == 0 else ys[i - 1], ys[i], stream=stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                w.w4a16_gemv(1, N, K, wq, sc, zp, xs[0] if i == 0 else ys[i - 1], ys[i], stream=stream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / reps
+    return {"gemvs": n, "shape": f"{N}x{K}", "chain_us_per_dependent_gemv": round(chain_us / n, 3),
+            "graph_us_per_dependent_launch": round(graph_us / n, 3), "chain_error_word": err}
+
+
 def check_chain(chain, ys):
     """Every output of the chain against the oracle's bound, each GEMV's
     input being its producer's GPU output (first K columns) times 2^-shift,
@@ -919,6 +973,7 @@ def main():
         "launches_per_step": 1,
         "down_splits": 1,
         "error_word": chain_err,
+        "handoff": handoff_costs(torch, args.seed),
     }
 
     # Outputs of the last full replay, for the sampled check.

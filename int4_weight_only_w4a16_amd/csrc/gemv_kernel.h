@@ -163,7 +163,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     float ssave[SHARE];
 #pragma unroll
     for (int u = 0; u < SHARE; ++u) {
-      const bool valid = u < n;
       __builtin_amdgcn_sched_barrier(0);  // keep tiles in request order
       // Pass this tile's registers through an (empty) volatile asm: the
       // asm statements stay in program order, and nothing computed from the
