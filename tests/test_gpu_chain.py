@@ -199,3 +199,31 @@ def test_chain_full_7b_step_oracle_sampled_and_repeat():
         again = chain.run()
         for a, b in zip(ys, again):
             assert np.array_equal(a, b)
+
+
+def test_chain_error_paths_from_the_host():
+    """Failure handling, forced from the host with every workgroup leaving
+    normally: a workspace smaller than the plan's is refused by the kernel
+    (error word 2, outputs untouched); a nonzero error word is sticky (later
+    runs return at once, outputs untouched) until the caller clears it."""
+    torch, _ = torch_dev()
+    chain = Chain(1, MIXED[:3], seed=25)
+    off = w.CHAIN_ERROR_OFFSET
+    err = lambda: int(chain.ws[off:off + 4].cpu().numpy().view(np.uint32)[0])
+    # too small a workspace (the header fits): the kernel refuses the plan
+    print("chain error path: short workspace", flush=True)
+    w.w4a16_chain_run(1, chain.plan, chain.ws[:256])
+    torch.cuda.synchronize()
+    assert err() == 2
+    assert all((o["y"].cpu().numpy() == -1).all() for o in chain.ops)  # nothing written
+    # sticky: a run on the full workspace with the error word still set does nothing
+    print("chain error path: sticky error word", flush=True)
+    w.w4a16_chain_run(1, chain.plan, chain.ws)
+    torch.cuda.synchronize()
+    assert err() == 2
+    assert all((o["y"].cpu().numpy() == -1).all() for o in chain.ops)
+    # cleared by the caller: the chain runs and checks out
+    chain.ws.zero_()
+    torch.cuda.synchronize()
+    ys = chain.run()
+    check_oracle(chain, ys, chain.inputs(ys))
