@@ -568,6 +568,82 @@ def decompose_pass(torch, seed, steps):
                       "launches_per_step": len(step.shapes), "steps_traced_each": steps}), flush=True)
 
 
+def _graph_cold_us(torch, launch, n, rounds=5, reps=3):
+    """Median microseconds per launch of `launch(stream)`, which makes `n`
+    launches over distinct buffers (more bytes than the caches hold), captured
+    once in a graph and replayed `reps` times per round."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        launch(stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            launch(stream)
+        torch.cuda.synchronize()
+        g.replay()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / (reps * n))
+    del g
+    return sorted(ts)[len(ts) // 2]
+
+
+def read_floor(torch, seed):
+    """Per 7B-shaped GEMV of the decode step: the time a plain read of its
+    weight, scale and zero bytes takes (the library's read probe at its best
+    grid), against the GEMV itself, both as back-to-back launches over
+    distinct cold buffers in one graph; the split-K GEMV of down at several
+    split counts; and the step both add up to (28 layers and lm_head). One
+    JSON line per shape, then one for the step."""
+    import int4_weight_only_w4a16_amd as w
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+    shapes = [(name, N, K) for name, N, K in synthetic.QWEN7B_LAYER] + [synthetic.QWEN7B_LM_HEAD]
+    sums = {"read": 0.0, "gemv": 0.0}
+    for name, N, K in shapes:
+        G = K // GROUP
+        nb = N * K // 2 + 2 * N * G + N * G // 2
+        copies = max(2, (768 << 20) // nb + 1)
+        bufs = [torch.ones((nb + 4095) // 4096 * 4096, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        by_grid = {}
+        for grid in (256, 512, 768, 1024, 2048, 4096):
+            by_grid[grid] = _graph_cold_us(
+                torch, lambda st, grid=grid: [w.w4a16_read_probe(b, grid, sink, nbytes=nb, stream=st) for b in bufs],
+                copies)
+        del bufs
+        sets = [synthetic.device_packed_weights(N, K, seed, 700 + c, dev) for c in range(copies)]
+        x = synthetic.device_activations(1, K, seed, 1, dev)
+        y = torch.empty((1, N), dtype=torch.int16, device=dev)
+        gemv = _graph_cold_us(torch, lambda st: [w.w4a16_gemv(1, N, K, *a, x, y, stream=st) for a in sets], copies)
+        row = {"shape": f"{name} {N}x{K}", "bytes": nb, "copies": copies,
+               "read_us_by_grid": {g: round(t, 2) for g, t in by_grid.items()},
+               "read_us": round(min(by_grid.values()), 2), "gemv_us": round(gemv, 2),
+               "gemv_over_read_us": round(gemv - min(by_grid.values()), 2)}
+        if name == "down_proj":
+            ws = torch.zeros(w.w4a16_splitk_workspace_bytes(1, N, 16), dtype=torch.uint8, device=dev)
+            row["gemv_splitk_us"] = {s: round(_graph_cold_us(
+                torch, lambda st, s=s: [w.w4a16_gemv_splitk(1, N, K, s, *a, x, y, ws, stream=st) for a in sets],
+                copies), 2) for s in (2, 4, 8, 16)}
+        print(json.dumps(row), flush=True)
+        times = 1 if (name, N, K) == synthetic.QWEN7B_LM_HEAD else synthetic.QWEN7B_LAYERS
+        sums["read"] += times * min(by_grid.values())
+        sums["gemv"] += times * gemv
+        del sets
+    total = sum(algorithmic_bytes(1, N, K) for _, N, K in step_shapes())
+    print(json.dumps({"step_launches": len(step_shapes()), "step_read_only_us": round(sums["read"], 1),
+                      "step_gemv_us": round(sums["gemv"], 1), "step_bytes": total,
+                      "step_at_80pct_of_peak_us": round(total / (0.8 * HBM_PEAK_GBPS) / 1e3, 1)}), flush=True)
+
+
 def decompose_summary(directory, steps, launches=113):
     """Step decomposition from a kernel trace of decompose_pass: per step,
     the wall span, the sum of kernel durations and the gaps between
@@ -769,6 +845,8 @@ def main():
     ap.add_argument("--decompose", type=int, metavar="STEPS",
                     help="trace STEPS graph and STEPS eager steps (for rocprofv3 --kernel-trace), then time both")
     ap.add_argument("--decompose-summary", metavar="DIR", help="step decomposition from a --decompose trace")
+    ap.add_argument("--read-floor", action="store_true",
+                    help="time a plain read of each 7B GEMV's bytes against the GEMV (graph, cold) instead")
     args = ap.parse_args()
 
     if args.trace_summary:
@@ -804,6 +882,9 @@ def main():
         return
     if args.decompose:
         decompose_pass(torch, args.seed, args.decompose)
+        return
+    if args.read_floor:
+        read_floor(torch, args.seed)
         return
 
     t_setup = time.perf_counter()
