@@ -139,3 +139,38 @@ def test_gemm_small_tiles_full_grid_repeatable(M):
     assert ok, worst
     for _ in range(4):
         assert np.array_equal(y, run_gemm(p)), "run-to-run difference"
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(300, 32776, 384, 1), (256, 65536, 256, 1), (520, 32904, 640, 3)])
+def test_gemm_large_grid_sampled(M, N, K, splits):
+    """Grids of 770 to 1300 tiles of 128 x 128, ragged in M (the last m block
+    partly past M) and in N (a short last column strip and a ragged row
+    tile), unsplit and split in 3. Sampled weight rows (strip and tile edges
+    included) against the oracle for all M rows, the rounded-weights bar,
+    bit-identical run to run, and (unsplit) rows 0..15 bit-identical to the
+    same rows computed in a 16-row tile: each output's fp32 order does not
+    depend on the tile's height."""
+    _say("large grid", M, N, K, splits)
+    rng = np.random.default_rng(N)
+    edges = [0, 15, 16, 127, 128, 255, 256, N - 17, N - 9, N - 8, N - 1]
+    rows = np.unique(np.concatenate([edges, rng.integers(0, N, 40)]))
+    q, s, z = synthetic.weights(N, K, seed=M, tensor_id=1)
+    p = Problem(M, N, K, q=q, s=s, z=z, x=synthetic.activations(M, K, seed=M, tensor_id=2))
+    if splits == 1:
+        y = run_gemm(p)
+        again = run_gemm(p)
+    else:
+        ws = p.splitk_workspace(splits)
+        y = p.gemm_splitk(splits, ws)
+        assert p.workspace_is_zero(ws)
+        again = p.gemm_splitk(splits, ws)
+    o = oracle.get()
+    ref, absref = o.gemv_packed(M, N, K, *p.packed, p.x, rows=rows)
+    ok, worst = oracle.bound_report(y[:, rows], ref, absref, o)
+    _say(M, N, K, splits, "worst", worst)
+    assert ok, worst
+    check_rounded_weights(p, y, rows)
+    assert np.array_equal(y, again), "run-to-run difference"
+    if splits == 1:
+        p16 = Problem(16, N, K, q=q, s=s, z=z, x=p.x[:16])
+        assert np.array_equal(run_gemm(p16), y[:16]), "rows differ from the 16-row tile"
