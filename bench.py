@@ -950,8 +950,10 @@ def main():
     # GEMM, the standalone fp16 dequantization, and for context the two-step
     # route (that dequantization, then torch's fp16 library GEMM). Matrix-core
     # runs on this GPU vary by several percent with what ran just before
-    # (power and clock state), so the three are timed in turn, three rounds,
-    # and each reports its median.
+    # (power and clock state; timed first on a device that had been running
+    # only memory-bound work, a GEMM read 5-15% slow), so the three first run
+    # under sustained load for a second, then are timed in turn, in a
+    # rotating order, five rounds, and each reports its median.
     import int4_weight_only_w4a16_amd as wl
     Mp = 2048
 
@@ -967,6 +969,21 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
 
+    def rotating_rounds(fns, rounds=5, settle_s=1.0):
+        """Times of each callable: after settle_s seconds of all of them in
+        turn, `rounds` rounds in a rotating order."""
+        names = list(fns)
+        t_end = time.perf_counter() + settle_s
+        while time.perf_counter() < t_end:
+            for n in names:
+                fns[n]()
+            torch.cuda.synchronize()
+        runs = {n: [] for n in names}
+        for r in range(rounds):
+            for n in names[r % len(names):] + names[:r % len(names)]:
+                runs[n].append(timed(fns[n]))
+        return runs
+
     prefill = {}
     for label, layer in (("gate_up", 2), ("down", 3)):
         _, Np, Kp = synthetic.QWEN7B_LAYER[layer]
@@ -974,11 +991,10 @@ def main():
         xp = synthetic.device_activations(Mp, Kp, args.seed, 9999, torch.device("cuda:0"))
         yp = torch.empty((Mp, Np), dtype=torch.int16, device="cuda:0")
         w16 = torch.empty((Np, Kp), dtype=torch.float16, device="cuda:0")
-        runs = {"gemm": [], "dq": [], "lib": []}
-        for _ in range(3):
-            runs["gemm"].append(timed(lambda: wl.w4a16_gemm(Mp, Np, Kp, wq_g, sc_g, zp_g, xp, yp)))
-            runs["dq"].append(timed(lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16)))
-            runs["lib"].append(timed(lambda: torch.matmul(xp.view(torch.float16), w16.t())))
+        fns = {"gemm": lambda: wl.w4a16_gemm(Mp, Np, Kp, wq_g, sc_g, zp_g, xp, yp),
+               "dq": lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16),
+               "lib": lambda: torch.matmul(xp.view(torch.float16), w16.t())}
+        runs = rotating_rounds(fns)
         gemm_us, dq_us, lib_us = (float(np.median(runs[k])) for k in ("gemm", "dq", "lib"))
         flops = 2.0 * Mp * Np * Kp
         dq_bytes = algorithmic_bytes(0, Np, Kp) + 2 * Np * Kp
@@ -1009,13 +1025,11 @@ def main():
         w16 = torch.empty((Np, Kp), dtype=torch.float16, device="cuda:0")
         splits = wl.w4a16_gemm_splitk_choose(Ms, Np, Kp)
         ws_g = torch.zeros(wl.w4a16_splitk_workspace_bytes(Ms, Np, splits), dtype=torch.uint8, device="cuda:0")
-        runs = {"gemm": [], "split": [], "dq": [], "lib": []}
-        for _ in range(3):
-            runs["gemm"].append(timed(lambda: wl.w4a16_gemm(Ms, Np, Kp, wq_g, sc_g, zp_g, xp, yp)))
-            runs["split"].append(timed(lambda: wl.w4a16_gemm_splitk(Ms, Np, Kp, splits, wq_g, sc_g, zp_g, xp, yp,
-                                                                    ws_g)))
-            runs["dq"].append(timed(lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16)))
-            runs["lib"].append(timed(lambda: torch.matmul(xp.view(torch.float16), w16.t())))
+        fns = {"gemm": lambda: wl.w4a16_gemm(Ms, Np, Kp, wq_g, sc_g, zp_g, xp, yp),
+               "split": lambda: wl.w4a16_gemm_splitk(Ms, Np, Kp, splits, wq_g, sc_g, zp_g, xp, yp, ws_g),
+               "dq": lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16),
+               "lib": lambda: torch.matmul(xp.view(torch.float16), w16.t())}
+        runs = rotating_rounds(fns)
         gemm_us, split_us, dq_us, lib_us = (float(np.median(runs[k])) for k in ("gemm", "split", "dq", "lib"))
         prefill_small[label] = {
             "shape": f"M={Ms} x {label} {Np}x{Kp}",
