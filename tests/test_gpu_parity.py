@@ -105,7 +105,7 @@ def test_verify27b_shapes(name, N, K, M):
 # ------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("M", range(1, 9))
-@pytest.mark.parametrize("N,K", [(1, 128), (15, 256), (17, 1152), (133, 640), (16, 32768)])
+@pytest.mark.parametrize("N,K", [(1, 128), (15, 256), (17, 1152), (133, 640), (16, 32768), (33, 65664)])
 def test_ragged_and_small(M, N, K):
     p = Problem(M, N, K, seed=M * 100 + N)
     p.check(p.gemv())
