@@ -521,6 +521,67 @@ def counter_summary(dirs):
         print(" | ".join(out))
 
 
+def gemm_counter_summary(dirs, fetch_scale=1.9998, write_scale=1.0):
+    """Per-dispatch counter means of the M = 2048 prefill GEMMs (128-row
+    tiles) in rocprofv3 --pmc runs of `bench.py --prefill-gemm`, one run per
+    directory, for gate+up 37888x3584 and down 3584x18944. FETCH_SIZE and
+    WRITE_SIZE are scaled by the plain copy kernel's factors (the GEMV
+    counter file's)."""
+    M = 2048
+    shapes = {"gate+up 37888x3584": (37888, 3584), "down 3584x18944": (3584, 18944)}
+    grids = {name: str((M + 127) // 128 * 256 * ((N + 127) // 128)) for name, (N, K) in shapes.items()}
+    vals = {name: {} for name in shapes}
+    for directory in dirs:
+        for r in _counter_rows(directory):
+            if "gemm_kernel" not in r["name"]:
+                continue
+            for name, g in grids.items():
+                if r["grid"] == g:
+                    for k, v in r.items():
+                        if k not in ("name", "grid", "wg"):
+                            vals[name].setdefault(k, []).append(v)
+    mean = {name: {k: sum(v) / len(v) for k, v in d.items()} for name, d in vals.items()}
+    count = {name: {k: len(v) for k, v in d.items()} for name, d in vals.items()}
+    names = list(shapes)
+    print(f"{'':40s}" + "".join(f"{n:>24s}" for n in names))
+
+    def row(label, f, fmt="{:,.0f}"):
+        cells = []
+        for n in names:
+            try:
+                cells.append(fmt.format(f(mean[n], *shapes[n])))
+            except (KeyError, ZeroDivisionError):
+                cells.append("-")
+        print(f"{label:40s}" + "".join(f"{c:>24s}" for c in cells))
+
+    disp = {n: min(count[n].values()) if count[n] else 0 for n in names}
+    print(f"{'dispatches averaged':40s}" + "".join(f"{disp[n]:>24d}" for n in names))
+    row("SQ_WAVES", lambda d, N, K: d["SQ_WAVES"])
+    row("SQ_INSTS_MFMA", lambda d, N, K: d["SQ_INSTS_MFMA"])
+    row("  M*N*K / (16*16*32)", lambda d, N, K: M * N * K / (16 * 16 * 32))
+    row("SQ_INSTS_VALU (includes MFMA)", lambda d, N, K: d["SQ_INSTS_VALU"])
+    row("  other VALU per MFMA", lambda d, N, K: (d["SQ_INSTS_VALU"] - d["SQ_INSTS_MFMA"]) / d["SQ_INSTS_MFMA"],
+        "{:.2f}")
+    row("SQ_INSTS_LDS", lambda d, N, K: d["SQ_INSTS_LDS"])
+    row("SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE %",
+        lambda d, N, K: 100 * d["SQ_LDS_BANK_CONFLICT"] / d["SQ_LDS_IDX_ACTIVE"], "{:.2f}")
+    row("SQ_VALU_MFMA_BUSY_CYCLES", lambda d, N, K: d["SQ_VALU_MFMA_BUSY_CYCLES"])
+    row("  / (1024 SIMDs x 2.4 GHz), us", lambda d, N, K: d["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / 2.4e3, "{:.1f}")
+    row("  flops / 2.5 PFLOP/s, us", lambda d, N, K: 2.0 * M * N * K / (MFMA_F16_PEAK_TFLOPS * 1e6), "{:.1f}")
+    row("SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES %", lambda d, N, K: 100 * d["SQ_WAIT_INST_ANY"] / d["SQ_WAVE_CYCLES"],
+        "{:.1f}")
+    row("SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES %",
+        lambda d, N, K: 100 * d["SQ_ACTIVE_INST_ANY"] / d["SQ_WAVE_CYCLES"], "{:.1f}")
+    row("SQ_INSTS_VMEM_RD per wave", lambda d, N, K: d["SQ_INSTS_VMEM_RD"] / d["SQ_WAVES"])
+    row("FETCH_SIZE (KiB)", lambda d, N, K: d["FETCH_SIZE"])
+    row("WRITE_SIZE (KiB)", lambda d, N, K: d["WRITE_SIZE"])
+    row("  M*N*2 B / 1024", lambda d, N, K: M * N * 2 / 1024)
+    row("scaled L2-miss reads (B)", lambda d, N, K: d["FETCH_SIZE"] * 1024 * fetch_scale)
+    row("algorithmic reads: weights + x (B)", lambda d, N, K: algorithmic_bytes(M, N, K) - 2 * M * N)
+    row("  reads / algorithmic reads", lambda d, N, K: d["FETCH_SIZE"] * 1024 * fetch_scale /
+        (algorithmic_bytes(M, N, K) - 2 * M * N), "{:.2f}")
+
+
 def read_ceiling_gbps(torch):
     """Plain-read ceiling of this device: the library's read probe (the
     GEMV's own non-temporal 16-byte loads, nothing stored) over 1 GiB at four
@@ -825,6 +886,109 @@ def run_configs(torch, seed, oracle_budget_s=3.0):
     return rows
 
 
+def prefill_gemm(torch, seed, weights):
+    """Prefill GEMM timings, M = 2048 on gate+up and down and M = 64 split-K
+    on qkv, o and down; weights(layer) gives the packed weights of the 7B
+    layer shape of that index. Returns the two JSON sections."""
+    # Prefill (M = 2048) on the gate+up and down shapes: the fused W4A16
+    # GEMM, the standalone fp16 dequantization, and for context the two-step
+    # route (that dequantization, then torch's fp16 library GEMM). Matrix-core
+    # runs on this GPU vary by several percent with what ran just before
+    # (power and clock state; timed first on a device that had been running
+    # only memory-bound work, a GEMM read 5-15% slow), so the three first run
+    # under sustained load for a second, then are timed in turn, in a
+    # rotating order, five rounds, and each reports its median.
+    import int4_weight_only_w4a16_amd as wl
+    Mp = 2048
+
+    def timed(fn, reps=10):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def rotating_rounds(fns, rounds=5, settle_s=1.0):
+        """Times of each callable: after settle_s seconds of all of them in
+        turn, `rounds` rounds in a rotating order."""
+        names = list(fns)
+        t_end = time.perf_counter() + settle_s
+        while time.perf_counter() < t_end:
+            for n in names:
+                fns[n]()
+            torch.cuda.synchronize()
+        runs = {n: [] for n in names}
+        for r in range(rounds):
+            for n in names[r % len(names):] + names[:r % len(names)]:
+                runs[n].append(timed(fns[n]))
+        return runs
+
+    prefill = {}
+    for label, layer in (("gate_up", 2), ("down", 3)):
+        _, Np, Kp = synthetic.QWEN7B_LAYER[layer]
+        wq_g, sc_g, zp_g = weights(layer)
+        xp = synthetic.device_activations(Mp, Kp, seed, 9999, torch.device("cuda:0"))
+        yp = torch.empty((Mp, Np), dtype=torch.int16, device="cuda:0")
+        w16 = torch.empty((Np, Kp), dtype=torch.float16, device="cuda:0")
+        fns = {"gemm": lambda: wl.w4a16_gemm(Mp, Np, Kp, wq_g, sc_g, zp_g, xp, yp),
+               "dq": lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16),
+               "lib": lambda: torch.matmul(xp.view(torch.float16), w16.t())}
+        runs = rotating_rounds(fns)
+        gemm_us, dq_us, lib_us = (float(np.median(runs[k])) for k in ("gemm", "dq", "lib"))
+        flops = 2.0 * Mp * Np * Kp
+        dq_bytes = algorithmic_bytes(0, Np, Kp) + 2 * Np * Kp
+        prefill[label] = {
+            "shape": f"M={Mp} x {label} {Np}x{Kp}",
+            "w4a16_gemm_us": round(gemm_us, 1),
+            "w4a16_gemm_TFLOPs": round(flops / (gemm_us * 1e-6) / 1e12, 1),
+            "w4a16_gemm_frac_of_mfma_f16_peak": round(flops / (gemm_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "dequant_f16_us": round(dq_us, 1),
+            "dequant_f16_GBps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1),
+            "dequant_f16_frac_of_hbm_peak": round(dq_bytes / (dq_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "torch_fp16_gemm_us": round(lib_us, 1),
+            "two_step_dequant_plus_torch_fp16_gemm_us": round(dq_us + lib_us, 1),
+        }
+        del xp, yp, w16
+
+    # Short prefill chunks (M = 64) leave the 128 x 128-tile GEMM with a few
+    # dozen workgroups on 256 compute units: the split-K GEMM at the split
+    # count the library chooses, against the unsplit one and the two-step
+    # route, timed in turn as above.
+    prefill_small = {}
+    Ms = 64
+    for label, layer in (("qkv", 0), ("o", 1), ("down", 3)):
+        _, Np, Kp = synthetic.QWEN7B_LAYER[layer]
+        wq_g, sc_g, zp_g = weights(layer)
+        xp = synthetic.device_activations(Ms, Kp, seed, 9998, torch.device("cuda:0"))
+        yp = torch.empty((Ms, Np), dtype=torch.int16, device="cuda:0")
+        w16 = torch.empty((Np, Kp), dtype=torch.float16, device="cuda:0")
+        splits = wl.w4a16_gemm_splitk_choose(Ms, Np, Kp)
+        ws_g = torch.zeros(wl.w4a16_splitk_workspace_bytes(Ms, Np, splits), dtype=torch.uint8, device="cuda:0")
+        fns = {"gemm": lambda: wl.w4a16_gemm(Ms, Np, Kp, wq_g, sc_g, zp_g, xp, yp),
+               "split": lambda: wl.w4a16_gemm_splitk(Ms, Np, Kp, splits, wq_g, sc_g, zp_g, xp, yp, ws_g),
+               "dq": lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16),
+               "lib": lambda: torch.matmul(xp.view(torch.float16), w16.t())}
+        runs = rotating_rounds(fns)
+        gemm_us, split_us, dq_us, lib_us = (float(np.median(runs[k])) for k in ("gemm", "split", "dq", "lib"))
+        prefill_small[label] = {
+            "shape": f"M={Ms} x {label} {Np}x{Kp}",
+            "splits": splits,
+            "w4a16_gemm_splitk_us": round(split_us, 1),
+            "w4a16_gemm_unsplit_us": round(gemm_us, 1),
+            "two_step_dequant_plus_torch_fp16_gemm_us": round(dq_us + lib_us, 1),
+            "splitk_TFLOPs": round(2.0 * Ms * Np * Kp / (split_us * 1e-6) / 1e12, 1),
+            "splitk_weight_GBps": round(algorithmic_bytes(0, Np, Kp) / (split_us * 1e-6) / 1e9, 1),
+        }
+        del xp, yp, w16, ws_g
+
+    return prefill, prefill_small
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -845,6 +1009,10 @@ def main():
     ap.add_argument("--decompose", type=int, metavar="STEPS",
                     help="trace STEPS graph and STEPS eager steps (for rocprofv3 --kernel-trace), then time both")
     ap.add_argument("--decompose-summary", metavar="DIR", help="step decomposition from a --decompose trace")
+    ap.add_argument("--gemm-counter-summary", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 --pmc runs of --prefill-gemm (one directory per counter set)")
+    ap.add_argument("--prefill-gemm", action="store_true",
+                    help="time only the prefill GEMM section (for counter passes) and print it as one JSON line")
     ap.add_argument("--read-floor", action="store_true",
                     help="time a plain read of each 7B GEMV's bytes against the GEMV (graph, cold) instead")
     args = ap.parse_args()
@@ -857,6 +1025,9 @@ def main():
         return
     if args.decompose_summary:
         decompose_summary(args.decompose_summary, args.decompose or 20)
+        return
+    if args.gemm_counter_summary:
+        gemm_counter_summary(args.gemm_counter_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the W4A16 GEMV path here is single-GPU "
@@ -885,6 +1056,12 @@ def main():
         return
     if args.read_floor:
         read_floor(torch, args.seed)
+        return
+    if args.prefill_gemm:
+        dev = torch.device("cuda:0")
+        pre, small = prefill_gemm(torch, args.seed, lambda layer: synthetic.device_packed_weights(
+            synthetic.QWEN7B_LAYER[layer][1], synthetic.QWEN7B_LAYER[layer][2], args.seed, layer, dev))
+        print(json.dumps({"prefill_gemm": pre, "prefill_gemm_small_m": small}), flush=True)
         return
 
     t_setup = time.perf_counter()
@@ -946,101 +1123,8 @@ def main():
     a8f_step_us = step.time_graph(a8f_step, args.steps, args.warmup) / args.steps * 1e6
     del a8_gate_up, a8_gemv, a8_step, a8f_gate_up, a8f_step
 
-    # Prefill (M = 2048) on the gate+up and down shapes: the fused W4A16
-    # GEMM, the standalone fp16 dequantization, and for context the two-step
-    # route (that dequantization, then torch's fp16 library GEMM). Matrix-core
-    # runs on this GPU vary by several percent with what ran just before
-    # (power and clock state; timed first on a device that had been running
-    # only memory-bound work, a GEMM read 5-15% slow), so the three first run
-    # under sustained load for a second, then are timed in turn, in a
-    # rotating order, five rounds, and each reports its median.
+    prefill, prefill_small = prefill_gemm(torch, args.seed, lambda layer: step.bufs[layer][3:6])
     import int4_weight_only_w4a16_amd as wl
-    Mp = 2048
-
-    def timed(fn, reps=10):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
-
-    def rotating_rounds(fns, rounds=5, settle_s=1.0):
-        """Times of each callable: after settle_s seconds of all of them in
-        turn, `rounds` rounds in a rotating order."""
-        names = list(fns)
-        t_end = time.perf_counter() + settle_s
-        while time.perf_counter() < t_end:
-            for n in names:
-                fns[n]()
-            torch.cuda.synchronize()
-        runs = {n: [] for n in names}
-        for r in range(rounds):
-            for n in names[r % len(names):] + names[:r % len(names)]:
-                runs[n].append(timed(fns[n]))
-        return runs
-
-    prefill = {}
-    for label, layer in (("gate_up", 2), ("down", 3)):
-        _, Np, Kp = synthetic.QWEN7B_LAYER[layer]
-        wq_g, sc_g, zp_g = step.bufs[layer][3:6]  # layer 0 weights of this shape
-        xp = synthetic.device_activations(Mp, Kp, args.seed, 9999, torch.device("cuda:0"))
-        yp = torch.empty((Mp, Np), dtype=torch.int16, device="cuda:0")
-        w16 = torch.empty((Np, Kp), dtype=torch.float16, device="cuda:0")
-        fns = {"gemm": lambda: wl.w4a16_gemm(Mp, Np, Kp, wq_g, sc_g, zp_g, xp, yp),
-               "dq": lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16),
-               "lib": lambda: torch.matmul(xp.view(torch.float16), w16.t())}
-        runs = rotating_rounds(fns)
-        gemm_us, dq_us, lib_us = (float(np.median(runs[k])) for k in ("gemm", "dq", "lib"))
-        flops = 2.0 * Mp * Np * Kp
-        dq_bytes = algorithmic_bytes(0, Np, Kp) + 2 * Np * Kp
-        prefill[label] = {
-            "shape": f"M={Mp} x {label} {Np}x{Kp}",
-            "w4a16_gemm_us": round(gemm_us, 1),
-            "w4a16_gemm_TFLOPs": round(flops / (gemm_us * 1e-6) / 1e12, 1),
-            "w4a16_gemm_frac_of_mfma_f16_peak": round(flops / (gemm_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-            "dequant_f16_us": round(dq_us, 1),
-            "dequant_f16_GBps": round(dq_bytes / (dq_us * 1e-6) / 1e9, 1),
-            "dequant_f16_frac_of_hbm_peak": round(dq_bytes / (dq_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "torch_fp16_gemm_us": round(lib_us, 1),
-            "two_step_dequant_plus_torch_fp16_gemm_us": round(dq_us + lib_us, 1),
-        }
-        del xp, yp, w16
-
-    # Short prefill chunks (M = 64) leave the 128 x 128-tile GEMM with a few
-    # dozen workgroups on 256 compute units: the split-K GEMM at the split
-    # count the library chooses, against the unsplit one and the two-step
-    # route, timed in turn as above.
-    prefill_small = {}
-    Ms = 64
-    for label, layer in (("qkv", 0), ("o", 1), ("down", 3)):
-        _, Np, Kp = synthetic.QWEN7B_LAYER[layer]
-        wq_g, sc_g, zp_g = step.bufs[layer][3:6]
-        xp = synthetic.device_activations(Ms, Kp, args.seed, 9998, torch.device("cuda:0"))
-        yp = torch.empty((Ms, Np), dtype=torch.int16, device="cuda:0")
-        w16 = torch.empty((Np, Kp), dtype=torch.float16, device="cuda:0")
-        splits = wl.w4a16_gemm_splitk_choose(Ms, Np, Kp)
-        ws_g = torch.zeros(wl.w4a16_splitk_workspace_bytes(Ms, Np, splits), dtype=torch.uint8, device="cuda:0")
-        fns = {"gemm": lambda: wl.w4a16_gemm(Ms, Np, Kp, wq_g, sc_g, zp_g, xp, yp),
-               "split": lambda: wl.w4a16_gemm_splitk(Ms, Np, Kp, splits, wq_g, sc_g, zp_g, xp, yp, ws_g),
-               "dq": lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16),
-               "lib": lambda: torch.matmul(xp.view(torch.float16), w16.t())}
-        runs = rotating_rounds(fns)
-        gemm_us, split_us, dq_us, lib_us = (float(np.median(runs[k])) for k in ("gemm", "split", "dq", "lib"))
-        prefill_small[label] = {
-            "shape": f"M={Ms} x {label} {Np}x{Kp}",
-            "splits": splits,
-            "w4a16_gemm_splitk_us": round(split_us, 1),
-            "w4a16_gemm_unsplit_us": round(gemm_us, 1),
-            "two_step_dequant_plus_torch_fp16_gemm_us": round(dq_us + lib_us, 1),
-            "splitk_TFLOPs": round(2.0 * Ms * Np * Kp / (split_us * 1e-6) / 1e12, 1),
-            "splitk_weight_GBps": round(algorithmic_bytes(0, Np, Kp) / (split_us * 1e-6) / 1e9, 1),
-        }
-        del xp, yp, w16, ws_g
 
     # Host quantizer (w4a16_quantize) on the qkv matrix's shape: fp16 in.
     wlib = wl
