@@ -36,7 +36,9 @@
  *    W4A16_OK without touching any pointer and without launching.
  *  - Device pointers must be 16-byte aligned. Outputs of a call that
  *    returns an error are unspecified.
- *  - No global state: every entry point is reentrant.
+ *  - No global state but the per-GPU accumulation array of
+ *    w4a16_gemv_splitk_noalloc (calls to that entry point on one GPU must be
+ *    ordered); every other entry point is reentrant.
  */
 #ifndef W4A16_H
 #define W4A16_H
