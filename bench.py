@@ -330,9 +330,10 @@ def check_chain(chain, ys):
         host = [t.cpu().numpy() for t in (o["wq"], o["scales"], o["zeros"])]
         wq_h, sc_h, zp_h = host[0], host[1].view(np.uint8), host[2]
         if o["kind"] == chain.w.CHAIN_SWIGLU:
-            NP = (N + 15) // 16 * 16
-            r2, a2 = orc.gemv_packed(M, 2 * NP, K, wq_h, sc_h, zp_h, x_h)
-            half = lambda a, h: a.reshape(M, NP // 16, 2, 16)[:, :, h, :].reshape(M, NP)[:, :N]
+            # packed rows: per 16-row tile, 8 gate rows then the 8 up rows of the same outputs
+            NT = (N + 7) // 8
+            r2, a2 = orc.gemv_packed(M, 16 * NT, K, wq_h, sc_h, zp_h, x_h)
+            half = lambda a, h: a.reshape(M, NT, 2, 8)[:, :, h, :].reshape(M, 8 * NT)[:, :N]
             ref, bound = oracle.swiglu_bound(half(r2, 0), half(a2, 0), half(r2, 1), half(a2, 1))
             _, r = oracle.swiglu_report(ys[i], ref, bound, orc)
         else:
@@ -436,7 +437,7 @@ def counter_pass(torch, seed):
     import int4_weight_only_w4a16_amd as w
     dev = torch.device("cuda:0")
     for i, (label, M, N, K, kind) in enumerate(COUNTER_SHAPES):
-        rows = 2 * ((N + 15) // 16 * 16) if kind == "swiglu" else N
+        rows = 16 * ((N + 7) // 8) if kind == "swiglu" else N
         wq, sc, zp = synthetic.device_packed_weights(rows, K, seed, 7000 + i, dev)
         x = synthetic.device_activations(M, K, seed, 7000 + i, dev)
         y = torch.empty((M, N), dtype=torch.int16, device=dev)
@@ -501,7 +502,7 @@ def counter_summary(dirs):
     print(" | ".join(cols))
     for m in merged:
         M, N, K = m["M"], m["N"], m["K"]
-        rows = 2 * ((N + 15) // 16 * 16) if m["kind"] == "swiglu" else N
+        rows = 16 * ((N + 7) // 8) if m["kind"] == "swiglu" else N
         alg = algorithmic_bytes(M, rows, K) if m["kind"] != "swiglu" else algorithmic_bytes(M, rows, K) - 2 * M * rows + 2 * M * N
         out = [m["label"], str(m.get("grid", "?")), str(m.get("wg", "?")), f"{alg / 1e6:.2f}"]
         f = m.get("FETCH_SIZE")

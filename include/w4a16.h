@@ -115,13 +115,14 @@ int w4a16_pack(int N, int K, const uint8_t* q, const uint16_t* s, const uint8_t*
 /*
  * Host packer for the fused gate/up + SwiGLU GEMV (w4a16_gemv_swiglu).
  * Gate and up are two F x K matrices in the logical form of w4a16_pack
- * (qg, sg, zg and qu, su, zu). Their 16-row blocks are interleaved -- gate
- * rows 16j .. 16j+15, then the up rows 16j .. 16j+15 -- into one matrix of
- * 2 * roundup(F, 16) rows (rows past F within a block are zero), which is
- * packed as by w4a16_pack. That interleave is what lets SwiGLU run in
- * registers (the 4-bit matrix-vector kernel of the qengine page, "How it
- * works"). Output buffers: w4a16_packed_sizes(2 * roundup(F, 16), K) bytes.
- * Errors: as w4a16_pack, and W4A16_EINVAL when 2 * roundup(F, 16) exceeds
+ * (qg, sg, zg and qu, su, zu). They are interleaved in blocks of 8 rows --
+ * gate rows 8j .. 8j+7, then the up rows 8j .. 8j+7, so that each 16-row
+ * tile of the layout holds both projections of 8 outputs -- into one
+ * matrix of 16 * ceil(F/8) rows (rows past F within a tile are zero),
+ * which is packed as by w4a16_pack. That interleave is what lets SwiGLU run
+ * in registers (the 4-bit matrix-vector kernel of the qengine page, "How it
+ * works"). Output buffers: w4a16_packed_sizes(16 * ceil(F/8), K) bytes.
+ * Errors: as w4a16_pack, and W4A16_EINVAL when 16 * ceil(F/8) exceeds
  * INT32_MAX. Host only; allocates nothing.
  */
 int w4a16_pack_gate_up(int F, int K, const uint8_t* qg, const uint16_t* sg, const uint8_t* zg,
@@ -178,10 +179,11 @@ int w4a16_gemv(int M, int N, int K, const void* Wq, const void* scales, const vo
  * MLP the pages' 7B shapes come from; its placement in registers, right
  * after the gate and up sums, follows the qengine page ("How it works").
  * Saves the separate activation launch and the 2 * M * 2F bytes of the
- * intermediate gate/up output. Deterministic and batch invariant like
- * w4a16_gemv. Each wave's share of K must fit one round of requests: K is
- * at most 5120 for every M (7168 for M <= 2), else W4A16_EUNSUPPORTED.
- * Errors: as w4a16_gemv, plus that one.
+ * intermediate gate/up output. Each tile's gate and up sums are the
+ * plain GEMV's sums of its rows (the same waves and shares as w4a16_gemv
+ * on the packed matrix), so the call is deterministic and batch invariant
+ * like w4a16_gemv and takes any K it takes. Errors: as w4a16_gemv, and
+ * W4A16_EUNSUPPORTED when 16 * ceil(F/8) exceeds INT32_MAX.
  */
 int w4a16_gemv_swiglu(int M, int F, int K, const void* Wq, const void* scales, const void* zeros,
                       const void* x, void* y, void* stream);

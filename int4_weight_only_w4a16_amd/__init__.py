@@ -177,7 +177,7 @@ def w4a16_pack_gate_up(qg, sg, zg, qu, su, zu):
     G = K // GROUP if K % GROUP == 0 else -1
     if qu.shape != (F, K) or any(a.shape != (F, G) for a in (sg, su, zg, zu)):
         raise W4A16Error(W4A16_EINVAL, "w4a16_pack_gate_up")
-    wb, sb, zb = w4a16_packed_sizes(2 * ((F + 15) // 16 * 16), K)
+    wb, sb, zb = w4a16_packed_sizes(16 * ((F + 7) // 8), K)  # 8 gate + 8 up rows per 16-row tile
     wq, sp, zp = np.empty(wb, np.uint8), np.empty(sb, np.uint8), np.empty(zb, np.uint8)
     _check(lib().w4a16_pack_gate_up(F, K, qg.ctypes.data, sg.ctypes.data, zg.ctypes.data, qu.ctypes.data,
                                     su.ctypes.data, zu.ctypes.data, wq.ctypes.data, sp.ctypes.data,

@@ -102,27 +102,6 @@ int choose_splits(int N, int K) {
   return splits > 16 ? 16 : splits;
 }
 
-// Plan of the fused gate/up + SwiGLU launch: one gate/up pair of row tiles
-// per workgroup, H waves on each tile (the fewest powers of two, at most 8,
-// whose shares hold at most 7 tiles), shares of 4, 5 or 7 (5 at most with 16
-// waves, the register rule for every M). Every share is one round, so K is
-// at most 8 * 5 * 128 = 5120; larger K is refused (plan_supported).
-// Depends on K only, so rows are batch invariant as in plan_for.
-w4a16::LaunchPlan plan_swiglu(int K) {
-  const int groups = K / W4A16_GROUP;
-  int half = 1;
-  while (half < 8 && (groups + half - 1) / half > 7) half *= 2;
-  const int per = (groups + half - 1) / half;
-  w4a16::LaunchPlan plan;
-  plan.engine = w4a16::kEngineMfma;
-  plan.splits = 1;
-  plan.tiles_per_wg = 1;
-  plan.epilogue = w4a16::kEpiSwiglu;
-  plan.waves = 2 * half;
-  plan.share = per <= 4 ? 4 : (per <= 5 ? 5 : 7);
-  return plan;
-}
-
 // Split count for w4a16_gemm_splitk, measured on MI355X (7B-shaped
 // matrices, M = 1 .. 2048). Each split adds a pass of 64-bit atomics over
 // its output tile, whose cost grows with the tile's rows, against
@@ -233,7 +212,12 @@ extern "C" int w4a16_gemv_swiglu(int M, int F, int K, const void* Wq, const void
   const int rc = check_shape(M, F, K);
   if (rc != W4A16_OK) return rc == 1 ? W4A16_OK : rc;
   if (!pointers_ok({Wq, scales, zeros, x, y})) return W4A16_EINVAL;
-  const w4a16::LaunchPlan plan = plan_swiglu(K);
+  // The plain GEMV's plan for the packed matrix (ceil(F/8) row tiles of 16
+  // rows): the same waves and shares, so rows stay batch invariant, and any
+  // K the GEMV takes.
+  if ((int64_t(F) + 7) / 8 * 16 > INT32_MAX) return W4A16_EUNSUPPORTED;
+  w4a16::LaunchPlan plan = plan_for(M, 16 * ((F + 7) / 8), K, 1);
+  plan.epilogue = w4a16::kEpiSwiglu;
   if (!w4a16::plan_supported(M, K, plan)) return W4A16_EUNSUPPORTED;
   if (w4a16::launch_gemv(M, F, K, plan, Wq, scales, zeros, x, y, nullptr, stream) != 0) return W4A16_EHIP;
   return W4A16_OK;

@@ -47,8 +47,8 @@
 // runs out sets the workspace error word and every workgroup leaves.
 //
 // The arithmetic of an item is that of the standalone kernels with the same
-// waves and shares (w4a16_gemv: 4 waves per tile at 28 groups; SwiGLU: 4 +
-// 4 waves; w4a16_gemv_splitk: 8 waves of the split's range), so each output
+// waves and shares (w4a16_gemv and w4a16_gemv_swiglu: 4 waves per tile at
+// 28 groups; w4a16_gemv_splitk: 8 waves of the split's range), so each output
 // equals theirs bit for bit where the plans coincide.
 #include <hip/hip_runtime.h>
 
@@ -97,7 +97,7 @@ struct alignas(16) OpDev {
   uint64_t xt_off;       // workspace offset of the producer's tagged output (x_src >= 0)
   uint64_t acc_off;      // workspace offset of the split-K words [M][N] (splits > 1)
   int32_t N, K, G, kind;
-  int32_t splits, tp, wpt, row_tiles;       // tiles per item, waves per tile, output row tiles
+  int32_t splits, tp, wpt, row_tiles;       // tiles per item, waves per tile, matrix row tiles
   int32_t per_split, items, item_begin, x_shift;
   int32_t x_stride;   // producer's N: row stride of its tagged output, in words
   int32_t sentinel;   // word of the producer's tagged output polled before staging
@@ -256,13 +256,8 @@ struct Share {
 __device__ __forceinline__ Share share_of(const Walk& w, int wave) {
   const int sh = w.wpt_log2();
   const int lt = wave >> sh, wi = wave & ((1 << sh) - 1);
-  int64_t tile;
-  if (w.kind() == W4A16_CHAIN_SWIGLU) {
-    tile = 2 * int64_t(w.tg) + lt;  // gate tile 2 tg, up tile 2 tg + 1
-  } else {
-    tile = int64_t(w.tg) * w.tp() + lt;
-    if (tile >= w.row_tiles) tile = w.row_tiles - 1;  // a pair's missing second tile: valid, never stored
-  }
+  int64_t tile = int64_t(w.tg) * w.tp() + lt;
+  if (tile >= w.row_tiles) tile = w.row_tiles - 1;  // a pair's missing second tile: valid, never stored
   const int ng = w.g_end - w.g_beg;
   const int beg = w.g_beg + ((wi * ng) >> sh) + w.rd * kShare;
   const int end = w.g_beg + (((wi + 1) * ng) >> sh);
@@ -490,23 +485,27 @@ __global__ __launch_bounds__(kThreads, 4) void chain_kernel(const Header* __rest
     const float* pb = part + size_t(slot) * kWaves * GG::kRedWave;
     W4A16_GLOBAL uint32_t* yt = gptr<uint32_t>(wsa + d.yt_off);
     W4A16_GLOBAL uint16_t* yd = gptr<uint16_t>(d.y);
+    // A GEMV tile has 16 outputs per activation row; a SwiGLU tile 8, the
+    // gate sums of its rows 0-7 and the up sums of rows 8-15.
     const bool pair = d.kind == W4A16_CHAIN_SWIGLU;
-    const int tiles_out = pair ? 1 : d.tp;
-    const int n_out = tiles_out * MR * 16;
+    const int per_tile = pair ? MR * 8 : MR * 16;
+    const int n_out = d.tp * per_tile;
     for (int idx = lane; idx < ((n_out + 63) & ~63); idx += 64) {
       const int id = idx < n_out ? idx : n_out - 1;
-      const int lt = id / (MR * 16), rem = id - lt * MR * 16, m = rem >> 4, r = rem & 15;
+      const int lt = id / per_tile, rem = id - lt * per_tile;
+      const int m = pair ? rem >> 3 : rem >> 4, r = pair ? rem & 7 : rem & 15;
       const int sl = ((m >> 2) * GG::kRows + (m & 3)) * 16 + r;
-      const int w0 = pair ? 0 : lt * d.wpt;
+      const int w0 = lt * d.wpt;
       float sum = pb[w0 * GG::kRedWave + sl];
-      for (int w2 = 1; w2 < (pair ? 4 : d.wpt); ++w2) sum += pb[(w0 + w2) * GG::kRedWave + sl];
+      for (int w2 = 1; w2 < d.wpt; ++w2) sum += pb[(w0 + w2) * GG::kRedWave + sl];
       if (pair) {
-        float up = pb[4 * GG::kRedWave + sl];
-        for (int w2 = 5; w2 < 8; ++w2) up += pb[w2 * GG::kRedWave + sl];
-        sum = sum / (1.f + expf(-sum)) * up;  // silu(gate) * up
+        float up = pb[w0 * GG::kRedWave + sl + 8];
+        for (int w2 = 1; w2 < d.wpt; ++w2) up += pb[(w0 + w2) * GG::kRedWave + sl + 8];
+        sum = sum / (1.f + expf(-sum)) * up;  // silu(gate) * up, rounded to fp32 (as in w4a16_gemv_swiglu)
+        asm volatile("" : "+v"(sum));
       }
-      const int64_t t = pair ? tg : int64_t(tg) * d.tp + lt;
-      const int64_t n = t * kTileRows + r;
+      const int64_t t = int64_t(tg) * d.tp + lt;
+      const int64_t n = t * (pair ? 8 : kTileRows) + r;
       if (idx < n_out && t < d.row_tiles && n < d.N) {
         const int64_t oi = int64_t(m) * d.N + n;
         bool write = true;
@@ -696,16 +695,13 @@ bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15
 // plan), else 8 waves per tile (one tile per item), each taking its share
 // in rounds of at most 7 tiles. (8 waves per tile for the narrow GEMVs of a
 // 7B step -- shorter shares, more items -- measured slower: 1329 against
-// 1246 us per step.) A SwiGLU item is a gate tile and its up tile, 4 waves
-// each.
-void chain_geometry(int kind, int G, int splits, int* wpt, int* tp, int* rounds) {
+// 1246 us per step.) A SwiGLU matrix (gate rows 0-7 and up rows 8-15 of
+// each tile, 8 outputs per tile) takes the same geometry.
+void chain_geometry(int G, int splits, int* wpt, int* tp, int* rounds) {
   constexpr int share = w4a16::chain::kShare;
   const int range = (G + splits - 1) / splits;
   const int cap4 = splits > 1 ? 5 : share;
-  if (kind == W4A16_CHAIN_SWIGLU) {
-    *wpt = 4, *tp = 1;
-    *rounds = ((range + 3) / 4 + share - 1) / share;
-  } else if ((range + 3) / 4 <= cap4) {
+  if ((range + 3) / 4 <= cap4) {
     *wpt = 4, *tp = 2, *rounds = 1;
   } else {
     *wpt = 8, *tp = 1;
@@ -736,9 +732,9 @@ extern "C" int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, voi
     if (o.x_src < -1 || o.x_src >= j) return W4A16_EINVAL;
     if (o.x_src < 0 && !aligned16(o.x)) return W4A16_EINVAL;
     if (o.x_src >= 0 && (ops[o.x_src].N < o.K || o.x_shift < 0 || o.x_shift > 24)) return W4A16_EINVAL;
-    const int64_t row_tiles = (int64_t(o.N) + 15) / 16;
+    const int64_t row_tiles = o.kind == W4A16_CHAIN_SWIGLU ? (int64_t(o.N) + 7) / 8 : (int64_t(o.N) + 15) / 16;
     int wpt, tp, rounds;
-    chain_geometry(o.kind, G, o.splits, &wpt, &tp, &rounds);
+    chain_geometry(G, o.splits, &wpt, &tp, &rounds);
     const int64_t items = (row_tiles + tp - 1) / tp * o.splits;
     total += items;
     if (total >= (int64_t(1) << 30) || row_tiles >= (int64_t(1) << 26)) return W4A16_EUNSUPPORTED;
@@ -780,8 +776,8 @@ extern "C" int w4a16_chain_plan(int M, int n_ops, const w4a16_chain_op* ops, voi
     e.G = o.K / W4A16_GROUP;
     e.kind = o.kind;
     e.splits = o.splits;
-    e.row_tiles = int32_t((int64_t(o.N) + 15) / 16);
-    chain_geometry(o.kind, e.G, o.splits, &e.wpt, &e.tp, &e.rounds);
+    e.row_tiles = int32_t(o.kind == W4A16_CHAIN_SWIGLU ? (int64_t(o.N) + 7) / 8 : (int64_t(o.N) + 15) / 16);
+    chain_geometry(e.G, o.splits, &e.wpt, &e.tp, &e.rounds);
     e.per_split = (e.row_tiles + e.tp - 1) / e.tp;
     e.items = e.per_split * o.splits;
     e.item_begin = begin;

@@ -23,17 +23,13 @@ namespace dev {
 // and requests the next row tile's round before computing the current one).
 // The waves' partial sums meet in LDS (double-buffered across row tiles, one
 // barrier per row tile) and are added in wave order.
-// EPI == kEpiSwiglu: the matrix's row tiles alternate gate (2j) and up
-// (2j+1) rows of the same 16 outputs. Workgroup j runs both tiles at once:
-// waves [0, WAVES/2) split the K range of the gate tile, the other half the
-// same K range of the up tile (R = 1), and the sums meet in LDS, where
-// y[m][16j + i] = fp16(silu(g) * u), silu(g) = g / (1 + e^-g) in fp32. N is
-// the output width (the matrix has 2 * ceil(N/16) row tiles). Every wave
-// stages its own x slice when all slices fit in 64 KiB; otherwise wave w of
-// the gate half stages the slice that wave w of the up half also reads (one
-// LDS barrier after staging). Every share fits one round: the host launches
-// nothing else, and a workgroup exits at once (all of it) if the shape
-// would need more.
+// EPI == kEpiSwiglu: row tile j of the matrix holds the gate rows of
+// outputs 8j .. 8j+7 in its rows 0-7 and their up rows in rows 8-15, so a
+// workgroup runs exactly the plain GEMV's waves and shares, and its
+// cross-wave sum holds both projections of 8 outputs: y[m][8j + i] =
+// fp16(silu(g) * u) with g the sum of row i, u that of row i + 8 and
+// silu(g) = g / (1 + e^-g) in fp32. N is the output width (the matrix has
+// ceil(N/8) row tiles); never with split K.
 // Writes fp16 y[MR][N] directly when `acc` is null. Otherwise (split-K,
 // gridDim.y splits) each workgroup adds its fp32 partial sums, in the
 // fixed-point word format of splitk_addend(), to acc[MR][N] (one uint64 per
@@ -66,13 +62,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   float* red = reinterpret_cast<float*>(smem);           // [2][WAVES][4][kRows][16]
 
   const int G = K / kGroup;
-  constexpr bool kPair = EPI == kEpiSwiglu;
-  static_assert(!kPair || (R == 1 && WAVES % 2 == 0), "SwiGLU: one gate/up pair, half the waves on each");
-  constexpr int kHalf = kPair ? WAVES / 2 : WAVES;  // waves sharing one row tile's K range
-  // SwiGLU halves read one shared x slice per wave pair (staged by the gate
-  // wave, behind an LDS barrier) only when private slices would not fit.
-  constexpr bool kSharedX = kPair && !swiglu_private_x(MR, WAVES, SHARE);
-  const int64_t row_tiles = (kPair ? 2 : 1) * ((int64_t(N) + kTileRows - 1) / kTileRows);
+  constexpr bool kRows8 = EPI == kEpiSwiglu;  // 8 outputs per row tile: gate rows 0-7, up rows 8-15
+  const int64_t row_tiles = kRows8 ? (int64_t(N) + 7) / 8 : (int64_t(N) + kTileRows - 1) / kTileRows;
   const int split = blockIdx.y;  // splits == gridDim.y, passed as an argument
   // The split's groups. No division for the usual unsplit launch; else a
   // 32-bit one (split * G < 31 * 2^24): the 64-bit division compiled to
@@ -82,21 +73,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   const int ng = g_end - g_beg;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps share bounds scalar
-  const int half = kPair ? wave / kHalf : 0;                   // SwiGLU: 0 gate, 1 up
-  const int wave_in = kPair ? wave - half * kHalf : wave;      // index among the tile's waves
   const int piece = lane >> 4;  // which 8-column piece of each 32 columns
   const int rlane = lane & 15;  // weight row within the tile
   const uint32_t magic = kMagic1024;
-  if constexpr (kPair) {
-    // Workgroup-uniform (K and the grid only): the single-round layout the
-    // shared x slices and the one staging barrier rely on.
-    if (splits != 1 || ng < kHalf || (ng + kHalf - 1) / kHalf > SHARE) return;
-  }
-  const int share_beg = g_beg + (wave_in * ng) / kHalf;
-  const int share_end = g_beg + ((wave_in + 1) * ng) / kHalf;
+  const int share_beg = g_beg + (wave * ng) / WAVES;
+  const int share_end = g_beg + ((wave + 1) * ng) / WAVES;
   const int mm = rlane < MR ? rlane : MR - 1;  // activation row feeding A-operand row rlane
   _Float16* xw = reinterpret_cast<_Float16*>(smem + 2 * kRed * sizeof(float)) +
-                 (kGlobalX ? 0 : (kSharedX ? wave_in : wave) * MR * kXRow);  // x slice [MR][kXRow]
+                 (kGlobalX ? 0 : wave * MR * kXRow);  // x slice [MR][kXRow]
   int parity = 0;
 
   // Copy x[:, 128*g0 : 128*(g0+n)) into this wave's LDS slice (synchronous).
@@ -218,18 +202,33 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < kOut; ++j) {
+      if constexpr (kRows8) {
+        // Output (m, i) of the tile: gate row i, up row i + 8.
+        const int idx = min(tid + j * WAVES * 64, MR * 8 - 1);
+        const int m = idx >> 3, i = idx & 7;
+        const int slot = ((m >> 2) * kRows + (m & 3)) * 16 + i;
+        float g = rb[slot], u = rb[slot + 8];
+#pragma unroll
+        for (int w2 = 1; w2 < WAVES; ++w2) {
+          g += rb[w2 * kRedWave + slot];
+          u += rb[w2 * kRedWave + slot + 8];
+        }
+        // silu(gate) * up, rounded to fp32 before the fp16 store rounds it
+        // again: held in a register, the product cannot be fused into the
+        // store's conversion (a single-rounding v_fma_mix, which the compiler
+        // picks for some code shapes only), so every kernel computing this
+        // epilogue rounds the same way.
+        float su = g / (1.f + expf(-g)) * u;
+        asm volatile("" : "+v"(su));
+        out[j] = su;
+        continue;
+      }
       const int idx = min(tid + j * WAVES * 64, MR * 16 - 1);  // one wave has fewer lanes than 8 x 16 outputs
       const int m = idx >> 4, i = idx & 15;
       const int slot = ((m >> 2) * kRows + (m & 3)) * 16 + i;
       float sum = rb[slot];
 #pragma unroll
-      for (int w2 = 1; w2 < kHalf; ++w2) sum += rb[w2 * kRedWave + slot];
-      if constexpr (kPair) {
-        float up = rb[kHalf * kRedWave + slot];
-#pragma unroll
-        for (int w2 = kHalf + 1; w2 < WAVES; ++w2) up += rb[w2 * kRedWave + slot];
-        sum = sum / (1.f + expf(-sum)) * up;  // silu(gate) * up
-      }
+      for (int w2 = 1; w2 < WAVES; ++w2) sum += rb[w2 * kRedWave + slot];
       out[j] = sum;
     }
     parity ^= 1;
@@ -237,6 +236,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   auto store_tile = [&](int64_t t, const float (&out)[kOut]) {
 #pragma unroll
     for (int j = 0; j < kOut; ++j) {
+      if constexpr (kRows8) {
+        const int idx = tid + j * WAVES * 64;
+        const int m = idx >> 3, i = idx & 7;
+        const int64_t nn = t * 8 + i;
+        if (idx < MR * 8 && nn < N) y[int64_t(m) * N + nn] = (_Float16)out[j];
+        continue;
+      }
       const int idx = tid + j * WAVES * 64;
       const int m = idx >> 4, i = idx & 15;
       const int64_t nn = t * kTileRows + i;
@@ -256,13 +262,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
   };
 
   // This workgroup's row tiles: t0 + r * gridDim.x for r < R (the host
-  // launches ceil(row tiles / R) workgroups, so t0 is in range); for SwiGLU
-  // the wave's half of the pair 2 t0, 2 t0 + 1, while the outputs are tile
-  // t0 of y. Tiles past the end are computed on a clamped (valid) tile and
-  // never stored.
+  // launches ceil(row tiles / R) workgroups, so t0 is in range). Tiles past
+  // the end are computed on a clamped (valid) tile and never stored.
   const int64_t t0 = blockIdx.x;
-  auto tile_of = [&](int r) { return kPair ? 2 * t0 + half : t0 + int64_t(r) * gridDim.x; };
-  auto out_tile_of = [&](int r) { return kPair ? t0 : tile_of(r); };
+  auto tile_of = [&](int r) { return t0 + int64_t(r) * gridDim.x; };
   auto clamp_tile = [&](int64_t t) { return t < row_tiles ? t : row_tiles - 1; };
   float sums[R][kOut];
 
@@ -288,39 +291,30 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
         constexpr int kRowChunks = SHARE * (kGroup / 8);
         constexpr int kXSteps = (MR * kRowChunks + 63) / 64;
         const int xlast = share_n * (kGroup / 8) - 1;
-        const bool stages_x = !kSharedX || half == 0;  // wave-uniform
         auto chunk = [&](int j, int& m, int& cc) {  // clamped: unconditional, in bounds
           const int c = min(lane + 64 * j, MR * kRowChunks - 1);
           m = MR == 1 ? 0 : c / kRowChunks;
           cc = min(c - m * kRowChunks, xlast);
         };
         u32x4 xv[kXSteps];
-        if (stages_x) {
 #pragma unroll
-          for (int j = 0; j < kXSteps; ++j) {
-            int m, cc;
-            chunk(j, m, cc);
-            xv[j] = *reinterpret_cast<const u32x4*>(x + int64_t(m) * K + int64_t(share_beg) * kGroup + cc * 8);
-          }
+        for (int j = 0; j < kXSteps; ++j) {
+          int m, cc;
+          chunk(j, m, cc);
+          xv[j] = *reinterpret_cast<const u32x4*>(x + int64_t(m) * K + int64_t(share_beg) * kGroup + cc * 8);
         }
         __builtin_amdgcn_sched_barrier(0);
         load_round(rr[0], p.wlane, p.sword, p.zword, share_beg, share_n);
         __builtin_amdgcn_sched_barrier(0);
-        if (stages_x) {
 #pragma unroll
-          for (int j = 0; j < kXSteps; ++j) {  // clamped chunks rewrite a chunk with its own data
-            int m, cc;
-            chunk(j, m, cc);
-            *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) = xv[j];
-          }
+        for (int j = 0; j < kXSteps; ++j) {  // clamped chunks rewrite a chunk with its own data
+          int m, cc;
+          chunk(j, m, cc);
+          *reinterpret_cast<u32x4*>(xw + m * kXRow + cc * 8) = xv[j];
         }
-        if constexpr (kSharedX) {
-          lds_barrier();  // the up half reads what the gate half staged; weights stay in flight
-        } else {
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
       } else {
         load_round(rr[0], p.wlane, p.sword, p.zword, share_beg, share_n);
       }
@@ -337,10 +331,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
       compute_round(rr[r & 1], share_beg, share_n, acc);
       reduce_tile(acc, sums[r]);
     }
-  } else if constexpr (!kPair) {
+  } else {
     // Long K (several rounds per share, x restaged per round) or an empty
-    // share (a K range with fewer groups than waves): plain loop. (Never for
-    // SwiGLU, whose shapes were checked above.)
+    // share (a K range with fewer groups than waves): plain loop.
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const TilePtrs p = tile_ptrs(clamp_tile(tile_of(r)));
@@ -357,9 +350,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
       reduce_tile(acc, sums[r]);
     }
   }
-  if (!acc) {
+  if (!acc || kRows8) {  // (the host never pairs kEpiSwiglu with split K)
 #pragma unroll
-    for (int r = 0; r < R; ++r) store_tile(out_tile_of(r), sums[r]);
+    for (int r = 0; r < R; ++r) store_tile(tile_of(r), sums[r]);
     return;
   }
   // Split-K: one relaxed device-scope atomic add per output and row tile.
@@ -394,7 +387,8 @@ constexpr size_t lds_for() {
 template <int MR, int WAVES, int SHARE, int ENGINE, int R, int EPI>
 hipError_t launch_typed(int N, int K, const LaunchPlan& plan, const void* wq, const void* scales,
                         const void* zeros, const void* x, void* y, unsigned long long* acc, hipStream_t stream) {
-  const int64_t row_tiles = (int64_t(N) + kTileRows - 1) / kTileRows;  // output tiles for SwiGLU
+  const int64_t row_tiles = EPI == kEpiSwiglu ? (int64_t(N) + 7) / 8  // 8 outputs per tile
+                                                  : (int64_t(N) + kTileRows - 1) / kTileRows;
   const int64_t grid = (row_tiles + R - 1) / R;
   constexpr size_t lds = lds_for<MR, WAVES, SHARE, ENGINE, EPI>();
   if constexpr (lds > kDefaultLdsLimit) {
@@ -417,14 +411,13 @@ hipError_t launch_shape(int N, int K, const LaunchPlan& plan, const void* wq, co
     if (plan.waves == W && plan.share == S && plan.tiles_per_wg == RR && plan.epilogue == EP)              \
       return launch_typed<MR, W, S, ENGINE, RR, EP>(N, K, plan, wq, scales, zeros, x, y, acc, stream); \
   }
-#define W4A16_SHARES(W, RR)                                                                             \
-  W4A16_CASE(W, 2, RR, kEpiStore) W4A16_CASE(W, 3, RR, kEpiStore) W4A16_CASE(W, 4, RR, kEpiStore)        \
-  W4A16_CASE(W, 5, RR, kEpiStore) W4A16_CASE(W, 7, RR, kEpiStore) W4A16_CASE(W, 8, RR, kEpiStore)        \
-  W4A16_CASE(W, 10, RR, kEpiStore)
-  W4A16_SHARES(1, 1) W4A16_SHARES(2, 1) W4A16_SHARES(4, 1) W4A16_SHARES(8, 1) W4A16_SHARES(16, 1)
-#define W4A16_PAIR(W) W4A16_CASE(W, 4, 1, kEpiSwiglu) W4A16_CASE(W, 5, 1, kEpiSwiglu) W4A16_CASE(W, 7, 1, kEpiSwiglu)
-  W4A16_PAIR(2) W4A16_PAIR(4) W4A16_PAIR(8) W4A16_PAIR(16)
-#undef W4A16_PAIR
+#define W4A16_SHARES(W, EP)                                                                             \
+  W4A16_CASE(W, 2, 1, EP) W4A16_CASE(W, 3, 1, EP) W4A16_CASE(W, 4, 1, EP) W4A16_CASE(W, 5, 1, EP)        \
+  W4A16_CASE(W, 7, 1, EP) W4A16_CASE(W, 8, 1, EP) W4A16_CASE(W, 10, 1, EP)
+#define W4A16_WAVES(EP) \
+  W4A16_SHARES(1, EP) W4A16_SHARES(2, EP) W4A16_SHARES(4, EP) W4A16_SHARES(8, EP) W4A16_SHARES(16, EP)
+  W4A16_WAVES(kEpiStore) W4A16_WAVES(kEpiSwiglu)
+#undef W4A16_WAVES
 #undef W4A16_SHARES
 #undef W4A16_CASE
   return hipErrorInvalidValue;

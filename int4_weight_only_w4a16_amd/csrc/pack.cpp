@@ -139,19 +139,20 @@ extern "C" int w4a16_pack_gate_up(int F, int K, const uint8_t* qg, const uint16_
   if (!shape_ok(F, K)) return W4A16_EINVAL;
   if (F == 0) return W4A16_OK;
   if (!qg || !sg || !zg || !qu || !su || !zu || !wq_out || !s_out || !z_out) return W4A16_EINVAL;
-  // 16-row blocks interleaved: packed rows 32j .. 32j+15 are gate rows
-  // 16j .. 16j+15, the next 16 the up rows of the same outputs; rows past
-  // F within a block are zero. The result has 2 * roundup(F, 16) rows,
-  // which w4a16_packed_sizes must be able to describe.
-  const int64_t G = K / W4A16_GROUP, rows = 32 * ((int64_t(F) + 15) / 16);
+  // 8-row blocks interleaved inside each 16-row tile: packed rows
+  // 16j .. 16j+7 are gate rows 8j .. 8j+7, packed rows 16j+8 .. 16j+15 the
+  // up rows of the same outputs; rows past F within a tile are zero. The
+  // result has 16 * ceil(F/8) rows, which w4a16_packed_sizes must be able
+  // to describe.
+  const int64_t G = K / W4A16_GROUP, rows = 16 * ((int64_t(F) + 7) / 8);
   if (rows > INT32_MAX) return W4A16_EINVAL;
   return pack_rows(
       rows, K,
       [&](int64_t r) {
-        const int64_t f = 16 * (r / 32) + r % 16;
+        const int64_t f = 8 * (r / 16) + r % 8;
         if (f >= F) return RowData{nullptr, nullptr, nullptr};
-        return (r % 32) < 16 ? RowData{qg + f * K, sg + f * G, zg + f * G}
-                             : RowData{qu + f * K, su + f * G, zu + f * G};
+        return (r % 16) < 8 ? RowData{qg + f * K, sg + f * G, zg + f * G}
+                            : RowData{qu + f * K, su + f * G, zu + f * G};
       },
       wq_out, s_out, z_out);
 }

@@ -38,7 +38,7 @@ enum Engine : int {
 // What the GEMV kernel does with its sums.
 enum Epilogue : int {
   kEpiStore = 0,   // y = fp16(sum) (or the split-K atomic accumulation)
-  kEpiSwiglu = 1,  // row tiles 2j (gate) and 2j+1 (up), half the waves each -> y = fp16(silu(gate) * up)
+  kEpiSwiglu = 1,  // row tile j: rows 0-7 gate, 8-15 up of outputs 8j..8j+7 -> y = fp16(silu(gate) * up)
 };
 
 // Launch parameters chosen by the front end for one GEMV shape.
@@ -48,20 +48,16 @@ struct LaunchPlan {
   int share;   // tiles a wave requests at once (2 .. 10); longer shares take several rounds
   int splits;  // K ranges (gridDim.y); 1 for the plain GEMV
   int tiles_per_wg;  // row tiles per workgroup: 1 (gridDim.x = row tiles)
-  int epilogue;      // Epilogue (kEpiSwiglu: tiles_per_wg 1, waves = 2 x the waves per row tile)
+  int epilogue;      // Epilogue (kEpiSwiglu: splits 1)
 };
 
 // Instantiated (waves, share) per engine and M: those that fit in registers
-// without spilling, one row tile per workgroup. The SwiGLU epilogue: MFMA,
-// one gate/up pair per workgroup (2, 4, 8 or 16 waves in two halves),
-// shares of 4, 5 or 7, within the register rule of the plain kernel of as
-// many waves. (Several row tiles per workgroup and a VALU dot2 engine were
+// without spilling, one row tile per workgroup; the SwiGLU epilogue for the
+// same set. (Several row tiles per workgroup and a VALU dot2 engine were
 // measured and dropped: the plans never chose them.)
 constexpr bool instantiated(int mr, int waves, int share, int engine, int r, int epi = kEpiStore) {
   if (r != 1) return false;
-  if (epi == kEpiSwiglu)
-    return engine == kEngineMfma && (waves == 2 || waves == 4 || waves == 8 || waves == 16) &&
-           (share == 4 || share == 5 || share == 7) && instantiated(mr, waves, share, engine, 1);
+  if (epi != kEpiStore && epi != kEpiSwiglu) return false;
   if (engine == kEngineMfmaGlobalX) return waves == 16 ? share <= 3 : share <= 4;
   if (engine != kEngineMfma) return false;
   if (waves == 16) return mr <= 2 ? share <= 10 : share <= 5;
@@ -75,9 +71,6 @@ constexpr size_t reduction_lds_bytes(int mr, int waves, int engine) {
   return 2 * size_t(waves) * 4 * (mr < 4 ? mr : 4) * 16 * sizeof(float);
 }
 
-// SwiGLU: every wave stages its own x slice when all the slices fit in
-// 64 KiB; otherwise wave w of the gate half stages the slice that wave w of
-// the up half also reads, behind one LDS barrier.
 // Halves per row of a wave's staged x slice: share * 128, plus 32 when
 // there are several rows. An MFMA A-operand read takes rows 0 .. M-1 at
 // four 16-byte column pieces; at an unpadded stride (a multiple of 256
@@ -87,19 +80,12 @@ constexpr size_t reduction_lds_bytes(int mr, int waves, int engine) {
 // two passes anyway). One row is a broadcast and needs no padding.
 constexpr int gemv_x_row(int mr, int share) { return share * kGroup + (mr > 1 ? 32 : 0); }
 
-constexpr bool swiglu_private_x(int mr, int waves, int share) {
-  return size_t(waves) * mr * gemv_x_row(mr, share) * 2 <= 64 * 1024;
-}
-
 // Dynamic LDS of a GEMV workgroup: the reduction buffers, then one x slice
-// [M][gemv_x_row] fp16 per wave (per pair of waves for SwiGLU when the
-// halves share slices; none when x is read from global memory).
+// [M][gemv_x_row] fp16 per wave (none when x is read from global memory).
 constexpr size_t gemv_lds_bytes(int mr, int waves, int share, int engine, int epi) {
+  (void)epi;
   return reduction_lds_bytes(mr, waves, engine) +
-         (engine == kEngineMfmaGlobalX
-              ? 0
-              : size_t(epi == kEpiSwiglu && !swiglu_private_x(mr, waves, share) ? waves / 2 : waves) * mr *
-                    gemv_x_row(mr, share) * 2);
+         (engine == kEngineMfmaGlobalX ? 0 : size_t(waves) * mr * gemv_x_row(mr, share) * 2);
 }
 
 // Largest dynamic LDS a GEMV workgroup may use: gfx950's 160 KiB per

@@ -114,12 +114,7 @@ bool plan_supported(int M, int K, const LaunchPlan& plan) {
   const int w = plan.waves, sh = plan.share;
   if (!(w == 1 || w == 2 || w == 4 || w == 8 || w == 16)) return false;
   if (!(sh == 2 || sh == 3 || sh == 4 || sh == 5 || sh == 7 || sh == 8 || sh == 10)) return false;
-  if (plan.epilogue == kEpiSwiglu) {
-    // One round per wave, every wave with at least one group (the kernel
-    // relies on it for its one staging barrier).
-    const int groups = K / kGroup, half = plan.waves / 2;
-    if (plan.splits != 1 || groups < half || (groups + half - 1) / half > plan.share) return false;
-  }
+  if (plan.epilogue == kEpiSwiglu && plan.splits != 1) return false;
   if (!instantiated(M, w, sh, plan.engine, plan.tiles_per_wg, plan.epilogue)) return false;
   return lds_bytes(M, K, plan) <= kMaxLdsBytes;
 }

@@ -76,24 +76,25 @@ def test_pack_edge_patterns(orc):
             assert np.array_equal(a, b)
 
 
-def _interleave_16(a_gate, a_up, fill=0):
-    """Row blocks of 16: gate block j, then up block j (rows past F zero)."""
+def _interleave_8(a_gate, a_up, fill=0):
+    """16-row tiles of 8 gate rows and the 8 up rows of the same outputs
+    (rows past F zero): tile j holds gate 8j .. 8j+7, then up 8j .. 8j+7."""
     F = a_gate.shape[0]
-    blocks = (F + 15) // 16
-    out = np.full((32 * blocks,) + a_gate.shape[1:], fill, a_gate.dtype)
+    tiles = (F + 7) // 8
+    out = np.full((16 * tiles,) + a_gate.shape[1:], fill, a_gate.dtype)
     for f in range(F):
-        out[32 * (f // 16) + f % 16] = a_gate[f]
-        out[32 * (f // 16) + f % 16 + 16] = a_up[f]
+        out[16 * (f // 8) + f % 8] = a_gate[f]
+        out[16 * (f // 8) + f % 8 + 8] = a_up[f]
     return out
 
 
-@pytest.mark.parametrize("F,K", [(1, 128), (16, 256), (40, 896), (77, 640)])
-def test_pack_gate_up_is_the_16_row_interleave(orc, F, K):
-    """w4a16_pack_gate_up == the oracle's packing of the 16-row interleave."""
+@pytest.mark.parametrize("F,K", [(1, 128), (8, 256), (16, 256), (40, 896), (77, 640)])
+def test_pack_gate_up_is_the_8_row_interleave(orc, F, K):
+    """w4a16_pack_gate_up == the oracle's packing of the 8-row interleave."""
     qg, sg, zg = synthetic.weights(F, K, seed=F, tensor_id=1)
     qu, su, zu = synthetic.weights(F, K, seed=F, tensor_id=2)
     mine = w.w4a16_pack_gate_up(qg, sg, zg, qu, su, zu)
-    ref = orc.pack(_interleave_16(qg, qu), _interleave_16(sg, su), _interleave_16(zg, zu))
+    ref = orc.pack(_interleave_8(qg, qu), _interleave_8(sg, su), _interleave_8(zg, zu))
     for a, b in zip(mine, ref):
         assert np.array_equal(a, b)
     L = w.lib()

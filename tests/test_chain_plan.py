@@ -44,7 +44,7 @@ def make_ops(M, spec):
     fake = Fake()
     ops = []
     for kind, N, K, splits, x_src, x_shift in spec:
-        rows = 2 * ((N + 15) // 16 * 16) if kind == w.CHAIN_SWIGLU else N
+        rows = 16 * ((N + 7) // 8) if kind == w.CHAIN_SWIGLU else N
         wb, sb, zb = w.w4a16_packed_sizes(rows, K)
         ops.append(dict(kind=kind, N=N, K=K, splits=splits, x_src=x_src, x_shift=x_shift,
                         wq=fake.alloc(wb), scales=fake.alloc(sb), zeros=fake.alloc(zb),
@@ -63,10 +63,7 @@ def share_of(d, i, wave, rd=0):
     per_split = int(d["per_split"])
     split, tg = i // per_split, i % per_split
     lt, wi = wave // int(d["wpt"]), wave % int(d["wpt"])
-    if d["kind"] == w.CHAIN_SWIGLU:
-        tile = 2 * tg + lt
-    else:
-        tile = min(tg * int(d["tp"]) + lt, int(d["row_tiles"]) - 1)
+    tile = min(tg * int(d["tp"]) + lt, int(d["row_tiles"]) - 1)
     G, S, wpt = int(d["G"]), int(d["splits"]), int(d["wpt"])
     g_beg = 0 if S == 1 else split * G // S
     g_end = G if S == 1 else (split + 1) * G // S
@@ -85,13 +82,14 @@ def walk(plan, ops, sizes, M):
     ws_bytes = int(h["ws_bytes"])
     lanes = np.arange(LANES)
     rlane = lanes & 15
-    covered = [np.zeros((int(e["row_tiles"]) * (2 if e["kind"] == w.CHAIN_SWIGLU else 1), int(e["G"])), np.int32)
-               for e in d]
+    covered = [np.zeros((int(e["row_tiles"]), int(e["G"])), np.int32) for e in d]
     written = [np.zeros((M, int(e["N"])), np.int32) for e in d]
     for j, e in enumerate(d):
         o = ops[j]
         G, N = int(e["G"]), int(e["N"])
-        matrix_rows = 2 * ((N + 15) // 16 * 16) if e["kind"] == w.CHAIN_SWIGLU else N
+        # a SwiGLU matrix: 8 outputs per 16-row tile (gate rows 0-7, up rows 8-15)
+        matrix_rows = 16 * ((N + 7) // 8) if e["kind"] == w.CHAIN_SWIGLU else N
+        assert int(e["row_tiles"]) == (matrix_rows + 15) // 16
         wb, sb, zb = w.w4a16_packed_sizes(matrix_rows, int(e["K"]))
         assert sizes[int(e["wq"])] == wb and sizes[int(e["sw"])] == sb and sizes[int(e["zw"])] == zb
         if e["x_src"] >= 0:
@@ -125,7 +123,7 @@ def walk(plan, ops, sizes, M):
                     continue
                 assert 0 <= tile < covered[j].shape[0]
                 unclamped = (i % int(e["per_split"])) * int(e["tp"]) + wave // int(e["wpt"])
-                if e["kind"] == w.CHAIN_SWIGLU or unclamped < int(e["row_tiles"]):
+                if unclamped < int(e["row_tiles"]):
                     covered[j][tile, beg:beg + n] += 1  # a pair's missing second tile repeats the last, unstored
                 q0 = tile * G
                 gg = beg + np.minimum(np.arange(SHARE), n - 1)
@@ -136,12 +134,12 @@ def walk(plan, ops, sizes, M):
                 assert ((q0 + gg) * 8 + (rlane.max() >> 3) * 4 + 4 <= zb).all()
             # outputs of the item (its epilogue)
             split, tg = i // int(e["per_split"]), i % int(e["per_split"])
-            tiles_out = 1 if e["kind"] == w.CHAIN_SWIGLU else int(e["tp"])
-            for lt in range(tiles_out):
-                t = tg if e["kind"] == w.CHAIN_SWIGLU else tg * int(e["tp"]) + lt
+            per_tile = 8 if e["kind"] == w.CHAIN_SWIGLU else 16
+            for lt in range(int(e["tp"])):
+                t = tg * int(e["tp"]) + lt
                 if t >= int(e["row_tiles"]):
                     continue
-                n_idx = t * 16 + np.arange(16)
+                n_idx = t * per_tile + np.arange(per_tile)
                 n_idx = n_idx[n_idx < N]
                 if split == int(e["splits"]) - 1:  # counted once per output
                     written[j][:, n_idx] += 1
@@ -155,17 +153,17 @@ def walk(plan, ops, sizes, M):
 def test_mixed_chain_plan_walk(M):
     spec = [(w.CHAIN_GEMV, 520, 1024, 1, -1, 0),      # external x, pairs of tiles, ragged last pair
             (w.CHAIN_GEMV, 300, 512, 2, 0, 3),        # split K from a producer, ragged N
-            (w.CHAIN_SWIGLU, 200, 256, 1, 1, 2),      # gate/up pair from the split GEMV's output
+            (w.CHAIN_SWIGLU, 200, 256, 1, 1, 2),      # gate/up rows from the split GEMV's output, ragged
             (w.CHAIN_GEMV, 96, 128, 1, 2, 0),         # one group: empty shares
             (w.CHAIN_GEMV, 64, 7168, 1, -1, 0),       # 8 waves per tile
             (w.CHAIN_GEMV, 33, 4864, 4, -1, 0),       # split, 8 waves, ragged
             (w.CHAIN_GEMV, 40, 128 * 57, 1, -1, 0),   # 8 waves, two rounds (7 + 1 tiles at most)
-            (w.CHAIN_SWIGLU, 48, 5120, 1, -1, 0),     # gate/up pairs in two rounds
+            (w.CHAIN_SWIGLU, 36, 128 * 57, 1, -1, 0), # gate/up rows, 8 waves, two rounds, ragged
             (w.CHAIN_GEMV, 3584, 18944, 1, -1, 0)]    # unsplit down projection: three rounds
     ops, sizes = make_ops(M, spec)
     plan, ws = w.w4a16_chain_plan(M, ops)
     h, d = walk(plan, ops, sizes, M)
-    assert list(d["wpt"]) == [4, 4, 4, 4, 8, 4, 8, 4, 8] and list(d["tp"]) == [2, 2, 1, 2, 1, 2, 1, 1, 1]
+    assert list(d["wpt"]) == [4, 4, 4, 4, 8, 4, 8, 8, 8] and list(d["tp"]) == [2, 2, 2, 2, 1, 2, 1, 1, 1]
     assert list(d["rounds"]) == [1, 1, 1, 1, 1, 1, 2, 2, 3]
     assert ws == h["ws_bytes"]
 

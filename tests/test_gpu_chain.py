@@ -33,7 +33,7 @@ class Chain:
         torch, dev = torch_dev()
         self.M, self.spec, self.ops, self.logical = M, spec, [], []
         for i, (kind, N, K, splits, x_src, x_shift) in enumerate(spec):
-            rows = 2 * ((N + 15) // 16 * 16) if kind == w.CHAIN_SWIGLU else N
+            rows = 16 * ((N + 7) // 8) if kind == w.CHAIN_SWIGLU else N
             if device_weights:
                 wq, sc, zp = synthetic.device_packed_weights(rows, K, seed, 100 + i, dev)
                 self.logical.append(None)
@@ -95,9 +95,10 @@ def check_oracle(chain, ys, xs, only=None):
             host = [t.cpu().numpy() for t in (o["wq"], o["scales"], o["zeros"])]
             wq, sp, zp = host[0], host[1].view(np.uint8), host[2]
             if o["kind"] == w.CHAIN_SWIGLU:
-                NP = (N + 15) // 16 * 16
-                r2, a2 = orc.gemv_packed(M, 2 * NP, K, wq, sp, zp, xs[i])
-                blk = lambda a, h: a.reshape(M, NP // 16, 2, 16)[:, :, h, :].reshape(M, NP)[:, :N]
+                # packed rows: per 16-row tile, 8 gate rows then the 8 up rows of the same outputs
+                NT = (N + 7) // 8
+                r2, a2 = orc.gemv_packed(M, 16 * NT, K, wq, sp, zp, xs[i])
+                blk = lambda a, h: a.reshape(M, NT, 2, 8)[:, :, h, :].reshape(M, 8 * NT)[:, :N]
                 ref, bound = oracle.swiglu_bound(blk(r2, 0), blk(a2, 0), blk(r2, 1), blk(a2, 1))
                 ok, r = oracle.swiglu_report(ys[i], ref, bound, orc)
             else:
