@@ -127,14 +127,14 @@ def standalone(o, x_bits, M):
 
 MIXED = [(w.CHAIN_GEMV, 520, 1024, 1, -1, 0),     # external x, tile pairs, ragged last pair
          (w.CHAIN_GEMV, 300, 512, 2, 0, 3),       # split K, fed by GEMV 0
-         (w.CHAIN_SWIGLU, 200, 256, 1, 1, 2),     # gate/up pair fed by the split GEMV
+         (w.CHAIN_SWIGLU, 200, 256, 1, 1, 2),     # gate/up rows fed by the split GEMV (25 tiles: a clamped pair)
          (w.CHAIN_GEMV, 96, 128, 1, 2, 0),        # one group (empty shares), fed by the SwiGLU output
          (w.CHAIN_GEMV, 64, 7168, 1, -1, 0),      # 8 waves per tile
          (w.CHAIN_GEMV, 33, 4864, 4, -1, 0),      # split, ragged
          (w.CHAIN_GEMV, 1000, 512, 1, 0, 3),      # a second consumer of GEMV 0
          (w.CHAIN_GEMV, 7296, 256, 1, -1, 0),     # a wide producer
          (w.CHAIN_GEMV, 40, 7296, 1, 7, 2),       # 8 waves, shares in two rounds, fed by GEMV 7
-         (w.CHAIN_SWIGLU, 48, 5120, 1, -1, 0),    # gate/up pairs in two rounds
+         (w.CHAIN_SWIGLU, 36, 7296, 1, -1, 0),    # gate/up rows, 8 waves, shares in two rounds, ragged
          (w.CHAIN_GEMV, 200, 18944, 1, -1, 0)]    # three rounds
 
 
