@@ -1,0 +1,60 @@
+"""GPU parity on seeded random shapes: the GEMV, the split-K GEMV at the
+library's chosen split and the fused gate/up + SwiGLU GEMV, each against the
+oracle's bound, over shapes drawn so that the launch planner takes many of
+its paths (1 to 16 waves, every share size, x from LDS or from global memory,
+one or several rounds per share, ragged N and ragged 8-row tiles)."""
+import numpy as np
+import pytest
+
+import int4_weight_only_w4a16_amd as w
+import oracle
+from tests.gpu_common import Problem
+from tests.test_gpu_swiglu import SwigluProblem
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes(seed, count, max_macs):
+    """(M, N, K) with K a multiple of 128 and M * N * K at most max_macs (N
+    drawn after K, so long K comes with narrow N)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        M = int(rng.integers(1, 9))
+        G = int(rng.choice([1, 2, 3, 5, 7, 8, 12, 20, 28, 37, 40, 64, 96, 136, 148, 160]))
+        K = 128 * G
+        N = int(rng.integers(1, max(2, min(2600, max_macs // (M * K)))))
+        out.append((M, N, K))
+    return out
+
+
+GEMV_SHAPES = _shapes(2026, 20, 24_000_000)
+SWIGLU_SHAPES = _shapes(2027, 10, 12_000_000)
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_SHAPES)
+def test_random_gemv_and_chosen_split(M, N, K):
+    print(f"[random] gemv M={M} N={N} K={K}", flush=True)
+    p = Problem(M, N, K, seed=M * 7919 + N * 31 + K)
+    ref, absref = p.reference()
+    o = oracle.get()
+    y = p.gemv()
+    ok, worst = oracle.bound_report(y, ref, absref, o)
+    assert ok, (M, N, K, worst)
+    assert np.array_equal(y, p.gemv()), "run-to-run difference"
+    splits = w.w4a16_splitk_choose(M, N, K)
+    if splits > 1:
+        print(f"[random] splitk {splits}", flush=True)
+        ws = p.splitk_workspace(splits)
+        ys = p.gemv_splitk(splits, ws)
+        ok, worst = oracle.bound_report(ys, ref, absref, o)
+        assert ok, (M, N, K, splits, worst)
+        assert np.array_equal(ys, p.gemv_splitk(splits, ws)), "split-K run-to-run difference"
+        assert p.workspace_is_zero(ws)
+
+
+@pytest.mark.parametrize("M,F,K", SWIGLU_SHAPES)
+def test_random_swiglu(M, F, K):
+    print(f"[random] swiglu M={M} F={F} K={K}", flush=True)
+    sp = SwigluProblem(M, F, K, seed=F * 13 + K)
+    sp.check(sp.run())
