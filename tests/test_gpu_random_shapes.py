@@ -2,13 +2,16 @@
 library's chosen split and the fused gate/up + SwiGLU GEMV, each against the
 oracle's bound, over shapes drawn so that the launch planner takes many of
 its paths (1 to 16 waves, every share size, x from LDS or from global memory,
-one or several rounds per share, ragged N and ragged 8-row tiles)."""
+one or several rounds per share, ragged N and ragged 8-row tiles); and the
+prefill GEMM at its chosen split for 9 to 300 rows (every workgroup height),
+also against the product with the fp16-rounded weights."""
 import numpy as np
 import pytest
 
 import int4_weight_only_w4a16_amd as w
 import oracle
 from tests.gpu_common import Problem
+from tests.test_gpu_gemm import check_rounded_weights
 from tests.test_gpu_swiglu import SwigluProblem
 
 pytestmark = pytest.mark.gpu
@@ -30,6 +33,9 @@ def _shapes(seed, count, max_macs):
 
 GEMV_SHAPES = _shapes(2026, 20, 24_000_000)
 SWIGLU_SHAPES = _shapes(2027, 10, 12_000_000)
+_rng = np.random.default_rng(2028)
+GEMM_SHAPES = [(int(m), int(n), 128 * int(g)) for m, n, g in
+               zip(_rng.integers(9, 301, 10), _rng.integers(1, 700, 10), _rng.choice([1, 3, 7, 28, 40, 96, 148], 10))]
 
 
 @pytest.mark.parametrize("M,N,K", GEMV_SHAPES)
@@ -58,3 +64,17 @@ def test_random_swiglu(M, F, K):
     print(f"[random] swiglu M={M} F={F} K={K}", flush=True)
     sp = SwigluProblem(M, F, K, seed=F * 13 + K)
     sp.check(sp.run())
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_random_gemm_chosen_split(M, N, K):
+    splits = w.w4a16_gemm_splitk_choose(M, N, K)
+    print(f"[random] gemm M={M} N={N} K={K} splits={splits}", flush=True)
+    p = Problem(M, N, K, seed=M * 101 + N + K)
+    ws = p.splitk_workspace(splits)
+    y = p.gemm_splitk(splits, ws)
+    p.check(y)
+    check_rounded_weights(p, y)
+    assert np.array_equal(y, p.gemm_splitk(splits, ws)), "run-to-run difference"
+    if splits > 1:
+        assert p.workspace_is_zero(ws)
