@@ -956,13 +956,14 @@ def prefill_gemm(torch, seed, weights):
         }
         del xp, yp, w16
 
-    # Short prefill chunks (M = 64) leave the 128 x 128-tile GEMM with a few
-    # dozen workgroups on 256 compute units: the split-K GEMM at the split
-    # count the library chooses, against the unsplit one and the two-step
-    # route, timed in turn as above.
+    # Short prefill chunks (M = 64, and M = 128 for the narrow matrices)
+    # leave the 128 x 128-tile GEMM with a few dozen workgroups on 256 compute
+    # units: the split-K GEMM at the split count the library chooses, with
+    # the atomic combine and with the two-stage (partials) combine, against
+    # the unsplit one and the two-step route, timed in turn as above.
     prefill_small = {}
-    Ms = 64
-    for label, layer in (("qkv", 0), ("o", 1), ("down", 3)):
+    for label, layer, Ms in (("qkv", 0, 64), ("o", 1, 64), ("down", 3, 64), ("qkv_m128", 0, 128),
+                             ("down_m128", 3, 128)):
         _, Np, Kp = synthetic.QWEN7B_LAYER[layer]
         wq_g, sc_g, zp_g = weights(layer)
         xp = synthetic.device_activations(Ms, Kp, seed, 9998, torch.device("cuda:0"))
@@ -970,22 +971,28 @@ def prefill_gemm(torch, seed, weights):
         w16 = torch.empty((Np, Kp), dtype=torch.float16, device="cuda:0")
         splits = wl.w4a16_gemm_splitk_choose(Ms, Np, Kp)
         ws_g = torch.zeros(wl.w4a16_splitk_workspace_bytes(Ms, Np, splits), dtype=torch.uint8, device="cuda:0")
+        psplits = wl.w4a16_gemm_partials_choose(Ms, Np, Kp)
+        part_g = torch.empty(wl.w4a16_gemm_partials_bytes(Ms, Np, psplits), dtype=torch.uint8, device="cuda:0")
         fns = {"gemm": lambda: wl.w4a16_gemm(Ms, Np, Kp, wq_g, sc_g, zp_g, xp, yp),
                "split": lambda: wl.w4a16_gemm_splitk(Ms, Np, Kp, splits, wq_g, sc_g, zp_g, xp, yp, ws_g),
+               "partials": lambda: wl.w4a16_gemm_splitk_partials(Ms, Np, Kp, psplits, wq_g, sc_g, zp_g, xp, yp, part_g),
                "dq": lambda: wl.w4a16_dequant_f16(Np, Kp, wq_g, sc_g, zp_g, w16),
                "lib": lambda: torch.matmul(xp.view(torch.float16), w16.t())}
         runs = rotating_rounds(fns)
-        gemm_us, split_us, dq_us, lib_us = (float(np.median(runs[k])) for k in ("gemm", "split", "dq", "lib"))
+        gemm_us, split_us, part_us, dq_us, lib_us = (float(np.median(runs[k]))
+                                                     for k in ("gemm", "split", "partials", "dq", "lib"))
         prefill_small[label] = {
-            "shape": f"M={Ms} x {label} {Np}x{Kp}",
+            "shape": f"M={Ms} x {label.split('_')[0]} {Np}x{Kp}",
             "splits": splits,
             "w4a16_gemm_splitk_us": round(split_us, 1),
+            "partials_splits": psplits,
+            "w4a16_gemm_splitk_partials_us": round(part_us, 1),
             "w4a16_gemm_unsplit_us": round(gemm_us, 1),
             "two_step_dequant_plus_torch_fp16_gemm_us": round(dq_us + lib_us, 1),
             "splitk_TFLOPs": round(2.0 * Ms * Np * Kp / (split_us * 1e-6) / 1e12, 1),
             "splitk_weight_GBps": round(algorithmic_bytes(0, Np, Kp) / (split_us * 1e-6) / 1e9, 1),
         }
-        del xp, yp, w16, ws_g
+        del xp, yp, w16, ws_g, part_g
 
     return prefill, prefill_small
 

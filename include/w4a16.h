@@ -374,6 +374,46 @@ int w4a16_gemm_splitk(int M, int N, int K, int splits, const void* Wq, const voi
                       const void* x, void* y, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Bytes of the fp32 partials buffer w4a16_gemm_splitk_partials needs for an
+ * M x N output in `splits` ranges: 4 * splits * M * N, rounded up to a
+ * multiple of 16. Returns 0 for a negative size or splits < 1.
+ */
+size_t w4a16_gemm_partials_bytes(int M, int N, int splits);
+
+/*
+ * Split count this library recommends for w4a16_gemm_splitk_partials (1: do
+ * not split): about two workgroups per compute unit for the output tiles
+ * of w4a16_gemm (none from 256 tiles on), at least 4 groups of K per range,
+ * at most 16. Returns 0 for an invalid shape or one w4a16_gemm does not
+ * support.
+ */
+int w4a16_gemm_partials_choose(int M, int N, int K);
+
+/*
+ * w4a16_gemm with K divided into `splits` contiguous ranges, combined in two
+ * stages ("CodeAlign-Runtime", Level 4: partial sums, then one final
+ * reduction) instead of by atomics: each (tile, range) workgroup stores its
+ * fp32 partial sums to partials[z][M][N] (z = the range), and a second
+ * launch on the same stream writes y[m][n] = fp16(partials[0][m][n] + ... +
+ * partials[splits-1][m][n]), added in range order in fp32. Deterministic
+ * (bit-identical run to run) and within the workload's bound; not
+ * bit-identical to w4a16_gemm_splitk, whose exact fixed-point combine
+ * rounds differently. The atomics that combine costs grow with M * N *
+ * splits; these plain stores and the final pass do not, so narrow matrices
+ * at prefill sizes (M = 16 .. 384) split further for the same price.
+ * partials: device memory, 16-byte aligned, at least
+ * w4a16_gemm_partials_bytes(M, N, splits) bytes, needing no initial contents
+ * (every element is written before it is read); calls that may overlap in
+ * time need different buffers. 1 <= splits <= min(K/128, 31); splits == 1
+ * is w4a16_gemm and does not touch the buffer. Errors: as w4a16_gemm, plus
+ * W4A16_EINVAL for a bad split count, a NULL or misaligned buffer, or one
+ * shorter than w4a16_gemm_partials_bytes.
+ */
+int w4a16_gemm_splitk_partials(int M, int N, int K, int splits, const void* Wq, const void* scales,
+                               const void* zeros, const void* x, void* y, void* partials, size_t partials_bytes,
+                               void* stream);
+
+/*
  * Standalone dequantization, for paths that want the fp16 matrix itself
  * (a GEMM over many activation rows, for instance): W_out[n][k] =
  * fp16((q - z) * s), the exact product rounded once to nearest even, for

@@ -27,7 +27,8 @@ EXPORTS = ("w4a16_layout_id", "w4a16_check_layout", "w4a16_packed_sizes", "w4a16
            "w4a16_unpack",
            "w4a16_gemv", "w4a16_gemv_swiglu", "w4a16_splitk_workspace_bytes", "w4a16_splitk_choose",
            "w4a16_gemv_splitk", "w4a16_gemv_splitk_noalloc", "w4a16_act_quant_i8", "w4a16_gemv_a8", "w4a16_gemv_a8_fused", "w4a16_gemm", "w4a16_gemm_splitk_choose",
-           "w4a16_gemm_splitk", "w4a16_dequant_f16",
+           "w4a16_gemm_splitk", "w4a16_gemm_partials_bytes", "w4a16_gemm_partials_choose", "w4a16_gemm_splitk_partials",
+           "w4a16_dequant_f16",
            "w4a16_dequant_f32", "w4a16_read_probe", "w4a16_chain_plan", "w4a16_chain_run", "w4a16_strerror")
 
 
@@ -96,6 +97,11 @@ def lib():
         L.w4a16_gemm_splitk_choose.restype = _i
         L.w4a16_gemm_splitk_choose.argtypes = [_i, _i, _i]
         L.w4a16_gemm_splitk.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+        L.w4a16_gemm_partials_bytes.restype = _sz
+        L.w4a16_gemm_partials_bytes.argtypes = [_i, _i, _i]
+        L.w4a16_gemm_partials_choose.restype = _i
+        L.w4a16_gemm_partials_choose.argtypes = [_i, _i, _i]
+        L.w4a16_gemm_splitk_partials.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
         L.w4a16_act_quant_i8.argtypes = [_i, _i, _p, _p, _p, _p, _p]
         L.w4a16_gemv_a8.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]
         L.w4a16_gemv_a8_fused.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p]
@@ -290,6 +296,25 @@ def w4a16_gemm_splitk(M, N, K, splits, Wq, scales, zeros, x, y, workspace, ws_by
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().w4a16_gemm_splitk(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
                                    _ptr(workspace), ws_bytes, _stream(stream)), "w4a16_gemm_splitk")
+
+
+def w4a16_gemm_partials_bytes(M, N, splits):
+    return lib().w4a16_gemm_partials_bytes(M, N, splits)
+
+
+def w4a16_gemm_partials_choose(M, N, K):
+    return lib().w4a16_gemm_partials_choose(M, N, K)
+
+
+def w4a16_gemm_splitk_partials(M, N, K, splits, Wq, scales, zeros, x, y, partials, partials_bytes=None, stream=None):
+    """Device: split-K GEMM combined in two stages (fp32 partials, then a
+    final pass in split order). partials: device buffer of at least
+    w4a16_gemm_partials_bytes(M, N, splits) bytes, no initial contents."""
+    if partials_bytes is None:
+        partials_bytes = partials.numel() * partials.element_size()
+    _check(lib().w4a16_gemm_splitk_partials(M, N, K, splits, _ptr(Wq), _ptr(scales), _ptr(zeros), _ptr(x), _ptr(y),
+                                            _ptr(partials), partials_bytes, _stream(stream)),
+           "w4a16_gemm_splitk_partials")
 
 
 def w4a16_dequant_f16(N, K, Wq, scales, zeros, W_out, stream=None):

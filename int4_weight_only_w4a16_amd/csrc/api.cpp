@@ -1,5 +1,6 @@
 // C-ABI front end of libw4a16.so: argument checks, launch planning and error
 // mapping for the device entry points declared in include/w4a16.h.
+#include <algorithm>
 #include <cstdint>
 
 #include "w4a16.h"
@@ -132,6 +133,28 @@ int choose_gemm_splits(int M, int N, int K) {
   }
   splits = splits > groups / 4 ? groups / 4 : splits;
   splits = splits > w4a16::kMaxSplits ? w4a16::kMaxSplits : splits;
+  return splits < 1 ? 1 : int(splits);
+}
+
+// Split count for w4a16_gemm_splitk_partials, fitted to a sweep of split
+// counts on MI355X (7B-shaped matrices, M = 16 .. 384). With W the output
+// tiles of w4a16_gemm: none from 256 tiles on; else about 160 workgroups
+// (ceil(160 / W) splits), raised toward 20 groups of K per split while the
+// grid stays within 256 workgroups (the long-K down projection), at most 16
+// splits and at least 4 groups each. More splits than that lost: each adds
+// 4 * M * N bytes of partials, written once and read once more. (qkv
+// 4608x3584 at M = 128: 19.2 us in 4, 20.1 in 7, 23.0 in 14; down
+// 3584x18944 at M = 384: 66.6 us in 3, 75.6 in 4, 86.4 in 2.)
+int choose_gemm_partials(int M, int N, int K) {
+  const int groups = K / W4A16_GROUP;
+  const int bm = 16 * w4a16::gemm_m_blocks(M);
+  const int64_t wgs = (int64_t(M) + bm - 1) / bm * ((int64_t(N) + 127) / 128);
+  if (wgs >= 256) return 1;
+  int64_t splits = (160 + wgs - 1) / wgs;
+  const int64_t long_k = std::min<int64_t>((groups + 19) / 20, 256 / wgs);
+  if (long_k > splits) splits = long_k;
+  if (splits > 16) splits = 16;
+  if (splits > groups / 4) splits = groups / 4;
   return splits < 1 ? 1 : int(splits);
 }
 
@@ -274,6 +297,31 @@ extern "C" int w4a16_gemm_splitk(int M, int N, int K, int splits, const void* Wq
   if (ws_bytes < w4a16::splitk_workspace_bytes(M, N)) return W4A16_EINVAL;
   auto* ws = static_cast<unsigned long long*>(workspace);
   if (w4a16::launch_gemm(M, N, K, splits, Wq, scales, zeros, x, y, ws, stream) != 0) return W4A16_EHIP;
+  return W4A16_OK;
+}
+
+extern "C" size_t w4a16_gemm_partials_bytes(int M, int N, int splits) {
+  if (M < 0 || N < 0 || splits < 1) return 0;
+  return w4a16::gemm_partials_bytes(M, N, splits);
+}
+
+extern "C" int w4a16_gemm_partials_choose(int M, int N, int K) {
+  if (K < W4A16_GROUP || K % W4A16_GROUP != 0 || M < 1 || N < 1 || K >= w4a16::kGemmMaxK) return 0;
+  return choose_gemm_partials(M, N, K);
+}
+
+extern "C" int w4a16_gemm_splitk_partials(int M, int N, int K, int splits, const void* Wq, const void* scales,
+                                          const void* zeros, const void* x, void* y, void* partials,
+                                          size_t partials_bytes, void* stream) {
+  if (K < W4A16_GROUP || K % W4A16_GROUP != 0 || M < 0 || N < 0) return W4A16_EINVAL;
+  if (splits < 1 || splits > K / W4A16_GROUP || splits > w4a16::kMaxSplits) return W4A16_EINVAL;
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (K >= w4a16::kGemmMaxK) return W4A16_EUNSUPPORTED;
+  if (splits == 1) return w4a16_gemm(M, N, K, Wq, scales, zeros, x, y, stream);
+  if (!pointers_ok({Wq, scales, zeros, x, y, partials})) return W4A16_EINVAL;
+  if (partials_bytes < w4a16::gemm_partials_bytes(M, N, splits)) return W4A16_EINVAL;
+  if (w4a16::launch_gemm(M, N, K, splits, Wq, scales, zeros, x, y, nullptr, stream, static_cast<float*>(partials)) != 0)
+    return W4A16_EHIP;
   return W4A16_OK;
 }
 

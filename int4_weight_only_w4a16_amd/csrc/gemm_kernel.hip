@@ -23,6 +23,8 @@
 //    two register buffers. (Weights two groups ahead, which needs x staged
 //    through registers, measured 10% slower: the multiply is not waiting
 //    on memory as much as on issue.)
+#include <algorithm>
+
 #include "w4a16_device.h"
 
 namespace w4a16 {
@@ -36,18 +38,22 @@ constexpr int kOStride = kGemmBN + 8;       // halves per LDS row of the output 
 constexpr size_t gemm_lds_bytes(int mb) { return size_t(2) * 16 * mb * kGroup * 2; }
 static_assert(size_t(16) * kOStride * 2 <= gemm_lds_bytes(1), "output tile must fit the x buffers");
 
-// Split-K (splits > 1, ws non-null): workgroup (.., .., z) multiplies only
-// the z-th of `splits` contiguous group ranges and adds its fp32 partial
-// sums to ws, one uint64 word per output, in the fixed-point format of
-// splitk_addend(); the add that completes an output's count writes y and
-// zeroes the word (exact and order-free, as in the split-K GEMV).
+// Split-K (splits > 1): workgroup (.., .., z) multiplies only the z-th of
+// `splits` contiguous group ranges. With ws non-null it adds its fp32
+// partial sums to ws, one uint64 word per output, in the fixed-point format
+// of splitk_addend(); the add that completes an output's count writes y and
+// zeroes the word (exact and order-free, as in the split-K GEMV). With part
+// non-null instead it stores them, plain fp32, to part[z][M][N], and
+// splitk_sum_kernel adds the splits afterwards in split order (the
+// two-stage partial-then-final reduction): no atomics, whose cost grows with
+// M * N * splits (a third of the launch for 4608 x 3584 at M = 64).
 template <int MB>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int splits,
                                                    const uint8_t* __restrict__ wq,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros,
                                                    const _Float16* __restrict__ x, _Float16* __restrict__ y,
-                                                   unsigned long long* __restrict__ ws) {
+                                                   unsigned long long* __restrict__ ws, float* __restrict__ part) {
   constexpr int kBM = 16 * MB;           // activation rows per workgroup
   constexpr int kXTile = kBM * kGroup;   // halves of one staged x group
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -271,6 +277,24 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
   }
   if (i < ng) step(i, wa, wb);
 
+  if (part) {
+    // This split's partial sums, plain fp32 stores: a wave instruction
+    // writes 64-byte runs of four rows.
+    float* pz = part + int64_t(blockIdx.z) * M * N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kGemmNB; ++nb) {
+        const int64_t n = (tw + nb) * kTileRows + rlane;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = m0 + mb * 16 + piece * 4 + r;
+          if (m < M && n < N && tw + nb < NT) pz[m * N + n] = acc[mb][nb][r];
+        }
+      }
+    return;
+  }
+
   if (ws) {
     // Split-K: one relaxed device-scope atomic add per output. A lane's adds
     // go out 16 at a time (two row blocks) before their results are
@@ -365,13 +389,37 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
   }
 }
 
+// Final stage of the partials combine: y[i] = fp16(part[0][i] + part[1][i] +
+// ... + part[S-1][i]), added in split order in fp32, for i < count = M * N.
+// VEC: four consecutive outputs per thread (count a multiple of 4).
+template <bool VEC>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ part, int64_t count, int splits,
+                                                         _Float16* __restrict__ y) {
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  if constexpr (VEC) {
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; 4 * i < count; i += stride) {
+      f32x4v s = *reinterpret_cast<const f32x4v*>(part + 4 * i);
+      for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4v*>(part + int64_t(z) * count + 4 * i);
+      *reinterpret_cast<half4_t*>(y + 4 * i) = half4_t{(_Float16)s[0], (_Float16)s[1], (_Float16)s[2], (_Float16)s[3]};
+    }
+  } else {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < count; i += stride) {
+      float s = part[i];
+      for (int z = 1; z < splits; ++z) s += part[int64_t(z) * count + i];
+      y[i] = (_Float16)s;
+    }
+  }
+}
+
 }  // namespace dev
 
 namespace {
 
 template <int MB>
 int launch_gemm_mb(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
-                   const void* x, void* y, unsigned long long* ws, hipStream_t stream) {
+                   const void* x, void* y, unsigned long long* ws, float* part, hipStream_t stream) {
   static std::atomic<uint64_t> raised{0};  // devices on which the kernel's LDS limit is raised
   const size_t lds = dev::gemm_lds_bytes(MB);
   const hipError_t e = dev::raise_lds_limit(reinterpret_cast<const void*>(&dev::gemm_kernel<MB>), lds, raised);
@@ -382,20 +430,34 @@ int launch_gemm_mb(int M, int N, int K, int splits, const void* wq, const void* 
   return int(dev::launch_kernel(&dev::gemm_kernel<MB>, grid, dim3(256), lds, stream, M, N, K, splits,
                                 static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
                                 static_cast<const uint8_t*>(zeros), static_cast<const _Float16*>(x),
-                                static_cast<_Float16*>(y), splits > 1 ? ws : nullptr));
+                                static_cast<_Float16*>(y), splits > 1 && !part ? ws : nullptr,
+                                splits > 1 ? part : nullptr));
 }
 
 }  // namespace
 
 int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
-                const void* x, void* y, unsigned long long* ws, void* stream) {
+                const void* x, void* y, unsigned long long* ws, void* stream, float* part) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc;
   switch (gemm_m_blocks(M)) {
-    case 1: return launch_gemm_mb<1>(M, N, K, splits, wq, scales, zeros, x, y, ws, s);
-    case 2: return launch_gemm_mb<2>(M, N, K, splits, wq, scales, zeros, x, y, ws, s);
-    case 4: return launch_gemm_mb<4>(M, N, K, splits, wq, scales, zeros, x, y, ws, s);
-    default: return launch_gemm_mb<8>(M, N, K, splits, wq, scales, zeros, x, y, ws, s);
+    case 1: rc = launch_gemm_mb<1>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+    case 2: rc = launch_gemm_mb<2>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+    case 4: rc = launch_gemm_mb<4>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+    default: rc = launch_gemm_mb<8>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
   }
+  if (rc != 0 || !part || splits < 2) return rc;
+  // The final stage, on the same stream: about four outputs per thread
+  // at once, 1024 workgroups at most (a grid-stride loop takes the rest).
+  const int64_t count = int64_t(M) * N;
+  const bool vec = (count & 3) == 0;
+  const int64_t items = vec ? count / 4 : count;
+  const unsigned grid = unsigned(std::min<int64_t>((items + 255) / 256, 1024));
+  hipError_t e = vec ? dev::launch_kernel(&dev::splitk_sum_kernel<true>, dim3(grid), dim3(256), 0, s,
+                                          static_cast<const float*>(part), count, splits, static_cast<_Float16*>(y))
+                     : dev::launch_kernel(&dev::splitk_sum_kernel<false>, dim3(grid), dim3(256), 0, s,
+                                          static_cast<const float*>(part), count, splits, static_cast<_Float16*>(y));
+  return int(e);
 }
 
 }  // namespace w4a16

@@ -162,9 +162,16 @@ constexpr int kGemmMaxK = 1 << 25;
 // cover M, up to 8. A 128-row tile at M = 16 spends 7/8 of its matrix-core
 // work on padding rows.
 constexpr int gemm_m_blocks(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
-// splits > 1 takes `ws`, the split-K workspace above (all zero); 1 ignores it.
+// splits > 1 takes `ws`, the split-K workspace above (all zero), or, when
+// `part` is non-null, fp32 partials part[splits][M][N] summed by a second
+// launch; 1 ignores both.
 int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
-                const void* x, void* y, unsigned long long* ws, void* stream);
+                const void* x, void* y, unsigned long long* ws, void* stream, float* part = nullptr);
+// Bytes of the fp32 partials of w4a16_gemm_splitk_partials: 4 * splits * M * N,
+// rounded up to 16.
+constexpr size_t gemm_partials_bytes(int M, int N, int splits) {
+  return (size_t(4) * size_t(splits) * size_t(M) * size_t(N) + 15) / 16 * 16;
+}
 int launch_dequant_f16(int N, int K, const void* wq, const void* scales, const void* zeros, void* out,
                        void* stream);
 int launch_read_probe(const void* buf, size_t bytes, int grid, void* sink, void* stream);

@@ -76,6 +76,19 @@ class Problem:
         torch.cuda.synchronize()
         return y.cpu().numpy().view(np.uint16)
 
+    def gemm_partials(self, splits, part=None):
+        """w4a16_gemm_splitk_partials; a fresh buffer is filled with NaN bits
+        first (the call must write every partial before reading it)."""
+        torch, dev = torch_dev()
+        y = self.new_y()
+        if part is None:
+            part = torch.full((max(16, w.w4a16_gemm_partials_bytes(self.M, self.N, splits)),), 0xFF,
+                              dtype=torch.uint8, device=dev)
+        w.w4a16_gemm_splitk_partials(self.M, self.N, self.K, splits, self.wq_d, self.sp_d, self.zp_d, self.x_d, y,
+                                     part)
+        torch.cuda.synchronize()
+        return y.cpu().numpy().view(np.uint16)
+
     def workspace_is_zero(self, ws):
         """Every split-K call leaves its accumulation words at zero."""
         return not ws.cpu().numpy().any()

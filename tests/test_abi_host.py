@@ -271,3 +271,27 @@ def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(w, "_lib", None)
     with pytest.raises(ImportError):
         w.lib()
+
+
+def test_gemm_partials_sizes_choice_and_argument_checks():
+    """w4a16_gemm_splitk_partials: the buffer size, the split choice and the
+    argument checks that return before any launch (no GPU touched)."""
+    L = w.lib()
+    assert w.w4a16_gemm_partials_bytes(3, 5, 2) == 128  # 4 * 2 * 3 * 5 = 120, rounded up to 16
+    assert w.w4a16_gemm_partials_bytes(64, 4608, 4) == 4 * 4 * 64 * 4608
+    assert w.w4a16_gemm_partials_bytes(-1, 5, 2) == 0 and w.w4a16_gemm_partials_bytes(3, 5, 0) == 0
+    for M, N, K in [(16, 4608, 3584), (128, 3584, 18944), (384, 4608, 3584), (64, 37888, 3584)]:
+        s = w.w4a16_gemm_partials_choose(M, N, K)
+        assert 1 <= s <= min(16, K // 128 // 4 if K // 128 >= 4 else 1)
+    assert w.w4a16_gemm_partials_choose(64, 37888, 3584) == 1  # enough output tiles already
+    assert w.w4a16_gemm_partials_choose(16, 64, 200) == 0       # K not a multiple of 128
+    fake = 1 << 20
+    ptrs = [fake] * 5
+    need = w.w4a16_gemm_partials_bytes(64, 300, 4)
+    assert L.w4a16_gemm_splitk_partials(64, 300, 1024, 4, *ptrs, fake, need - 16, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemm_splitk_partials(64, 300, 1024, 4, *ptrs, None, need, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemm_splitk_partials(64, 300, 1024, 4, *ptrs, fake + 8, need, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemm_splitk_partials(64, 300, 1024, 9, *ptrs, fake, need, None) == w.W4A16_EINVAL  # > K/128
+    assert L.w4a16_gemm_splitk_partials(64, 300, 1024, 0, *ptrs, fake, need, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemm_splitk_partials(64, 300, 200, 2, *ptrs, fake, need, None) == w.W4A16_EINVAL
+    assert L.w4a16_gemm_splitk_partials(0, 300, 1024, 4, *ptrs, None, 0, None) == w.W4A16_OK

@@ -174,3 +174,28 @@ def test_gemm_large_grid_sampled(M, N, K, splits):
     if splits == 1:
         p16 = Problem(16, N, K, q=q, s=s, z=z, x=p.x[:16])
         assert np.array_equal(run_gemm(p16), y[:16]), "rows differ from the 16-row tile"
+
+
+# The two-stage (partials) split-K combine: every output within the bound and
+# the rounded-weight check, bit-identical on a repeat, on a buffer whose old
+# contents are NaN bits; ragged M and N, output counts with and without a
+# multiple of 4 (the final stage's two paths), split counts 2 .. 16 and the
+# library's choice.
+@pytest.mark.parametrize("M,N,K,splits", [(16, 896, 896, 2), (33, 257, 1280, 3), (64, 301, 2048, 5),
+                                          (97, 129, 3584, 7), (128, 600, 18944, 16), (200, 37, 640, 4),
+                                          (9, 11, 384, 3), (300, 1000, 1152, 0), (64, 4608, 3584, 0),
+                                          (384, 3584, 18944, 0)])
+def test_gemm_partials_against_oracle(M, N, K, splits):
+    if splits == 0:
+        splits = w.w4a16_gemm_partials_choose(M, N, K)
+    _say("partials", M, N, K, splits)
+    p = Problem(M, N, K, seed=M * 3 + N)
+    y = p.gemm_partials(splits)
+    _say(M, N, K, splits, "worst", p.check(y))
+    check_rounded_weights(p, y)
+    assert np.array_equal(y, p.gemm_partials(splits)), "run-to-run difference"
+
+
+def test_gemm_partials_one_split_is_the_gemm():
+    p = Problem(40, 300, 1024, seed=5)
+    assert np.array_equal(p.gemm_partials(1), run_gemm(p))

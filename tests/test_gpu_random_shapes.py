@@ -4,7 +4,8 @@ oracle's bound, over shapes drawn so that the launch planner takes many of
 its paths (1 to 16 waves, every share size, x from LDS or from global memory,
 one or several rounds per share, ragged N and ragged 8-row tiles); and the
 prefill GEMM at its chosen split for 9 to 300 rows (every workgroup height),
-also against the product with the fp16-rounded weights."""
+with the atomic and with the two-stage combine, also against the product with
+the fp16-rounded weights."""
 import numpy as np
 import pytest
 
@@ -78,3 +79,8 @@ def test_random_gemm_chosen_split(M, N, K):
     assert np.array_equal(y, p.gemm_splitk(splits, ws)), "run-to-run difference"
     if splits > 1:
         assert p.workspace_is_zero(ws)
+    ps = w.w4a16_gemm_partials_choose(M, N, K)
+    print(f"[random] gemm partials splits={ps}", flush=True)
+    yp = p.gemm_partials(ps)
+    p.check(yp)
+    check_rounded_weights(p, yp)
