@@ -440,7 +440,7 @@ int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* sca
                 const void* x, void* y, unsigned long long* ws, void* stream, float* part) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc;
-  switch (gemm_m_blocks(M)) {
+  switch (splits > 1 ? gemm_m_blocks(M) : gemm_m_blocks_unsplit(M, N)) {
     case 1: rc = launch_gemm_mb<1>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
     case 2: rc = launch_gemm_mb<2>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
     case 4: rc = launch_gemm_mb<4>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;

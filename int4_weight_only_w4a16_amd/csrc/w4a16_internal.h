@@ -162,6 +162,21 @@ constexpr int kGemmMaxK = 1 << 25;
 // cover M, up to 8. A 128-row tile at M = 16 spends 7/8 of its matrix-core
 // work on padding rows.
 constexpr int gemm_m_blocks(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
+// An unsplit launch above 64 rows takes 64-row tiles where their grid still
+// fits one workgroup per CU (ceil(M/64) x 128-column strips <= 256: a narrow
+// matrix, whose 128-row grid leaves most CUs idle), or where the second of
+// two 128-row tiles would be at most half used (128 < M <= 192); 128-row
+// tiles otherwise. Measured on MI355X (7B shapes, unsplit, µs): 3584x18944 at
+// M = 192 124.0 against 146.7, at M = 512 122.1 against 147.0; 4608x3584 at
+// M = 448 29.3 against 31.3 (at M = 512, 288 workgroups: 33.7 against 31.6);
+// 37888x3584 at M = 160 79.1 against 88.7, at M = 320 114.2 against 110.4.
+// Split launches keep gemm_m_blocks, to which their split rules are fitted.
+// Each output's sum is the same sequence of MFMAs for every tile height.
+constexpr int gemm_m_blocks_unsplit(int M, int N) {
+  if (M <= 64) return gemm_m_blocks(M);
+  const long long strips = (static_cast<long long>(N) + 127) / 128;
+  return ((static_cast<long long>(M) + 63) / 64 * strips <= 256 || (M > 128 && M <= 192)) ? 4 : 8;
+}
 // splits > 1 takes `ws`, the split-K workspace above (all zero), or, when
 // `part` is non-null, fp32 partials part[splits][M][N] summed by a second
 // launch; 1 ignores both.

@@ -1,10 +1,12 @@
 """GPU parity of the W4A16 GEMM for many activation rows (w4a16_gemm, and
 w4a16_gemm_splitk) and of its weights (w4a16_dequant_f16), through the C
 ABI, against the fp64 oracle. The shapes cover each workgroup height (16,
-32, 64 and 128 rows: M <= 16, <= 32, <= 64 and above) with ragged M and N,
-and both tile orders (the XCD band order needs 4k m blocks and 8k tiles per
-split: 500x250 and 1000x300 here, split in 3 at 500x250, the chosen split
-at M = 512 on 3584x18944, and the prefill-sized calls).
+32, 64 and 128 rows: M <= 16, <= 32, <= 64 and above; unsplit launches above
+64 rows take 64-row tiles on narrow matrices and at 129-192 rows, so 100x20000,
+257x8300 and 450x4347 are there for the unsplit 128-row tile) with ragged M
+and N, and both tile orders (the XCD band order needs 4k m blocks and 8k tiles
+per split: 500x250, 1000x300 and 450x4347 here, split in 3 at 500x250, the
+chosen split at M = 512 on 3584x18944, and the prefill-sized calls).
 
 Bars: every output within the workload bound 2e-3 * sum|w x| + 1e-5 of the
 oracle's fp64 product; and, tighter, within fp32 accumulation and fp16
@@ -50,7 +52,8 @@ def check_rounded_weights(p, y, rows=None):
 @pytest.mark.parametrize("M,N,K", [(9, 37, 384), (16, 896, 896), (130, 200, 640), (128, 128, 128),
                                    (300, 1000, 1152), (257, 4608, 3584), (64, 301, 256), (200, 1031, 128),
                                    (1, 50, 256), (17, 300, 640), (32, 129, 384), (33, 257, 1280), (48, 160, 128),
-                                   (65, 144, 512), (500, 250, 384), (1000, 300, 256)])
+                                   (65, 144, 512), (500, 250, 384), (1000, 300, 256),
+                                   (100, 20000, 384), (257, 8300, 256), (450, 4347, 256)])
 def test_gemm_against_oracle(M, N, K):
     _say("shape", M, N, K)
     p = Problem(M, N, K, seed=M + N)
