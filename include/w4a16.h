@@ -281,8 +281,11 @@ int w4a16_gemv_splitk_noalloc(int M, int N, int K, int splits, const void* Wq, c
  * output rounding of sum_k fp16w * x -- inside the workload's bound
  * 2e-3 * sum|w x| + 1e-5, the weight rounding taking at most 2^-11 of it.
  * A workgroup covers 16, 32, 64 or 128 rows of x (the fewest of these that
- * cover M) and 128 of W. Deterministic (fixed order), but not bit-equal to
- * w4a16_gemv, whose
+ * cover M; above 64 rows, 64 where the grid of 64-row tiles holds at most
+ * 256 workgroups, or where M is 129 .. 192, and 128 otherwise)
+ * and 128 of W. Each output's sum is the same sequence of products for
+ * every tile height, so row m of the result does not depend on M.
+ * Deterministic (fixed order), but not bit-equal to w4a16_gemv, whose
  * weights are exact (q - z) scaled per group. The standalone dequant + MFMA
  * GEMM variant the AWQ dequantization page builds in two steps, here in
  * one. Errors: W4A16_EINVAL (shape, NULL, alignment), W4A16_EUNSUPPORTED
@@ -382,10 +385,12 @@ size_t w4a16_gemm_partials_bytes(int M, int N, int splits);
 
 /*
  * Split count this library recommends for w4a16_gemm_splitk_partials (1: do
- * not split): about two workgroups per compute unit for the output tiles
- * of w4a16_gemm (none from 256 tiles on), at least 4 groups of K per range,
- * at most 16. Returns 0 for an invalid shape or one w4a16_gemm does not
- * support.
+ * not split). With W the output tiles of a split launch (128 columns by 16,
+ * 32, 64 or 128 rows, the fewest that cover M): none from 256 tiles on; else
+ * about 160 workgroups in all, more for a long K (toward 20 groups of K per
+ * range while the grid stays within 256 workgroups); at least 4 groups of K
+ * per range, at most 16 ranges. Returns 0 for an invalid shape or one
+ * w4a16_gemm does not support.
  */
 int w4a16_gemm_partials_choose(int M, int N, int K);
 
