@@ -47,7 +47,7 @@ static_assert(size_t(16) * kOStride * 2 <= gemm_lds_bytes(1), "output tile must 
 // splitk_sum_kernel adds the splits afterwards in split order (the
 // two-stage partial-then-final reduction): no atomics, whose cost grows with
 // M * N * splits (a third of the launch for 4608 x 3584 at M = 64).
-template <int MB>
+template <int MB, bool REGX>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int splits,
                                                    const uint8_t* __restrict__ wq,
                                                    const uint16_t* __restrict__ scales,
@@ -240,42 +240,98 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
     }
   };
 
-  // One step per group: request the next group's x (into the other LDS
-  // buffer, last read before the previous barrier) and weights (the last
-  // step re-requests the last group: in bounds, unused), multiply this
-  // group, wait for the x requests only, and meet at an LDS-only barrier.
-  // The requests are unconditional and the two weight buffers alternate
-  // statically (the loop is unrolled by two), so the only wait before the
-  // multiply is for the weights requested one step earlier; a branch around
-  // the requests or a register copy between the buffers let the compiler
-  // wait for all of them, and __syncthreads() would wait for every
-  // outstanding load too.
-  W wa, wb;
-  auto step = [&](int i, const W& cur, W& nxt) {  // step i multiplies group g_beg + i
-    const int gn = g_beg + (i + 1 < ng ? i + 1 : ng - 1);
-    load_x(gn, (i & 1) ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(gn, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(i & 1, cur);
-    // The x requests are global-to-LDS requests, which need not complete in
-    // order with the weight loads issued after them (see load_lds16), so the
-    // only wait that guarantees the next x buffer is complete before the
-    // barrier is a full one. It also waits for the weights requested this
-    // step, which the next step needs first anyway.
+  static_assert(!REGX || MB <= 4, "the register pipeline is built for tiles of at most 64 rows");
+  if constexpr (REGX) {
+    // Register pipeline (tiles of 16-64 rows on grids that leave CUs
+    // without a second workgroup): each workgroup streams a whole strip of
+    // weights, so the requests in flight, not the products, set the pace.
+    // x of a group is MB 16-byte loads per lane here, so both x and the
+    // weights go through registers, kDepth groups ahead: step i writes group i's x (requested kDepth steps earlier) into
+    // LDS buffer i & 1 (last read by step i - 2, which every wave finished
+    // before the previous step's barrier), requests group i + kDepth's x
+    // into the registers just written out, meets the others at an LDS-only
+    // barrier, multiplies, and requests group i + kDepth's weights into the
+    // registers it multiplied. Ordinary loads retire in order, so each wait
+    // is an exact count that leaves the later groups' requests in flight.
+    // The LDS slots and their swizzle are those of load_x. Past the last
+    // group the requests repeat it (in bounds, unused).
+    constexpr int kDepth = 4;
+    struct XR {
+      u32x4 v[MB];
+    };
+    auto load_xr = [&](int g, XR& r) {
+      const _Float16* xg = x + m0 * K + int64_t(g) * kGroup;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) r.v[j] = *reinterpret_cast<const u32x4*>(xg + x_off[j]);
+    };
+    auto group = [&](int i) { return g_beg + (i < ng ? i : ng - 1); };
+    XR xr[kDepth];
+    W wr[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      load_xr(group(d), xr[d]);
+      load_w(group(d), wr[d]);
+    }
+    auto step = [&](int i, XR& xc, W& wc) {  // step i multiplies group g_beg + i
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        *reinterpret_cast<u32x4*>(xs + (i & 1) * kXTile + (wave * MB + j) * 512 + lane * 8) = xc.v[j];
+      __builtin_amdgcn_sched_barrier(0);
+      load_xr(group(i + kDepth), xc);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      compute(i & 1, wc);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(group(i + kDepth), wc);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int i = 0;
+    for (; i + kDepth <= ng; i += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) step(i + d, xr[d], wr[d]);
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (i + d < ng) step(i + d, xr[d], wr[d]);  // ng is the same for the whole workgroup
+    lds_barrier();  // the LDS epilogue below reuses the x buffers
+  } else {
+    // One step per group: request the next group's x (into the other LDS
+    // buffer, last read before the previous barrier) and weights (the last
+    // step re-requests the last group: in bounds, unused), multiply this
+    // group, wait for the x requests only, and meet at an LDS-only barrier.
+    // The requests are unconditional and the two weight buffers alternate
+    // statically (the loop is unrolled by two), so the only wait before the
+    // multiply is for the weights requested one step earlier; a branch around
+    // the requests or a register copy between the buffers let the compiler
+    // wait for all of them, and __syncthreads() would wait for every
+    // outstanding load too.
+    W wa, wb;
+    auto step = [&](int i, const W& cur, W& nxt) {  // step i multiplies group g_beg + i
+      const int gn = g_beg + (i + 1 < ng ? i + 1 : ng - 1);
+      load_x(gn, (i & 1) ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(gn, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(i & 1, cur);
+      // The x requests are global-to-LDS requests, which need not complete in
+      // order with the weight loads issued after them (see load_lds16), so the
+      // only wait that guarantees the next x buffer is complete before the
+      // barrier is a full one. It also waits for the weights requested this
+      // step, which the next step needs first anyway.
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+      lds_barrier();
+    };
+    load_x(g_beg, 0);
+    load_w(g_beg, wa);
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     lds_barrier();
-  };
-  load_x(g_beg, 0);
-  load_w(g_beg, wa);
-  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
-  lds_barrier();
-  int i = 0;
-  for (; i + 1 < ng; i += 2) {
-    step(i, wa, wb);
-    step(i + 1, wb, wa);
+    int i = 0;
+    for (; i + 1 < ng; i += 2) {
+      step(i, wa, wb);
+      step(i + 1, wb, wa);
+    }
+    if (i < ng) step(i, wa, wb);
   }
-  if (i < ng) step(i, wa, wb);
 
   if (part) {
     // This split's partial sums, plain fp32 stores: a wave instruction
@@ -417,17 +473,18 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
 
 namespace {
 
-template <int MB>
+template <int MB, bool REGX>
 int launch_gemm_mb(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
                    const void* x, void* y, unsigned long long* ws, float* part, hipStream_t stream) {
   static std::atomic<uint64_t> raised{0};  // devices on which the kernel's LDS limit is raised
   const size_t lds = dev::gemm_lds_bytes(MB);
-  const hipError_t e = dev::raise_lds_limit(reinterpret_cast<const void*>(&dev::gemm_kernel<MB>), lds, raised);
+  const hipError_t e =
+      dev::raise_lds_limit(reinterpret_cast<const void*>(&dev::gemm_kernel<MB, REGX>), lds, raised);
   if (e != hipSuccess) return int(e);
   const int64_t NT = (int64_t(N) + kTileRows - 1) / kTileRows;
   const dim3 grid(unsigned((M + 16 * MB - 1) / (16 * MB)),
                   unsigned((NT + dev::kGemmBN / kTileRows - 1) / (dev::kGemmBN / kTileRows)), unsigned(splits));
-  return int(dev::launch_kernel(&dev::gemm_kernel<MB>, grid, dim3(256), lds, stream, M, N, K, splits,
+  return int(dev::launch_kernel(&dev::gemm_kernel<MB, REGX>, grid, dim3(256), lds, stream, M, N, K, splits,
                                 static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
                                 static_cast<const uint8_t*>(zeros), static_cast<const _Float16*>(x),
                                 static_cast<_Float16*>(y), splits > 1 && !part ? ws : nullptr,
@@ -440,11 +497,19 @@ int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* sca
                 const void* x, void* y, unsigned long long* ws, void* stream, float* part) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc;
-  switch (splits > 1 ? gemm_m_blocks(M) : gemm_m_blocks_unsplit(M, N)) {
-    case 1: rc = launch_gemm_mb<1>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
-    case 2: rc = launch_gemm_mb<2>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
-    case 4: rc = launch_gemm_mb<4>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
-    default: rc = launch_gemm_mb<8>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+  const int mb = splits > 1 ? gemm_m_blocks(M) : gemm_m_blocks_unsplit(M, N);
+  // The 64-row tile takes the register pipeline only on grids of fewer
+  // than 256 workgroups: on wider ones (37888 x 3584 at M = 48-64, 296
+  // workgroups) its extra registers cost a wave per SIMD and 3-4%.
+  const int64_t wgs = (int64_t(M) + 16 * mb - 1) / (16 * mb) * ((int64_t(N) + 127) / 128) * splits;
+  switch (mb) {
+    case 1: rc = launch_gemm_mb<1, true>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+    case 2: rc = launch_gemm_mb<2, true>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+    case 4:
+      rc = wgs < 256 ? launch_gemm_mb<4, true>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s)
+                     : launch_gemm_mb<4, false>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s);
+      break;
+    default: rc = launch_gemm_mb<8, false>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
   }
   if (rc != 0 || !part || splits < 2) return rc;
   // The final stage, on the same stream: about four outputs per thread
