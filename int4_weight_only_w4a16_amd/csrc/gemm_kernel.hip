@@ -47,7 +47,7 @@ static_assert(size_t(16) * kOStride * 2 <= gemm_lds_bytes(1), "output tile must 
 // splitk_sum_kernel adds the splits afterwards in split order (the
 // two-stage partial-then-final reduction): no atomics, whose cost grows with
 // M * N * splits (a third of the launch for 4608 x 3584 at M = 64).
-template <int MB, bool REGX>
+template <int MB>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int splits,
                                                    const uint8_t* __restrict__ wq,
                                                    const uint16_t* __restrict__ scales,
@@ -240,13 +240,13 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
     }
   };
 
-  static_assert(!REGX || MB <= 4, "the register pipeline is built for tiles of at most 64 rows");
-  if constexpr (REGX) {
-    // Register pipeline (tiles of 16-64 rows on grids that leave CUs
-    // without a second workgroup): each workgroup streams a whole strip of
-    // weights, so the requests in flight, not the products, set the pace.
-    // x of a group is MB 16-byte loads per lane here, so both x and the
-    // weights go through registers, kDepth groups ahead: step i writes group i's x (requested kDepth steps earlier) into
+  if constexpr (MB <= 4) {
+    // Register pipeline (tiles of 16-64 rows): each workgroup streams a
+    // whole strip of weights, so the requests in flight, not the products,
+    // set the pace. x of a group is MB 16-byte loads per lane here, so both
+    // x and the weights go through registers, kDepth groups ahead (two for
+    // the 64-row tile, which then keeps three waves per SIMD; four for the
+    // others; a sweep of 2-8 put these first): step i writes group i's x (requested kDepth steps earlier) into
     // LDS buffer i & 1 (last read by step i - 2, which every wave finished
     // before the previous step's barrier), requests group i + kDepth's x
     // into the registers just written out, meets the others at an LDS-only
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(int M, int N, int K, int s
     // is an exact count that leaves the later groups' requests in flight.
     // The LDS slots and their swizzle are those of load_x. Past the last
     // group the requests repeat it (in bounds, unused).
-    constexpr int kDepth = 4;
+    constexpr int kDepth = MB == 4 ? 2 : 4;
     struct XR {
       u32x4 v[MB];
     };
@@ -473,18 +473,17 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
 
 namespace {
 
-template <int MB, bool REGX>
+template <int MB>
 int launch_gemm_mb(int M, int N, int K, int splits, const void* wq, const void* scales, const void* zeros,
                    const void* x, void* y, unsigned long long* ws, float* part, hipStream_t stream) {
   static std::atomic<uint64_t> raised{0};  // devices on which the kernel's LDS limit is raised
   const size_t lds = dev::gemm_lds_bytes(MB);
-  const hipError_t e =
-      dev::raise_lds_limit(reinterpret_cast<const void*>(&dev::gemm_kernel<MB, REGX>), lds, raised);
+  const hipError_t e = dev::raise_lds_limit(reinterpret_cast<const void*>(&dev::gemm_kernel<MB>), lds, raised);
   if (e != hipSuccess) return int(e);
   const int64_t NT = (int64_t(N) + kTileRows - 1) / kTileRows;
   const dim3 grid(unsigned((M + 16 * MB - 1) / (16 * MB)),
                   unsigned((NT + dev::kGemmBN / kTileRows - 1) / (dev::kGemmBN / kTileRows)), unsigned(splits));
-  return int(dev::launch_kernel(&dev::gemm_kernel<MB, REGX>, grid, dim3(256), lds, stream, M, N, K, splits,
+  return int(dev::launch_kernel(&dev::gemm_kernel<MB>, grid, dim3(256), lds, stream, M, N, K, splits,
                                 static_cast<const uint8_t*>(wq), static_cast<const uint16_t*>(scales),
                                 static_cast<const uint8_t*>(zeros), static_cast<const _Float16*>(x),
                                 static_cast<_Float16*>(y), splits > 1 && !part ? ws : nullptr,
@@ -497,19 +496,11 @@ int launch_gemm(int M, int N, int K, int splits, const void* wq, const void* sca
                 const void* x, void* y, unsigned long long* ws, void* stream, float* part) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc;
-  const int mb = splits > 1 ? gemm_m_blocks(M) : gemm_m_blocks_unsplit(M, N);
-  // The 64-row tile takes the register pipeline only on grids of fewer
-  // than 256 workgroups: on wider ones (37888 x 3584 at M = 48-64, 296
-  // workgroups) its extra registers cost a wave per SIMD and 3-4%.
-  const int64_t wgs = (int64_t(M) + 16 * mb - 1) / (16 * mb) * ((int64_t(N) + 127) / 128) * splits;
-  switch (mb) {
-    case 1: rc = launch_gemm_mb<1, true>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
-    case 2: rc = launch_gemm_mb<2, true>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
-    case 4:
-      rc = wgs < 256 ? launch_gemm_mb<4, true>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s)
-                     : launch_gemm_mb<4, false>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s);
-      break;
-    default: rc = launch_gemm_mb<8, false>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+  switch (splits > 1 ? gemm_m_blocks(M) : gemm_m_blocks_unsplit(M, N)) {
+    case 1: rc = launch_gemm_mb<1>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+    case 2: rc = launch_gemm_mb<2>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+    case 4: rc = launch_gemm_mb<4>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
+    default: rc = launch_gemm_mb<8>(M, N, K, splits, wq, scales, zeros, x, y, ws, part, s); break;
   }
   if (rc != 0 || !part || splits < 2) return rc;
   // The final stage, on the same stream: about four outputs per thread

@@ -4,8 +4,8 @@ ABI, against the fp64 oracle. The shapes cover each workgroup height (16,
 32, 64 and 128 rows: M <= 16, <= 32, <= 64 and above; unsplit launches above
 64 rows take 64-row tiles on narrow matrices and at 129-192 rows, so 100x20000,
 257x8300 and 450x4347 are there for the unsplit 128-row tile; tiles of 16-64
-rows take a register pipeline, except 64-row tiles on grids of 256 or more
-workgroups: 40x33000 and the 48-row full grid) with ragged M
+rows take a register pipeline, 40x33000 and the 48-row full grid on wide
+grids) with ragged M
 and N, and both tile orders (the XCD band order needs 4k m blocks and 8k tiles
 per split: 500x250, 1000x300 and 450x4347 here, split in 3 at 500x250, the
 chosen split at M = 512 on 3584x18944, and the prefill-sized calls).
@@ -133,8 +133,7 @@ def test_gemm_splitk_chosen_sampled(M, N, K):
 @pytest.mark.parametrize("M", [8, 16, 32, 48])
 def test_gemm_small_tiles_full_grid_repeatable(M):
     """16-, 32- and 48-row calls on a gate+up-sized grid (296 column tiles,
-    several workgroups per CU; the 48-row call takes the 64-row tile without
-    the register pipeline): sampled rows against the oracle, and five runs bit
+    several workgroups per CU): sampled rows against the oracle, and five runs bit
     for bit equal. (Staged-x requests counted as complete too early showed
     exactly here: run-to-run differences far outside the bound.)"""
     N, K = 37888, 3584
